@@ -1,0 +1,40 @@
+"""Load the hand-worked cases under tests/golden/ as workloads."""
+import json
+import os
+
+import numpy as np
+
+from adapter_lora_bgmv_amd.workloads import AdapterSpec, Workload, f32_to_bf16_bits
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _arr(v, dtype):
+    a = np.array(v, dtype=np.float32)
+    return f32_to_bf16_bits(a) if dtype == "bf16" else a
+
+
+def hand_workload(case, dtype="f32"):
+    ad = [AdapterSpec(rank=r, alpha=al, adapter_scale=s, rslora=rs)
+          for (s, al, r, rs) in case["adapters"]]
+    kw = dict(name=case["name"], dtype=dtype, k_in=case["k_in"], n_out=case["n_out"],
+              max_rank=case["max_rank"], W=_arr(case["W"], dtype), A=_arr(case["A"], dtype),
+              B=_arr(case["B"], dtype), x=_arr(case["x"], dtype), adapters=ad, kind=case["kind"])
+    if case["kind"] == "decode":
+        ss = np.array(case["seq_slot"], np.int32)
+        # the hand cases give the device-side seq_slot buffer itself (with -1 rows), so
+        # callers pass meta["seq_slot"] straight to the apply rather than building it
+        kw.update(adapter_slots=ss, padded_n=len(ss), active=0, meta={"seq_slot": ss})
+    elif case["kind"] == "segmented":
+        kw.update(seg_indptr=np.array(case["seg_indptr"], np.int32),
+                  seg_slot=np.array(case["seg_slot"], np.int32))
+    else:
+        kw.update(n_experts=case["n_experts"], top_k=case["top_k"],
+                  indices=np.array(case["indices"], np.int32),
+                  token_slot=np.array(case["token_slot"], np.int32))
+    return Workload(**kw)
