@@ -1,0 +1,119 @@
+// common.hpp -- types, bf16 helpers and MFMA wrappers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lora {
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Row keys of the plan: a row that takes no delta, and a row that is not
+// written at all (outside every segment / an expert id out of range).
+constexpr int kSkip = -1;
+constexpr int kDrop = -2;
+
+enum Mode : int { kModeDecode = 0, kModeSegmented = 1, kModeMoe = 2 };
+
+__device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float((uint32_t)b << 16); }
+
+// f32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ u16 f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u16)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (u16)(u >> 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D = A(16x32) * B(32x16) + C.  Lane l holds A row l%16, B column l%16, each
+// with k = 8*(l/16) .. +7; D column l%16, rows 4*(l/16) .. +3.
+__device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint4 z4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+__device__ __forceinline__ uint4 ldg16(const void *p) { return *(const uint4 *)p; }
+
+__device__ __forceinline__ uint32_t pack2(u16 lo, u16 hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
+
+// The route-resolve rule of every entry point: slot in range, both table
+// entries non-NULL, scale non-zero.  Returns the table index or kSkip.
+__device__ __forceinline__ int resolve_slot(int slot, int expert, int max_loras, int n_experts,
+                                            const void *const *a_table,
+                                            const void *const *b_table,
+                                            const float *scale_table) {
+  if (slot < 0 || slot >= max_loras) return kSkip;
+  int idx = slot * n_experts + expert;
+  if (a_table[idx] == nullptr || b_table[idx] == nullptr) return kSkip;
+  if (scale_table[slot] == 0.0f) return kSkip;
+  return idx;
+}
+
+// Routing inputs of one call, in the form the caller handed them over.
+struct Routing {
+  int mode;                 // Mode
+  const int32_t *seq_slot;  // decode: [n]
+  const int32_t *seg_indptr;  // segmented: [n_seg+1]
+  const int32_t *seg_slot;    // segmented: [n_seg]
+  int n_seg;
+  const int32_t *indices;     // moe: [n]
+  const int32_t *token_slot;  // moe: [n / top_k]
+  int top_k;
+  int n_experts;              // 1 unless moe
+};
+
+struct RouteDev {
+  const void *const *a_table;
+  const void *const *b_table;
+  const float *scale_table;
+  int max_loras;
+  int n_experts;
+  int R;  // max_rank
+};
+
+// Segment of row r (binary search over seg_indptr), or -1.
+__device__ __forceinline__ int segment_of(const int32_t *indptr, int n_seg, int r) {
+  if (n_seg <= 0 || r < indptr[0] || r >= indptr[n_seg]) return -1;
+  int lo = 0, hi = n_seg - 1;  // find last g with indptr[g] <= r
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (indptr[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  // empty segments share a start; the last one with indptr[g] <= r and r <
+  // indptr[g+1] is the owner
+  return lo;
+}
+
+// Per-row routing: the W group (expert) and the pair table index, or
+// kSkip (base only) / kDrop (row not written).  `scale_idx` gets the scale
+// table index (the adapter).
+__device__ __forceinline__ int row_route(const Routing &rt, const RouteDev &rd, bool has_lora,
+                                         int r, int *group, int *scale_idx) {
+  *group = 0;
+  *scale_idx = 0;
+  int slot = -1, expert = 0;
+  if (rt.mode == kModeDecode) {
+    slot = rt.seq_slot ? rt.seq_slot[r] : -1;
+  } else if (rt.mode == kModeSegmented) {
+    int g = segment_of(rt.seg_indptr, rt.n_seg, r);
+    if (g < 0) return kDrop;
+    slot = rt.seg_slot[g];
+  } else {
+    expert = rt.indices[r];
+    if (expert < 0 || expert >= rt.n_experts) return kDrop;
+    *group = expert;
+    if (!has_lora) return kSkip;  // token_slot may be NULL for a base-only call
+    slot = rt.token_slot[r / rt.top_k];
+  }
+  if (!has_lora) return kSkip;
+  *scale_idx = slot;
+  return resolve_slot(slot, expert, rd.max_loras, rd.n_experts, rd.a_table, rd.b_table,
+                      rd.scale_table);
+}
+
+}  // namespace lora

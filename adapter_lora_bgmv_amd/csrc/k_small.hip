@@ -1,0 +1,138 @@
+// k_small.hip -- the f32 path (all entry points) and the standalone expand-and-fold.
+//
+// The f32 path is the single-projection workload (a 256x256 f32 matrix, rank
+// 8): a handful of rows, launch-latency bound.  One workgroup handles one row
+// and a block of outputs; lanes stride along the contraction and a fixed
+// xor-butterfly reduces each dot, so every result is reproducible.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace lora {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+template <typename T> __device__ __forceinline__ float ld(const T *p, size_t i);
+template <> __device__ __forceinline__ float ld<float>(const float *p, size_t i) { return p[i]; }
+template <> __device__ __forceinline__ float ld<u16>(const u16 *p, size_t i) { return bf2f(p[i]); }
+
+template <typename T> __device__ __forceinline__ void st(T *p, size_t i, float v);
+template <> __device__ __forceinline__ void st<float>(float *p, size_t i, float v) { p[i] = v; }
+template <> __device__ __forceinline__ void st<u16>(u16 *p, size_t i, float v) { p[i] = f2bf(v); }
+
+// ---------------------------------------------------------------- f32 shrink
+// t[i, k] = A_s[k, :] . x_i  (ferrox LoraDelta::project), rows that skip untouched.
+__global__ __launch_bounds__(256) void shrink_f32_kernel(RouteDev rd, Routing rt, const float *x,
+                                                         int x_stride, int k_in, float *t) {
+  const int i = blockIdx.x;
+  int group, sidx;
+  const int q = row_route(rt, rd, true, i, &group, &sidx);
+  if (q < 0) return;
+  const float *A = (const float *)rd.a_table[q];
+  const float *xi = x + (size_t)i * x_stride;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int k = wave; k < rd.R; k += 4) {
+    float acc = 0.f;
+    for (int c = lane; c < k_in; c += 64) acc += A[(size_t)k * k_in + c] * xi[c];
+    acc = wave_sum(acc);
+    if (lane == 0) t[(size_t)i * rd.R + k] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- f32 apply
+// y_i = W x_i + s B_s (A_s x_i), one row per blockIdx.y, 64 outputs per block.
+__global__ __launch_bounds__(256) void apply_f32_kernel(RouteDev rd, Routing rt, bool has_lora,
+                                                        const float *W, long long w_group_stride,
+                                                        int w_stride, const float *x,
+                                                        int x_stride, int k_in, int n_out,
+                                                        float *y, int y_stride) {
+  __shared__ float tsh[256];
+  const int i = blockIdx.y;
+  int group, sidx;
+  const int q = row_route(rt, rd, has_lora, i, &group, &sidx);
+  if (q == kDrop) return;
+  const float *xi = x + (size_t)i * x_stride;
+  const float *Wg = W + (size_t)group * (size_t)w_group_stride;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (q >= 0) {
+    const float *A = (const float *)rd.a_table[q];
+    for (int k = wave; k < rd.R; k += 4) {
+      float acc = 0.f;
+      for (int c = lane; c < k_in; c += 64) acc += A[(size_t)k * k_in + c] * xi[c];
+      acc = wave_sum(acc);
+      if (lane == 0) tsh[k] = acc;
+    }
+  }
+  __syncthreads();
+  const int o_end = min(n_out, (int)(blockIdx.x + 1) * 64);
+  for (int o = blockIdx.x * 64 + wave; o < o_end; o += 4) {
+    float acc = 0.f;
+    for (int c = lane; c < k_in; c += 64) acc += Wg[(size_t)o * w_stride + c] * xi[c];
+    acc = wave_sum(acc);
+    if (q >= 0) {
+      const float *B = (const float *)rd.b_table[q];
+      float d = 0.f;
+      for (int k = lane; k < rd.R; k += 64) d += B[(size_t)o * rd.R + k] * tsh[k];
+      d = wave_sum(d);
+      acc = acc + rd.scale_table[sidx] * d;
+    }
+    if (lane == 0) y[(size_t)i * y_stride + o] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- expand + fold
+// y[i, o] = y[i, o] + s * (B_s t_i)[o] for rows that resolve; others untouched.
+// One thread per output; t_i staged in LDS; the rank sum runs k ascending.
+template <typename T>
+__global__ __launch_bounds__(256) void expand_fold_kernel(RouteDev rd, const int32_t *seq_slot,
+                                                          const float *t, T *y, int y_stride,
+                                                          int n_out) {
+  __shared__ float tsh[256];
+  const int i = blockIdx.y;
+  const int s = seq_slot[i];
+  const int q = resolve_slot(s, 0, rd.max_loras, 1, rd.a_table, rd.b_table, rd.scale_table);
+  if (q < 0) return;
+  for (int k = threadIdx.x; k < rd.R; k += 256) tsh[k] = t[(size_t)i * rd.R + k];
+  __syncthreads();
+  const int o = blockIdx.x * 256 + threadIdx.x;
+  if (o >= n_out) return;
+  const T *B = (const T *)rd.b_table[q];
+  float d = 0.f;
+  for (int k = 0; k < rd.R; ++k) d += ld(B, (size_t)o * rd.R + k) * tsh[k];
+  const size_t yi = (size_t)i * y_stride + o;
+  st(y, yi, ld((const T *)y, yi) + rd.scale_table[s] * d);
+}
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_shrink_f32(const RouteDev &rd, const Routing &rt, const float *x, int x_stride,
+                             int k_in, int n, float *t, hipStream_t st) {
+  hipLaunchKernelGGL(shrink_f32_kernel, dim3(n), dim3(256), 0, st, rd, rt, x, x_stride, k_in, t);
+  return hipGetLastError();
+}
+
+hipError_t launch_apply_f32(const RouteDev &rd, const Routing &rt, bool has_lora, const float *W,
+                            long long w_group_stride, int w_stride, const float *x, int x_stride,
+                            int k_in, int n_out, int n, float *y, int y_stride, hipStream_t st) {
+  dim3 grid((n_out + 63) / 64, n);
+  hipLaunchKernelGGL(apply_f32_kernel, grid, dim3(256), 0, st, rd, rt, has_lora, W,
+                     w_group_stride, w_stride, x, x_stride, k_in, n_out, y, y_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_expand_fold(const RouteDev &rd, int dtype, const int32_t *seq_slot,
+                              const float *t, void *y, int y_stride, int n_out, int n,
+                              hipStream_t st) {
+  dim3 grid((n_out + 255) / 256, n);
+  if (dtype == 0)
+    hipLaunchKernelGGL(expand_fold_kernel<float>, grid, dim3(256), 0, st, rd, seq_slot, t,
+                       (float *)y, y_stride, n_out);
+  else
+    hipLaunchKernelGGL(expand_fold_kernel<u16>, grid, dim3(256), 0, st, rd, seq_slot, t,
+                       (u16 *)y, y_stride, n_out);
+  return hipGetLastError();
+}
+
+}  // namespace lora

@@ -1,0 +1,79 @@
+// launch.hpp -- internal launchers the C ABI (lora_host.cpp) calls.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace lora {
+
+// Plan written by the prep kernel for the main kernel: row order grouped by
+// (W group, pair), and the main kernel's row tiles.
+struct PlanDev {
+  int *pos_row;   // [n] original row at sorted position
+  int *pos_pair;  // [n] table index, kSkip, at sorted position
+  int4 *tiles;    // [max_mtiles] {group, start, count, 0}
+  int *n_tiles;   // [1]
+};
+
+struct PrepArgs {
+  RouteDev rd;
+  Routing rt;
+  bool has_lora;
+  const u16 *x;
+  int x_stride;
+  int k_in;
+  int n;
+  float *t;       // [n][R] shrink output (may be null when !has_lora)
+  int n_pairs;    // table entries = max_loras * n_experts
+  int do_plan;    // block 0 writes the plan
+  PlanDev plan;
+  int tile_rows;  // main kernel rows per tile
+  int n_units;    // shrink units launched (grid = do_plan + n_units)
+};
+
+struct GemmArgs {
+  const u16 *W;
+  long long w_group_stride;
+  int w_row_stride;
+  const u16 *x;
+  int x_row_stride;
+  u16 *y;
+  int y_row_stride;
+  int n_out, k_in;
+  PlanDev plan;
+  int max_mtiles, n_ntiles;
+  int has_lora;
+  const void *const *b_table;
+  const float *scale_table;
+  int n_experts;
+  const float *t;
+  int R;
+  int splits, k_per_split;
+  float *partials;
+  unsigned *counters;
+};
+
+// Rows per shrink unit.
+constexpr int kShrinkRows = 16;
+// Largest key space the one-workgroup plan handles (LDS histogram).
+constexpr int kMaxKeys = 4096;
+// Largest batch the plan / shrink handle (row keys live in LDS).
+constexpr int kMaxPlanRows = 8192;
+
+size_t prep_lds_bytes(const PrepArgs &a);
+
+hipError_t launch_shrink_f32(const RouteDev &rd, const Routing &rt, const float *x, int x_stride,
+                             int k_in, int n, float *t, hipStream_t st);
+hipError_t launch_apply_f32(const RouteDev &rd, const Routing &rt, bool has_lora, const float *W,
+                            long long w_group_stride, int w_stride, const float *x, int x_stride,
+                            int k_in, int n_out, int n, float *y, int y_stride, hipStream_t st);
+hipError_t launch_expand_fold(const RouteDev &rd, int dtype, const int32_t *seq_slot,
+                              const float *t, void *y, int y_stride, int n_out, int n,
+                              hipStream_t st);
+hipError_t launch_prep(const PrepArgs &a, hipStream_t st);
+hipError_t launch_gemm(const GemmArgs &a, int to, int tr, hipStream_t st);
+
+}  // namespace lora

@@ -1,0 +1,503 @@
+// lora_host.cpp -- the C ABI declared in include/lora_mi355x.h.
+//
+// Host side only: argument validation (before any launch), the scale and
+// seq_slot helpers, the launch geometry and the workspace layout.  Nothing
+// here allocates, frees, synchronises or reads device memory.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/lora_mi355x.h"
+#include "launch.hpp"
+
+using namespace lora;
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_err() { g_err[0] = 0; }
+
+int launch_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(LORA_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return LORA_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ------------------------------------------------------------ device check
+int g_dev_ok[64];  // 0 unknown, 1 gfx950, -1 other
+
+int check_device(const char *what) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess)
+    return fail(LORA_ERR_LAUNCH, "%s: no HIP device is current", what);
+  if (dev < 0 || dev >= 64) return fail(LORA_ERR_LAUNCH, "%s: device index %d out of range", what, dev);
+  if (g_dev_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+      return fail(LORA_ERR_LAUNCH, "%s: cannot query device %d", what, dev);
+    g_dev_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    if (g_dev_ok[dev] < 0)
+      return fail(LORA_ERR_LAUNCH, "%s: device %d is %s, the kernels are built for gfx950 only",
+                  what, dev, prop.gcnArchName);
+  }
+  if (g_dev_ok[dev] < 0) return fail(LORA_ERR_LAUNCH, "%s: device %d is not a gfx950", what, dev);
+  return LORA_OK;
+}
+
+// ------------------------------------------------------------ tiling
+struct Cfg {
+  int to, tr, splits, k_per_split, max_mtiles, n_ntiles;
+};
+
+int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// Tile shape and split factor.  The split factor depends on (op, n, k_in)
+// only, never on n_out, so every output element's reduction order is the
+// same whether a fused projection is applied whole or part by part.
+Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups) {
+  Cfg c;
+  if (op == LORA_OP_MOE_GATHER) {
+    c.to = 128; c.tr = 64; c.splits = 1;
+  } else if (n <= 64) {
+    c.to = 64; c.tr = 64; c.splits = clampi(k_in / 512, 1, 8);
+  } else {
+    c.to = 128; c.tr = 128; c.splits = n <= 128 ? clampi(k_in / 1024, 1, 4) : 1;
+  }
+  const int kslabs = (k_in + 63) / 64;
+  c.k_per_split = ((kslabs + c.splits - 1) / c.splits) * 64;
+  c.max_mtiles = (n + c.tr - 1) / c.tr + (op == LORA_OP_MOE_GATHER ? groups : 0);
+  c.n_ntiles = (n_out + c.to - 1) / c.to;
+  return c;
+}
+
+struct WsLayout {
+  size_t counters, pos_row, pos_pair, tiles, n_tiles, t, partials, total;
+};
+
+size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const Cfg &c, int n, int R) {
+  WsLayout w;
+  size_t off = 0;
+  const size_t ntile = (size_t)c.max_mtiles * c.n_ntiles;
+  w.counters = off; off = up256(off + (c.splits > 1 ? ntile * 4 : 0));
+  w.pos_row = off; off = up256(off + (size_t)n * 4);
+  w.pos_pair = off; off = up256(off + (size_t)n * 4);
+  w.tiles = off; off = up256(off + (size_t)c.max_mtiles * 16);
+  w.n_tiles = off; off = up256(off + 16);
+  w.t = off; off = up256(off + (size_t)n * R * 4);
+  w.partials = off;
+  off = up256(off + (c.splits > 1 ? ntile * c.splits * c.to * c.tr * 4 : 0));
+  w.total = off;
+  return w;
+}
+
+constexpr uint32_t kMaxRows = 16384;
+constexpr uint32_t kMaxRank = 256;
+
+// ------------------------------------------------------------ validation
+int check_dtype(int32_t dtype, const char *what) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16)
+    return fail(LORA_ERR_DTYPE, "%s: dtype %d is neither LORA_F32 (0) nor LORA_BF16 (1)", what, dtype);
+  return LORA_OK;
+}
+
+// Checks shared by every call on a [n_out x k_in] projection.
+int check_proj(const char *what, int32_t dtype, uint32_t n_out, uint32_t k_in, uint32_t n,
+               uint32_t x_row_stride, uint32_t y_row_stride, uint32_t w_row_stride) {
+  if (int e = check_dtype(dtype, what)) return e;
+  if (n_out == 0 || k_in == 0)
+    return fail(LORA_ERR_SHAPE, "%s: [n_out %u x k_in %u]: both dimensions must be >= 1", what, n_out, k_in);
+  if (n > kMaxRows)
+    return fail(LORA_ERR_SHAPE, "%s: [n_out %u x k_in %u]: n %u rows exceeds the limit %u", what, n_out,
+                k_in, n, kMaxRows);
+  if (x_row_stride < k_in)
+    return fail(LORA_ERR_STRIDE, "%s: [n_out %u x k_in %u]: x_row_stride %u < k_in %u", what, n_out, k_in,
+                x_row_stride, k_in);
+  if (y_row_stride < n_out)
+    return fail(LORA_ERR_STRIDE, "%s: [n_out %u x k_in %u]: y_row_stride %u < n_out %u", what, n_out, k_in,
+                y_row_stride, n_out);
+  if (w_row_stride < k_in)
+    return fail(LORA_ERR_STRIDE, "%s: [n_out %u x k_in %u]: w_row_stride %u < k_in %u", what, n_out, k_in,
+                w_row_stride, k_in);
+  if (dtype == LORA_BF16) {
+    if (k_in % 8 || n_out % 8)
+      return fail(LORA_ERR_UNSUPPORTED,
+                  "%s: [n_out %u x k_in %u]: bf16 needs n_out and k_in to be multiples of 8", what, n_out,
+                  k_in);
+    if (x_row_stride % 8 || y_row_stride % 8 || w_row_stride % 8)
+      return fail(LORA_ERR_UNSUPPORTED,
+                  "%s: [n_out %u x k_in %u]: bf16 needs row strides that are multiples of 8 "
+                  "(x_row_stride %u, y_row_stride %u, w_row_stride %u)",
+                  what, n_out, k_in, x_row_stride, y_row_stride, w_row_stride);
+  }
+  return LORA_OK;
+}
+
+int check_rank(const char *what, int32_t dtype, uint32_t n_out, uint32_t k_in, uint32_t R) {
+  if (R == 0 || R > kMaxRank)
+    return fail(LORA_ERR_SHAPE, "%s: [n_out %u x k_in %u] at max_rank %u: max_rank must be in 1..%u", what,
+                n_out, k_in, R, kMaxRank);
+  if (dtype == LORA_BF16 && R % 16)
+    return fail(LORA_ERR_UNSUPPORTED,
+                "%s: [n_out %u x k_in %u] at max_rank %u: bf16 pools must pad max_rank to a multiple of 16",
+                what, n_out, k_in, R);
+  return LORA_OK;
+}
+
+int check_route(const char *what, const lora_route *r, int32_t dtype, uint32_t n_out, uint32_t k_in) {
+  if (!r->a_table || !r->b_table || !r->scale_table)
+    return fail(LORA_ERR_NULL_PTR, "%s: route tables must be non-NULL (a_table %p, b_table %p, scale_table %p)",
+                what, (const void *)r->a_table, (const void *)r->b_table, (const void *)r->scale_table);
+  if (r->dtype != dtype)
+    return fail(LORA_ERR_DTYPE, "%s: route dtype %d differs from the call's dtype %d", what, r->dtype, dtype);
+  if (r->k_in != k_in || r->n_out != n_out)
+    return fail(LORA_ERR_SHAPE, "%s: route is [n_out %u x k_in %u] but the projection is [n_out %u x k_in %u]",
+                what, r->n_out, r->k_in, n_out, k_in);
+  if (r->max_loras == 0 || r->max_loras + 1 > (uint32_t)kMaxKeys)
+    return fail(LORA_ERR_SHAPE, "%s: [n_out %u x k_in %u]: max_loras %u must be in 1..%d", what, n_out, k_in,
+                r->max_loras, kMaxKeys - 1);
+  return check_rank(what, dtype, n_out, k_in, r->max_rank);
+}
+
+RouteDev route_dev(const lora_route *r) {
+  RouteDev d{};
+  if (r) {
+    d.a_table = r->a_table;
+    d.b_table = r->b_table;
+    d.scale_table = r->scale_table;
+    d.max_loras = (int)r->max_loras;
+    d.n_experts = 1;
+    d.R = (int)r->max_rank;
+  }
+  return d;
+}
+
+Routing routing_decode(const int32_t *seq_slot) {
+  Routing rt{};
+  rt.mode = kModeDecode;
+  rt.seq_slot = seq_slot;
+  rt.n_experts = 1;
+  rt.top_k = 1;
+  return rt;
+}
+
+// The bf16 fused path shared by the three apply entry points.
+int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, bool has_lora,
+              uint32_t n_out, uint32_t k_in, const void *W, long long w_group_stride,
+              uint32_t w_row_stride, const void *x, uint32_t x_row_stride, uint32_t n, void *y,
+              uint32_t y_row_stride, void *workspace, size_t workspace_bytes, int groups,
+              hipStream_t st) {
+  const int R = has_lora ? rd.R : 0;
+  const Cfg c = choose_cfg(op, (int)n, (int)n_out, (int)k_in, groups);
+  const WsLayout L = ws_layout(c, (int)n, R);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(LORA_ERR_WORKSPACE,
+                "%s: [n_out %u x k_in %u] at max_rank %d, n %u: workspace %p of %zu bytes, %zu needed", what,
+                n_out, k_in, R, n, workspace, workspace_bytes, L.total);
+  if (!aligned16(workspace))
+    return fail(LORA_ERR_UNSUPPORTED, "%s: workspace %p is not 16-byte aligned", what, workspace);
+  char *ws = (char *)workspace;
+  PlanDev plan{(int *)(ws + L.pos_row), (int *)(ws + L.pos_pair), (int4 *)(ws + L.tiles),
+               (int *)(ws + L.n_tiles)};
+
+  PrepArgs pa{};
+  pa.rd = rd;
+  pa.rt = rt;
+  pa.has_lora = has_lora;
+  pa.x = (const u16 *)x;
+  pa.x_stride = (int)x_row_stride;
+  pa.k_in = (int)k_in;
+  pa.n = (int)n;
+  pa.t = (float *)(ws + L.t);
+  pa.n_pairs = has_lora ? rd.max_loras * rd.n_experts : 0;
+  pa.do_plan = 1;
+  pa.plan = plan;
+  pa.tile_rows = c.tr;
+  pa.n_units = has_lora ? (int)((n + kShrinkRows - 1) / kShrinkRows) + (int)std::min<uint32_t>(n, pa.n_pairs) : 0;
+  if (int e = launch_status(launch_prep(pa, st), what)) return e;
+
+  GemmArgs ga{};
+  ga.W = (const u16 *)W;
+  ga.w_group_stride = w_group_stride;
+  ga.w_row_stride = (int)w_row_stride;
+  ga.x = (const u16 *)x;
+  ga.x_row_stride = (int)x_row_stride;
+  ga.y = (u16 *)y;
+  ga.y_row_stride = (int)y_row_stride;
+  ga.n_out = (int)n_out;
+  ga.k_in = (int)k_in;
+  ga.plan = plan;
+  ga.max_mtiles = c.max_mtiles;
+  ga.n_ntiles = c.n_ntiles;
+  ga.has_lora = has_lora;
+  ga.b_table = rd.b_table;
+  ga.scale_table = rd.scale_table;
+  ga.n_experts = rd.n_experts > 0 ? rd.n_experts : 1;
+  ga.t = pa.t;
+  ga.R = R;
+  ga.splits = c.splits;
+  ga.k_per_split = c.k_per_split;
+  ga.partials = (float *)(ws + L.partials);
+  ga.counters = (unsigned *)(ws + L.counters);
+  return launch_status(launch_gemm(ga, c.to, c.tr, st), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *lora_last_error(void) { return g_err; }
+
+const char *lora_version(void) { return "lora_mi355x 0.1 (gfx950)"; }
+
+int lora_init(void) {
+  clear_err();
+  return check_device("lora_init");
+}
+
+double lora_scale(double adapter_scale, double alpha, uint32_t rank, int32_t rslora) {
+  if (alpha == 0.0) return adapter_scale;
+  if (rank == 0) return 0.0;
+  return rslora ? adapter_scale * alpha / std::sqrt((double)rank) : adapter_scale * alpha / (double)rank;
+}
+
+int lora_scale_table(uint32_t n_adapters, const double *adapter_scale, const double *alpha,
+                     const uint32_t *rank, const int32_t *rslora, uint32_t max_loras, float *out) {
+  clear_err();
+  if (!out || (n_adapters && (!adapter_scale || !alpha || !rank || !rslora)))
+    return fail(LORA_ERR_NULL_PTR, "lora_scale_table: NULL array for %u adapters", n_adapters);
+  for (uint32_t k = 0; k < n_adapters && k < max_loras; ++k)
+    if (rank[k] == 0) return fail(LORA_ERR_SHAPE, "lora_scale_table: adapter %u has rank 0", k);
+  for (uint32_t k = 0; k < max_loras; ++k)
+    out[k] = k < n_adapters ? (float)lora_scale(adapter_scale[k], alpha[k], rank[k], rslora[k]) : 0.0f;
+  return LORA_OK;
+}
+
+int lora_build_seq_slot(const int32_t *adapter_slots, uint32_t n, uint32_t padded_n, int32_t active,
+                        int32_t *out) {
+  clear_err();
+  if ((n && !adapter_slots) || (padded_n && !out))
+    return fail(LORA_ERR_NULL_PTR, "lora_build_seq_slot: NULL array (n %u, padded_n %u)", n, padded_n);
+  if (n > padded_n)
+    return fail(LORA_ERR_SHAPE, "lora_build_seq_slot: n %u real rows exceed padded_n %u", n, padded_n);
+  for (uint32_t i = 0; i < padded_n; ++i) out[i] = i < n ? (adapter_slots[i] >= 0 ? adapter_slots[i] : active) : -1;
+  return LORA_OK;
+}
+
+size_t lora_workspace_bytes(int32_t op, int32_t dtype, uint32_t n_rows, uint32_t n_out, uint32_t k_in,
+                            uint32_t max_rank, uint32_t n_groups) {
+  if (dtype != LORA_BF16 || n_rows == 0) return 0;
+  const Cfg c = choose_cfg(op, (int)n_rows, (int)n_out, (int)k_in, (int)(n_groups ? n_groups : 1));
+  return ws_layout(c, (int)n_rows, (int)max_rank).total;
+}
+
+int lora_shrink(const lora_route *route, const void *x, uint32_t x_row_stride, const int32_t *seq_slot,
+                uint32_t n, float *t, void *stream) {
+  clear_err();
+  const char *what = "lora_shrink";
+  if (!route) return fail(LORA_ERR_NULL_PTR, "%s: route is NULL", what);
+  if (int e = check_proj(what, route->dtype, route->n_out, route->k_in, n, x_row_stride, route->n_out,
+                         route->k_in))
+    return e;
+  if (int e = check_route(what, route, route->dtype, route->n_out, route->k_in)) return e;
+  if (n == 0) return LORA_OK;
+  if (!x || !seq_slot || !t)
+    return fail(LORA_ERR_NULL_PTR, "%s: [n_out %u x k_in %u]: x %p, seq_slot %p, t %p must be non-NULL", what,
+                route->n_out, route->k_in, x, (const void *)seq_slot, (void *)t);
+  if (route->dtype == LORA_BF16 && (!aligned16(x) || !aligned16(t)))
+    return fail(LORA_ERR_UNSUPPORTED, "%s: bf16 needs 16-byte aligned x %p and t %p", what, x, (void *)t);
+  if (int e = check_device(what)) return e;
+  const RouteDev rd = route_dev(route);
+  const Routing rt = routing_decode(seq_slot);
+  hipStream_t st = (hipStream_t)stream;
+  if (route->dtype == LORA_F32)
+    return launch_status(launch_shrink_f32(rd, rt, (const float *)x, (int)x_row_stride, (int)route->k_in, (int)n,
+                                           t, st),
+                         what);
+  PrepArgs pa{};
+  pa.rd = rd;
+  pa.rt = rt;
+  pa.has_lora = true;
+  pa.x = (const u16 *)x;
+  pa.x_stride = (int)x_row_stride;
+  pa.k_in = (int)route->k_in;
+  pa.n = (int)n;
+  pa.t = t;
+  pa.n_pairs = (int)route->max_loras;
+  pa.do_plan = 0;
+  pa.n_units = (int)((n + kShrinkRows - 1) / kShrinkRows) + (int)std::min<uint32_t>(n, route->max_loras);
+  return launch_status(launch_prep(pa, st), what);
+}
+
+int lora_expand_fold(const lora_route *route, const float *t, const int32_t *seq_slot, uint32_t n, void *y,
+                     uint32_t y_row_stride, void *stream) {
+  clear_err();
+  const char *what = "lora_expand_fold";
+  if (!route) return fail(LORA_ERR_NULL_PTR, "%s: route is NULL", what);
+  if (int e = check_proj(what, route->dtype, route->n_out, route->k_in, n, route->k_in, y_row_stride,
+                         route->k_in))
+    return e;
+  if (int e = check_route(what, route, route->dtype, route->n_out, route->k_in)) return e;
+  if (n == 0) return LORA_OK;
+  if (!t || !seq_slot || !y)
+    return fail(LORA_ERR_NULL_PTR, "%s: [n_out %u x k_in %u]: t %p, seq_slot %p, y %p must be non-NULL", what,
+                route->n_out, route->k_in, (const void *)t, (const void *)seq_slot, y);
+  if (int e = check_device(what)) return e;
+  return launch_status(launch_expand_fold(route_dev(route), route->dtype, seq_slot, t, y, (int)y_row_stride,
+                                          (int)route->n_out, (int)n, (hipStream_t)stream),
+                       what);
+}
+
+int lora_apply(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W, uint32_t w_row_stride,
+               const lora_route *route, const void *x, uint32_t x_row_stride, const int32_t *seq_slot,
+               uint32_t n, void *y, uint32_t y_row_stride, void *workspace, size_t workspace_bytes,
+               void *stream) {
+  clear_err();
+  const char *what = "lora_apply";
+  if (int e = check_proj(what, dtype, n_out, k_in, n, x_row_stride, y_row_stride, w_row_stride)) return e;
+  if (route) {
+    if (int e = check_route(what, route, dtype, n_out, k_in)) return e;
+  }
+  if (n == 0) return LORA_OK;
+  if (!W || !x || !y || (route && !seq_slot))
+    return fail(LORA_ERR_NULL_PTR, "%s: [n_out %u x k_in %u]: W %p, x %p, y %p%s must be non-NULL", what, n_out,
+                k_in, W, x, y, route ? " and seq_slot" : "");
+  if (dtype == LORA_BF16 && (!aligned16(W) || !aligned16(x) || !aligned16(y)))
+    return fail(LORA_ERR_UNSUPPORTED, "%s: bf16 needs 16-byte aligned W %p, x %p, y %p", what, W, x, y);
+  if (int e = check_device(what)) return e;
+  const RouteDev rd = route_dev(route);
+  const Routing rt = routing_decode(route ? seq_slot : nullptr);
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == LORA_F32)
+    return launch_status(launch_apply_f32(rd, rt, route != nullptr, (const float *)W, 0, (int)w_row_stride,
+                                          (const float *)x, (int)x_row_stride, (int)k_in, (int)n_out, (int)n,
+                                          (float *)y, (int)y_row_stride, st),
+                         what);
+  return run_fused(what, LORA_OP_APPLY, rt, rd, route != nullptr, n_out, k_in, W, 0, w_row_stride, x,
+                   x_row_stride, n, y, y_row_stride, workspace, workspace_bytes, 1, st);
+}
+
+int lora_apply_segmented(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W, uint32_t w_row_stride,
+                         const lora_route *route, const void *x, uint32_t x_row_stride,
+                         const int32_t *seg_indptr, const int32_t *seg_slot, uint32_t n_seg, uint32_t n, void *y,
+                         uint32_t y_row_stride, void *workspace, size_t workspace_bytes, void *stream) {
+  clear_err();
+  const char *what = "lora_apply_segmented";
+  if (int e = check_proj(what, dtype, n_out, k_in, n, x_row_stride, y_row_stride, w_row_stride)) return e;
+  if (route) {
+    if (int e = check_route(what, route, dtype, n_out, k_in)) return e;
+  }
+  if (n == 0) return LORA_OK;
+  if (!W || !x || !y || !seg_indptr || (n_seg && !seg_slot))
+    return fail(LORA_ERR_NULL_PTR,
+                "%s: [n_out %u x k_in %u]: W %p, x %p, y %p, seg_indptr %p, seg_slot %p must be non-NULL", what,
+                n_out, k_in, W, x, y, (const void *)seg_indptr, (const void *)seg_slot);
+  if (dtype == LORA_BF16 && (!aligned16(W) || !aligned16(x) || !aligned16(y)))
+    return fail(LORA_ERR_UNSUPPORTED, "%s: bf16 needs 16-byte aligned W %p, x %p, y %p", what, W, x, y);
+  if (int e = check_device(what)) return e;
+  const RouteDev rd = route_dev(route);
+  Routing rt{};
+  rt.mode = kModeSegmented;
+  rt.seg_indptr = seg_indptr;
+  rt.seg_slot = seg_slot;
+  rt.n_seg = (int)n_seg;
+  rt.n_experts = 1;
+  rt.top_k = 1;
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == LORA_F32)
+    return launch_status(launch_apply_f32(rd, rt, route != nullptr, (const float *)W, 0, (int)w_row_stride,
+                                          (const float *)x, (int)x_row_stride, (int)k_in, (int)n_out, (int)n,
+                                          (float *)y, (int)y_row_stride, st),
+                         what);
+  return run_fused(what, LORA_OP_SEGMENTED, rt, rd, route != nullptr, n_out, k_in, W, 0, w_row_stride, x,
+                   x_row_stride, n, y, y_row_stride, workspace, workspace_bytes, 1, st);
+}
+
+int lora_apply_moe_gather(int32_t dtype, uint32_t n_experts, uint32_t n_out, uint32_t k_in,
+                          const void *W_experts, uint64_t expert_stride, uint32_t w_row_stride,
+                          const lora_route_moe *route, const void *x, uint32_t x_row_stride,
+                          const int32_t *indices, uint32_t top_k, const int32_t *token_slot, uint32_t n_tokens,
+                          void *y, uint32_t y_row_stride, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  clear_err();
+  const char *what = "lora_apply_moe_gather";
+  if (top_k == 0 || n_experts == 0)
+    return fail(LORA_ERR_SHAPE, "%s: [n_out %u x k_in %u]: n_experts %u and top_k %u must be >= 1", what, n_out,
+                k_in, n_experts, top_k);
+  const uint64_t rows64 = (uint64_t)n_tokens * top_k;
+  if (rows64 > kMaxRows)
+    return fail(LORA_ERR_SHAPE, "%s: [n_out %u x k_in %u]: n_tokens %u x top_k %u rows exceed the limit %u", what,
+                n_out, k_in, n_tokens, top_k, kMaxRows);
+  const uint32_t n = (uint32_t)rows64;
+  if (int e = check_proj(what, dtype, n_out, k_in, n, x_row_stride, y_row_stride, w_row_stride)) return e;
+  if (expert_stride < (uint64_t)(n_out - 1) * w_row_stride + k_in && n_experts > 1)
+    return fail(LORA_ERR_STRIDE, "%s: [n_out %u x k_in %u]: expert_stride %llu is smaller than one expert", what,
+                n_out, k_in, (unsigned long long)expert_stride);
+  if (dtype == LORA_BF16 && expert_stride % 8)
+    return fail(LORA_ERR_UNSUPPORTED, "%s: bf16 needs expert_stride %llu to be a multiple of 8", what,
+                (unsigned long long)expert_stride);
+  if ((uint64_t)n_experts > (uint64_t)kMaxKeys)
+    return fail(LORA_ERR_SHAPE, "%s: n_experts %u exceeds %d", what, n_experts, kMaxKeys);
+  RouteDev rd{};
+  if (route) {
+    if (!route->a_table || !route->b_table || !route->scale_table)
+      return fail(LORA_ERR_NULL_PTR, "%s: route tables must be non-NULL", what);
+    if (route->dtype != dtype)
+      return fail(LORA_ERR_DTYPE, "%s: route dtype %d differs from the call's dtype %d", what, route->dtype, dtype);
+    if (route->k_in != k_in || route->n_out != n_out || route->n_experts != n_experts)
+      return fail(LORA_ERR_SHAPE,
+                  "%s: route is [n_out %u x k_in %u] over %u experts but the call is [n_out %u x k_in %u] over %u",
+                  what, route->n_out, route->k_in, route->n_experts, n_out, k_in, n_experts);
+    if (route->max_loras == 0 || (uint64_t)n_experts * (route->max_loras + 1) > (uint64_t)kMaxKeys)
+      return fail(LORA_ERR_SHAPE, "%s: n_experts %u x (max_loras %u + 1) must be at most %d", what, n_experts,
+                  route->max_loras, kMaxKeys);
+    if (int e = check_rank(what, dtype, n_out, k_in, route->max_rank)) return e;
+    rd.a_table = route->a_table;
+    rd.b_table = route->b_table;
+    rd.scale_table = route->scale_table;
+    rd.max_loras = (int)route->max_loras;
+    rd.n_experts = (int)n_experts;
+    rd.R = (int)route->max_rank;
+  }
+  if (n == 0) return LORA_OK;
+  if (!W_experts || !x || !y || !indices || (route && !token_slot))
+    return fail(LORA_ERR_NULL_PTR, "%s: [n_out %u x k_in %u]: W_experts, x, y, indices%s must be non-NULL", what,
+                n_out, k_in, route ? ", token_slot" : "");
+  if (dtype == LORA_BF16 && (!aligned16(W_experts) || !aligned16(x) || !aligned16(y)))
+    return fail(LORA_ERR_UNSUPPORTED, "%s: bf16 needs 16-byte aligned W_experts %p, x %p, y %p", what, W_experts,
+                x, y);
+  if (int e = check_device(what)) return e;
+  Routing rt{};
+  rt.mode = kModeMoe;
+  rt.indices = indices;
+  rt.token_slot = token_slot;
+  rt.top_k = (int)top_k;
+  rt.n_experts = (int)n_experts;
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == LORA_F32)
+    return launch_status(launch_apply_f32(rd, rt, route != nullptr, (const float *)W_experts,
+                                          (long long)expert_stride, (int)w_row_stride, (const float *)x,
+                                          (int)x_row_stride, (int)k_in, (int)n_out, (int)n, (float *)y,
+                                          (int)y_row_stride, st),
+                         what);
+  return run_fused(what, LORA_OP_MOE_GATHER, rt, rd, route != nullptr, n_out, k_in, W_experts,
+                   (long long)expert_stride, w_row_stride, x, x_row_stride, n, y, y_row_stride, workspace,
+                   workspace_bytes, (int)n_experts, st);
+}
+
+}  // extern "C"
