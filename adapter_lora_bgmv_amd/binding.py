@@ -25,7 +25,8 @@ STATUS = {0: "LORA_OK", -1: "LORA_ERR_SHAPE", -2: "LORA_ERR_NULL_PTR", -3: "LORA
 # every symbol include/lora_mi355x.h declares
 EXPORTS = ("lora_last_error", "lora_version", "lora_init", "lora_scale", "lora_scale_table",
            "lora_build_seq_slot", "lora_workspace_bytes", "lora_shrink", "lora_expand_fold",
-           "lora_apply", "lora_apply_segmented", "lora_apply_moe_gather")
+           "lora_apply", "lora_apply_segmented", "lora_apply_moe_gather",
+           "lora_set_profile_events")
 
 
 class LoraError(RuntimeError):
@@ -56,6 +57,9 @@ def lib() -> C.CDLL:
         return _lib
     if not LIB_PATH.exists():
         raise RuntimeError(f"HIP library missing: {LIB_PATH} (run __graft_entry__.build())")
+    # torch first: its HIP runtime (same soname) is then the one the library binds
+    # to, so torch's streams and device pointers are valid in the library's calls
+    import torch  # noqa: F401
     L = C.CDLL(str(LIB_PATH))
     u32, i32, vp, sz = C.c_uint32, C.c_int32, C.c_void_p, C.c_size_t
     L.lora_last_error.restype = C.c_char_p
@@ -64,6 +68,7 @@ def lib() -> C.CDLL:
     L.lora_scale.argtypes = [C.c_double, C.c_double, u32, i32]
     L.lora_scale_table.argtypes = [u32, vp, vp, vp, vp, u32, vp]
     L.lora_build_seq_slot.argtypes = [vp, u32, u32, i32, vp]
+    L.lora_set_profile_events.argtypes = [vp, u32]
     L.lora_workspace_bytes.restype = sz
     L.lora_workspace_bytes.argtypes = [i32, i32, u32, u32, u32, u32, u32]
     RP = C.POINTER(lora_route)
@@ -137,6 +142,15 @@ def lora_build_seq_slot(adapter_slots, padded_n: int, active: int) -> np.ndarray
     _check(lib().lora_build_seq_slot(a.ctypes.data if len(a) else None, len(a), int(padded_n),
                                      int(active), out.ctypes.data))
     return out[:padded_n]
+
+
+def lora_set_profile_events(events: Optional[Sequence[int]]):
+    """Raw hipEvent_t handles (ints) the fused calls record around their kernels, or None."""
+    if not events:
+        _check(lib().lora_set_profile_events(None, 0))
+        return
+    arr = (C.c_void_p * len(events))(*events)
+    _check(lib().lora_set_profile_events(arr, len(events)))
 
 
 def lora_workspace_bytes(op: int, dtype: int, n_rows: int, n_out: int, k_in: int, max_rank: int,

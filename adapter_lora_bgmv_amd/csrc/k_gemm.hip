@@ -1,10 +1,23 @@
 // k_gemm.hip -- the fused apply: y = W x + s B (A x), bf16 MFMA, f32 accumulate.
 //
-// A workgroup owns an output tile of TO output features x TR rows (rows in
+// A workgroup owns an output tile of BO output features x BR rows (rows in
 // the plan's grouped order, gathered from x and scattered to y).  The
 // contraction over k_in runs on v_mfma_f32_16x16x32_bf16 with W as the A
-// operand (output features) and the gathered x rows as the B operand; both
-// tiles are staged through LDS in double-buffered 64-wide k slabs.
+// operand and the gathered x rows as the B operand.
+//
+// Staging: a CU takes in far more bytes per second through the LDS-DMA path
+// (global_load_lds_dwordx4) than through loads into registers, so both
+// operands go to LDS that way.  Each DMA instruction moves exactly one MFMA
+// operand fragment -- 16 rows x 32 k, 1 KB, lane l holding row l%16, k
+// 8*(l/16)..+7 -- into a contiguous 1 KB LDS block, so the MFMA's operand read
+// is a linear, conflict-free ds_read_b128.  A stage is one 32-wide k step (one
+// fragment per 16-row block); NS stages form a ring with NS-1 stages in
+// flight.  The waits are explicit (s_waitcnt vmcnt + s_barrier): a stage is
+// consumed only after every wave's DMA for it has landed.
+//
+// Ragged tiles: rows past the tile's end (x) or past n_out (W) load a valid
+// row instead; they only feed output rows and columns that are never stored.
+// A k tail that does not fill a stage is zeroed in LDS once it has landed.
 //
 // The low-rank term rides the same accumulators as a k-extension that runs
 // FIRST, before the base contraction (ferrox lora.rs "expand + fold"; atlas
@@ -12,10 +25,10 @@
 // output the same way):
 //     acc[o, i] += sum_kappa B_q[o, kappa] * T[i, kappa]
 // where T holds s_q * t_i split into a bf16 high and low part (so the f32
-// intermediate t is carried at ~16 mantissa bits), and rows of another pair,
-// or skipped rows, contribute exact zeros.  Starting from +0, a skipped row's
-// accumulator is still +0 when the base contraction begins, so its output is
-// bit-identical to the base-only launch of the same shape.
+// intermediate t is carried at ~16 significant bits), and rows of another
+// pair, or skipped rows, contribute exact zeros.  Starting from +0, a skipped
+// row's accumulator is still +0 when the base contraction begins, so its
+// output is bit-identical to the base-only launch of the same shape.
 //
 // Split-K: `splits` workgroups share a tile, each over its own k range; the
 // last to arrive (a device-scope counter) sums the partial tiles in split
@@ -26,6 +39,8 @@
 
 namespace lora {
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 // The bf16 high part of v, or (part != 0) the bf16 rounding of what the
 // high part leaves over; hi + lo carries v to about 16 significant bits.
 __device__ __forceinline__ u16 hilo(float v, int part) {
@@ -33,20 +48,66 @@ __device__ __forceinline__ u16 hilo(float v, int part) {
   return part ? f2bf(v - bf2f(hi)) : hi;
 }
 
-template <int TO, int TR>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs p) {
-  constexpr int BK = 64, PITCH = BK + 8;  // u16 per LDS row; +16 B breaks bank aliasing
-  constexpr int WO = TO / 2, WR = TR / 2;
-  constexpr int NBO = WO / 16, NBR = WR / 16;
-  constexpr int NW = TO * 8 / 256, NX = TR * 8 / 256;  // 16-byte chunks per thread per slab
-  static_assert(NW >= 1 && NX >= 1, "tile too small for 256 threads");
-  __shared__ __attribute__((aligned(16))) u16 Ws[2][TO * PITCH];
-  __shared__ __attribute__((aligned(16))) u16 Xs[2][TR * PITCH];
-  __shared__ int s_row[TR], s_pair[TR];
+// s_waitcnt with only the vector-memory counter constrained (<= n).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Waits until at most `stages_younger` stages of `PER` DMA instructions each
+// are still in flight (0 <= stages_younger <= MAXS).
+template <int PER, int MAXS>
+__device__ __forceinline__ void wait_stages(int stages_younger) {
+  if constexpr (MAXS >= 6) { if (stages_younger >= 6) { wait_vmcnt<6 * PER>(); return; } }
+  if constexpr (MAXS >= 5) { if (stages_younger == 5) { wait_vmcnt<5 * PER>(); return; } }
+  if constexpr (MAXS >= 4) { if (stages_younger == 4) { wait_vmcnt<4 * PER>(); return; } }
+  if constexpr (MAXS >= 3) { if (stages_younger == 3) { wait_vmcnt<3 * PER>(); return; } }
+  if constexpr (MAXS >= 2) { if (stages_younger == 2) { wait_vmcnt<2 * PER>(); return; } }
+  if constexpr (MAXS >= 1) { if (stages_younger == 1) { wait_vmcnt<PER>(); return; } }
+  wait_vmcnt<0>();
+}
+
+// One LDS-DMA instruction: 16 bytes per lane from `g` into the wave's 1 KB
+// LDS block at byte address `lds` (lane l lands at lds + 16 l).  Issued as
+// assembly so that the compiler adds no waits of its own around the LDS
+// reads that follow; every wait on these transfers is explicit.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+// Workgroup barrier that the compiler may not move memory accesses across.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BO, int BR, int WGO, int WGR, int NS>
+__global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
+  constexpr int NW = WGO * WGR;
+  constexpr int WO = BO / WGO, WR = BR / WGR;  // wave tile
+  constexpr int NBO = WO / 16, NBR = WR / 16;  // fragment blocks per wave
+  constexpr int FO = BO / 16, FR = BR / 16;    // fragment blocks per tile
+  constexpr int SB = FO + FR;                  // fragments per stage (one 32-wide k step)
+  constexpr int LPW = SB / NW;                 // DMA instructions per wave per stage
+  static_assert(SB % NW == 0, "stage fragments must split evenly over the waves");
+  static_assert((NS - 2) * LPW < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint4 ring[NS][SB][64];
+  __shared__ int s_row[BR], s_pair[BR];
+  __shared__ const u16 *s_bq[BR];  // the row's B_pair, or null
+  __shared__ float s_sig[BR];      // the row's scale
   __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wo = wave & 1, wr = wave >> 1;
+  const int wo = wave % WGO, wr = wave / WGO;
   int bid = blockIdx.x;
   const int z = bid % p.splits;
   bid /= p.splits;
@@ -54,11 +115,14 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs p) {
   const int mt = bid / p.n_ntiles;
   if (mt >= *p.plan.n_tiles) return;
   const int4 tile = p.plan.tiles[mt];
-  const int o0 = nt * TO;
-  for (int i = tid; i < TR; i += 256) {
+  const int o0 = nt * BO;
+  for (int i = tid; i < BR; i += NW * 64) {
     const bool in = i < tile.z;
+    const int q = in ? p.plan.pos_pair[tile.y + i] : kSkip;
     s_row[i] = in ? p.plan.pos_row[tile.y + i] : -1;
-    s_pair[i] = in ? p.plan.pos_pair[tile.y + i] : kSkip;
+    s_pair[i] = q;
+    s_bq[i] = (p.has_lora && q >= 0) ? (const u16 *)p.b_table[q] : nullptr;
+    s_sig[i] = (p.has_lora && q >= 0) ? p.scale_table[q / p.n_experts] : 0.f;
   }
   __syncthreads();
 
@@ -68,46 +132,75 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs p) {
 #pragma unroll
     for (int b = 0; b < NBR; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-
   // ---------------------------------------------------------- k-extension
+  // Items are (run of equal pairs within a 16-row block, 32-wide kappa step);
+  // the loads of up to G items are issued together before their MFMAs, so
+  // the extension costs a few memory latencies, not one per item.
   if (p.has_lora && z == 0) {
     const int R = p.R, nks = 2 * R / 32;
+    constexpr int G = NBO <= 2 ? 8 : (NBO <= 4 ? 4 : 2);
+    const int myr = lane & 15;
+    int br = 0, i = 0, ks = 0;  // iterator: next item to load
+    auto run_end = [&](int b, int i0) {
+      const int l0 = wr * WR + b * 16, q = s_pair[l0 + i0];
+      int j = i0 + 1;
+      while (j < 16 && s_pair[l0 + j] == q) ++j;
+      return j;
+    };
+    // skip to the first run that has a pair
+    auto settle = [&]() {
+      while (br < NBR) {
+        if (i >= 16) { ++br; i = 0; continue; }
+        if (s_pair[wr * WR + br * 16 + i] >= 0) return;
+        i = run_end(br, i);
+      }
+    };
+    settle();
+    while (br < NBR) {
+      uint4 bv[G][NBO], tv[G];
+      int ibr[G], ns = 0;
 #pragma unroll
-    for (int br = 0; br < NBR; ++br) {
-      const int l0 = wr * WR + br * 16;
-      const int myr = lane & 15;
-      const int grow = s_row[l0 + myr];
-      int i = 0;
-      while (i < 16) {
-        const int q = s_pair[l0 + i];
-        int j = i + 1;
-        while (j < 16 && s_pair[l0 + j] == q) ++j;
-        if (q >= 0) {
-          const u16 *Bq = (const u16 *)p.b_table[q];
-          const float sig = p.scale_table[q / p.n_experts];
-          const bool mine = myr >= i && myr < j && grow >= 0;
-          for (int ks = 0; ks < nks; ++ks) {
-            const int kap = ks * 32 + (lane >> 4) * 8;
-            const int part = kap >= R;
-            const int r0 = kap - part * R;
-            uint4 tv = z4();
-            if (mine) {
-              const f32x4 t0 = *(const f32x4 *)(p.t + (size_t)grow * R + r0);
-              const f32x4 t1 = *(const f32x4 *)(p.t + (size_t)grow * R + r0 + 4);
-              tv = make_uint4(pack2(hilo(sig * t0[0], part), hilo(sig * t0[1], part)),
-                              pack2(hilo(sig * t0[2], part), hilo(sig * t0[3], part)),
-                              pack2(hilo(sig * t1[0], part), hilo(sig * t1[1], part)),
-                              pack2(hilo(sig * t1[2], part), hilo(sig * t1[3], part)));
-            }
+      for (int g = 0; g < G; ++g) {
+        ibr[g] = -1;
+        if (br >= NBR) continue;
+        const int l0 = wr * WR + br * 16;
+        const int j = run_end(br, i);
+        const u16 *Bq = s_bq[l0 + i];
+        const float sig = s_sig[l0 + i];
+        const int kap = ks * 32 + (lane >> 4) * 8;
+        const int part = kap >= R;
+        const int r0 = kap - part * R;
 #pragma unroll
-            for (int bo = 0; bo < NBO; ++bo) {
-              const int o = o0 + wo * WO + bo * 16 + (lane & 15);
-              const uint4 bv = o < p.n_out ? ldg16(Bq + (size_t)o * R + r0) : z4();
-              acc[bo][br] = mfma16(bv, tv, acc[bo][br]);
-            }
-          }
+        for (int bo = 0; bo < NBO; ++bo) {
+          const int o = min(o0 + wo * WO + bo * 16 + (lane & 15), p.n_out - 1);
+          bv[g][bo] = ldg16(Bq + (size_t)o * R + r0);
         }
-        i = j;
+        const int grow = s_row[l0 + myr];
+        tv[g] = z4();
+        if (myr >= i && myr < j && grow >= 0) {
+          const float *tp = p.t + (size_t)grow * R + r0;
+          const f32x4 t0 = *(const f32x4 *)tp, t1 = *(const f32x4 *)(tp + 4);
+          tv[g] = make_uint4(pack2(hilo(sig * t0[0], part), hilo(sig * t0[1], part)),
+                             pack2(hilo(sig * t0[2], part), hilo(sig * t0[3], part)),
+                             pack2(hilo(sig * t1[0], part), hilo(sig * t1[1], part)),
+                             pack2(hilo(sig * t1[2], part), hilo(sig * t1[3], part)));
+        }
+        ibr[g] = br;
+        ++ns;
+        if (++ks == nks) {  // next run
+          ks = 0;
+          i = j;
+          settle();
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if (g >= ns) break;
+#pragma unroll
+        for (int b = 0; b < NBR; ++b)
+          if (ibr[g] == b)
+#pragma unroll
+            for (int bo = 0; bo < NBO; ++bo) acc[bo][b] = mfma16(bv[g][bo], tv[g], acc[bo][b]);
       }
     }
   }
@@ -115,91 +208,104 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs p) {
   // ---------------------------------------------------------- base contraction
   const int kb = min(z * p.k_per_split, p.k_in);
   const int ke = min(kb + p.k_per_split, p.k_in);
+  const int nstage = (ke - kb + 31) / 32;
   const u16 *Wg = p.W + (size_t)tile.x * (size_t)p.w_group_stride;
-  if (kb < ke) {
-    uint4 wreg[NW], xreg[NX];
-    auto gload = [&](int k0) {
+  // this lane's source row for each DMA it issues (the same in every stage)
+  const u16 *src[LPW];
 #pragma unroll
-      for (int j = 0; j < NW; ++j) {
-        const int c = tid + 256 * j, r = c >> 3, kk = k0 + (c & 7) * 8;
-        const int o = o0 + r;
-        wreg[j] = (o < p.n_out && kk < ke) ? ldg16(Wg + (size_t)o * p.w_row_stride + kk) : z4();
+  for (int j = 0; j < LPW; ++j) {
+    const int b = wave + NW * j;  // fragment of the stage
+    const u16 *rowp;
+    if (b < FO) {
+      const int o = min(o0 + b * 16 + (lane & 15), p.n_out - 1);
+      rowp = Wg + (size_t)o * p.w_row_stride;
+    } else {
+      int r = s_row[(b - FO) * 16 + (lane & 15)];
+      if (r < 0) r = s_row[0];
+      rowp = p.x + (size_t)r * p.x_row_stride;
+    }
+    src[j] = rowp + (lane >> 4) * 8;
+  }
+  // Every wave issues exactly LPW DMA instructions per stage, so the vmcnt
+  // waits count stages exactly.  Lanes whose k chunk lies past the range read
+  // a valid piece of their row instead; the tail stage zeroes those LDS
+  // entries after it lands.
+  auto issue = [&](int st) {
+    const int k0 = kb + st * 32;
+    const int kk = k0 + (lane >> 4) * 8 < ke ? k0 : 0;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) dma16(src[j] + kk, lds_addr(&ring[st % NS][wave + NW * j][0]));
+  };
+  if (nstage > 0) {
+    for (int st = 0; st < NS - 1 && st < nstage; ++st) issue(st);
+    for (int st = 0; st < nstage; ++st) {
+      // stage st has landed for this wave once at most min(NS-2, nstage-1-st)
+      // younger stages remain in flight
+      wait_stages<LPW, NS - 2>(min(NS - 2, nstage - 1 - st));
+      block_barrier();  // ... and for every wave
+      uint4(*slot)[64] = ring[st % NS];
+      const int k0 = kb + st * 32;
+      if (k0 + 32 > ke) {  // tail stage: zero what lies past the k range
+        if (k0 + (lane >> 4) * 8 >= ke)
+          for (int f = wave; f < SB; f += NW) slot[f][lane] = z4();
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        block_barrier();
       }
+      if (st + NS - 1 < nstage) issue(st + NS - 1);
+      uint4 af[NBO], bf[NBR];
 #pragma unroll
-      for (int j = 0; j < NX; ++j) {
-        const int c = tid + 256 * j, r = c >> 3, kk = k0 + (c & 7) * 8;
-        const int row = s_row[r];
-        xreg[j] = (row >= 0 && kk < ke) ? ldg16(p.x + (size_t)row * p.x_row_stride + kk) : z4();
-      }
-    };
-    auto swrite = [&](int buf) {
+      for (int bo = 0; bo < NBO; ++bo) af[bo] = slot[wo * NBO + bo][lane];
 #pragma unroll
-      for (int j = 0; j < NW; ++j) {
-        const int c = tid + 256 * j;
-        *(uint4 *)&Ws[buf][(c >> 3) * PITCH + (c & 7) * 8] = wreg[j];
-      }
+      for (int b = 0; b < NBR; ++b) bf[b] = slot[FO + wr * NBR + b][lane];
 #pragma unroll
-      for (int j = 0; j < NX; ++j) {
-        const int c = tid + 256 * j;
-        *(uint4 *)&Xs[buf][(c >> 3) * PITCH + (c & 7) * 8] = xreg[j];
-      }
-    };
-    gload(kb);
-    swrite(0);
-    __syncthreads();
-    int cur = 0;
-    for (int k0 = kb; k0 < ke; k0 += BK) {
-      const bool more = k0 + BK < ke;
-      if (more) gload(k0 + BK);
+      for (int bo = 0; bo < NBO; ++bo)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int col = ks * 32 + (lane >> 4) * 8;
-        uint4 af[NBO], bf[NBR];
-#pragma unroll
-        for (int bo = 0; bo < NBO; ++bo)
-          af[bo] = *(const uint4 *)&Ws[cur][(wo * WO + bo * 16 + (lane & 15)) * PITCH + col];
-#pragma unroll
-        for (int br = 0; br < NBR; ++br)
-          bf[br] = *(const uint4 *)&Xs[cur][(wr * WR + br * 16 + (lane & 15)) * PITCH + col];
-#pragma unroll
-        for (int bo = 0; bo < NBO; ++bo)
-#pragma unroll
-          for (int br = 0; br < NBR; ++br) acc[bo][br] = mfma16(af[bo], bf[br], acc[bo][br]);
-      }
-      if (more) swrite(cur ^ 1);
-      __syncthreads();
-      cur ^= 1;
+        for (int b = 0; b < NBR; ++b) acc[bo][b] = mfma16(af[bo], bf[b], acc[bo][b]);
     }
   }
 
   // ---------------------------------------------------------- split-K fixup
   if (p.splits > 1) {
-    constexpr int TT = TO * TR;
+    constexpr int TT = BO * BR;
     const int tl = mt * p.n_ntiles + nt;
     float *part = p.partials + (size_t)tl * p.splits * TT;
+    // Partials travel through device-coherent (sc1) stores and loads, so no
+    // L2-wide writeback or invalidate is needed: the stores are complete
+    // (s_waitcnt) before the arrival counter moves, and the last arrival
+    // reads them coherently.
 #pragma unroll
     for (int bo = 0; bo < NBO; ++bo)
 #pragma unroll
       for (int br = 0; br < NBR; ++br) {
         const int idx = ((wave * NBO + bo) * NBR + br) * 64 + lane;
-        *(f32x4 *)(part + (size_t)z * TT + idx * 4) = acc[bo][br];
+        float *dst = part + (size_t)z * TT + idx * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __hip_atomic_store(dst + e, acc[bo][br][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&p.counters[tl], 1u) == (unsigned)(p.splits - 1);
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(&p.counters[tl], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (unsigned)(p.splits - 1);
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
 #pragma unroll
     for (int bo = 0; bo < NBO; ++bo)
 #pragma unroll
       for (int br = 0; br < NBR; ++br) {
         const int idx = ((wave * NBO + bo) * NBR + br) * 64 + lane;
-        f32x4 s = *(const f32x4 *)(part + idx * 4);
-        for (int zz = 1; zz < p.splits; ++zz) s += *(const f32x4 *)(part + (size_t)zz * TT + idx * 4);
+        f32x4 s;
+        for (int zz = 0; zz < p.splits; ++zz) {
+          const float *srcp = part + (size_t)zz * TT + idx * 4;
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = __hip_atomic_load(srcp + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          s = zz == 0 ? v : s + v;
+        }
         acc[bo][br] = s;
       }
-    if (tid == 0) p.counters[tl] = 0u;
+    if (tid == 0) __hip_atomic_store(&p.counters[tl], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---------------------------------------------------------- epilogue
@@ -222,11 +328,15 @@ hipError_t launch_gemm(const GemmArgs &a, int to, int tr, hipStream_t st) {
   const int grid = a.max_mtiles * a.n_ntiles * a.splits;
   if (grid == 0) return hipSuccess;
   if (to == 64 && tr == 64)
-    hipLaunchKernelGGL((gemm_bf16_kernel<64, 64>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<64, 64, 2, 2, 8>), dim3(grid), dim3(256), 0, st, a);
   else if (to == 128 && tr == 64)
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 64>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 64, 4, 1, 8>), dim3(grid), dim3(256), 0, st, a);
   else if (to == 128 && tr == 128)
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, 6>), dim3(grid), dim3(256), 0, st, a);
+  else if (to == 256 && tr == 64)
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 64, 4, 1, 5>), dim3(grid), dim3(256), 0, st, a);
+  else if (to == 256 && tr == 256)
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 4>), dim3(grid), dim3(512), 0, st, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

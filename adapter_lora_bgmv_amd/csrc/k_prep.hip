@@ -120,20 +120,35 @@ __device__ void plan_block(const PrepArgs &a, int *lds) {
   if (tid == 0) *a.plan.n_tiles = ntiles;
 }
 
+// Pair of row r (or kSkip / kDrop), from the LDS cache when the batch fits it.
+__device__ __forceinline__ int cached_route(const PrepArgs &a, const int *qv, int r) {
+  if (qv) return qv[r];
+  int g, ad;
+  return row_route(a.rt, a.rd, true, r, &g, &ad);
+}
+
+// One shrink unit: up to 16 rows sharing one pair, over one k chunk.
+// t_part[kz][row][0:R] = x[row, chunk] . A_pair[:, chunk]^T; the consumer sums
+// the k_splits partials in kz order.
 __device__ void shrink_unit(const PrepArgs &a, int u, int *lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = a.n_pairs;
+  const int KS = a.k_splits;
+  const int kz = u % KS;
+  u /= KS;
   int *cnt = lds;             // [P]
   int *wsum = cnt + P;        // [4]
   int *info = wsum + 4;       // [4]
   int *rows = info + 4;       // [16]
   f32x4 *red = (f32x4 *)(lds + ((P + 24 + 3) & ~3));  // [3][4][64]
+  int *qv = a.n <= kRowCache ? (int *)(red + 3 * 4 * 64) : nullptr;  // [n]
 
   for (int p = tid; p < P; p += 256) cnt[p] = 0;
   __syncthreads();
   for (int r = tid; r < a.n; r += 256) {
     int g, ad;
     const int q = row_route(a.rt, a.rd, true, r, &g, &ad);
+    if (qv) qv[r] = q;
     if (q >= 0) atomicAdd(&cnt[q], 1);
   }
   __syncthreads();
@@ -158,15 +173,11 @@ __device__ void shrink_unit(const PrepArgs &a, int u, int *lds) {
   const int m = (a.n + 255) / 256;
   const int rb = min(tid * m, a.n), re = min(rb + m, a.n);
   int c = 0;
-  for (int r = rb; r < re; ++r) {
-    int g, ad;
-    c += row_route(a.rt, a.rd, true, r, &g, &ad) == pstar;
-  }
+  for (int r = rb; r < re; ++r) c += cached_route(a, qv, r) == pstar;
   int total_rows;
   int k = block_exclusive(c, wsum, &total_rows);
   for (int r = rb; r < re && k < first + kShrinkRows; ++r) {
-    int g, ad;
-    if (row_route(a.rt, a.rd, true, r, &g, &ad) != pstar) continue;
+    if (cached_route(a, qv, r) != pstar) continue;
     if (k >= first) rows[k - first] = r;
     ++k;
   }
@@ -177,10 +188,15 @@ __device__ void shrink_unit(const PrepArgs &a, int u, int *lds) {
   const int R = a.rd.R, nrb = R / 16, K = a.k_in;
   const int myrow = (lane & 15) < nrows ? rows[lane & 15] : -1;
   const u16 *xr = myrow >= 0 ? a.x + (size_t)myrow * a.x_stride : nullptr;
-  const int ksteps = (K + 31) / 32, kq = (ksteps + 3) / 4;
-  const int kb = min(wave * kq * 32, K), ke = min(kb + kq * 32, K);
+  // this unit's k chunk, cut in 32-wide steps; wave w takes steps w, w+4, ...
+  const int chunk = ((K + KS - 1) / KS + 127) / 128 * 128;
+  const int kc0 = min(kz * chunk, K), kc1 = min(kc0 + chunk, K);
+  const int nsteps = (kc1 - kc0 + 31) / 32;
   const int koff = (lane >> 4) * 8;
-  const uint4 zero = make_uint4(0, 0, 0, 0);
+  // k_splits == 1: this unit writes the final t.  Otherwise it writes its
+  // partial through device-coherent (sc1) stores and the last of the unit's
+  // k_splits workgroups to arrive sums them in chunk order.
+  float *tout = KS == 1 ? a.t_final : a.t + (size_t)kz * a.n * R;
 
   for (int rb0 = 0; rb0 < nrb; rb0 += 4) {
     const int nb = min(4, nrb - rb0);
@@ -188,19 +204,19 @@ __device__ void shrink_unit(const PrepArgs &a, int u, int *lds) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const u16 *Ab = A + (size_t)(rb0 * 16 + (lane & 15)) * K;
-    for (int k0 = kb; k0 < ke; k0 += 128) {
-      uint4 xv[4], av[4][4];
+    for (int s0 = wave; s0 < nsteps; s0 += 4 * 8) {
+      uint4 xv[8], av[8][4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int kk = k0 + s * 32 + koff;
-        const bool in = kk < ke;
-        xv[s] = (xr && in) ? ldg16(xr + kk) : zero;
+      for (int s = 0; s < 8; ++s) {
+        const int kk = kc0 + (s0 + 4 * s) * 32 + koff;
+        const bool in = kk < kc1;
+        xv[s] = (xr && in) ? ldg16(xr + kk) : z4();
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          av[s][j] = (in && j < nb) ? ldg16(Ab + (size_t)j * 16 * K + kk) : zero;
+          av[s][j] = (in && j < nb) ? ldg16(Ab + (size_t)j * 16 * K + kk) : z4();
       }
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int s = 0; s < 8; ++s)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           if (j < nb) acc[j] = mfma16(av[s][j], xv[s], acc[j]);
@@ -214,16 +230,40 @@ __device__ void shrink_unit(const PrepArgs &a, int u, int *lds) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (j >= nb) continue;
-        f32x4 s = acc[j];
-        s += red[(0 * 4 + j) * 64 + lane];
-        s += red[(1 * 4 + j) * 64 + lane];
-        s += red[(2 * 4 + j) * 64 + lane];
+        f32x4 v = acc[j];
+        v += red[(0 * 4 + j) * 64 + lane];
+        v += red[(1 * 4 + j) * 64 + lane];
+        v += red[(2 * 4 + j) * 64 + lane];
         // D column = lane%16 (the row), D rows = ranks 4*(lane/16) .. +3 of block rb0+j
-        *(f32x4 *)(a.t + (size_t)myrow * R + (rb0 + j) * 16 + (lane >> 4) * 4) = s;
+        float *dst = tout + (size_t)myrow * R + (rb0 + j) * 16 + (lane >> 4) * 4;
+        if (KS == 1) {
+          *(f32x4 *)dst = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            __hip_atomic_store(dst + e, v[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
     __syncthreads();
   }
+  if (KS == 1) return;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    info[2] = __hip_atomic_fetch_add(&a.counters[u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (unsigned)(KS - 1);
+  __syncthreads();
+  if (!info[2]) return;
+  for (int e = tid; e < nrows * R; e += 256) {
+    const int i = e / R, r = e - i * R;
+    const size_t off = (size_t)rows[i] * R + r;
+    float v = 0.f;
+    for (int z = 0; z < KS; ++z)
+      v += __hip_atomic_load(a.t + (size_t)z * a.n * R + off, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a.t_final[off] = v;
+  }
+  if (tid == 0) __hip_atomic_store(&a.counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
@@ -240,12 +280,14 @@ size_t prep_lds_bytes(const PrepArgs &a) {
   const int NG = a.rt.n_experts;
   const int NK = NG * (ml + 1);
   size_t plan = a.do_plan ? (size_t)(2 * NK + NG + 8) * 4 : 0;
-  size_t shr = a.n_units ? (size_t)((a.n_pairs + 24 + 3) & ~3) * 4 + 3 * 4 * 64 * 16 : 0;
+  size_t shr = a.n_units ? (size_t)((a.n_pairs + 24 + 3) & ~3) * 4 + 3 * 4 * 64 * 16 +
+                               (a.n <= kRowCache ? (size_t)a.n * 4 : 0)
+                         : 0;
   return plan > shr ? plan : shr;
 }
 
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st) {
-  const int grid = a.do_plan + a.n_units;
+  const int grid = a.do_plan + a.n_units * a.k_splits;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(prep_kernel, dim3(grid), dim3(256), prep_lds_bytes(a), st, a);
   return hipGetLastError();

@@ -26,12 +26,15 @@ struct PrepArgs {
   int x_stride;
   int k_in;
   int n;
-  float *t;       // [n][R] shrink output (may be null when !has_lora)
+  float *t;        // [k_splits][n][R] partial shrink sums (k_splits > 1)
+  float *t_final;  // [n][R] the shrink's output
+  unsigned *counters;  // [n_units] arrival counters (k_splits > 1), zero between calls
+  int k_splits;    // k chunks per shrink unit
   int n_pairs;    // table entries = max_loras * n_experts
   int do_plan;    // block 0 writes the plan
   PlanDev plan;
   int tile_rows;  // main kernel rows per tile
-  int n_units;    // shrink units launched (grid = do_plan + n_units)
+  int n_units;    // shrink units (grid = do_plan + n_units * k_splits)
 };
 
 struct GemmArgs {
@@ -49,19 +52,38 @@ struct GemmArgs {
   const void *const *b_table;
   const float *scale_table;
   int n_experts;
-  const float *t;
+  const float *t;  // [n][R] the shrink's output
   int R;
   int splits, k_per_split;
   float *partials;
   unsigned *counters;
 };
 
+struct SkinnyArgs {
+  const u16 *W;
+  int w_row_stride;
+  const u16 *x;
+  int x_row_stride;
+  u16 *y;
+  int y_row_stride;
+  int n_out, k_in, n;
+  RouteDev rd;
+  Routing rt;
+  int has_lora;
+  const float *t;  // [n][R] the shrink's output
+  int R;
+};
+
+// Largest batch and rank the decode-shaped kernel takes.
+constexpr int kSkinnyMaxRows = 64;
+constexpr int kSkinnyMaxRank = 64;
+
 // Rows per shrink unit.
 constexpr int kShrinkRows = 16;
 // Largest key space the one-workgroup plan handles (LDS histogram).
 constexpr int kMaxKeys = 4096;
-// Largest batch the plan / shrink handle (row keys live in LDS).
-constexpr int kMaxPlanRows = 8192;
+// Batches up to this many rows keep their resolved routes in LDS during the shrink.
+constexpr int kRowCache = 8192;
 
 size_t prep_lds_bytes(const PrepArgs &a);
 
@@ -75,5 +97,6 @@ hipError_t launch_expand_fold(const RouteDev &rd, int dtype, const int32_t *seq_
                               hipStream_t st);
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &a, int to, int tr, hipStream_t st);
+hipError_t launch_skinny(const SkinnyArgs &a, hipStream_t st);
 
 }  // namespace lora

@@ -19,6 +19,12 @@ using namespace lora;
 namespace {
 
 thread_local char g_err[512];
+thread_local hipEvent_t g_prof[3];
+thread_local bool g_prof_on = false;
+
+void prof_record(int i, hipStream_t st) {
+  if (g_prof_on) (void)hipEventRecord(g_prof[i], st);
+}
 
 int fail(int code, const char *fmt, ...) {
   va_list ap;
@@ -61,21 +67,35 @@ int check_device(const char *what) {
 // ------------------------------------------------------------ tiling
 struct Cfg {
   int to, tr, splits, k_per_split, max_mtiles, n_ntiles;
+  bool skinny;   // decode-shaped kernel (no plan, no split-K)
+  int units;     // upper bound of shrink units
+  int t_splits;  // k chunks of the shrink; the consumer sums the partials
 };
 
 int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-// Tile shape and split factor.  The split factor depends on (op, n, k_in)
-// only, never on n_out, so every output element's reduction order is the
-// same whether a fused projection is applied whole or part by part.
-Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups) {
+// Tile shape and split factor.  Up to 128 rows the split factor depends on
+// (op, n, k_in) only, never on n_out, so every output element's reduction
+// order is the same whether a fused projection is applied whole or part by
+// part; larger batches pick it from the tile count to fill the chip.
+Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pairs) {
   Cfg c;
+  c.skinny = op == LORA_OP_APPLY && n <= kSkinnyMaxRows && R <= kSkinnyMaxRank;
+  c.units = R > 0 ? (n + kShrinkRows - 1) / kShrinkRows + std::min(n, n_pairs) : 0;
+  // Shrink k chunks: enough workgroups to cover the chip for small batches,
+  // chunks of at least 128 columns.  A function of (n, k_in) only, so the
+  // workspace size does not depend on the routing.
+  c.t_splits = R > 0 ? clampi(512 / ((n + kShrinkRows - 1) / kShrinkRows), 1, std::min(8, std::max(1, k_in / 128))) : 1;
   if (op == LORA_OP_MOE_GATHER) {
-    c.to = 128; c.tr = 64; c.splits = 1;
+    c.to = 256; c.tr = 64; c.splits = 1;
   } else if (n <= 64) {
-    c.to = 64; c.tr = 64; c.splits = clampi(k_in / 512, 1, 8);
+    c.to = 64; c.tr = 64; c.splits = clampi(k_in / 1024, 1, 8);
+  } else if (n <= 128) {
+    c.to = 128; c.tr = 128; c.splits = clampi(k_in / 1024, 1, 4);
   } else {
-    c.to = 128; c.tr = 128; c.splits = n <= 128 ? clampi(k_in / 1024, 1, 4) : 1;
+    c.to = 256; c.tr = 256;
+    const int tiles = ((n + 255) / 256) * ((n_out + 255) / 256);
+    c.splits = clampi(307 / tiles, 1, std::min(8, std::max(1, k_in / 1024)));
   }
   const int kslabs = (k_in + 63) / 64;
   c.k_per_split = ((kslabs + c.splits - 1) / c.splits) * 64;
@@ -85,7 +105,7 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups) {
 }
 
 struct WsLayout {
-  size_t counters, pos_row, pos_pair, tiles, n_tiles, t, partials, total;
+  size_t counters, shrink_counters, pos_row, pos_pair, tiles, n_tiles, t, t_final, partials, total;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -93,15 +113,17 @@ size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 WsLayout ws_layout(const Cfg &c, int n, int R) {
   WsLayout w;
   size_t off = 0;
-  const size_t ntile = (size_t)c.max_mtiles * c.n_ntiles;
+  const size_t ntile = c.skinny ? 0 : (size_t)c.max_mtiles * c.n_ntiles;
   w.counters = off; off = up256(off + (c.splits > 1 ? ntile * 4 : 0));
+  w.shrink_counters = off; off = up256(off + (c.t_splits > 1 ? (size_t)c.units * 4 : 0));
   w.pos_row = off; off = up256(off + (size_t)n * 4);
   w.pos_pair = off; off = up256(off + (size_t)n * 4);
   w.tiles = off; off = up256(off + (size_t)c.max_mtiles * 16);
   w.n_tiles = off; off = up256(off + 16);
-  w.t = off; off = up256(off + (size_t)n * R * 4);
+  w.t = off; off = up256(off + (c.t_splits > 1 ? (size_t)c.t_splits * n * R * 4 : 0));
+  w.t_final = off; off = up256(off + (size_t)n * R * 4);
   w.partials = off;
-  off = up256(off + (c.splits > 1 ? ntile * c.splits * c.to * c.tr * 4 : 0));
+  off = up256(off + (c.splits > 1 && !c.skinny ? ntile * c.splits * c.to * c.tr * 4 : 0));
   w.total = off;
   return w;
 }
@@ -196,6 +218,17 @@ Routing routing_decode(const int32_t *seq_slot) {
   return rt;
 }
 
+// The f32 path is one kernel; it records the profile events as an empty prep
+// followed by the kernel, like the fused path.
+template <typename F>
+int run_f32_timed(const char *what, F launch, hipStream_t st) {
+  prof_record(0, st);
+  prof_record(1, st);
+  const int e = launch_status(launch(), what);
+  prof_record(2, st);
+  return e;
+}
+
 // The bf16 fused path shared by the three apply entry points.
 int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, bool has_lora,
               uint32_t n_out, uint32_t k_in, const void *W, long long w_group_stride,
@@ -203,7 +236,8 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
               uint32_t y_row_stride, void *workspace, size_t workspace_bytes, int groups,
               hipStream_t st) {
   const int R = has_lora ? rd.R : 0;
-  const Cfg c = choose_cfg(op, (int)n, (int)n_out, (int)k_in, groups);
+  const int n_pairs = has_lora ? rd.max_loras * rd.n_experts : 0;
+  const Cfg c = choose_cfg(op, (int)n, (int)n_out, (int)k_in, groups, R, n_pairs);
   const WsLayout L = ws_layout(c, (int)n, R);
   if (!workspace || workspace_bytes < L.total)
     return fail(LORA_ERR_WORKSPACE,
@@ -224,12 +258,37 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
   pa.k_in = (int)k_in;
   pa.n = (int)n;
   pa.t = (float *)(ws + L.t);
-  pa.n_pairs = has_lora ? rd.max_loras * rd.n_experts : 0;
-  pa.do_plan = 1;
+  pa.t_final = (float *)(ws + L.t_final);
+  pa.counters = (unsigned *)(ws + L.shrink_counters);
+  pa.k_splits = c.t_splits;
+  pa.n_pairs = n_pairs;
+  pa.do_plan = c.skinny ? 0 : 1;
   pa.plan = plan;
   pa.tile_rows = c.tr;
-  pa.n_units = has_lora ? (int)((n + kShrinkRows - 1) / kShrinkRows) + (int)std::min<uint32_t>(n, pa.n_pairs) : 0;
+  pa.n_units = c.units;
+  prof_record(0, st);
   if (int e = launch_status(launch_prep(pa, st), what)) return e;
+  prof_record(1, st);
+  if (c.skinny) {
+    SkinnyArgs sa{};
+    sa.W = (const u16 *)W;
+    sa.w_row_stride = (int)w_row_stride;
+    sa.x = (const u16 *)x;
+    sa.x_row_stride = (int)x_row_stride;
+    sa.y = (u16 *)y;
+    sa.y_row_stride = (int)y_row_stride;
+    sa.n_out = (int)n_out;
+    sa.k_in = (int)k_in;
+    sa.n = (int)n;
+    sa.rd = rd;
+    sa.rt = rt;
+    sa.has_lora = has_lora;
+    sa.t = pa.t_final;
+    sa.R = R;
+    const int e = launch_status(launch_skinny(sa, st), what);
+    prof_record(2, st);
+    return e;
+  }
 
   GemmArgs ga{};
   ga.W = (const u16 *)W;
@@ -248,13 +307,15 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
   ga.b_table = rd.b_table;
   ga.scale_table = rd.scale_table;
   ga.n_experts = rd.n_experts > 0 ? rd.n_experts : 1;
-  ga.t = pa.t;
+  ga.t = pa.t_final;
   ga.R = R;
   ga.splits = c.splits;
   ga.k_per_split = c.k_per_split;
   ga.partials = (float *)(ws + L.partials);
   ga.counters = (unsigned *)(ws + L.counters);
-  return launch_status(launch_gemm(ga, c.to, c.tr, st), what);
+  const int e = launch_status(launch_gemm(ga, c.to, c.tr, st), what);
+  prof_record(2, st);
+  return e;
 }
 
 }  // namespace
@@ -262,6 +323,19 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
 extern "C" {
 
 const char *lora_last_error(void) { return g_err; }
+
+int lora_set_profile_events(void *const *events, uint32_t n) {
+  clear_err();
+  if (n == 0) {
+    g_prof_on = false;
+    return LORA_OK;
+  }
+  if (n < 3 || !events || !events[0] || !events[1] || !events[2])
+    return fail(LORA_ERR_NULL_PTR, "lora_set_profile_events: need 3 non-NULL events, got %u", n);
+  for (int i = 0; i < 3; ++i) g_prof[i] = (hipEvent_t)events[i];
+  g_prof_on = true;
+  return LORA_OK;
+}
 
 const char *lora_version(void) { return "lora_mi355x 0.1 (gfx950)"; }
 
@@ -302,7 +376,10 @@ int lora_build_seq_slot(const int32_t *adapter_slots, uint32_t n, uint32_t padde
 size_t lora_workspace_bytes(int32_t op, int32_t dtype, uint32_t n_rows, uint32_t n_out, uint32_t k_in,
                             uint32_t max_rank, uint32_t n_groups) {
   if (dtype != LORA_BF16 || n_rows == 0) return 0;
-  const Cfg c = choose_cfg(op, (int)n_rows, (int)n_out, (int)k_in, (int)(n_groups ? n_groups : 1));
+  // pairs are counted generously: any table size the call may use
+  const int groups = (int)(n_groups ? n_groups : 1);
+  const Cfg c = choose_cfg(op, (int)n_rows, (int)n_out, (int)k_in, groups, (int)max_rank,
+                           max_rank ? (int)n_rows : 0);
   return ws_layout(c, (int)n_rows, (int)max_rank).total;
 }
 
@@ -338,6 +415,8 @@ int lora_shrink(const lora_route *route, const void *x, uint32_t x_row_stride, c
   pa.k_in = (int)route->k_in;
   pa.n = (int)n;
   pa.t = t;
+  pa.t_final = t;
+  pa.k_splits = 1;  // t is the caller's [n][max_rank] output: whole k per unit
   pa.n_pairs = (int)route->max_loras;
   pa.do_plan = 0;
   pa.n_units = (int)((n + kShrinkRows - 1) / kShrinkRows) + (int)std::min<uint32_t>(n, route->max_loras);
@@ -384,10 +463,9 @@ int lora_apply(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W, uint
   const Routing rt = routing_decode(route ? seq_slot : nullptr);
   hipStream_t st = (hipStream_t)stream;
   if (dtype == LORA_F32)
-    return launch_status(launch_apply_f32(rd, rt, route != nullptr, (const float *)W, 0, (int)w_row_stride,
+    return run_f32_timed(what, [&] { return launch_apply_f32(rd, rt, route != nullptr, (const float *)W, 0, (int)w_row_stride,
                                           (const float *)x, (int)x_row_stride, (int)k_in, (int)n_out, (int)n,
-                                          (float *)y, (int)y_row_stride, st),
-                         what);
+                                          (float *)y, (int)y_row_stride, st); }, st);
   return run_fused(what, LORA_OP_APPLY, rt, rd, route != nullptr, n_out, k_in, W, 0, w_row_stride, x,
                    x_row_stride, n, y, y_row_stride, workspace, workspace_bytes, 1, st);
 }
@@ -420,10 +498,9 @@ int lora_apply_segmented(int32_t dtype, uint32_t n_out, uint32_t k_in, const voi
   rt.top_k = 1;
   hipStream_t st = (hipStream_t)stream;
   if (dtype == LORA_F32)
-    return launch_status(launch_apply_f32(rd, rt, route != nullptr, (const float *)W, 0, (int)w_row_stride,
+    return run_f32_timed(what, [&] { return launch_apply_f32(rd, rt, route != nullptr, (const float *)W, 0, (int)w_row_stride,
                                           (const float *)x, (int)x_row_stride, (int)k_in, (int)n_out, (int)n,
-                                          (float *)y, (int)y_row_stride, st),
-                         what);
+                                          (float *)y, (int)y_row_stride, st); }, st);
   return run_fused(what, LORA_OP_SEGMENTED, rt, rd, route != nullptr, n_out, k_in, W, 0, w_row_stride, x,
                    x_row_stride, n, y, y_row_stride, workspace, workspace_bytes, 1, st);
 }
@@ -490,11 +567,10 @@ int lora_apply_moe_gather(int32_t dtype, uint32_t n_experts, uint32_t n_out, uin
   rt.n_experts = (int)n_experts;
   hipStream_t st = (hipStream_t)stream;
   if (dtype == LORA_F32)
-    return launch_status(launch_apply_f32(rd, rt, route != nullptr, (const float *)W_experts,
+    return run_f32_timed(what, [&] { return launch_apply_f32(rd, rt, route != nullptr, (const float *)W_experts,
                                           (long long)expert_stride, (int)w_row_stride, (const float *)x,
                                           (int)x_row_stride, (int)k_in, (int)n_out, (int)n, (float *)y,
-                                          (int)y_row_stride, st),
-                         what);
+                                          (int)y_row_stride, st); }, st);
   return run_fused(what, LORA_OP_MOE_GATHER, rt, rd, route != nullptr, n_out, k_in, W_experts,
                    (long long)expert_stride, w_row_stride, x, x_row_stride, n, y, y_row_stride, workspace,
                    workspace_bytes, (int)n_experts, st);

@@ -45,10 +45,12 @@
  *    launch returns LORA_ERR_LAUNCH with the HIP error text.
  *  - Workspace: the fused entry points take a caller-owned device
  *    workspace of at least lora_workspace_bytes(...) bytes.  It must be
- *    zero-filled once before its first use; every call that returns LORA_OK
- *    leaves the words that must start at zero at zero again (no memset is
- *    recorded into a captured graph).  Concurrent calls sharing one
- *    workspace race.
+ *    zero-filled before its first use with a given problem shape (op,
+ *    n_rows, n_out, k_in, max_rank, n_groups); every call that returns
+ *    LORA_OK leaves the words that must start at zero at zero again, so the
+ *    same shape can be called again with no memset (none is recorded into a
+ *    captured graph).  Reusing one workspace for another shape needs a new
+ *    zero fill.  Concurrent calls sharing one workspace race.
  */
 #ifndef LORA_MI355X_H
 #define LORA_MI355X_H
@@ -165,6 +167,17 @@ int lora_build_seq_slot(const int32_t *adapter_slots, uint32_t n, uint32_t padde
  */
 size_t lora_workspace_bytes(int32_t op, int32_t dtype, uint32_t n_rows, uint32_t n_out,
                             uint32_t k_in, uint32_t max_rank, uint32_t n_groups);
+
+/*
+ * Measurement aid (atlas lora_delta.rs lora_no_apply doc: apply cost is
+ * measured apart from everything else).  With n >= 3 HIP events set, every
+ * later fused call on the calling thread (lora_apply, lora_apply_segmented,
+ * lora_apply_moe_gather) records events[0] on its stream before its first
+ * kernel, events[1] between the prep kernel (route plan + shrink) and the
+ * fused GEMM, and events[2] after the GEMM.  n == 0 switches it off.
+ * events is [host]; the events themselves are the caller's hipEvent_t.
+ */
+int lora_set_profile_events(void *const *events, uint32_t n);
 
 /* ------------------------------------------------------------ kernels */
 

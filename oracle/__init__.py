@@ -97,9 +97,14 @@ class Oracle:
                                            C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_int, _i32p,
                                            C.c_int, _i32p, _i32p, C.c_int, _f64p]
         L.orc_mutant.restype = C.c_int
+        L.orc_threads.restype = C.c_int
         self.L = L
 
     # -------------------------------------------------------------- helpers
+    @property
+    def threads(self) -> int:
+        return int(self.L.orc_threads())
+
     @property
     def mutant(self) -> int:
         return int(self.L.orc_mutant())

@@ -34,6 +34,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORC_F32 0
 #define ORC_BF16 1
@@ -356,3 +359,12 @@ void orc_apply_moe_gather(const void *W, long long expert_stride, int w_stride,
 }
 
 int orc_mutant(void) { return ORC_MUTANT; }
+
+/* Threads an OpenMP loop here uses (1 without OpenMP). */
+int orc_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

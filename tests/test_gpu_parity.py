@@ -67,6 +67,8 @@ SMALL = [
     (3, "bf16", 4096, 72, 5, 3, 64),      # split-K 8, five rows
     (4, "bf16", 264, 520, 150, 9, 48),    # two row tiles, ragged n_out tile
     (5, "bf16", 64, 64, 1, 2, 16),        # one row
+    (8, "bf16", 2048, 192, 20, 4, 128),   # rank 128: tiled GEMM with split-K 4
+    (9, "bf16", 3072, 128, 100, 5, 16),   # 100 rows: 128-row tiles, split-K 3
     (6, "f32", 96, 80, 13, 5, 16),
     (7, "f32", 37, 29, 9, 3, 5),          # f32 takes any shape
 ]
@@ -372,3 +374,20 @@ def test_full_config_parity(orc, name):
         yb = dw.run(route=False).clone()
         torch.cuda.synchronize()
         assert np.array_equal(bf16_bits(dw.y)[57:], bf16_bits(yb)[57:])
+
+
+def test_decode_batch_equals_per_row_calls():
+    """atlas apply_lora_bgmv doc: the batched call equals n one-row calls.  On the
+    decode path every output element is reduced in the same order whatever the
+    batch, so the equality holds bit for bit."""
+    wl = WL.random_small(70, dtype="bf16", k=1536, n_out=96, n=24, n_slots=4, max_rank=32)
+    dw = DeviceWorkload(wl)
+    whole = bf16_bits(dw.run().clone())
+    for i in range(dw.n):
+        one = WL.Workload(name="one", dtype="bf16", k_in=wl.k_in, n_out=wl.n_out,
+                          max_rank=wl.max_rank, W=wl.W, A=wl.A, B=wl.B, x=wl.x[i:i + 1],
+                          adapters=wl.adapters, adapter_slots=dw.seq_slot_host[i:i + 1],
+                          padded_n=1, meta={"seq_slot": dw.seq_slot_host[i:i + 1]})
+        d1 = DeviceWorkload(one)
+        yi = bf16_bits(d1.run().clone())
+        assert np.array_equal(yi[0], whole[i]), i
