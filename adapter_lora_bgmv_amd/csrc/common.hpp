@@ -41,6 +41,35 @@ __device__ __forceinline__ uint4 ldg16(const void *p) { return *(const uint4 *)p
 
 __device__ __forceinline__ uint32_t pack2(u16 lo, u16 hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
 
+// s_waitcnt with only the vector-memory counter constrained (<= n).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One LDS-DMA instruction: 16 bytes per lane from `g` into the wave's 1 KB
+// LDS block at byte address `lds` (lane l lands at lds + 16 l).  Issued as
+// assembly so that the compiler adds no waits of its own around the LDS
+// reads that follow; every wait on these transfers is explicit.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+// Workgroup barrier that the compiler may not move memory accesses across.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // The route-resolve rule of every entry point: slot in range, both table
 // entries non-NULL, scale non-zero.  Returns the table index or kSkip.
 __device__ __forceinline__ int resolve_slot(int slot, int expert, int max_loras, int n_experts,

@@ -39,20 +39,11 @@
 
 namespace lora {
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 // The bf16 high part of v, or (part != 0) the bf16 rounding of what the
 // high part leaves over; hi + lo carries v to about 16 significant bits.
 __device__ __forceinline__ u16 hilo(float v, int part) {
   const u16 hi = f2bf(v);
   return part ? f2bf(v - bf2f(hi)) : hi;
-}
-
-// s_waitcnt with only the vector-memory counter constrained (<= n).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // Waits until at most `stages_younger` stages of `PER` DMA instructions each
@@ -66,28 +57,6 @@ __device__ __forceinline__ void wait_stages(int stages_younger) {
   if constexpr (MAXS >= 2) { if (stages_younger == 2) { wait_vmcnt<2 * PER>(); return; } }
   if constexpr (MAXS >= 1) { if (stages_younger == 1) { wait_vmcnt<PER>(); return; } }
   wait_vmcnt<0>();
-}
-
-// One LDS-DMA instruction: 16 bytes per lane from `g` into the wave's 1 KB
-// LDS block at byte address `lds` (lane l lands at lds + 16 l).  Issued as
-// assembly so that the compiler adds no waits of its own around the LDS
-// reads that follow; every wait on these transfers is explicit.
-__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(lds)
-               : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
-}
-
-// Workgroup barrier that the compiler may not move memory accesses across.
-__device__ __forceinline__ void block_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 template <int BO, int BR, int WGO, int WGR, int NS>

@@ -59,7 +59,9 @@ struct GemmArgs {
   unsigned *counters;
 };
 
-struct SkinnyArgs {
+// The decode-shaped apply (k_decode.hip): main launch (base partial tiles and
+// the shrink) + epilogue launch, n <= 64 rows.
+struct DecodeArgs {
   const u16 *W;
   int w_row_stride;
   const u16 *x;
@@ -68,15 +70,28 @@ struct SkinnyArgs {
   int y_row_stride;
   int n_out, k_in, n;
   RouteDev rd;
-  Routing rt;
+  const int32_t *seq_slot;
   int has_lora;
-  const float *t;  // [n][R] the shrink's output
   int R;
+  int S, k_per_split;   // k split of the base contraction
+  int n_tiles;          // ceil(n_out / kDecodeTileOut)
+  int n_chunks, chunk;  // k ranges of the shrink partials: the S splits, k_per_split wide
+  float *partials;      // [n_tiles][S][64 rows][kDecodeTileOut] partial tiles
+  float *t_part;        // [n_chunks][n][R] shrink partials, one per k range
+  int *row_q;           // [64] each row's slot or kSkip, for the epilogue
+  float *row_sig;       // [64] each row's scale
+  const u16 **row_b;    // [64] each row's B
 };
 
-// Largest batch and rank the decode-shaped kernel takes.
-constexpr int kSkinnyMaxRows = 64;
-constexpr int kSkinnyMaxRank = 64;
+// Largest batch the decode kernels take, their tile width, LDS scratch,
+// largest k split, k steps per wave in flight together, largest shrink chunk
+// count.
+constexpr int kDecodeMaxRows = 64;
+constexpr int kDecodeTileOut = 64;
+constexpr int kDecodeLds = 128 * 1024;
+constexpr int kDecodeMaxSplit = 8;
+constexpr int kDecodeBatch = 4;
+constexpr int kDecodeMaxChunks = kDecodeMaxSplit;
 
 // Rows per shrink unit.
 constexpr int kShrinkRows = 16;
@@ -97,6 +112,7 @@ hipError_t launch_expand_fold(const RouteDev &rd, int dtype, const int32_t *seq_
                               hipStream_t st);
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &a, int to, int tr, hipStream_t st);
-hipError_t launch_skinny(const SkinnyArgs &a, hipStream_t st);
+hipError_t launch_decode_main(const DecodeArgs &a, hipStream_t st);
+hipError_t launch_decode_epilogue(const DecodeArgs &a, hipStream_t st);
 
 }  // namespace lora

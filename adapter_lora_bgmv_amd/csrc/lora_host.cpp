@@ -19,7 +19,7 @@ using namespace lora;
 namespace {
 
 thread_local char g_err[512];
-thread_local hipEvent_t g_prof[3];
+thread_local hipEvent_t g_prof[4];
 thread_local bool g_prof_on = false;
 
 void prof_record(int i, hipStream_t st) {
@@ -67,7 +67,7 @@ int check_device(const char *what) {
 // ------------------------------------------------------------ tiling
 struct Cfg {
   int to, tr, splits, k_per_split, max_mtiles, n_ntiles;
-  bool skinny;   // decode-shaped kernel (no plan, no split-K)
+  bool decode;   // the one-launch decode kernel (k_decode.hip)
   int units;     // upper bound of shrink units
   int t_splits;  // k chunks of the shrink; the consumer sums the partials
 };
@@ -80,13 +80,15 @@ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 // part; larger batches pick it from the tile count to fill the chip.
 Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pairs) {
   Cfg c;
-  c.skinny = op == LORA_OP_APPLY && n <= kSkinnyMaxRows && R <= kSkinnyMaxRank;
+  c.decode = op == LORA_OP_APPLY && n <= kDecodeMaxRows;
   c.units = R > 0 ? (n + kShrinkRows - 1) / kShrinkRows + std::min(n, n_pairs) : 0;
   // Shrink k chunks: enough workgroups to cover the chip for small batches,
   // chunks of at least 128 columns.  A function of (n, k_in) only, so the
   // workspace size does not depend on the routing.
   c.t_splits = R > 0 ? clampi(512 / ((n + kShrinkRows - 1) / kShrinkRows), 1, std::min(8, std::max(1, k_in / 128))) : 1;
-  if (op == LORA_OP_MOE_GATHER) {
+  if (c.decode) {
+    c.to = kDecodeTileOut; c.tr = kDecodeMaxRows; c.splits = clampi(k_in / 1024, 1, 8);
+  } else if (op == LORA_OP_MOE_GATHER) {
     c.to = 256; c.tr = 64; c.splits = 1;
   } else if (n <= 64) {
     c.to = 64; c.tr = 64; c.splits = clampi(k_in / 1024, 1, 8);
@@ -97,23 +99,37 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
     const int tiles = ((n + 255) / 256) * ((n_out + 255) / 256);
     c.splits = clampi(307 / tiles, 1, std::min(8, std::max(1, k_in / 1024)));
   }
-  const int kslabs = (k_in + 63) / 64;
-  c.k_per_split = ((kslabs + c.splits - 1) / c.splits) * 64;
+  if (c.decode) {
+    const int ksteps = (k_in + 31) / 32;
+    c.k_per_split = ((ksteps + c.splits - 1) / c.splits) * 32;
+  } else {
+    const int kslabs = (k_in + 63) / 64;
+    c.k_per_split = ((kslabs + c.splits - 1) / c.splits) * 64;
+  }
   c.max_mtiles = (n + c.tr - 1) / c.tr + (op == LORA_OP_MOE_GATHER ? groups : 0);
   c.n_ntiles = (n_out + c.to - 1) / c.to;
   return c;
 }
 
 struct WsLayout {
-  size_t counters, shrink_counters, pos_row, pos_pair, tiles, n_tiles, t, t_final, partials, total;
+  size_t counters, shrink_counters, pos_row, pos_pair, tiles, n_tiles, t, t_final, partials, rows, total;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-WsLayout ws_layout(const Cfg &c, int n, int R) {
-  WsLayout w;
+WsLayout ws_layout(const Cfg &c, int n, int R, int k_in) {
+  WsLayout w{};
   size_t off = 0;
-  const size_t ntile = c.skinny ? 0 : (size_t)c.max_mtiles * c.n_ntiles;
+  if (c.decode) {  // partial tiles; shrink partials; per-row routes
+    const size_t nchunks = R > 0 ? (size_t)c.splits : 0;  // the shrink's k ranges are the splits
+    w.partials = off;
+    off = up256(off + (c.splits > 1 || R > 0 ? (size_t)c.n_ntiles * c.splits * 64 * kDecodeTileOut * 4 : 0));
+    w.t = off; off = up256(off + nchunks * n * R * 4);
+    w.rows = off; off = up256(off + (R > 0 ? 64 * (4 + 4 + 8) : 0));
+    w.total = off;
+    return w;
+  }
+  const size_t ntile = (size_t)c.max_mtiles * c.n_ntiles;
   w.counters = off; off = up256(off + (c.splits > 1 ? ntile * 4 : 0));
   w.shrink_counters = off; off = up256(off + (c.t_splits > 1 ? (size_t)c.units * 4 : 0));
   w.pos_row = off; off = up256(off + (size_t)n * 4);
@@ -123,7 +139,7 @@ WsLayout ws_layout(const Cfg &c, int n, int R) {
   w.t = off; off = up256(off + (c.t_splits > 1 ? (size_t)c.t_splits * n * R * 4 : 0));
   w.t_final = off; off = up256(off + (size_t)n * R * 4);
   w.partials = off;
-  off = up256(off + (c.splits > 1 && !c.skinny ? ntile * c.splits * c.to * c.tr * 4 : 0));
+  off = up256(off + (c.splits > 1 ? ntile * c.splits * c.to * c.tr * 4 : 0));
   w.total = off;
   return w;
 }
@@ -226,6 +242,7 @@ int run_f32_timed(const char *what, F launch, hipStream_t st) {
   prof_record(1, st);
   const int e = launch_status(launch(), what);
   prof_record(2, st);
+  prof_record(3, st);
   return e;
 }
 
@@ -238,7 +255,7 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
   const int R = has_lora ? rd.R : 0;
   const int n_pairs = has_lora ? rd.max_loras * rd.n_experts : 0;
   const Cfg c = choose_cfg(op, (int)n, (int)n_out, (int)k_in, groups, R, n_pairs);
-  const WsLayout L = ws_layout(c, (int)n, R);
+  const WsLayout L = ws_layout(c, (int)n, R, (int)k_in);
   if (!workspace || workspace_bytes < L.total)
     return fail(LORA_ERR_WORKSPACE,
                 "%s: [n_out %u x k_in %u] at max_rank %d, n %u: workspace %p of %zu bytes, %zu needed", what,
@@ -246,6 +263,39 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
   if (!aligned16(workspace))
     return fail(LORA_ERR_UNSUPPORTED, "%s: workspace %p is not 16-byte aligned", what, workspace);
   char *ws = (char *)workspace;
+  if (c.decode) {
+    DecodeArgs da{};
+    da.W = (const u16 *)W;
+    da.w_row_stride = (int)w_row_stride;
+    da.x = (const u16 *)x;
+    da.x_row_stride = (int)x_row_stride;
+    da.y = (u16 *)y;
+    da.y_row_stride = (int)y_row_stride;
+    da.n_out = (int)n_out;
+    da.k_in = (int)k_in;
+    da.n = (int)n;
+    da.rd = rd;
+    da.seq_slot = rt.seq_slot;
+    da.has_lora = has_lora;
+    da.R = R;
+    da.S = c.splits;
+    da.k_per_split = c.k_per_split;
+    da.n_tiles = c.n_ntiles;
+    da.chunk = c.k_per_split;
+    da.n_chunks = R > 0 ? c.splits : 0;
+    da.partials = (float *)(ws + L.partials);
+    da.t_part = (float *)(ws + L.t);
+    da.row_q = (int *)(ws + L.rows);
+    da.row_sig = (float *)(ws + L.rows + 64 * 4);
+    da.row_b = (const u16 **)(ws + L.rows + 64 * 8);
+    prof_record(0, st);
+    prof_record(1, st);
+    if (int e = launch_status(launch_decode_main(da, st), what)) return e;
+    prof_record(2, st);
+    const int e = launch_status(launch_decode_epilogue(da, st), what);
+    prof_record(3, st);
+    return e;
+  }
   PlanDev plan{(int *)(ws + L.pos_row), (int *)(ws + L.pos_pair), (int4 *)(ws + L.tiles),
                (int *)(ws + L.n_tiles)};
 
@@ -262,33 +312,13 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
   pa.counters = (unsigned *)(ws + L.shrink_counters);
   pa.k_splits = c.t_splits;
   pa.n_pairs = n_pairs;
-  pa.do_plan = c.skinny ? 0 : 1;
+  pa.do_plan = 1;
   pa.plan = plan;
   pa.tile_rows = c.tr;
   pa.n_units = c.units;
   prof_record(0, st);
   if (int e = launch_status(launch_prep(pa, st), what)) return e;
   prof_record(1, st);
-  if (c.skinny) {
-    SkinnyArgs sa{};
-    sa.W = (const u16 *)W;
-    sa.w_row_stride = (int)w_row_stride;
-    sa.x = (const u16 *)x;
-    sa.x_row_stride = (int)x_row_stride;
-    sa.y = (u16 *)y;
-    sa.y_row_stride = (int)y_row_stride;
-    sa.n_out = (int)n_out;
-    sa.k_in = (int)k_in;
-    sa.n = (int)n;
-    sa.rd = rd;
-    sa.rt = rt;
-    sa.has_lora = has_lora;
-    sa.t = pa.t_final;
-    sa.R = R;
-    const int e = launch_status(launch_skinny(sa, st), what);
-    prof_record(2, st);
-    return e;
-  }
 
   GemmArgs ga{};
   ga.W = (const u16 *)W;
@@ -315,6 +345,7 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
   ga.counters = (unsigned *)(ws + L.counters);
   const int e = launch_status(launch_gemm(ga, c.to, c.tr, st), what);
   prof_record(2, st);
+  prof_record(3, st);
   return e;
 }
 
@@ -330,9 +361,9 @@ int lora_set_profile_events(void *const *events, uint32_t n) {
     g_prof_on = false;
     return LORA_OK;
   }
-  if (n < 3 || !events || !events[0] || !events[1] || !events[2])
-    return fail(LORA_ERR_NULL_PTR, "lora_set_profile_events: need 3 non-NULL events, got %u", n);
-  for (int i = 0; i < 3; ++i) g_prof[i] = (hipEvent_t)events[i];
+  if (n < 4 || !events || !events[0] || !events[1] || !events[2] || !events[3])
+    return fail(LORA_ERR_NULL_PTR, "lora_set_profile_events: need 4 non-NULL events, got %u", n);
+  for (int i = 0; i < 4; ++i) g_prof[i] = (hipEvent_t)events[i];
   g_prof_on = true;
   return LORA_OK;
 }
@@ -380,7 +411,7 @@ size_t lora_workspace_bytes(int32_t op, int32_t dtype, uint32_t n_rows, uint32_t
   const int groups = (int)(n_groups ? n_groups : 1);
   const Cfg c = choose_cfg(op, (int)n_rows, (int)n_out, (int)k_in, groups, (int)max_rank,
                            max_rank ? (int)n_rows : 0);
-  return ws_layout(c, (int)n_rows, (int)max_rank).total;
+  return ws_layout(c, (int)n_rows, (int)max_rank, (int)k_in).total;
 }
 
 int lora_shrink(const lora_route *route, const void *x, uint32_t x_row_stride, const int32_t *seq_slot,

@@ -58,6 +58,7 @@ def parse():
     p.add_argument("--config", default="decode_bgmv")
     p.add_argument("--no-others", action="store_true", help="skip the other workloads")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    p.add_argument("--no-base", action="store_true", help="skip the base-only (no adapter) timing")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run one 256 MiB device copy, a known-size reference for "
@@ -112,18 +113,60 @@ def algorithmic_counts(wl, scale_table):
     base_flops = 2.0 * n * o * k
     shrink_flops = 2.0 * active * R * k
     expand_flops = 2.0 * active * R * o
-    return {
+    out = {
         "rows": n, "adapted_rows": active, "touched_pairs": touched,
         "path_bytes": w_bytes + a_bytes + b_bytes + x_bytes + y_bytes,
-        # the fused GEMM: W, touched B, x, y, and the f32 t it reads
-        "main_bytes": w_bytes + b_bytes + x_bytes + y_bytes + t_bytes,
-        "main_flops": base_flops + expand_flops,
-        "prep_bytes": a_bytes + x_bytes + t_bytes,
         "path_flops": base_flops + shrink_flops + expand_flops,
     }
+    if decode_path(wl):
+        # main launch: W and x once, the touched A once, t out; the epilogue
+        # launch reads the touched B and t and writes y
+        out.update(main_bytes=w_bytes + x_bytes + a_bytes + t_bytes, main_flops=base_flops + shrink_flops,
+                   main_kernel="decode_main_kernel (base partial tiles + shrink)")
+    else:
+        # the fused GEMM: W, touched B, x, y, and the f32 t it reads
+        out.update(main_bytes=w_bytes + b_bytes + x_bytes + y_bytes + t_bytes, main_flops=base_flops + expand_flops,
+                   main_kernel="gemm_bf16_kernel (fused base + expand + fold)")
+    return out
+
+
+def decode_path(wl):
+    """The decode kernels take lora_apply batches of at most 64 rows in bf16."""
+    return wl.kind == "decode" and wl.dtype == "bf16" and len(wl.x) <= 64
 
 
 # ------------------------------------------------------------------ GPU timing
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+def hip_timing_events(n):
+    """n HIP events for timing only: no system-scope fence when recorded, so a
+    record adds no cache writeback to the span it closes.  The HIP runtime is
+    the one torch loaded (same soname)."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = []
+    for _ in range(n):
+        e = ctypes.c_void_p()
+        rc = hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+        evs.append(e)
+    return hip, evs
+
+
+def hip_elapsed_ms(hip, a, b):
+    import ctypes
+    ms = ctypes.c_float()
+    rc = hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+    if rc != 0:
+        raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+    return ms.value
+
+
 def time_workload(name, steps, warmup, apply=True):
     import torch
     from adapter_lora_bgmv_amd import binding as B
@@ -164,23 +207,24 @@ def time_workload(name, steps, warmup, apply=True):
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / steps
 
-    # per-kernel durations: events recorded by the library around its kernels
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for trio in evs:
-        for e in trio:
-            e.record()
-    torch.cuda.synchronize()
+    # per-kernel durations: HIP events the library records around its
+    # kernels, created without the system-scope fence (timing-only events)
+    hip, evs = hip_timing_events(4 * steps)
     for i in range(steps):
-        B.lora_set_profile_events([e.cuda_event for e in evs[i]])
+        B.lora_set_profile_events([evs[4 * i + j].value for j in range(4)])
         dws[i % R].run(route=apply)
     B.lora_set_profile_events(None)
     torch.cuda.synchronize()
-    prep_ms = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(steps)])
-    main_ms = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(steps)])
+    spans = np.array([[hip_elapsed_ms(hip, evs[4 * i + a], evs[4 * i + a + 1]) for a in range(3)]
+                      for i in range(steps)])
+    prep_ms, main_ms, post_ms = spans[:, 0], spans[:, 1], spans[:, 2]
+    for e in evs:
+        hip.hipEventDestroy(e)
     return wl, counts, {"steps": steps, "rotate": R, "ms_per_step": ms_per_step,
                         "prep_us_mean": float(prep_ms.mean() * 1e3),
                         "main_us_mean": float(main_ms.mean() * 1e3),
-                        "main_us_median": float(np.median(main_ms) * 1e3)}
+                        "main_us_median": float(np.median(main_ms) * 1e3),
+                        "post_us_mean": float(post_ms.mean() * 1e3)}
 
 
 def summarize(name, counts, t, base_t=None):
@@ -192,6 +236,7 @@ def summarize(name, counts, t, base_t=None):
         "rows_per_s": counts["adapted_rows"] / step_s if counts["adapted_rows"] else counts["rows"] / step_s,
         "prep_us": round(t["prep_us_mean"], 2),
         "main_us": round(t["main_us_mean"], 2),
+        "post_us": round(t["post_us_mean"], 2),
         "path_GBps": counts["path_bytes"] / step_s / 1e9,
         "path_TFLOPs": counts["path_flops"] / step_s / 1e12,
         "main_GBps": counts["main_bytes"] / main_s / 1e9,
@@ -272,7 +317,7 @@ def main():
     name = a.config
     print(f"# bench: {name} steps={a.steps} warmup={a.warmup}", file=sys.stderr, flush=True)
     wl, counts, t = time_workload(name, a.steps, a.warmup)
-    _, _, tb = time_workload(name, a.steps, a.warmup, apply=False)
+    tb = None if a.no_base else time_workload(name, a.steps, a.warmup, apply=False)[2]
     head = summarize(name, counts, t, tb)
     print(f"# {name}: {json.dumps(head)}", file=sys.stderr, flush=True)
 
@@ -292,9 +337,9 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": head["main_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    kname = "skinny_bf16_kernel" if counts["rows"] <= 64 else "gemm_bf16_kernel"
+    kname = counts["main_kernel"].split(" ")[0]
     roof["traffic"] = measured_traffic(kname, name)
-    roof["kernel"] = f"{kname} (fused base + expand + fold)"
+    roof["kernel"] = counts["main_kernel"]
     roof["algorithmic_bytes_per_launch"] = counts["main_bytes"]
     roof["avg_launch_us"] = head["main_us"]
 
@@ -318,7 +363,7 @@ def main():
         "config": {"workload": WORKLOAD_TEXT[name], "rows": counts["rows"],
                    "adapted_rows": counts["adapted_rows"], "touched_slots": counts["touched_pairs"],
                    "path_GBps": head["path_GBps"], "path_frac_of_hbm_peak": head["path_GBps"] / HBM_PEAK_GBPS,
-                   "prep_us": head["prep_us"], "main_us": head["main_us"],
+                   "prep_us": head["prep_us"], "main_us": head["main_us"], "post_us": head["post_us"],
                    "base_only_ms_per_step": head.get("base_only_ms_per_step"),
                    "base_only_main_us": head.get("base_only_main_us")},
         "roofline": roof,

@@ -170,12 +170,15 @@ size_t lora_workspace_bytes(int32_t op, int32_t dtype, uint32_t n_rows, uint32_t
 
 /*
  * Measurement aid (atlas lora_delta.rs lora_no_apply doc: apply cost is
- * measured apart from everything else).  With n >= 3 HIP events set, every
+ * measured apart from everything else).  With n >= 4 HIP events set, every
  * later fused call on the calling thread (lora_apply, lora_apply_segmented,
- * lora_apply_moe_gather) records events[0] on its stream before its first
- * kernel, events[1] between the prep kernel (route plan + shrink) and the
- * fused GEMM, and events[2] after the GEMM.  n == 0 switches it off.
- * events is [host]; the events themselves are the caller's hipEvent_t.
+ * lora_apply_moe_gather) records on its stream events[0] before its first
+ * kernel, events[1] right before its main kernel (after the route plan and
+ * shrink kernel where there is one), events[2] right after the main kernel,
+ * and events[3] after its last kernel (the decode epilogue where there is
+ * one).  n == 0 switches it off.  events is [host]; the events themselves are
+ * the caller's hipEvent_t.  Returns LORA_ERR_NULL_PTR for 0 < n < 4 or a NULL
+ * event.
  */
 int lora_set_profile_events(void *const *events, uint32_t n);
 

@@ -63,12 +63,14 @@ SMALL = [
     # (seed, dtype, k, n_out, n, n_slots, max_rank)
     (0, "bf16", 96, 80, 13, 5, 16),
     (1, "bf16", 200, 136, 70, 6, 32),     # n > 64: 128-row tiles, split 1
-    (2, "bf16", 1032, 264, 40, 4, 16),    # ragged k tail, split-K 2
-    (3, "bf16", 4096, 72, 5, 3, 64),      # split-K 8, five rows
+    (2, "bf16", 1032, 264, 40, 4, 16),    # ragged k tail and shrink chunk
+    (3, "bf16", 4096, 72, 5, 3, 64),      # split-K 4, five rows
     (4, "bf16", 264, 520, 150, 9, 48),    # two row tiles, ragged n_out tile
     (5, "bf16", 64, 64, 1, 2, 16),        # one row
-    (8, "bf16", 2048, 192, 20, 4, 128),   # rank 128: tiled GEMM with split-K 4
+    (8, "bf16", 2048, 192, 20, 4, 128),   # rank 128, split-K 2
     (9, "bf16", 3072, 128, 100, 5, 16),   # 100 rows: 128-row tiles, split-K 3
+    (13, "bf16", 160, 88, 7, 3, 16),      # second row block of a tile cut at 8 rows
+    (14, "bf16", 1536, 56, 33, 20, 64),   # one ragged tile, 20 slots, rank 64
     (6, "f32", 96, 80, 13, 5, 16),
     (7, "f32", 37, 29, 9, 3, 5),          # f32 takes any shape
 ]
