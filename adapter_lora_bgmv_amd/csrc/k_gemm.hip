@@ -25,8 +25,8 @@
 // output the same way):
 //     acc[o, i] += sum_kappa B_q[o, kappa] * T[i, kappa]
 // where T holds s_q * t_i split into a bf16 high and low part (so the f32
-// intermediate t is carried at ~16 significant bits), and rows of another
-// pair, or skipped rows, contribute exact zeros.  Starting from +0, a skipped
+// intermediate t is carried at ~16 significant bits; the shrink writes it),
+// and rows of another pair, or skipped rows, contribute exact zeros.  Starting from +0, a skipped
 // row's accumulator is still +0 when the base contraction begins, so its
 // output is bit-identical to the base-only launch of the same shape.
 //
@@ -34,17 +34,12 @@
 // last to arrive (a device-scope counter) sums the partial tiles in split
 // order and writes y, so results do not depend on arrival order.  The
 // extension always runs in split 0.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace lora {
-
-// The bf16 high part of v, or (part != 0) the bf16 rounding of what the
-// high part leaves over; hi + lo carries v to about 16 significant bits.
-__device__ __forceinline__ u16 hilo(float v, int part) {
-  const u16 hi = f2bf(v);
-  return part ? f2bf(v - bf2f(hi)) : hi;
-}
 
 // Waits until at most `stages_younger` stages of `PER` DMA instructions each
 // are still in flight (0 <= stages_younger <= MAXS).
@@ -64,25 +59,42 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int NW = WGO * WGR;
   constexpr int WO = BO / WGO, WR = BR / WGR;  // wave tile
   constexpr int NBO = WO / 16, NBR = WR / 16;  // fragment blocks per wave
-  constexpr int FO = BO / 16, FR = BR / 16;    // fragment blocks per tile
-  constexpr int SB = FO + FR;                  // fragments per stage (one 32-wide k step)
-  constexpr int LPW = SB / NW;                 // DMA instructions per wave per stage
-  static_assert(SB % NW == 0, "stage fragments must split evenly over the waves");
-  static_assert((NS - 2) * LPW < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(16))) uint4 ring[NS][SB][64];
+  constexpr int RS = BO + BR;                  // rows of a stage: W rows, then x rows
+  constexpr int SI = RS / 8;                   // DMA instructions per stage (8 rows x 128 B each)
+  constexpr int LPW = SI / NW;                 // DMA instructions per wave per stage
+  static_assert(SI % NW == 0, "stage rows must split evenly over the waves");
+  static_assert(NS >= 2 && (NS - 2) * LPW < 64, "ring depth / vmcnt range");
+  // A stage is 64 k columns of every row of the tile, row-major, 128 B per
+  // row, its eight 16-byte chunks stored XOR-swizzled by row (chunk c of row
+  // r at slot c ^ ((r >> 1) & 7)) so that the MFMA fragment reads below hit
+  // distinct banks.
+  __shared__ __attribute__((aligned(16))) uint4 ring[NS][RS * 8];
   __shared__ int s_row[BR], s_pair[BR];
   __shared__ const u16 *s_bq[BR];  // the row's B_pair, or null
-  __shared__ float s_sig[BR];      // the row's scale
   __shared__ int s_last;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wo = wave % WGO, wr = wave / WGO;
-  int bid = blockIdx.x;
-  const int z = bid % p.splits;
-  bid /= p.splits;
-  const int nt = bid % p.n_ntiles;
-  const int mt = bid / p.n_ntiles;
-  if (mt >= *p.plan.n_tiles) return;
+  // Tile order: the chip hands workgroups to its 8 XCDs in turn, each XCD
+  // with its own L2.  So the workgroups of one XCD get a contiguous range of
+  // logical ids, and consecutive ids walk the output tiles in groups of up to
+  // 8 row tiles (rows fastest): an XCD's workgroups share a few W tiles and a
+  // few x tiles, which its L2 then serves.  The split index is the fastest,
+  // so the split-0 workgroups (the LoRA extension) spread over every XCD.
+  const int mtiles = *p.plan.n_tiles;  // row tiles the plan made (<= max_mtiles)
+  const int ntile_all = mtiles * p.n_ntiles;
+  const int grid = ntile_all * p.splits;
+  const int b = blockIdx.x;
+  if (b >= grid) return;
+  const int xq = grid / 8, xr = grid % 8, xcd = b % 8;
+  const int id = xcd * xq + min(xcd, xr) + b / 8;  // each XCD: a contiguous id range
+  const int z = id % p.splits;
+  const int r = id / p.splits;
+  const int gm0 = r / (8 * p.n_ntiles) * 8;  // first row tile of the group
+  const int gsz = min(8, mtiles - gm0);
+  const int rr = r - gm0 * p.n_ntiles;
+  const int mt = gm0 + rr % gsz;
+  const int nt = rr / gsz;
   const int4 tile = p.plan.tiles[mt];
   const int o0 = nt * BO;
   for (int i = tid; i < BR; i += NW * 64) {
@@ -91,7 +103,6 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
     s_row[i] = in ? p.plan.pos_row[tile.y + i] : -1;
     s_pair[i] = q;
     s_bq[i] = (p.has_lora && q >= 0) ? (const u16 *)p.b_table[q] : nullptr;
-    s_sig[i] = (p.has_lora && q >= 0) ? p.scale_table[q / p.n_experts] : 0.f;
   }
   __syncthreads();
 
@@ -101,11 +112,104 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
 #pragma unroll
     for (int b = 0; b < NBR; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // ---------------------------------------------------------- base contraction
+  const int kb = min(z * p.k_per_split, p.k_in);
+  const int ke = min(kb + p.k_per_split, p.k_in);
+  const int nstage = (ke - kb + 63) / 64;
+  const u16 *Wg = p.W + (size_t)tile.x * (size_t)p.w_group_stride;
+  // Each DMA instruction moves 8 whole 128-byte row segments (full cache
+  // lines): lane l takes row 8i + l/8 of the stage and the chunk that belongs
+  // at slot l%8 of that row.  This lane's rows are the same in every stage.
+  const u16 *src[LPW];
+  int sch[LPW];  // element offset of this lane's chunk within the 64 columns
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int rr = (wave + NW * j) * 8 + (lane >> 3);  // row of the stage
+    const u16 *rowp;
+    if (rr < BO) {
+      const int o = min(o0 + rr, p.n_out - 1);
+      rowp = Wg + (size_t)o * p.w_row_stride;
+    } else {
+      int r = s_row[rr - BO];
+      if (r < 0) r = s_row[0];
+      rowp = p.x + (size_t)r * p.x_row_stride;
+    }
+    src[j] = rowp;
+    sch[j] = ((lane & 7) ^ ((rr >> 1) & 7)) * 8;
+  }
+  // Every wave issues exactly LPW DMA instructions per stage, so the vmcnt
+  // waits count stages exactly.  Lanes whose chunk lies past the k range read
+  // column 0 of their row instead and zero their landed chunk afterwards.
+  auto issue = [&](int st) {
+    const int k0 = kb + st * 64;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int kk = k0 + sch[j] < ke ? k0 + sch[j] : 0;
+      dma16(src[j] + kk, lds_addr(&ring[st % NS][(wave + NW * j) * 64]));
+    }
+  };
+  // the first NS - 1 stages go out before the extension, so its latency and
+  // theirs overlap
+  for (int st = 0; st < NS - 1 && st < nstage; ++st) issue(st);
+
   // ---------------------------------------------------------- k-extension
   // Items are (run of equal pairs within a 16-row block, 32-wide kappa step);
   // the loads of up to G items are issued together before their MFMAs, so
   // the extension costs a few memory latencies, not one per item.
-  if (p.has_lora && z == 0) {
+  // When every row of the wave's range that has a pair has the same one (a
+  // prefill segment, an expert's rows of one adapter), the B fragments of a
+  // kappa step serve all NBR row blocks: each step loads them once and the
+  // extension is a few rounds of loads.
+  int upair = kSkip;
+  bool uniform = p.has_lora && z == 0;
+  if (uniform) {
+    for (int i = 0; i < WR; ++i) {  // LDS broadcast reads, the same for every lane
+      const int q = s_pair[wr * WR + i];
+      if (q < 0) continue;
+      if (upair < 0) upair = q;
+      else if (q != upair) { uniform = false; break; }
+    }
+    uniform = uniform && upair >= 0;
+  }
+  if (uniform) {
+    const int R = p.R, nks = 2 * R / 32;
+    const int l0 = wr * WR;
+    const u16 *Bq = nullptr;
+    for (int i = 0; i < WR; ++i)
+      if (s_pair[l0 + i] == upair) { Bq = s_bq[l0 + i]; break; }
+    const u16 *trow[NBR];  // the row's s * t (high parts, then remainders), or null
+#pragma unroll
+    for (int b = 0; b < NBR; ++b) {
+      const int li = l0 + b * 16 + (lane & 15);
+      trow[b] = s_pair[li] == upair ? p.tt + (size_t)s_row[li] * 2 * R : nullptr;
+    }
+    // kappa steps per round: two, or one where the accumulators leave no room
+    constexpr int ES = NBO >= 8 ? 1 : 2;
+    for (int ks0 = 0; ks0 < nks; ks0 += ES) {
+      uint4 bv[ES][NBO], tv[ES][NBR];
+#pragma unroll
+      for (int s = 0; s < ES; ++s) {
+        const int kap = (ks0 + s) * 32 + (lane >> 4) * 8;
+        const int r0 = kap >= R ? kap - R : kap;
+        const bool in = ks0 + s < nks;
+#pragma unroll
+        for (int bo = 0; bo < NBO; ++bo) {
+          const int o = min(o0 + wo * WO + bo * 16 + (lane & 15), p.n_out - 1);
+          bv[s][bo] = in ? ldg16(Bq + (size_t)o * R + r0) : z4();
+        }
+#pragma unroll
+        for (int b = 0; b < NBR; ++b) tv[s][b] = in && trow[b] ? ldg16(trow[b] + kap) : z4();
+      }
+#pragma unroll
+      for (int s = 0; s < ES; ++s) {
+        if (ks0 + s >= nks) break;
+#pragma unroll
+        for (int b = 0; b < NBR; ++b)
+#pragma unroll
+          for (int bo = 0; bo < NBO; ++bo) acc[bo][b] = mfma16(bv[s][bo], tv[s][b], acc[bo][b]);
+      }
+    }
+  } else if (p.has_lora && z == 0) {
     const int R = p.R, nks = 2 * R / 32;
     constexpr int G = NBO <= 2 ? 8 : (NBO <= 4 ? 4 : 2);
     const int myr = lane & 15;
@@ -135,25 +239,15 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
         const int l0 = wr * WR + br * 16;
         const int j = run_end(br, i);
         const u16 *Bq = s_bq[l0 + i];
-        const float sig = s_sig[l0 + i];
         const int kap = ks * 32 + (lane >> 4) * 8;
-        const int part = kap >= R;
-        const int r0 = kap - part * R;
+        const int r0 = kap >= R ? kap - R : kap;
 #pragma unroll
         for (int bo = 0; bo < NBO; ++bo) {
           const int o = min(o0 + wo * WO + bo * 16 + (lane & 15), p.n_out - 1);
           bv[g][bo] = ldg16(Bq + (size_t)o * R + r0);
         }
         const int grow = s_row[l0 + myr];
-        tv[g] = z4();
-        if (myr >= i && myr < j && grow >= 0) {
-          const float *tp = p.t + (size_t)grow * R + r0;
-          const f32x4 t0 = *(const f32x4 *)tp, t1 = *(const f32x4 *)(tp + 4);
-          tv[g] = make_uint4(pack2(hilo(sig * t0[0], part), hilo(sig * t0[1], part)),
-                             pack2(hilo(sig * t0[2], part), hilo(sig * t0[3], part)),
-                             pack2(hilo(sig * t1[0], part), hilo(sig * t1[1], part)),
-                             pack2(hilo(sig * t1[2], part), hilo(sig * t1[3], part)));
-        }
+        tv[g] = myr >= i && myr < j && grow >= 0 ? ldg16(p.tt + (size_t)grow * 2 * R + kap) : z4();
         ibr[g] = br;
         ++ns;
         if (++ks == nks) {  // next run
@@ -174,63 +268,53 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
     }
   }
 
-  // ---------------------------------------------------------- base contraction
-  const int kb = min(z * p.k_per_split, p.k_in);
-  const int ke = min(kb + p.k_per_split, p.k_in);
-  const int nstage = (ke - kb + 31) / 32;
-  const u16 *Wg = p.W + (size_t)tile.x * (size_t)p.w_group_stride;
-  // this lane's source row for each DMA it issues (the same in every stage)
-  const u16 *src[LPW];
+  // Stage st is in LDS for every wave: wait for this wave's DMAs (at most
+  // `younger` stages issued after it may stay in flight), zero the chunks
+  // this wave fetched past the k range, then the barrier.
+  auto landed = [&](int st, int younger) {
+    wait_stages<LPW, (NS > 2 ? NS - 2 : 0)>(younger);
+    const int k0 = kb + st * 64;
+    if (k0 + 64 > ke) {
 #pragma unroll
-  for (int j = 0; j < LPW; ++j) {
-    const int b = wave + NW * j;  // fragment of the stage
-    const u16 *rowp;
-    if (b < FO) {
-      const int o = min(o0 + b * 16 + (lane & 15), p.n_out - 1);
-      rowp = Wg + (size_t)o * p.w_row_stride;
-    } else {
-      int r = s_row[(b - FO) * 16 + (lane & 15)];
-      if (r < 0) r = s_row[0];
-      rowp = p.x + (size_t)r * p.x_row_stride;
+      for (int j = 0; j < LPW; ++j)
+        if (k0 + sch[j] >= ke) ring[st % NS][(wave + NW * j) * 64 + lane] = z4();
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     }
-    src[j] = rowp + (lane >> 4) * 8;
-  }
-  // Every wave issues exactly LPW DMA instructions per stage, so the vmcnt
-  // waits count stages exactly.  Lanes whose k chunk lies past the range read
-  // a valid piece of their row instead; the tail stage zeroes those LDS
-  // entries after it lands.
-  auto issue = [&](int st) {
-    const int k0 = kb + st * 32;
-    const int kk = k0 + (lane >> 4) * 8 < ke ? k0 : 0;
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) dma16(src[j] + kk, lds_addr(&ring[st % NS][wave + NW * j][0]));
+    block_barrier();
   };
-  if (nstage > 0) {
-    for (int st = 0; st < NS - 1 && st < nstage; ++st) issue(st);
-    for (int st = 0; st < nstage; ++st) {
-      // stage st has landed for this wave once at most min(NS-2, nstage-1-st)
-      // younger stages remain in flight
-      wait_stages<LPW, NS - 2>(min(NS - 2, nstage - 1 - st));
-      block_barrier();  // ... and for every wave
-      uint4(*slot)[64] = ring[st % NS];
-      const int k0 = kb + st * 32;
-      if (k0 + 32 > ke) {  // tail stage: zero what lies past the k range
-        if (k0 + (lane >> 4) * 8 >= ke)
-          for (int f = wave; f < SB; f += NW) slot[f][lane] = z4();
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-        block_barrier();
-      }
-      if (st + NS - 1 < nstage) issue(st + NS - 1);
-      uint4 af[NBO], bf[NBR];
+  // MFMA fragments of one 32-wide half h of a stage: lane l reads row l%16
+  // of the block, chunk 4h + l/16, at its swizzled slot.
+  uint4 af[2][NBO], bf[2][NBR];
+  auto fetch = [&](int st, auto hc) {
+    constexpr int h = decltype(hc)::value;
+    const uint4 *sl = ring[st % NS];
+    const int c = 4 * h + (lane >> 4);
 #pragma unroll
-      for (int bo = 0; bo < NBO; ++bo) af[bo] = slot[wo * NBO + bo][lane];
-#pragma unroll
-      for (int b = 0; b < NBR; ++b) bf[b] = slot[FO + wr * NBR + b][lane];
-#pragma unroll
-      for (int bo = 0; bo < NBO; ++bo)
-#pragma unroll
-        for (int b = 0; b < NBR; ++b) acc[bo][b] = mfma16(af[bo], bf[b], acc[bo][b]);
+    for (int bo = 0; bo < NBO; ++bo) {
+      const int r = (wo * NBO + bo) * 16 + (lane & 15);
+      af[h][bo] = sl[r * 8 + (c ^ ((r >> 1) & 7))];
     }
+#pragma unroll
+    for (int b = 0; b < NBR; ++b) {
+      const int r = BO + (wr * NBR + b) * 16 + (lane & 15);
+      bf[h][b] = sl[r * 8 + (c ^ ((r >> 1) & 7))];
+    }
+  };
+  auto mma = [&](auto hc) {
+    constexpr int h = decltype(hc)::value;
+#pragma unroll
+    for (int bo = 0; bo < NBO; ++bo)
+#pragma unroll
+      for (int b = 0; b < NBR; ++b) acc[bo][b] = mfma16(af[h][bo], bf[h][b], acc[bo][b]);
+  };
+  for (int st = 0; st < nstage; ++st) {
+    landed(st, min(NS - 2, nstage - 1 - st));
+    // every wave is done with stage st - 1: its ring slot takes stage st + NS - 1
+    if (st + NS - 1 < nstage) issue(st + NS - 1);
+    fetch(st, std::integral_constant<int, 0>{});
+    fetch(st, std::integral_constant<int, 1>{});  // read while the first half's MFMAs run
+    mma(std::integral_constant<int, 0>{});
+    mma(std::integral_constant<int, 1>{});
   }
 
   // ---------------------------------------------------------- split-K fixup
@@ -296,16 +380,17 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
 hipError_t launch_gemm(const GemmArgs &a, int to, int tr, hipStream_t st) {
   const int grid = a.max_mtiles * a.n_ntiles * a.splits;
   if (grid == 0) return hipSuccess;
+  // ring depth: as many 64-column stages as fit in about 128 KB of LDS
   if (to == 64 && tr == 64)
     hipLaunchKernelGGL((gemm_bf16_kernel<64, 64, 2, 2, 8>), dim3(grid), dim3(256), 0, st, a);
   else if (to == 128 && tr == 64)
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 64, 4, 1, 8>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 64, 4, 1, 6>), dim3(grid), dim3(256), 0, st, a);
   else if (to == 128 && tr == 128)
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, 6>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, 4>), dim3(grid), dim3(256), 0, st, a);
   else if (to == 256 && tr == 64)
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 64, 4, 1, 5>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 64, 4, 1, 3>), dim3(grid), dim3(256), 0, st, a);
   else if (to == 256 && tr == 256)
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 4>), dim3(grid), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 2>), dim3(grid), dim3(512), 0, st, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -46,37 +46,107 @@ __device__ int block_exscan(int *a, int L, int *wsum) {
   return total;
 }
 
-// Exclusive prefix of one int per thread across the block; *total gets the sum.
-__device__ int block_exclusive(int v0, int *wsum, int *total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int v = v0;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int u = __shfl_up(v, off, 64);
-    if (lane >= off) v += u;
+// ------------------------------------------------------------------ routing
+// Every row's route is computed once per workgroup into a packed LDS word:
+// (key + 1) << 13 | (pair + 2), key = the plan's sort key (-1: row not
+// written), pair = table index, kSkip or kDrop.  Keys and pairs are below
+// kMaxKeys = 4096.
+__device__ __forceinline__ int pk_key(int w) { return (w >> 13) - 1; }
+__device__ __forceinline__ int pk_pair(int w) { return (w & 0x1fff) - 2; }
+
+// Segment tables up to this many entries are copied to LDS for the routing.
+constexpr int kSegLds = 4096;
+__device__ __forceinline__ bool seg_in_lds(const Routing &rt) {
+  return rt.mode == kModeSegmented && rt.n_seg + 1 <= kSegLds;
+}
+
+// The segment of row r from an LDS copy of seg_indptr (binary search).
+__device__ __forceinline__ int segment_lds(const int *ip, int n_seg, int r) {
+  if (n_seg <= 0 || r < ip[0] || r >= ip[n_seg]) return -1;
+  int lo = 0, hi = n_seg - 1;  // last g with ip[g] <= r
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (ip[mid] <= r) lo = mid; else hi = mid - 1;
   }
-  if (lane == 63) wsum[wave] = v;
-  __syncthreads();
-  int pre = 0;
-  for (int w = 0; w < wave; ++w) pre += wsum[w];
-  *total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-  __syncthreads();
-  return pre + v - v0;
+  return lo;
 }
 
-// Sort key of a row: W group major, then adapter, the skip bucket last in
-// its group.  -1 for a row that is not written.
-__device__ __forceinline__ int row_key(const PrepArgs &a, int r, int *pair) {
-  int g, ad;
-  const int q = row_route(a.rt, a.rd, a.has_lora, r, &g, &ad);
-  *pair = q;
-  if (q == kDrop) return -1;
+// Routes rows row0 + tid + 256 j (j < 8) into pk[]: every load of the batch
+// (the slot inputs, then the three route tables) in flight together.  `seg`
+// is an LDS copy of seg_indptr (segmented calls), or null.
+__device__ __forceinline__ void route_all(const PrepArgs &a, int *pk, const int *seg, int row0) {
   const int ml = a.has_lora ? a.rd.max_loras : 0;
-  return g * (ml + 1) + (q >= 0 ? ad : ml);
+  const RouteDev &rd = a.rd;
+  const Routing &rt = a.rt;
+  {
+    const int r0 = row0 + (int)threadIdx.x;
+    int slot[8], expert[8], drop[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = r0 + 256 * j;
+      const bool live = r < a.n;
+      int sl = -1, ex = 0, dr = !live;
+      if (live && rt.mode == kModeDecode) {
+        sl = rt.seq_slot ? rt.seq_slot[r] : -1;
+      } else if (live && rt.mode == kModeSegmented) {
+        const int g = seg ? segment_lds(seg, rt.n_seg, r) : segment_of(rt.seg_indptr, rt.n_seg, r);
+        dr = g < 0;
+        sl = g < 0 ? -1 : rt.seg_slot[g];
+      } else if (live) {
+        const int e = rt.indices[r];
+        dr = e < 0 || e >= rt.n_experts;
+        ex = dr ? 0 : e;
+        sl = a.has_lora && !dr ? rt.token_slot[r / rt.top_k] : -1;
+      }
+      slot[j] = sl;
+      expert[j] = ex;
+      drop[j] = dr;
+    }
+    uint64_t ta[8], tb[8];
+    float sc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {  // the three tables, index 0 standing in for rows without a slot
+      const bool in = a.has_lora && !drop[j] && slot[j] >= 0 && slot[j] < rd.max_loras;
+      const int idx = in ? slot[j] * rd.n_experts + expert[j] : 0;
+      ta[j] = in ? (uint64_t)(uintptr_t)rd.a_table[idx] : 0ull;
+      tb[j] = in ? (uint64_t)(uintptr_t)rd.b_table[idx] : 0ull;
+      sc[j] = in ? rd.scale_table[slot[j]] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = r0 + 256 * j;
+      const bool ok = ta[j] != 0ull && tb[j] != 0ull && sc[j] != 0.0f;
+      const int q = drop[j] ? kDrop : (ok ? slot[j] * rd.n_experts + expert[j] : kSkip);
+      const int key = drop[j] ? -1 : expert[j] * (ml + 1) + (q >= 0 ? slot[j] : ml);
+      if (r < a.n) pk[r] = ((key + 1) << 13) | (q + 2);
+    }
+  }
 }
 
-__device__ void plan_block(const PrepArgs &a, int *lds) {
-  const int tid = threadIdx.x;
+// Adds to cnt[k] the number of rows with k = f(pk[r]) >= 0.  Each wave takes
+// 64 rows at a time: the values held by many of its lanes are counted with
+// one atomic each (a prefill segment, an expert), the rest lane by lane.
+template <typename F>
+__device__ __forceinline__ void count_rows(const int *pk, int n, int *cnt, F f) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int r0 = wave * 64; r0 < n; r0 += 256) {
+    const int r = r0 + lane;
+    int k = r < n ? f(pk[r]) : -1;
+    uint64_t todo = __ballot(k >= 0);
+    for (int round = 0; round < 2 && todo; ++round) {
+      const int leader = __ffsll((unsigned long long)todo) - 1;
+      const int v = __builtin_amdgcn_readlane(k, leader);
+      const uint64_t m = __ballot(k == v);
+      if (lane == leader) atomicAdd(&cnt[v], (int)__popcll(m));
+      if (k == v) k = -1;
+      todo &= ~m;
+    }
+    if (k >= 0) atomicAdd(&cnt[k], 1);
+  }
+}
+
+__device__ __forceinline__ void plan_block(const PrepArgs &a, int *lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ml = a.has_lora ? a.rd.max_loras : 0;
   const int NG = a.rt.n_experts;
   const int NK = NG * (ml + 1);
@@ -84,26 +154,57 @@ __device__ void plan_block(const PrepArgs &a, int *lds) {
   int *fill = cnt + NK + 1;  // [NK]
   int *gt = fill + NK;       // [NG+1] tiles per group, then tile starts
   int *wsum = gt + NG + 1;   // [4]
+  int *pk = wsum + 4;        // [n] the rows' packed routes
   for (int k = tid; k < NK + 1; k += 256) cnt[k] = 0;
   for (int k = tid; k < NK; k += 256) fill[k] = 0;
-  __syncthreads();
-  for (int r = tid; r < a.n; r += 256) {
-    int q;
-    const int key = row_key(a, r, &q);
-    if (key >= 0) atomicAdd(&cnt[key], 1);
+  if (a.routes) {  // eight loads per thread in flight at a time
+    for (int r0 = tid; r0 < a.n; r0 += 256 * 8) {
+      int v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = r0 + 256 * j < a.n ? a.routes[r0 + 256 * j] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (r0 + 256 * j < a.n) pk[r0 + 256 * j] = v[j];
+    }
+  } else {  // no route buffer (the standalone shrink): route here
+    for (int r0 = 0; r0 < a.n; r0 += 256 * 8) route_all(a, pk, nullptr, r0);
   }
+  __syncthreads();
+  count_rows(pk, a.n, cnt, [](int w) { return pk_key(w); });
   __syncthreads();
   const int total = block_exscan(cnt, NK, wsum);
   if (tid == 0) cnt[NK] = total;
   __syncthreads();
-  for (int r = tid; r < a.n; r += 256) {
-    int q;
-    const int key = row_key(a, r, &q);
-    if (key < 0) continue;
-    const int pos = cnt[key] + atomicAdd(&fill[key], 1);
-    a.plan.pos_row[pos] = r;
-    a.plan.pos_pair[pos] = q;
+  // scatter: the keys many of a wave's 64 rows share take one atomic each
+  // (those rows keep their order), the rest one atomic per row
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int r0 = wave * 64; r0 < a.n; r0 += 256) {
+    const int r = r0 + lane;
+    const int w = r < a.n ? pk[r] : 0;
+    int k = r < a.n ? pk_key(w) : -1;
+    uint64_t todo = __ballot(k >= 0);
+    for (int round = 0; round < 2 && todo; ++round) {
+      const int leader = __ffsll((unsigned long long)todo) - 1;
+      const int v = __builtin_amdgcn_readlane(k, leader);
+      const uint64_t m = __ballot(k == v);
+      int base = 0;
+      if (lane == leader) base = atomicAdd(&fill[v], (int)__popcll(m));
+      base = __builtin_amdgcn_readlane(base, leader);
+      if (k == v) {
+        const int pos = cnt[v] + base + (int)__popcll(m & below);
+        a.plan.pos_row[pos] = r;
+        a.plan.pos_pair[pos] = pk_pair(w);
+        k = -1;
+      }
+      todo &= ~m;
+    }
+    if (k >= 0) {
+      const int pos = cnt[k] + atomicAdd(&fill[k], 1);
+      a.plan.pos_row[pos] = r;
+      a.plan.pos_pair[pos] = pk_pair(w);
+    }
   }
+  __syncthreads();
   // row tiles: group g owns sorted positions [cnt[g*(ml+1)], cnt[(g+1)*(ml+1)])
   for (int g = tid; g < NG; g += 256) {
     const int len = cnt[(g + 1) * (ml + 1)] - cnt[g * (ml + 1)];
@@ -121,16 +222,24 @@ __device__ void plan_block(const PrepArgs &a, int *lds) {
 }
 
 // Pair of row r (or kSkip / kDrop), from the LDS cache when the batch fits it.
-__device__ __forceinline__ int cached_route(const PrepArgs &a, const int *qv, int r) {
-  if (qv) return qv[r];
-  int g, ad;
-  return row_route(a.rt, a.rd, true, r, &g, &ad);
-}
 
 // One shrink unit: up to 16 rows sharing one pair, over one k chunk.
 // t_part[kz][row][0:R] = x[row, chunk] . A_pair[:, chunk]^T; the consumer sums
 // the k_splits partials in kz order.
-__device__ void shrink_unit(const PrepArgs &a, int u, int *lds) {
+
+// The GEMM's copy of t: s * t split into a bf16 high part and the bf16
+// rounding of what it leaves over (hi + lo carries s * t to ~16 bits).
+__device__ __forceinline__ void store_tt(u16 *tt, int R, int row, int r, float s, const float *v, int nv) {
+  u16 *dst = tt + (size_t)row * 2 * R;
+  for (int e = 0; e < nv; ++e) {
+    const float w = s * v[e];
+    const u16 hi = f2bf(w);
+    dst[r + e] = hi;
+    dst[R + r + e] = f2bf(w - bf2f(hi));
+  }
+}
+
+__device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = a.n_pairs;
   const int KS = a.k_splits;
@@ -139,18 +248,25 @@ __device__ void shrink_unit(const PrepArgs &a, int u, int *lds) {
   int *cnt = lds;             // [P]
   int *wsum = cnt + P;        // [4]
   int *info = wsum + 4;       // [4]
-  int *rows = info + 4;       // [16]
-  f32x4 *red = (f32x4 *)(lds + ((P + 24 + 3) & ~3));  // [3][4][64]
-  int *qv = a.n <= kRowCache ? (int *)(red + 3 * 4 * 64) : nullptr;  // [n]
+  int *rows = info + 4;       // [kShrinkRows]
+  f32x4 *red = (f32x4 *)(lds + ((P + 8 + kShrinkRows + 3) & ~3));  // [3][4][kShrinkRows/16][64]
+  int *pk = (int *)(red + 3 * 4 * (kShrinkRows / 16) * 64);  // [n] the rows' packed routes
 
   for (int p = tid; p < P; p += 256) cnt[p] = 0;
-  __syncthreads();
-  for (int r = tid; r < a.n; r += 256) {
-    int g, ad;
-    const int q = row_route(a.rt, a.rd, true, r, &g, &ad);
-    if (qv) qv[r] = q;
-    if (q >= 0) atomicAdd(&cnt[q], 1);
+  if (a.routes) {  // eight loads per thread in flight at a time
+    for (int r0 = tid; r0 < a.n; r0 += 256 * 8) {
+      int v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = r0 + 256 * j < a.n ? a.routes[r0 + 256 * j] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (r0 + 256 * j < a.n) pk[r0 + 256 * j] = v[j];
+    }
+  } else {  // no route buffer (the standalone shrink): route here
+    for (int r0 = 0; r0 < a.n; r0 += 256 * 8) route_all(a, pk, nullptr, r0);
   }
+  __syncthreads();
+  count_rows(pk, a.n, cnt, [](int w) { return pk_pair(w); });
   __syncthreads();
   for (int p = tid; p < P; p += 256) cnt[p] = (cnt[p] + kShrinkRows - 1) / kShrinkRows;
   __syncthreads();
@@ -169,25 +285,53 @@ __device__ void shrink_unit(const PrepArgs &a, int u, int *lds) {
   const int pstar = info[0];
   const int first = info[1] * kShrinkRows;
 
-  // rows of pstar, in row order, ranks [first, first + 16)
-  const int m = (a.n + 255) / 256;
-  const int rb = min(tid * m, a.n), re = min(rb + m, a.n);
-  int c = 0;
-  for (int r = rb; r < re; ++r) c += cached_route(a, qv, r) == pstar;
-  int total_rows;
-  int k = block_exclusive(c, wsum, &total_rows);
-  for (int r = rb; r < re && k < first + kShrinkRows; ++r) {
-    if (cached_route(a, qv, r) != pstar) continue;
-    if (k >= first) rows[k - first] = r;
-    ++k;
+  // rows of pstar in row order, ranks [first, first + kShrinkRows): thread t
+  // counts them in its 16-row span, an exclusive scan gives its first rank
+  {
+    constexpr int SPAN = 16;
+    int c = 0;
+    // every thread runs the same number of rounds (the barriers inside)
+    for (int base = 0; base < a.n; base += 256 * SPAN) {
+      const int r0 = base + tid * SPAN;
+      int mine = 0;
+#pragma unroll
+      for (int j = 0; j < SPAN; ++j) mine += r0 + j < a.n && pk_pair(pk[r0 + j]) == pstar;
+      int pre = mine;  // inclusive scan over the block, then over earlier spans
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(pre, off, 64);
+        if (lane >= off) pre += t;
+      }
+      if (lane == 63) wsum[wave] = pre;
+      __syncthreads();
+      int wpre = 0;
+      for (int w = 0; w < wave; ++w) wpre += wsum[w];
+      const int round_total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+      int k = c + wpre + pre - mine;  // rank of this span's first match
+      for (int j = 0; j < SPAN && mine; ++j) {
+        if (r0 + j < a.n && pk_pair(pk[r0 + j]) == pstar) {
+          if (k >= first && k < first + kShrinkRows) rows[k - first] = r0 + j;
+          ++k;
+        }
+      }
+      c += round_total;
+      __syncthreads();
+    }
+    if (tid == 0) info[3] = c;
   }
   __syncthreads();
-  const int nrows = min(kShrinkRows, total_rows - first);
+  const int nrows = min(kShrinkRows, info[3] - first);
 
   const u16 *A = (const u16 *)a.rd.a_table[pstar];
   const int R = a.rd.R, nrb = R / 16, K = a.k_in;
-  const int myrow = (lane & 15) < nrows ? rows[lane & 15] : -1;
-  const u16 *xr = myrow >= 0 ? a.x + (size_t)myrow * a.x_stride : nullptr;
+  const float sig = a.rd.scale_table[pstar / a.rd.n_experts];
+  const int G = (nrows + 15) / 16;  // row groups of 16 (<= kShrinkRows / 16)
+  const u16 *xr[kShrinkRows / 16];
+#pragma unroll
+  for (int g = 0; g < kShrinkRows / 16; ++g) {
+    const int j = g * 16 + (lane & 15);
+    xr[g] = g < G && j < nrows ? a.x + (size_t)rows[j] * a.x_stride : nullptr;
+  }
   // this unit's k chunk, cut in 32-wide steps; wave w takes steps w, w+4, ...
   const int chunk = ((K + KS - 1) / KS + 127) / 128 * 128;
   const int kc0 = min(kz * chunk, K), kc1 = min(kc0 + chunk, K);
@@ -197,53 +341,68 @@ __device__ void shrink_unit(const PrepArgs &a, int u, int *lds) {
   // partial through device-coherent (sc1) stores and the last of the unit's
   // k_splits workgroups to arrive sums them in chunk order.
   float *tout = KS == 1 ? a.t_final : a.t + (size_t)kz * a.n * R;
+  constexpr int GR = kShrinkRows / 16;
 
-  for (int rb0 = 0; rb0 < nrb; rb0 += 4) {
+  for (int rb0 = 0; rb0 < nrb; rb0 += 4) {  // four rank blocks x the row groups at a time
     const int nb = min(4, nrb - rb0);
-    f32x4 acc[4];
+    f32x4 acc[4][GR];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int g = 0; g < GR; ++g) acc[j][g] = f32x4{0.f, 0.f, 0.f, 0.f};
     const u16 *Ab = A + (size_t)(rb0 * 16 + (lane & 15)) * K;
-    for (int s0 = wave; s0 < nsteps; s0 += 4 * 8) {
-      uint4 xv[8], av[8][4];
+    for (int s0 = wave; s0 < nsteps; s0 += 4 * 4) {  // four steps per wave in flight
+      uint4 xv[4][GR], av[4][4];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
+      for (int s = 0; s < 4; ++s) {
         const int kk = kc0 + (s0 + 4 * s) * 32 + koff;
         const bool in = kk < kc1;
-        xv[s] = (xr && in) ? ldg16(xr + kk) : z4();
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          av[s][j] = (in && j < nb) ? ldg16(Ab + (size_t)j * 16 * K + kk) : z4();
+        for (int g = 0; g < GR; ++g) xv[s][g] = (xr[g] && in) ? ldg16(xr[g] + kk) : z4();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) av[s][j] = (in && j < nb) ? ldg16(Ab + (size_t)j * 16 * K + kk) : z4();
       }
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (j < nb) acc[j] = mfma16(av[s][j], xv[s], acc[j]);
+#pragma unroll
+          for (int g = 0; g < GR; ++g)
+            if (j < nb && g < G) acc[j][g] = mfma16(av[s][j], xv[s][g], acc[j][g]);
     }
     if (wave > 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) red[((wave - 1) * 4 + j) * 64 + lane] = acc[j];
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < GR; ++g) red[(((wave - 1) * 4 + j) * GR + g) * 64 + lane] = acc[j][g];
     }
     __syncthreads();
-    if (wave == 0 && myrow >= 0) {
+    if (wave == 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (j >= nb) continue;
-        f32x4 v = acc[j];
-        v += red[(0 * 4 + j) * 64 + lane];
-        v += red[(1 * 4 + j) * 64 + lane];
-        v += red[(2 * 4 + j) * 64 + lane];
-        // D column = lane%16 (the row), D rows = ranks 4*(lane/16) .. +3 of block rb0+j
-        float *dst = tout + (size_t)myrow * R + (rb0 + j) * 16 + (lane >> 4) * 4;
-        if (KS == 1) {
-          *(f32x4 *)dst = v;
-        } else {
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            __hip_atomic_store(dst + e, v[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int g = 0; g < GR; ++g) {
+          const int i = g * 16 + (lane & 15);
+          if (j >= nb || i >= nrows) continue;
+          f32x4 v = acc[j][g];  // fixed order: wave 0, 1, 2, 3
+          v += red[((0 * 4 + j) * GR + g) * 64 + lane];
+          v += red[((1 * 4 + j) * GR + g) * 64 + lane];
+          v += red[((2 * 4 + j) * GR + g) * 64 + lane];
+          // D column = lane%16 (the row), D rows = ranks 4*(lane/16) .. +3 of block rb0+j
+          float *dst = tout + (size_t)rows[i] * R + (rb0 + j) * 16 + (lane >> 4) * 4;
+          if (KS == 1) {
+            *(f32x4 *)dst = v;
+            if (a.tt) {
+              const float vv[4] = {v[0], v[1], v[2], v[3]};
+              store_tt(a.tt, R, rows[i], (rb0 + j) * 16 + (lane >> 4) * 4, sig, vv, 4);
+            }
+          } else {
+            const uint64_t lo = (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32);
+            const uint64_t hi = (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32);
+            __hip_atomic_store((uint64_t *)dst, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store((uint64_t *)(dst + 2), hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
-      }
     }
     __syncthreads();
   }
@@ -255,15 +414,43 @@ __device__ void shrink_unit(const PrepArgs &a, int u, int *lds) {
               (unsigned)(KS - 1);
   __syncthreads();
   if (!info[2]) return;
-  for (int e = tid; e < nrows * R; e += 256) {
+  // the last of the unit's workgroups: t = sum of the k-chunk partials in
+  // chunk order, every chunk's load in flight together (8 bytes at a time)
+  for (int e = tid * 2; e < nrows * R; e += 256 * 2) {
     const int i = e / R, r = e - i * R;
     const size_t off = (size_t)rows[i] * R + r;
-    float v = 0.f;
-    for (int z = 0; z < KS; ++z)
-      v += __hip_atomic_load(a.t + (size_t)z * a.n * R + off, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    a.t_final[off] = v;
+    uint64_t v[kMaxShrinkSplits];
+#pragma unroll
+    for (int z = 0; z < kMaxShrinkSplits; ++z)
+      v[z] = z < KS ? __hip_atomic_load((uint64_t *)(a.t + (size_t)z * a.n * R + off), __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT)
+                    : 0ull;
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int z = 0; z < kMaxShrinkSplits; ++z) {
+      if (z >= KS) break;
+      s0 += __uint_as_float((uint32_t)v[z]);
+      s1 += __uint_as_float((uint32_t)(v[z] >> 32));
+    }
+    *(float2 *)(a.t_final + off) = make_float2(s0, s1);
+    if (a.tt) {
+      const float vv[2] = {s0, s1};
+      store_tt(a.tt, R, rows[i], r, sig, vv, 2);
+    }
   }
   if (tid == 0) __hip_atomic_store(&a.counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+
+// Every row's packed route, once per call (the plan and the shrink units read
+// it instead of routing all rows again in each workgroup).
+__global__ __launch_bounds__(256) void route_kernel(PrepArgs a) {
+  __shared__ int seg[kSegLds];
+  const bool sl = seg_in_lds(a.rt);
+  if (sl)
+    for (int g = threadIdx.x; g <= a.rt.n_seg; g += 256) seg[g] = a.rt.seg_indptr[g];
+  __syncthreads();
+  route_all(a, a.routes, sl ? seg : nullptr, (int)blockIdx.x * (256 * 8));
 }
 
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
@@ -279,9 +466,9 @@ size_t prep_lds_bytes(const PrepArgs &a) {
   const int ml = a.has_lora ? a.rd.max_loras : 0;
   const int NG = a.rt.n_experts;
   const int NK = NG * (ml + 1);
-  size_t plan = a.do_plan ? (size_t)(2 * NK + NG + 8) * 4 : 0;
-  size_t shr = a.n_units ? (size_t)((a.n_pairs + 24 + 3) & ~3) * 4 + 3 * 4 * 64 * 16 +
-                               (a.n <= kRowCache ? (size_t)a.n * 4 : 0)
+  size_t plan = a.do_plan ? (size_t)(2 * NK + NG + 8 + a.n) * 4 : 0;
+  size_t shr = a.n_units ? (size_t)((a.n_pairs + 8 + kShrinkRows + 3) & ~3) * 4 + 3 * 4 * (kShrinkRows / 16) * 64 * 16 +
+                               (size_t)a.n * 4
                          : 0;
   return plan > shr ? plan : shr;
 }
@@ -289,6 +476,7 @@ size_t prep_lds_bytes(const PrepArgs &a) {
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st) {
   const int grid = a.do_plan + a.n_units * a.k_splits;
   if (grid == 0) return hipSuccess;
+  if (a.routes) hipLaunchKernelGGL(route_kernel, dim3((a.n + 2047) / 2048), dim3(256), 0, st, a);
   hipLaunchKernelGGL(prep_kernel, dim3(grid), dim3(256), prep_lds_bytes(a), st, a);
   return hipGetLastError();
 }

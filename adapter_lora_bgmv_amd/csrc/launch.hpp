@@ -28,6 +28,7 @@ struct PrepArgs {
   int n;
   float *t;        // [k_splits][n][R] partial shrink sums (k_splits > 1)
   float *t_final;  // [n][R] the shrink's output
+  u16 *tt;         // [n][2R] or null: s_pair * t as bf16, high parts then remainders, for the GEMM
   unsigned *counters;  // [n_units] arrival counters (k_splits > 1), zero between calls
   int k_splits;    // k chunks per shrink unit
   int n_pairs;    // table entries = max_loras * n_experts
@@ -35,6 +36,7 @@ struct PrepArgs {
   PlanDev plan;
   int tile_rows;  // main kernel rows per tile
   int n_units;    // shrink units (grid = do_plan + n_units * k_splits)
+  int *routes;    // [n] every row's packed route (the route kernel writes it)
 };
 
 struct GemmArgs {
@@ -52,7 +54,8 @@ struct GemmArgs {
   const void *const *b_table;
   const float *scale_table;
   int n_experts;
-  const float *t;  // [n][R] the shrink's output
+  const u16 *tt;   // [n][2R] the shrink's output scaled by the pair's scale, bf16 high parts
+                   // (columns 0..R-1) and what they leave over (R..2R-1)
   int R;
   int splits, k_per_split;
   float *partials;
@@ -94,11 +97,11 @@ constexpr int kDecodeBatch = 4;
 constexpr int kDecodeMaxChunks = kDecodeMaxSplit;
 
 // Rows per shrink unit.
-constexpr int kShrinkRows = 16;
+constexpr int kShrinkRows = 64;
+// Largest k split of the shrink units.
+constexpr int kMaxShrinkSplits = 8;
 // Largest key space the one-workgroup plan handles (LDS histogram).
 constexpr int kMaxKeys = 4096;
-// Batches up to this many rows keep their resolved routes in LDS during the shrink.
-constexpr int kRowCache = 8192;
 
 size_t prep_lds_bytes(const PrepArgs &a);
 

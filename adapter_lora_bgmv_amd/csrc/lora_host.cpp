@@ -83,9 +83,9 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
   c.decode = op == LORA_OP_APPLY && n <= kDecodeMaxRows;
   c.units = R > 0 ? (n + kShrinkRows - 1) / kShrinkRows + std::min(n, n_pairs) : 0;
   // Shrink k chunks: enough workgroups to cover the chip for small batches,
-  // chunks of at least 128 columns.  A function of (n, k_in) only, so the
+  // chunks of at least 256 columns.  A function of (n, k_in) only, so the
   // workspace size does not depend on the routing.
-  c.t_splits = R > 0 ? clampi(512 / ((n + kShrinkRows - 1) / kShrinkRows), 1, std::min(8, std::max(1, k_in / 128))) : 1;
+  c.t_splits = R > 0 ? clampi(512 / ((n + kShrinkRows - 1) / kShrinkRows), 1, std::min(kMaxShrinkSplits, std::max(1, k_in / 256))) : 1;
   if (c.decode) {
     c.to = kDecodeTileOut; c.tr = kDecodeMaxRows; c.splits = clampi(k_in / 1024, 1, 8);
   } else if (op == LORA_OP_MOE_GATHER) {
@@ -112,7 +112,7 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
 }
 
 struct WsLayout {
-  size_t counters, shrink_counters, pos_row, pos_pair, tiles, n_tiles, t, t_final, partials, rows, total;
+  size_t counters, shrink_counters, pos_row, pos_pair, routes, tiles, n_tiles, t, t_final, tt, partials, rows, total;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -134,10 +134,12 @@ WsLayout ws_layout(const Cfg &c, int n, int R, int k_in) {
   w.shrink_counters = off; off = up256(off + (c.t_splits > 1 ? (size_t)c.units * 4 : 0));
   w.pos_row = off; off = up256(off + (size_t)n * 4);
   w.pos_pair = off; off = up256(off + (size_t)n * 4);
+  w.routes = off; off = up256(off + (size_t)n * 4);
   w.tiles = off; off = up256(off + (size_t)c.max_mtiles * 16);
   w.n_tiles = off; off = up256(off + 16);
   w.t = off; off = up256(off + (c.t_splits > 1 ? (size_t)c.t_splits * n * R * 4 : 0));
   w.t_final = off; off = up256(off + (size_t)n * R * 4);
+  w.tt = off; off = up256(off + (size_t)n * R * 4);  // [n][2R] bf16
   w.partials = off;
   off = up256(off + (c.splits > 1 ? ntile * c.splits * c.to * c.tr * 4 : 0));
   w.total = off;
@@ -309,6 +311,8 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
   pa.n = (int)n;
   pa.t = (float *)(ws + L.t);
   pa.t_final = (float *)(ws + L.t_final);
+  pa.tt = R > 0 ? (u16 *)(ws + L.tt) : nullptr;
+  pa.routes = (int *)(ws + L.routes);
   pa.counters = (unsigned *)(ws + L.shrink_counters);
   pa.k_splits = c.t_splits;
   pa.n_pairs = n_pairs;
@@ -337,7 +341,7 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
   ga.b_table = rd.b_table;
   ga.scale_table = rd.scale_table;
   ga.n_experts = rd.n_experts > 0 ? rd.n_experts : 1;
-  ga.t = pa.t_final;
+  ga.tt = pa.tt;
   ga.R = R;
   ga.splits = c.splits;
   ga.k_per_split = c.k_per_split;
