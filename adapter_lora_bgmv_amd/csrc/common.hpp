@@ -59,6 +59,28 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
                : "memory");
 }
 
+// Device-coherent 16-byte accesses (cache policy sc1) through a buffer
+// resource over [base, base + bytes): stores write through to the memory
+// side that every XCD shares and loads read from there, so results pass
+// between workgroups on different XCDs without an L2-wide writeback or
+// invalidate.  A wave's consecutive lanes at consecutive 16-byte offsets
+// make whole-line transfers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000);
+}
+constexpr int kCachePolicySc1 = 16;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+// The byte offset is voff (per lane) + soff (the same for the whole wave).
+__device__ __forceinline__ void st16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                              f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)voff, (int)soff,
+                                         kCachePolicySc1);
+}
+__device__ __forceinline__ f32x4 ld16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(f32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kCachePolicySc1));
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }

@@ -30,10 +30,13 @@
 // row's accumulator is still +0 when the base contraction begins, so its
 // output is bit-identical to the base-only launch of the same shape.
 //
-// Split-K: `splits` workgroups share a tile, each over its own k range; the
-// last to arrive (a device-scope counter) sums the partial tiles in split
+// Split-K: the workgroups that share a tile each take their own k range;
+// the last to arrive (a device-scope counter) sums the partial tiles in k
 // order and writes y, so results do not depend on arrival order.  The
-// extension always runs in split 0.
+// extension runs in the tile's last contributor (in k order), first thing in
+// its range.  A base-only accumulator that starts at +0 never ends at -0, so
+// the +0 the extension leaves in a skipped row's partial changes no sum.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -54,7 +57,10 @@ __device__ __forceinline__ void wait_stages(int stages_younger) {
   wait_vmcnt<0>();
 }
 
-template <int BO, int BR, int WGO, int WGR, int NS>
+// MODE: kOneTile (a workgroup per tile), kSplitK (classic split-K), kStreamK.
+enum { kOneTile = 0, kSplitK = 1, kStreamK = 2 };
+
+template <int BO, int BR, int WGO, int WGR, int NS, int MODE>
 __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
   constexpr int NW = WGO * WGR;
   constexpr int WO = BO / WGO, WR = BR / WGR;  // wave tile
@@ -75,28 +81,49 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wo = wave % WGO, wr = wave / WGO;
-  // Tile order: the chip hands workgroups to its 8 XCDs in turn, each XCD
-  // with its own L2.  So the workgroups of one XCD get a contiguous range of
-  // logical ids, and consecutive ids walk the output tiles in groups of up to
-  // 8 row tiles (rows fastest): an XCD's workgroups share a few W tiles and a
-  // few x tiles, which its L2 then serves.  The split index is the fastest,
-  // so the split-0 workgroups (the LoRA extension) spread over every XCD.
-  const int mtiles = *p.plan.n_tiles;  // row tiles the plan made (<= max_mtiles)
-  const int ntile_all = mtiles * p.n_ntiles;
-  const int grid = ntile_all * p.splits;
+  // Work partition.  A unit is one 64-wide k stage of one output tile; the
+  // tiles' units are numbered tile by tile, and workgroup w takes units
+  // [w U / G, (w+1) U / G).  With G = tiles x splits that is the classic
+  // split-K (each tile cut into the same `splits` k ranges, whatever the tile
+  // count); in stream-K mode G is one workgroup per CU and a workgroup's range
+  // may end inside a tile and go on into the next, so every CU gets the same
+  // number of stages and no second wave of workgroups trails the first.
+  // Row tiles: the plan's count (<= max_mtiles).  Stream-K partitions the
+  // largest count the call can make, so that the partition, and with it the
+  // partial tiles the workspace must hold, is fixed by the shapes alone; the
+  // units of tiles the plan did not make are skipped.
+  const int mreal = *p.plan.n_tiles;
+  const int mtiles = MODE == kStreamK ? p.max_mtiles : mreal;
+  const int ntiles = mtiles * p.n_ntiles;
+  const int nst = (p.k_in + 63) / 64;
+  const long long U = (long long)ntiles * nst;
+  const int G = MODE == kStreamK ? (int)min((long long)p.grid, U) : ntiles * p.splits;
   const int b = blockIdx.x;
-  if (b >= grid) return;
-  const int xq = grid / 8, xr = grid % 8, xcd = b % 8;
-  const int id = xcd * xq + min(xcd, xr) + b / 8;  // each XCD: a contiguous id range
-  const int z = id % p.splits;
-  const int r = id / p.splits;
-  const int gm0 = r / (8 * p.n_ntiles) * 8;  // first row tile of the group
+  if (b >= G) return;
+  // The chip hands workgroups to its 8 XCDs in turn, each XCD with its own
+  // L2: the workgroups of one XCD get a contiguous range of w, so they work
+  // on neighbouring tiles, which its L2 then serves.
+  const int xq = G / 8, xr = G % 8, xcd = b % 8;
+  const int w = xcd * xq + min(xcd, xr) + b / 8;
+  const long long u_beg = MODE == kStreamK ? (long long)w * U / G : 0;
+  const long long u_end = MODE == kStreamK ? (long long)(w + 1) * U / G : 0;
+  // the workgroup whose range holds unit u
+  auto owner = [&](long long u) { return (int)(((u + 1) * G - 1) / U); };
+
+  // One segment of the workgroup's range: tile t, its stages [sb, se);
+  // wf..wl are the tile's contributors.
+  auto segment = [&](int seg, int t, int sb, int se, int wf, int wl) {
+  // Tile order: groups of up to 8 row tiles, rows fastest, so consecutive
+  // tiles share W tiles and x tiles.
+  const int gm0 = t / (8 * p.n_ntiles) * 8;  // first row tile of the group
   const int gsz = min(8, mtiles - gm0);
-  const int rr = r - gm0 * p.n_ntiles;
-  const int mt = gm0 + rr % gsz;
-  const int nt = rr / gsz;
+  const int tg = t - gm0 * p.n_ntiles;  // place within the group
+  const int mt = gm0 + tg % gsz;
+  const int nt = tg / gsz;
+  if (mt >= mreal) return;  // every contributor skips it alike
   const int4 tile = p.plan.tiles[mt];
   const int o0 = nt * BO;
+  if (seg > 0) __syncthreads();  // the previous tile is done with s_row and the ring
   for (int i = tid; i < BR; i += NW * 64) {
     const bool in = i < tile.z;
     const int q = in ? p.plan.pos_pair[tile.y + i] : kSkip;
@@ -113,9 +140,9 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
     for (int b = 0; b < NBR; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // ---------------------------------------------------------- base contraction
-  const int kb = min(z * p.k_per_split, p.k_in);
-  const int ke = min(kb + p.k_per_split, p.k_in);
-  const int nstage = (ke - kb + 63) / 64;
+  const int kb = sb * 64;
+  const int ke = min(se * 64, p.k_in);
+  const int nstage = se - sb;
   const u16 *Wg = p.W + (size_t)tile.x * (size_t)p.w_group_stride;
   // Each DMA instruction moves 8 whole 128-byte row segments (full cache
   // lines): lane l takes row 8i + l/8 of the stage and the chunk that belongs
@@ -160,8 +187,12 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
   // prefill segment, an expert's rows of one adapter), the B fragments of a
   // kappa step serve all NBR row blocks: each step loads them once and the
   // extension is a few rounds of loads.
+  // The tile's last contributor (in k order) runs it, at the start of its
+  // range, where it delays no other segment of its own: its range begins in
+  // this tile whenever the tile has more than one contributor.
+  const bool do_ext = p.has_lora && w == wl;
   int upair = kSkip;
-  bool uniform = p.has_lora && z == 0;
+  bool uniform = do_ext;
   if (uniform) {
     for (int i = 0; i < WR; ++i) {  // LDS broadcast reads, the same for every lane
       const int q = s_pair[wr * WR + i];
@@ -209,9 +240,9 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
           for (int bo = 0; bo < NBO; ++bo) acc[bo][b] = mfma16(bv[s][bo], tv[s][b], acc[bo][b]);
       }
     }
-  } else if (p.has_lora && z == 0) {
+  } else if (do_ext) {
     const int R = p.R, nks = 2 * R / 32;
-    constexpr int G = NBO <= 2 ? 8 : (NBO <= 4 ? 4 : 2);
+    constexpr int G = NBO <= 2 ? 8 : (NBO <= 4 ? 4 : 1);
     const int myr = lane & 15;
     int br = 0, i = 0, ks = 0;  // iterator: next item to load
     auto run_end = [&](int b, int i0) {
@@ -318,47 +349,52 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
   }
 
   // ---------------------------------------------------------- split-K fixup
-  if (p.splits > 1) {
+  if (MODE != kOneTile && wf != wl) {
+    // Every contributor stores its partial tile, then moves the tile's
+    // arrival counter; the last to arrive sums the partials in k order (so
+    // the result does not depend on arrival order) and writes y.  A
+    // contributor's partial of its first tile sits in slot w, of its last
+    // tile in slot G + w.
     constexpr int TT = BO * BR;
-    const int tl = mt * p.n_ntiles + nt;
-    float *part = p.partials + (size_t)tl * p.splits * TT;
-    // Partials travel through device-coherent (sc1) stores and loads, so no
-    // L2-wide writeback or invalidate is needed: the stores are complete
-    // (s_waitcnt) before the arrival counter moves, and the last arrival
-    // reads them coherently.
+    // fragment (bo, br) of wave v sits at byte ((v NBO + bo) NBR + br) KB, lane l at +16 l
+    const int wbase = __builtin_amdgcn_readfirstlane(wave) * NBO * NBR * 1024;
+    const auto slot_rsrc = [&](int cw) {
+      const int first = MODE == kStreamK ? (int)((long long)cw * U / G / nst) : t;
+      // the same for every lane: keeps the resource in scalar registers
+      const int slot = __builtin_amdgcn_readfirstlane(cw + (t == first ? 0 : G));
+      return coherent_rsrc(p.partials + (size_t)slot * TT, TT * 4);
+    };
+    {
+      const auto rs = slot_rsrc(w);
 #pragma unroll
-    for (int bo = 0; bo < NBO; ++bo)
+      for (int bo = 0; bo < NBO; ++bo)
 #pragma unroll
-      for (int br = 0; br < NBR; ++br) {
-        const int idx = ((wave * NBO + bo) * NBR + br) * 64 + lane;
-        float *dst = part + (size_t)z * TT + idx * 4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          __hip_atomic_store(dst + e, acc[bo][br][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+        for (int br = 0; br < NBR; ++br)
+          st16_coherent(rs, lane * 16, wbase + (bo * NBR + br) * 1024, acc[bo][br]);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0)
-      s_last = __hip_atomic_fetch_add(&p.counters[tl], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               (unsigned)(p.splits - 1);
+      s_last = __hip_atomic_fetch_add(&p.counters[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (unsigned)(wl - wf);
     __syncthreads();
     if (!s_last) return;
+    // FB output blocks at a time: their loads for one contributor are in
+    // flight together, few enough to leave the accumulators in registers
+    constexpr int FB = NBO >= 4 ? 4 : NBO;
 #pragma unroll
-    for (int bo = 0; bo < NBO; ++bo)
+    for (int b0 = 0; b0 < NBO; b0 += FB)
+      for (int cw = wf; cw <= wl; ++cw) {
+        const auto rs = slot_rsrc(cw);
 #pragma unroll
-      for (int br = 0; br < NBR; ++br) {
-        const int idx = ((wave * NBO + bo) * NBR + br) * 64 + lane;
-        f32x4 s;
-        for (int zz = 0; zz < p.splits; ++zz) {
-          const float *srcp = part + (size_t)zz * TT + idx * 4;
-          f32x4 v;
+        for (int bo = b0; bo < b0 + FB; ++bo)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = __hip_atomic_load(srcp + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          s = zz == 0 ? v : s + v;
-        }
-        acc[bo][br] = s;
+          for (int br = 0; br < NBR; ++br) {
+            const f32x4 v = ld16_coherent(rs, lane * 16, wbase + (bo * NBR + br) * 1024);
+            acc[bo][br] = cw == wf ? v : acc[bo][br] + v;
+          }
       }
-    if (tid == 0) __hip_atomic_store(&p.counters[tl], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(&p.counters[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---------------------------------------------------------- epilogue
@@ -375,24 +411,42 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
       *(uint2 *)(p.y + (size_t)grow * p.y_row_stride + o) = pk;
     }
   }
+  };  // segment
+
+  if constexpr (MODE == kStreamK) {
+    int seg = 0;
+    for (long long u = u_beg; u < u_end; ++seg) {
+      const int t = (int)(u / nst);
+      const long long tu = (long long)t * nst;
+      const int sb = (int)(u - tu);
+      const int se = (int)(min(u_end, tu + nst) - tu);
+      u = tu + se;
+      segment(seg, t, sb, se, owner(tu), owner(tu + nst - 1));
+    }
+  } else {  // one segment; 32-bit arithmetic
+    const int t = w / p.splits;
+    const int j = w - t * p.splits;
+    segment(0, t, j * nst / p.splits, (j + 1) * nst / p.splits, t * p.splits, t * p.splits + p.splits - 1);
+  }
 }
 
 hipError_t launch_gemm(const GemmArgs &a, int to, int tr, hipStream_t st) {
-  const int grid = a.max_mtiles * a.n_ntiles * a.splits;
+  const long long units = (long long)a.max_mtiles * a.n_ntiles * ((a.k_in + 63) / 64);
+  const int grid = a.stream_k ? (int)std::min<long long>(a.grid, units) : a.max_mtiles * a.n_ntiles * a.splits;
   if (grid == 0) return hipSuccess;
   // ring depth: as many 64-column stages as fit in about 128 KB of LDS
-  if (to == 64 && tr == 64)
-    hipLaunchKernelGGL((gemm_bf16_kernel<64, 64, 2, 2, 8>), dim3(grid), dim3(256), 0, st, a);
-  else if (to == 128 && tr == 64)
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 64, 4, 1, 6>), dim3(grid), dim3(256), 0, st, a);
-  else if (to == 128 && tr == 128)
-    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, 2, 2, 4>), dim3(grid), dim3(256), 0, st, a);
-  else if (to == 256 && tr == 64)
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 64, 4, 1, 3>), dim3(grid), dim3(256), 0, st, a);
-  else if (to == 256 && tr == 256)
-    hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 2>), dim3(grid), dim3(512), 0, st, a);
+#define LORA_GEMM(BO, BR, WGO, WGR, NS, MODE) \
+  hipLaunchKernelGGL((gemm_bf16_kernel<BO, BR, WGO, WGR, NS, MODE>), dim3(grid), dim3(WGO * WGR * 64), 0, st, a)
+  const int mode = a.stream_k ? kStreamK : (a.splits > 1 ? kSplitK : kOneTile);
+  if (to == 64 && tr == 64 && mode == kOneTile) LORA_GEMM(64, 64, 2, 2, 8, kOneTile);
+  else if (to == 64 && tr == 64 && mode == kSplitK) LORA_GEMM(64, 64, 2, 2, 8, kSplitK);
+  else if (to == 128 && tr == 128 && mode == kOneTile) LORA_GEMM(128, 128, 2, 2, 4, kOneTile);
+  else if (to == 128 && tr == 128 && mode == kSplitK) LORA_GEMM(128, 128, 2, 2, 4, kSplitK);
+  else if (to == 256 && tr == 64 && mode == kOneTile) LORA_GEMM(256, 64, 4, 1, 3, kOneTile);
+  else if (to == 256 && tr == 256 && mode == kStreamK) LORA_GEMM(256, 256, 2, 4, 2, kStreamK);
   else
     return hipErrorInvalidValue;
+#undef LORA_GEMM
   return hipGetLastError();
 }
 

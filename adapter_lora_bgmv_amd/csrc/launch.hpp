@@ -37,6 +37,7 @@ struct PrepArgs {
   int tile_rows;  // main kernel rows per tile
   int n_units;    // shrink units (grid = do_plan + n_units * k_splits)
   int *routes;    // [n] every row's packed route (the route kernel writes it)
+  int stable;     // rows of one key keep their index order in the plan
 };
 
 struct GemmArgs {
@@ -57,10 +58,15 @@ struct GemmArgs {
   const u16 *tt;   // [n][2R] the shrink's output scaled by the pair's scale, bf16 high parts
                    // (columns 0..R-1) and what they leave over (R..2R-1)
   int R;
-  int splits, k_per_split;
-  float *partials;
-  unsigned *counters;
+  int splits;      // classic split-K: k ranges per tile
+  int stream_k;    // 1: `grid` workgroups share out all tiles' k stages evenly
+  int grid;
+  float *partials; // [slots][BO*BR] partial tiles
+  unsigned *counters;  // [tiles] arrival counters, zero between calls
 };
+
+// Workgroups of a stream-K launch: one per CU of the chip.
+constexpr int kStreamKGrid = 256;
 
 // The decode-shaped apply (k_decode.hip): main launch (base partial tiles and
 // the shrink) + epilogue launch, n <= 64 rows.

@@ -67,6 +67,8 @@ int check_device(const char *what) {
 // ------------------------------------------------------------ tiling
 struct Cfg {
   int to, tr, splits, k_per_split, max_mtiles, n_ntiles;
+  bool stream_k;      // the GEMM shares all tiles' k stages out over kStreamKGrid workgroups
+  int partial_slots;  // partial tiles the GEMM's split-K may store
   bool decode;   // the one-launch decode kernel (k_decode.hip)
   int units;     // upper bound of shrink units
   int t_splits;  // k chunks of the shrink; the consumer sums the partials
@@ -95,10 +97,9 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
   } else if (n <= 128) {
     c.to = 128; c.tr = 128; c.splits = clampi(k_in / 1024, 1, 4);
   } else {
-    c.to = 256; c.tr = 256;
-    const int tiles = ((n + 255) / 256) * ((n_out + 255) / 256);
-    c.splits = clampi(307 / tiles, 1, std::min(8, std::max(1, k_in / 1024)));
+    c.to = 256; c.tr = 256; c.splits = 1;
   }
+  c.stream_k = !c.decode && op != LORA_OP_MOE_GATHER && n > 128;
   if (c.decode) {
     const int ksteps = (k_in + 31) / 32;
     c.k_per_split = ((ksteps + c.splits - 1) / c.splits) * 32;
@@ -108,6 +109,15 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
   }
   c.max_mtiles = (n + c.tr - 1) / c.tr + (op == LORA_OP_MOE_GATHER ? groups : 0);
   c.n_ntiles = (n_out + c.to - 1) / c.to;
+  const long long tiles = (long long)c.max_mtiles * c.n_ntiles;
+  c.partial_slots = c.splits > 1 ? (int)(tiles * c.splits) : 0;
+  if (c.stream_k) {
+    // Partial tiles arise unless every workgroup's range is whole tiles; then
+    // a workgroup stores at most two (its first and its last tile).
+    const long long nst = (k_in + 63) / 64, U = tiles * nst;
+    const long long G = std::min<long long>(kStreamKGrid, U);
+    c.partial_slots = nst == 1 || (U % G == 0 && (U / G) % nst == 0) ? 0 : (int)(2 * G);
+  }
   return c;
 }
 
@@ -130,7 +140,7 @@ WsLayout ws_layout(const Cfg &c, int n, int R, int k_in) {
     return w;
   }
   const size_t ntile = (size_t)c.max_mtiles * c.n_ntiles;
-  w.counters = off; off = up256(off + (c.splits > 1 ? ntile * 4 : 0));
+  w.counters = off; off = up256(off + (c.partial_slots > 0 ? ntile * 4 : 0));
   w.shrink_counters = off; off = up256(off + (c.t_splits > 1 ? (size_t)c.units * 4 : 0));
   w.pos_row = off; off = up256(off + (size_t)n * 4);
   w.pos_pair = off; off = up256(off + (size_t)n * 4);
@@ -141,7 +151,7 @@ WsLayout ws_layout(const Cfg &c, int n, int R, int k_in) {
   w.t_final = off; off = up256(off + (size_t)n * R * 4);
   w.tt = off; off = up256(off + (size_t)n * R * 4);  // [n][2R] bf16
   w.partials = off;
-  off = up256(off + (c.splits > 1 ? ntile * c.splits * c.to * c.tr * 4 : 0));
+  off = up256(off + (size_t)c.partial_slots * c.to * c.tr * 4);
   w.total = off;
   return w;
 }
@@ -320,6 +330,9 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
   pa.plan = plan;
   pa.tile_rows = c.tr;
   pa.n_units = c.units;
+  // a stream-K tile's k ranges differ from tile to tile: a row's result
+  // depends on its tile, so the tiles must not depend on timing
+  pa.stable = c.stream_k;
   prof_record(0, st);
   if (int e = launch_status(launch_prep(pa, st), what)) return e;
   prof_record(1, st);
@@ -344,7 +357,8 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
   ga.tt = pa.tt;
   ga.R = R;
   ga.splits = c.splits;
-  ga.k_per_split = c.k_per_split;
+  ga.stream_k = c.stream_k;
+  ga.grid = kStreamKGrid;
   ga.partials = (float *)(ws + L.partials);
   ga.counters = (unsigned *)(ws + L.counters);
   const int e = launch_status(launch_gemm(ga, c.to, c.tr, st), what);

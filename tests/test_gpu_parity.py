@@ -378,6 +378,25 @@ def test_full_config_parity(orc, name):
         assert np.array_equal(bf16_bits(dw.y)[57:], bf16_bits(yb)[57:])
 
 
+@pytest.mark.parametrize("seed,k,n_out,n", [
+    (15, 2112, 1000, 300),   # 264 k stages over 256 workgroups: ranges cross tile edges
+    (16, 128, 8000, 2100),   # 288 tiles of 2 stages: ranges hold whole tiles and pieces
+])
+def test_stream_k_partition(orc, seed, k, n_out, n):
+    """Batches over 128 rows share every tile's k stages out evenly over one
+    workgroup per CU; a range that starts or ends inside a tile leaves a
+    partial tile, which the tile's last arrival sums in k order."""
+    wl = WL.random_small(seed, dtype="bf16", k=k, n_out=n_out, n=n, n_slots=6, max_rank=32)
+    dw = DeviceWorkload(wl)
+    first = bf16_bits(dw.run().clone())
+    again = bf16_bits(dw.run().clone())
+    torch.cuda.synchronize()
+    assert np.array_equal(first, again)  # the arrival order does not change the sums
+    rows = _sample_rows(n, extra=(0, n - 1), k=48, seed=seed)
+    ref = orc.run(wl, rows=rows, scale_table=dw.scale_table_host)
+    check(dw.y_host()[rows], ref, "bf16", wl.name)
+
+
 def test_decode_batch_equals_per_row_calls():
     """atlas apply_lora_bgmv doc: the batched call equals n one-row calls.  On the
     decode path every output element is reduced in the same order whatever the
