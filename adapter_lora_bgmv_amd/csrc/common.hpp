@@ -48,6 +48,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Waits until at most `stages_younger` stages of `PER` DMA instructions each
+// (0 <= stages_younger <= MAXS), plus X other vector-memory operations
+// issued after the stage waited for, are still in flight.
+template <int PER, int MAXS, int X = 0>
+__device__ __forceinline__ void wait_stages(int stages_younger) {
+  if constexpr (MAXS >= 6) { if (stages_younger >= 6) { wait_vmcnt<6 * PER + X>(); return; } }
+  if constexpr (MAXS >= 5) { if (stages_younger == 5) { wait_vmcnt<5 * PER + X>(); return; } }
+  if constexpr (MAXS >= 4) { if (stages_younger == 4) { wait_vmcnt<4 * PER + X>(); return; } }
+  if constexpr (MAXS >= 3) { if (stages_younger == 3) { wait_vmcnt<3 * PER + X>(); return; } }
+  if constexpr (MAXS >= 2) { if (stages_younger == 2) { wait_vmcnt<2 * PER + X>(); return; } }
+  if constexpr (MAXS >= 1) { if (stages_younger == 1) { wait_vmcnt<PER + X>(); return; } }
+  wait_vmcnt<X>();
+}
+
 // One LDS-DMA instruction: 16 bytes per lane from `g` into the wave's 1 KB
 // LDS block at byte address `lds` (lane l lands at lds + 16 l).  Issued as
 // assembly so that the compiler adds no waits of its own around the LDS
@@ -79,6 +93,14 @@ __device__ __forceinline__ void st16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t
 __device__ __forceinline__ f32x4 ld16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(f32x4,
                             __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kCachePolicySc1));
+}
+
+// The same with 4 bytes per lane (lane l lands at lds + 4 l).
+__device__ __forceinline__ void dma4(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {

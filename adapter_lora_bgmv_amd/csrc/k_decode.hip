@@ -5,24 +5,25 @@
 //
 // (ferrox lora.rs module doc; atlas lora_delta.rs apply_lora_bgmv: shrink,
 // then expand-and-fold).  At decode sizes the cost is streaming W once, and
-// what limits that on this chip is how many bytes each CU must take in: its
-// share of W plus the x columns its k range needs.  So:
+// what limits that on this chip is how fast the bytes reach the CUs: whole
+// 128-byte lines move far faster than the 64-byte half lines of MFMA
+// fragments loaded straight into registers.  So:
 //
-//  * decode_main_kernel: a workgroup owns a tile of 64 output features x all
-//    rows x one k range (k is split S ways; S depends on k_in only).  Each CU
-//    then takes in 128 KB of W and only 1/S of x.  The 8 waves take
-//    interleaved 32-wide k steps (W rows as the MFMA A operand, x rows as B,
-//    fragments loaded straight into registers, all of a wave's loads in
-//    flight together) and meet in LDS in a fixed order; the f32 partial tile
-//    goes to the workspace.  The shrink t = A_q x rides along: once its tile
-//    is stored, a workgroup runs one shrink unit (touched slot, 16-rank
-//    block, k chunk), which gathers the rows of its slot into MFMA columns,
-//    so each A_q is read once per call.  Nothing in this launch waits for
-//    another workgroup;
+//  * decode_main_kernel: a workgroup owns a tile of 128 output features x
+//    all rows x one k range of at most 512 columns (k is split S ways; S
+//    depends on k_in only).  Each 64-column stage of the tile's W rows and
+//    of the batch's x rows goes to LDS by LDS-DMA, whole lines, stored
+//    XOR-swizzled so the MFMA fragment reads hit distinct banks; a ring of
+//    stages keeps 120 KB in flight per CU.  The waves own disjoint (output
+//    block, row block) pairs over the whole range, so they need no
+//    reduction; the f32 partial tile goes to the workspace.  The shrink
+//    t = A_q x rides along: once its tile is stored, a workgroup runs shrink
+//    units (touched slot, 16-rank block) of its k range, each staging
+//    A_q's rows and the slot's x rows the same way, so each A_q is read once
+//    per call.  Nothing in this launch waits for another workgroup;
 //  * decode_epilogue_kernel: y = bf16(sum_z partial_z + s_q sum_r B_q[o, r]
-//    t_i[r]), the S partials in split order, t summed over its k chunks in
-//    chunk order, the rank sum in f32 in rank order, one rounding.
-// The shrink's k chunks are the base contraction's S k ranges.
+//    t_i[r]), the S partials in split order, t summed over the k ranges in
+//    range order, the rank sum in f32 in rank order, one rounding.
 // With no adapters and no k split the main launch stores y itself.
 // Skipped rows (slot < 0 or past the pool, NULL table entry, zero scale) get
 // no delta arithmetic, so they equal the base-only launch bit for bit.
@@ -35,10 +36,15 @@ namespace lora {
 
 namespace {
 
-constexpr int kNW = 8;                    // waves per workgroup
-constexpr int kMB = kDecodeTileOut / 16;  // W row blocks per tile
+constexpr int kNW = 8;                               // waves per workgroup
+constexpr int kTO = kDecodeTileOut;                  // output features per tile
+constexpr int kRS = kTO + kDecodeMaxRows;            // rows of a stage: W rows, then x rows
+constexpr int kLPW = kRS / 8 / kNW;                  // DMA instructions per wave per stage
+constexpr int kNS = 6;                               // ring depth: 6 x 24 KB
+static_assert(kLPW * 8 * kNW == kRS, "stage rows must split evenly over the waves");
 
 struct Rows {  // the batch's routes, resolved once per workgroup
+  int raw[64];        // seq_slot, as the caller gave it (LDS-DMA)
   int q[64];          // slot or kSkip
   const u16 *bq[64];  // the row's B (rows that resolve)
   float sig[64];      // the row's scale
@@ -48,18 +54,51 @@ struct Rows {  // the batch's routes, resolved once per workgroup
   int T;              // touched slots
 };
 
-// Resolves every row (wave 0; n <= 64, one row per lane) and groups the rows
-// by slot, slots numbered in order of first appearance: one round of
-// ballots per touched slot, no LDS round trips.
-__device__ void resolve_rows(const DecodeArgs &p, Rows &s) {
+// Routes, in three steps that keep their latency off the stream of W:
+// at the start wave 0 sends seq_slot to LDS by LDS-DMA (issued before the
+// first stage, so it has landed once that stage has); after the first stage
+// it loads the three table entries each slot needs into registers; after
+// the last stage, when they have long arrived, it resolves the rows by the
+// rule of resolve_slot and groups them by slot, slots numbered in order of
+// first appearance: one round of ballots per touched slot.
+constexpr int kEnt = 3;  // loads of fetch_entries
+struct RowEntries {
+  const void *a, *b;
+  float sc;
+  bool in;
+};
+
+__device__ __forceinline__ void fetch_slots(const DecodeArgs &p, Rows &s) {
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64 && p.has_lora)
+    dma4(p.seq_slot + min(lane, p.n - 1), lds_addr(&s.raw[0]));
+}
+
+__device__ __forceinline__ RowEntries fetch_entries(const DecodeArgs &p, const Rows &s) {
+  const int lane = threadIdx.x & 63;
+  RowEntries e{nullptr, nullptr, 0.f, false};
+  const int slot = lane < p.n ? s.raw[lane] : -1;
+  e.in = slot >= 0 && slot < p.rd.max_loras;
+  if (e.in) {
+    e.a = p.rd.a_table[slot];
+    e.b = p.rd.b_table[slot];
+    e.sc = p.rd.scale_table[slot];
+  }
+  return e;
+}
+
+__device__ void resolve_rows(Rows &s, const RowEntries &e) {
   const int lane = threadIdx.x & 63;
   if (threadIdx.x >= 64) return;
-  int q = kSkip;
-  if (p.has_lora && lane < p.n)
-    q = resolve_slot(p.seq_slot[lane], 0, p.rd.max_loras, 1, p.rd.a_table, p.rd.b_table, p.rd.scale_table);
+  // The entries pass through an empty asm here, so that the compiler tests
+  // them here, after the stream of W, and not right after their loads.
+  uint64_t a = (uint64_t)e.a, b = (uint64_t)e.b;
+  float sc = e.sc;
+  asm volatile("" : "+v"(a), "+v"(b), "+v"(sc));
+  const int q = e.in && a != 0 && b != 0 && sc != 0.f ? s.raw[lane] : kSkip;
   s.q[lane] = q;
-  s.bq[lane] = q >= 0 ? (const u16 *)p.rd.b_table[q] : nullptr;
-  s.sig[lane] = q >= 0 ? p.rd.scale_table[q] : 0.f;
+  s.bq[lane] = q >= 0 ? (const u16 *)b : nullptr;
+  s.sig[lane] = q >= 0 ? sc : 0.f;
   const uint64_t below = (1ull << lane) - 1ull;
   uint64_t todo = __ballot(q >= 0);
   int T = 0, pos = 0;
@@ -81,179 +120,243 @@ __device__ void resolve_rows(const DecodeArgs &p, Rows &s) {
   }
 }
 
-// One shrink unit (touched slot u, rank block rb, k chunk c): the chunk's
-// partial of t for the rows of slot u, ranks 16 rb .. 16 rb + 15.  The 8 waves
-// take the chunk's 32-wide steps in turn, four at a time with every load out
-// before their MFMAs, and meet in LDS (`red`, 32 KB) in a fixed order.
-__device__ void shrink_unit(const DecodeArgs &p, const Rows &s, int uidx, f32x4 (*red)[64]) {
+// Zeroes, after its stage has landed, each 16-byte chunk this lane fetched
+// from past the k range (it fetched column 0 of its row instead).
+__device__ __forceinline__ void zero_past(uint4 *slot, int k0, int ke, int chunk) {
+  if (k0 + chunk >= ke) *slot = z4();
+}
+
+// One shrink unit (touched slot u, rank block rb) of this workgroup's k
+// range: the range's partial of t for the rows of slot u, ranks 16 rb .. +15.
+// The range's stages of A_u's 16 rows and of the slot's x rows (gathered, up
+// to 64, in groups of 16) go to LDS in one go; wave g then takes row group g
+// through every stage.
+__device__ void shrink_unit(const DecodeArgs &p, const Rows &s, int uidx, int k0, int k1, uint4 *lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = p.k_in, R = p.R, RB = R / 16, nchunks = p.n_chunks;
-  const int c = uidx % nchunks, rb = (uidx / nchunks) % RB, u = uidx / (nchunks * RB);
+  const int R = p.R, RB = R / 16;
+  const int rb = uidx % RB, u = uidx / RB;
+  const int c = blockIdx.x % p.S;  // the k range: the partial's index
   const u16 *A = (const u16 *)p.rd.a_table[s.slot[u]];
   const int m = s.start[u + 1] - s.start[u];
   const int G = (m + 15) / 16;  // groups of 16 gathered rows (<= 4)
-  const int kb = c * p.chunk, ke = min(kb + p.chunk, K);
-  const int nsteps = (ke - kb + 31) / 32;
-  const int koff = (lane >> 4) * 8;
-  const u16 *ap = A + (size_t)(rb * 16 + (lane & 15)) * K + kb + koff;
-  const u16 *xp[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int j = g * 16 + (lane & 15);
-    xp[g] = g < G && j < m ? p.x + (size_t)s.list[s.start[u] + j] * p.x_row_stride + kb + koff : nullptr;
-  }
-  f32x4 acc[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int i0 = 0; wave + kNW * i0 < nsteps; i0 += 4) {
-    uint4 av[4], xv[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int st = wave + kNW * (i0 + i);
-      const bool in = st < nsteps && kb + st * 32 + koff < ke;
-      av[i] = in ? ldg16(ap + st * 32) : z4();
-#pragma unroll
-      for (int g = 0; g < 4; ++g) xv[i][g] = in && xp[g] ? ldg16(xp[g] + st * 32) : z4();
+  const int ns = (k1 - k0 + 63) / 64;
+  const int RU = 16 + 16 * G;   // rows of a unit stage: A's 16, then the x rows
+  const int per = RU / 8;       // DMA instructions per unit stage
+  for (int ii = wave; ii < ns * per; ii += kNW) {
+    const int st = ii / per, k8 = ii % per;
+    const int rr = k8 * 8 + (lane >> 3);  // row of the unit stage
+    const u16 *rowp;
+    if (rr < 16) {
+      rowp = A + (size_t)(rb * 16 + rr) * p.k_in;
+    } else {
+      const int j = min(rr - 16, m - 1);
+      rowp = p.x + (size_t)s.list[s.start[u] + j] * p.x_row_stride;
     }
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[g] = mfma16(av[i], xv[i][g], acc[g]);
+    const int kk = k0 + st * 64 + ((lane & 7) ^ ((rr >> 1) & 7)) * 8;
+    dma16(rowp + (kk < k1 ? kk : k0), lds_addr(lds + (st * RU + k8 * 8) * 8));
   }
-#pragma unroll
-  for (int g = 0; g < 4; ++g) red[wave * 4 + g][lane] = acc[g];
+  __builtin_amdgcn_s_waitcnt(0);
+  if (k0 + ns * 64 > k1) {  // the last stage runs past the chunk
+    for (int ii = wave; ii < ns * per; ii += kNW) {
+      const int st = ii / per, k8 = ii % per;
+      const int rr = k8 * 8 + (lane >> 3);
+      zero_past(lds + (st * RU + k8 * 8) * 8 + lane, k0 + st * 64, k1, ((lane & 7) ^ ((rr >> 1) & 7)) * 8);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  }
   __syncthreads();
-  // D holds ranks 4*(l/16)..+3 of gathered column l%16
-  for (int e = tid; e < G * 64; e += kNW * 64) {
-    const int g = e >> 6, l = e & 63, j = g * 16 + (l & 15);
-    if (j >= m) continue;
-    f32x4 v = red[g][l];
+  if (wave < G) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int ra = lane & 15, rx = 16 + wave * 16 + (lane & 15);
+    for (int st = 0; st < ns; ++st) {
+      const uint4 *sl = lds + st * RU * 8;
 #pragma unroll
-    for (int w = 1; w < kNW; ++w) v += red[w * 4 + g][l];
-    const int row = s.list[s.start[u] + j];
-    *(f32x4 *)(p.t_part + ((size_t)c * p.n + row) * R + rb * 16 + (l >> 4) * 4) = v;
+      for (int h = 0; h < 2; ++h) {
+        const int ch = 4 * h + (lane >> 4);
+        acc = mfma16(sl[ra * 8 + (ch ^ ((ra >> 1) & 7))], sl[rx * 8 + (ch ^ ((rx >> 1) & 7))], acc);
+      }
+    }
+    // D: ranks 4 (l/16) .. +3 of gathered row 16 g + l%16
+    const int j = wave * 16 + (lane & 15);
+    if (j < m) {
+      const int row = s.list[s.start[u] + j];
+      *(f32x4 *)(p.t_part + ((size_t)c * p.n + row) * R + rb * 16 + (lane >> 4) * 4) = acc;
+    }
   }
-  __syncthreads();  // red is reused by the next unit
+  __syncthreads();  // the ring is reused by the next unit
 }
 
 }  // namespace
 
-template <int NB>  // 16-row column blocks of the batch: n <= 16 * NB
-__global__ __launch_bounds__(kNW * 64, 2) void decode_main_kernel(DecodeArgs p) {
-  constexpr int NF = kMB * NB;  // accumulator fragments per wave
-  static_assert(kNW * kMB * 4 * 1024 <= kDecodeLds, "LDS scratch holds the reduction");
-  __shared__ __attribute__((aligned(16))) f32x4 red[kDecodeLds / 1024][64];
+// NB: 16-row blocks of the batch that hold rows (n <= 16 NB).  Wave w owns
+// output blocks OBW (w % (8 / OBW)) .. +OBW-1 and row blocks RBW (w / (8 / OBW)) ..
+template <int NB>
+__global__ __launch_bounds__(kNW * 64) void decode_main_kernel(DecodeArgs p) {
+  constexpr int OBW = NB == 4 ? 2 : 1;   // output blocks per wave
+  constexpr int RBW = NB == 4 ? 2 : NB;  // row blocks per wave
+  constexpr int OWAVES = kNW / OBW;      // waves across the output blocks
+  static_assert(OWAVES * OBW * 16 == kTO && (kNW / OWAVES) * RBW == NB, "wave tiling");
+  __shared__ __attribute__((aligned(16))) uint4 ring[kNS][kRS * 8];
   __shared__ Rows s;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = p.k_in;
   const int tl = blockIdx.x / p.S, z = blockIdx.x % p.S;
-  const int o0 = tl * kDecodeTileOut;
+  const int o0 = tl * kTO;
   const int kb = min(z * p.k_per_split, K), ke = min(kb + p.k_per_split, K);
-  const int nsteps = (ke - kb + 31) / 32;
-  const int nj = (nsteps - wave + kNW - 1) / kNW;  // this wave's steps: wave, wave + 8, ...
-  const int koff = (lane >> 4) * 8;
-  // rows past n_out read the last row instead; their outputs are never stored
-  const u16 *wr = p.W + kb + koff;
-  int wrow[kMB];
+  const int nstage = (ke - kb + 63) / 64;
+  // Each DMA instruction moves 8 whole 128-byte row segments: lane l takes
+  // row 8i + l/8 of the stage and the chunk that belongs at slot l%8 of it.
+  // Rows past n_out or past the batch read a valid row instead; their
+  // outputs are never stored.
+  const u16 *src[kLPW];
+  int sch[kLPW];
 #pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) wrow[mb] = min(o0 + mb * 16 + (lane & 15), p.n_out - 1);
-  const u16 *xr = p.x + (size_t)(lane & 15) * p.x_row_stride + kb + koff;
-  const size_t xstep = (size_t)16 * p.x_row_stride;
-  f32x4 acc[kMB][NB];
-#pragma unroll
-  for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[mb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // A wave's steps go out in batches of kDecodeBatch (all of them when k_in
-  // <= 1024 * S): every load of the batch is in flight before the first
-  // MFMA waits, so the loop costs one memory latency per batch.
-  uint4 wv[kDecodeBatch][kMB], xv[kDecodeBatch][NB];
-  auto load = [&](int d, int j) {
-    const int s0 = (wave + kNW * j) * 32;
-    const bool in = j < nj && kb + s0 + koff < ke;
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) wv[d][mb] = in ? ldg16(wr + (size_t)wrow[mb] * p.w_row_stride + s0) : z4();
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-      xv[d][b] = (in && b * 16 + (lane & 15) < p.n) ? ldg16(xr + b * xstep + s0) : z4();
-  };
-  for (int j0 = 0; j0 < nj; j0 += kDecodeBatch) {
-#pragma unroll
-    for (int d = 0; d < kDecodeBatch; ++d) load(d, j0 + d);
-    if (j0 == 0) resolve_rows(p, s);  // wave 0, while its first loads are in flight
-#pragma unroll
-    for (int d = 0; d < kDecodeBatch; ++d)
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) acc[mb][b] = mfma16(wv[d][mb], xv[d][b], acc[mb][b]);
+  for (int j = 0; j < kLPW; ++j) {
+    const int rr = (wave + kNW * j) * 8 + (lane >> 3);
+    src[j] = rr < kTO ? p.W + (size_t)min(o0 + rr, p.n_out - 1) * p.w_row_stride
+                      : p.x + (size_t)min(rr - kTO, p.n - 1) * p.x_row_stride;
+    sch[j] = ((lane & 7) ^ ((rr >> 1) & 7)) * 8;
   }
-  if (nj <= 0) resolve_rows(p, s);
-
-  // fixed-order reduction of the 8 waves through LDS
+  auto issue = [&](int st) {
+    const int k0 = kb + st * 64;
 #pragma unroll
-  for (int f = 0; f < NF; ++f) red[wave * NF + f][lane] = acc[f / NB][f % NB];
-  __syncthreads();
-  const bool direct = p.S == 1 && !p.has_lora;  // nothing left for an epilogue: store y now
-  float *part = p.partials + ((size_t)tl * p.S + z) * (64 * kDecodeTileOut);
-  for (int e = tid; e < NF * 64; e += kNW * 64) {
-    const int f = e >> 6, l = e & 63;
-    f32x4 v = red[f][l];
-#pragma unroll
-    for (int w = 1; w < kNW; ++w) v += red[w * NF + f][l];
-    // D layout: column (row) l%16 of block b, outputs 4*(l/16)..+3 of block mb
-    const int mb = f / NB, b = f % NB;
-    const int i = b * 16 + (l & 15), oo = mb * 16 + (l >> 4) * 4;
-    if (direct) {
-      if (i < p.n && o0 + oo < p.n_out)
-        *(uint2 *)(p.y + (size_t)i * p.y_row_stride + o0 + oo) =
-            make_uint2(pack2(f2bf(v[0]), f2bf(v[1])), pack2(f2bf(v[2]), f2bf(v[3])));
-    } else {
-      *(f32x4 *)(part + i * kDecodeTileOut + oo) = v;
+    for (int j = 0; j < kLPW; ++j) {
+      const int kk = k0 + sch[j] < ke ? k0 + sch[j] : kb;
+      dma16(src[j] + kk, lds_addr(&ring[st % kNS][(wave + kNW * j) * 64]));
     }
+  };
+  fetch_slots(p, s);
+  const int npro = min(kNS - 1, nstage);  // stages issued before the loop
+  for (int st = 0; st < npro; ++st) issue(st);
+  // wave 0: once seq_slot has landed (older than every stage), the table
+  // entries go out; they are younger than the first npro stages, so wave 0
+  // allows for them (kEnt more operations in flight) when it waits for those
+  RowEntries ent{nullptr, nullptr, 0.f, false};
+  const bool ents = p.has_lora && wave == 0;
+  if (ents) {
+    wait_stages<kLPW, kNS - 1>(npro);
+    ent = fetch_entries(p, s);
   }
+
+  const int ob0 = (wave % OWAVES) * OBW, rb0 = (wave / OWAVES) * RBW;
+  f32x4 acc[OBW][RBW];
+#pragma unroll
+  for (int a = 0; a < OBW; ++a)
+#pragma unroll
+    for (int b = 0; b < RBW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int st = 0; st < nstage; ++st) {
+    // stage st has landed for every wave (at most kNS - 2 younger stages in
+    // flight); chunks past the k range are zeroed first
+    if (ents && st < npro)
+      wait_stages<kLPW, kNS - 2, kEnt>(min(kNS - 2, nstage - 1 - st));
+    else
+      wait_stages<kLPW, kNS - 2>(min(kNS - 2, nstage - 1 - st));
+    if (kb + st * 64 + 64 > ke) {
+#pragma unroll
+      for (int j = 0; j < kLPW; ++j)
+        zero_past(&ring[st % kNS][(wave + kNW * j) * 64 + lane], kb + st * 64, ke, sch[j]);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    }
+    block_barrier();
+    // every wave is done with stage st - 1: its slot takes stage st + kNS - 1
+    if (st + kNS - 1 < nstage) issue(st + kNS - 1);
+    const uint4 *sl = ring[st % kNS];
+    uint4 af[2][OBW], bf[2][RBW];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = 4 * h + (lane >> 4);
+#pragma unroll
+      for (int a = 0; a < OBW; ++a) {
+        const int r = (ob0 + a) * 16 + (lane & 15);
+        af[h][a] = sl[r * 8 + (c ^ ((r >> 1) & 7))];
+      }
+#pragma unroll
+      for (int b = 0; b < RBW; ++b) {
+        const int r = kTO + (rb0 + b) * 16 + (lane & 15);
+        bf[h][b] = sl[r * 8 + (c ^ ((r >> 1) & 7))];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int a = 0; a < OBW; ++a)
+#pragma unroll
+        for (int b = 0; b < RBW; ++b) acc[a][b] = mfma16(af[h][a], bf[h][b], acc[a][b]);
+  }
+
+  // the routes first (the table entries arrived long ago; no store is
+  // outstanding yet that the wait for them would include)
+  if (p.has_lora) resolve_rows(s, ent);
+  // D layout: column (row) l%16 of the row block, outputs 4 (l/16) .. +3 of
+  // the output block
+  const bool direct = p.S == 1 && !p.has_lora;  // nothing left for an epilogue: store y now
+  float *part = p.partials + ((size_t)tl * p.S + z) * (kDecodeMaxRows * kTO);
+#pragma unroll
+  for (int a = 0; a < OBW; ++a)
+#pragma unroll
+    for (int b = 0; b < RBW; ++b) {
+      const int i = (rb0 + b) * 16 + (lane & 15), oo = (ob0 + a) * 16 + (lane >> 4) * 4;
+      if (i >= p.n) continue;
+      const f32x4 v = acc[a][b];
+      if (direct) {
+        if (o0 + oo < p.n_out)
+          *(uint2 *)(p.y + (size_t)i * p.y_row_stride + o0 + oo) =
+              make_uint2(pack2(f2bf(v[0]), f2bf(v[1])), pack2(f2bf(v[2]), f2bf(v[3])));
+      } else {
+        *(f32x4 *)(part + i * kTO + oo) = v;
+      }
+    }
   if (!p.has_lora) return;
-  __syncthreads();  // the routes are resolved and red is free
+  __syncthreads();  // the routes are resolved and the ring is free
   if (blockIdx.x == 0 && tid < 64) {  // the epilogue's per-row routes
     p.row_q[tid] = s.q[tid];
     p.row_sig[tid] = s.sig[tid];
     p.row_b[tid] = s.bq[tid];
   }
-  const int units = s.T * (p.R / 16) * p.n_chunks;
-  for (int uidx = blockIdx.x; uidx < units; uidx += gridDim.x) shrink_unit(p, s, uidx, red);
+  const int units = s.T * (p.R / 16);  // of this k range
+  for (int uidx = tl; uidx < units; uidx += p.n_tiles) shrink_unit(p, s, uidx, kb, ke, &ring[0][0]);
 }
 
-// y for 16 output features x all rows per workgroup, one thread per (row,
-// four features).  Every load that does not depend on another goes out
-// first: the row's route, the S partials, t's chunk partials.
+// y for 16 rows x 64 output features per workgroup, one thread per (row,
+// four features): t is then needed for 16 rows only.  Every load that does
+// not depend on another goes out first: the row's route, the S partials, t.
+constexpr int kEpiOut = 64;  // output features per epilogue workgroup
 __global__ __launch_bounds__(256) void decode_epilogue_kernel(DecodeArgs p) {
-  __shared__ __attribute__((aligned(16))) float st[64 * 256];  // t rows, n x R
+  __shared__ __attribute__((aligned(16))) float st[16 * 256];  // t of the 16 rows, 16 x R
   const int tid = threadIdx.x;
   const int R = p.R;
-  const int tl = blockIdx.x / 4;
-  const int i = tid >> 2, oo = (blockIdx.x % 4) * 16 + (tid & 3) * 4, o = tl * kDecodeTileOut + oo;
+  constexpr int OPT = kTO / kEpiOut;  // output groups per tile
+  const int rg = blockIdx.x % 4, og = blockIdx.x / 4;  // row group, output group
+  const int tl = og / OPT;
+  const int i = rg * 16 + (tid >> 4), oo = (og % OPT) * kEpiOut + (tid & 15) * 4, o = tl * kTO + oo;
+  if (rg * 16 >= p.n) return;  // no rows in this group
   const bool live = i < p.n && o < p.n_out;
   const bool lora = p.has_lora;
+  // the row's route: slot, B and scale load together
   const int q = live && lora ? p.row_q[i] : kSkip;
+  const u16 *rb_ = live && lora ? p.row_b[i] : nullptr;
+  const float sig = live && lora ? p.row_sig[i] : 0.f;
   f32x4 a[kDecodeMaxSplit];
-  const float *pp = p.partials + (size_t)tl * p.S * (64 * kDecodeTileOut) + i * kDecodeTileOut + oo;
+  const float *pp = p.partials + (size_t)tl * p.S * (kDecodeMaxRows * kTO) + i * kTO + oo;
 #pragma unroll
   for (int z = 0; z < kDecodeMaxSplit; ++z)
-    a[z] = live && z < p.S ? *(const f32x4 *)(pp + (size_t)z * (64 * kDecodeTileOut)) : f32x4{0.f, 0.f, 0.f, 0.f};
-  if (lora)  // stage t in LDS: the chunk partials summed in chunk order
-    for (int e = tid * 4; e < p.n * R; e += 256 * 4) {
-      f32x4 v[kDecodeMaxChunks];
+    a[z] = live && z < p.S ? *(const f32x4 *)(pp + (size_t)z * (kDecodeMaxRows * kTO)) : f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nr = min(16, p.n - rg * 16);  // rows of this group
+  if (lora)  // stage t of the group's rows in LDS: the k ranges' partials summed in range order
+    for (int e = tid * 4; e < nr * R; e += 256 * 4) {
+      const float *tp = p.t_part + (size_t)rg * 16 * R + e;
+      f32x4 w[kDecodeMaxSplit];
 #pragma unroll
-      for (int c = 0; c < kDecodeMaxChunks; ++c)
-        v[c] = c < p.n_chunks ? *(const f32x4 *)(p.t_part + (size_t)c * p.n * R + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < kDecodeMaxSplit; ++c)
+        w[c] = c < p.n_chunks ? *(const f32x4 *)(tp + (size_t)c * p.n * R) : f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 v = w[0];
 #pragma unroll
-      for (int c = 1; c < kDecodeMaxChunks; ++c)
-        if (c < p.n_chunks) v[0] += v[c];
-      *(f32x4 *)(st + e) = v[0];
+      for (int c = 1; c < kDecodeMaxSplit; ++c)
+        if (c < p.n_chunks) v += w[c];
+      *(f32x4 *)(st + e) = v;
     }
-  const u16 *Bq = q >= 0 ? p.row_b[i] + (size_t)o * R : nullptr;
+  const u16 *Bq = q >= 0 ? rb_ + (size_t)o * R : nullptr;
   uint4 b[2][4];  // ranks 0..15 of the thread's four B rows
 #pragma unroll
   for (int h = 0; h < 2; ++h)
@@ -266,7 +369,7 @@ __global__ __launch_bounds__(256) void decode_epilogue_kernel(DecodeArgs p) {
   for (int z = 1; z < kDecodeMaxSplit; ++z)  // split order
     if (z < p.S) v += a[z];
   if (q >= 0) {
-    const float *ti = st + i * R;
+    const float *ti = st + (i - rg * 16) * R;
     float d[4] = {0.f, 0.f, 0.f, 0.f};
     auto fma8 = [&](const uint4 *bb, int r0) {
       float tr[8];
@@ -290,7 +393,6 @@ __global__ __launch_bounds__(256) void decode_epilogue_kernel(DecodeArgs p) {
       for (int j = 0; j < 4; ++j) bb[j] = ldg16(Bq + (size_t)j * R + r0);
       fma8(bb, r0);
     }
-    const float sig = p.row_sig[i];
 #pragma unroll
     for (int j = 0; j < 4; ++j) v[j] = v[j] + sig * d[j];
   }
@@ -315,7 +417,7 @@ hipError_t launch_decode_main(const DecodeArgs &a, hipStream_t st) {
 
 hipError_t launch_decode_epilogue(const DecodeArgs &a, hipStream_t st) {
   if (a.S == 1 && !a.has_lora) return hipSuccess;  // the main launch stored y
-  hipLaunchKernelGGL(decode_epilogue_kernel, dim3(a.n_tiles * 4), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(decode_epilogue_kernel, dim3(a.n_tiles * (kTO / kEpiOut) * 4), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -44,19 +44,6 @@
 
 namespace lora {
 
-// Waits until at most `stages_younger` stages of `PER` DMA instructions each
-// are still in flight (0 <= stages_younger <= MAXS).
-template <int PER, int MAXS>
-__device__ __forceinline__ void wait_stages(int stages_younger) {
-  if constexpr (MAXS >= 6) { if (stages_younger >= 6) { wait_vmcnt<6 * PER>(); return; } }
-  if constexpr (MAXS >= 5) { if (stages_younger == 5) { wait_vmcnt<5 * PER>(); return; } }
-  if constexpr (MAXS >= 4) { if (stages_younger == 4) { wait_vmcnt<4 * PER>(); return; } }
-  if constexpr (MAXS >= 3) { if (stages_younger == 3) { wait_vmcnt<3 * PER>(); return; } }
-  if constexpr (MAXS >= 2) { if (stages_younger == 2) { wait_vmcnt<2 * PER>(); return; } }
-  if constexpr (MAXS >= 1) { if (stages_younger == 1) { wait_vmcnt<PER>(); return; } }
-  wait_vmcnt<0>();
-}
-
 // MODE: kOneTile (a workgroup per tile), kSplitK (classic split-K), kStreamK.
 enum { kOneTile = 0, kSplitK = 1, kStreamK = 2 };
 
@@ -78,6 +65,7 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
   __shared__ int s_row[BR], s_pair[BR];
   __shared__ const u16 *s_bq[BR];  // the row's B_pair, or null
   __shared__ int s_last;
+  __shared__ int s_run[BR], s_rend[BR], s_nrun;  // runs of equal pairs: [start, end)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wo = wave % WGO, wr = wave / WGO;
@@ -175,24 +163,177 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
       dma16(src[j] + kk, lds_addr(&ring[st % NS][(wave + NW * j) * 64]));
     }
   };
-  // the first NS - 1 stages go out before the extension, so its latency and
-  // theirs overlap
   for (int st = 0; st < NS - 1 && st < nstage; ++st) issue(st);
 
-  // ---------------------------------------------------------- k-extension
-  // Items are (run of equal pairs within a 16-row block, 32-wide kappa step);
-  // the loads of up to G items are issued together before their MFMAs, so
-  // the extension costs a few memory latencies, not one per item.
-  // When every row of the wave's range that has a pair has the same one (a
-  // prefill segment, an expert's rows of one adapter), the B fragments of a
-  // kappa step serve all NBR row blocks: each step loads them once and the
-  // extension is a few rounds of loads.
-  // The tile's last contributor (in k order) runs it, at the start of its
-  // range, where it delays no other segment of its own: its range begins in
-  // this tile whenever the tile has more than one contributor.
-  const bool do_ext = p.has_lora && w == wl;
+  // Stage st is in LDS for every wave: wait for this wave's DMAs (at most
+  // `younger` stages issued after it may stay in flight), zero the chunks
+  // this wave fetched past the k range, then the barrier.
+  auto landed = [&](int st, int younger) {
+    wait_stages<LPW, (NS > 2 ? NS - 2 : 0)>(younger);
+    const int k0 = kb + st * 64;
+    if (k0 + 64 > ke) {
+#pragma unroll
+      for (int j = 0; j < LPW; ++j)
+        if (k0 + sch[j] >= ke) ring[st % NS][(wave + NW * j) * 64 + lane] = z4();
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    }
+    block_barrier();
+  };
+  // MFMA fragments of one 32-wide half h of a stage: lane l reads row l%16
+  // of the block, chunk 4h + l/16, at its swizzled slot.
+  uint4 af[2][NBO], bf[2][NBR];
+  auto fetch = [&](int st, auto hc) {
+    constexpr int h = decltype(hc)::value;
+    const uint4 *sl = ring[st % NS];
+    const int c = 4 * h + (lane >> 4);
+#pragma unroll
+    for (int bo = 0; bo < NBO; ++bo) {
+      const int r = (wo * NBO + bo) * 16 + (lane & 15);
+      af[h][bo] = sl[r * 8 + (c ^ ((r >> 1) & 7))];
+    }
+#pragma unroll
+    for (int b = 0; b < NBR; ++b) {
+      const int r = BO + (wr * NBR + b) * 16 + (lane & 15);
+      bf[h][b] = sl[r * 8 + (c ^ ((r >> 1) & 7))];
+    }
+  };
+  auto mma = [&](auto hc) {
+    constexpr int h = decltype(hc)::value;
+#pragma unroll
+    for (int bo = 0; bo < NBO; ++bo)
+#pragma unroll
+      for (int b = 0; b < NBR; ++b) acc[bo][b] = mfma16(af[h][bo], bf[h][b], acc[bo][b]);
+  };
+  for (int st = 0; st < nstage; ++st) {
+    landed(st, min(NS - 2, nstage - 1 - st));
+    // every wave is done with stage st - 1: its ring slot takes stage st + NS - 1
+    if (st + NS - 1 < nstage) issue(st + NS - 1);
+    fetch(st, std::integral_constant<int, 0>{});
+    fetch(st, std::integral_constant<int, 1>{});  // read while the first half's MFMAs run
+    mma(std::integral_constant<int, 0>{});
+    mma(std::integral_constant<int, 1>{});
+  }
+
+  // ---------------------------------------------------------- LoRA term
+  // acc[o, i] += sum_kappa B_q[o, kappa mod R] T[i, kappa] over kappa < 2R,
+  // where row i of T holds s_q t_i as bf16 high parts (kappa < R) and the
+  // bf16 roundings of what they leave over (kappa >= R), and rows of another
+  // pair, or skipped rows, contribute exact zeros.  It runs after the base
+  // contraction: an accumulator that started at +0 is never -0 there, so the
+  // zeros leave a skipped row bit-identical to the base-only launch.
+  //
+  // The tile's rows are sorted by pair, so a pair is one run of rows.  With
+  // R dividing 64, T's rows go to LDS once (one or two 64-column chunks) and
+  // each run's B slice (BO rows x R, repeated to 64 columns) streams through
+  // an LDS-DMA ring, so every byte is fetched once per workgroup; only the
+  // waves whose rows meet the run do its MFMAs.  The tile's contributors
+  // share the runs out: contributor j takes runs j, j + C, j + 2C, ...
+  if (p.has_lora && p.R <= 64 && 64 % p.R == 0) {
+    constexpr int LPB = BO / 8 / NW;  // DMA instructions per wave per B stage
+    constexpr int LPT = BR / 8 / NW;  // per 64-column chunk of T
+    constexpr int kRing = NS * RS * 128, kT = 2 * BR * 128;
+    constexpr int EB = (kRing - kT) / (BO * 128) > 4 ? 4 : (kRing - kT) / (BO * 128);
+    static_assert(LPB * NW * 8 == BO && LPT * NW * 8 == BR, "rows must split evenly over the waves");
+    static_assert(EB >= 2, "the ring must hold T and two B stages");
+    const int R = p.R, nck = (2 * R + 63) / 64;
+    uint4 *const tlds = &ring[0][0];
+    uint4 *const blds = tlds + 2 * BR * 8;
+    block_barrier();  // every wave is done with the ring
+    if (wave == 0) {
+      const uint64_t below = (1ull << lane) - 1ull;
+      int ns = 0, ne = 0;
+      for (int i = lane; i < BR; i += 64) {
+        const int q = s_pair[i];
+        const bool st = q >= 0 && (i == 0 || s_pair[i - 1] != q);
+        const bool en = q >= 0 && (i + 1 == BR || s_pair[i + 1] != q);
+        const uint64_t ms = __ballot(st), me = __ballot(en);
+        if (st) s_run[ns + (int)__popcll(ms & below)] = i;
+        if (en) s_rend[ne + (int)__popcll(me & below)] = i + 1;
+        ns += (int)__popcll(ms);
+        ne += (int)__popcll(me);
+      }
+      if (lane == 0) s_nrun = ns;
+    }
+    block_barrier();
+    const int C = wl - wf + 1, jc = w - wf;
+    const int nmine = s_nrun > jc ? (s_nrun - jc + C - 1) / C : 0;
+    if (nmine > 0) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        if (c >= nck) break;
+#pragma unroll
+        for (int j = 0; j < LPT; ++j) {
+          const int rr = (wave + NW * j) * 8 + (lane >> 3);
+          int r = s_row[rr];
+          if (r < 0) r = s_row[0];
+          const int kap = 64 * c + ((lane & 7) ^ ((rr >> 1) & 7)) * 8;
+          dma16(p.tt + (size_t)r * 2 * R + (kap < 2 * R ? kap : 0),
+                lds_addr(tlds + c * BR * 8 + (wave + NW * j) * 64));
+        }
+      }
+      auto issue_b = [&](int s) {
+        const u16 *Bq = s_bq[s_run[jc + s * C]];
+#pragma unroll
+        for (int j = 0; j < LPB; ++j) {
+          const int rr = (wave + NW * j) * 8 + (lane >> 3);
+          const int o = min(o0 + rr, p.n_out - 1);
+          const int col = (((lane & 7) ^ ((rr >> 1) & 7)) * 8) & (R - 1);
+          dma16(Bq + (size_t)o * R + col, lds_addr(blds + (s % EB) * BO * 8 + (wave + NW * j) * 64));
+        }
+      };
+      for (int s = 0; s < EB - 1 && s < nmine; ++s) issue_b(s);
+      for (int s = 0; s < nmine; ++s) {
+        wait_stages<LPB, EB - 2>(min(EB - 2, nmine - 1 - s));  // T went out first
+        if (s == 0 && 2 * R < 64) {  // zero the columns past 2R
+#pragma unroll
+          for (int j = 0; j < LPT; ++j) {
+            const int rr = (wave + NW * j) * 8 + (lane >> 3);
+            if (((lane & 7) ^ ((rr >> 1) & 7)) * 8 >= 2 * R) tlds[(wave + NW * j) * 64 + lane] = z4();
+          }
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        }
+        block_barrier();
+        if (s + EB - 1 < nmine) issue_b(s + EB - 1);
+        const int i0 = s_run[jc + s * C], i1 = s_rend[jc + s * C];
+        if (i0 >= (wr + 1) * WR || i1 <= wr * WR) continue;  // none of this wave's rows
+        const uint4 *bs = blds + (s % EB) * BO * 8;
+        // one 32-column half of the B slice at a time: its fragments serve
+        // every row block and T chunk
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int c8 = 4 * h + (lane >> 4);
+#pragma unroll
+          for (int bo = 0; bo < NBO; ++bo) {
+            const int r = (wo * NBO + bo) * 16 + (lane & 15);
+            af[0][bo] = bs[r * 8 + (c8 ^ ((r >> 1) & 7))];
+          }
+#pragma unroll
+          for (int b = 0; b < NBR; ++b) {
+            const int rb0 = wr * WR + b * 16;
+            if (i0 >= rb0 + 16 || i1 <= rb0) continue;
+            const int r = rb0 + (lane & 15);
+            const bool in = r >= i0 && r < i1;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              if (c >= nck) break;
+              const uint4 tv = tlds[c * BR * 8 + r * 8 + (c8 ^ ((r >> 1) & 7))];
+              const uint4 tf = in ? tv : z4();
+#pragma unroll
+              for (int bo = 0; bo < NBO; ++bo) acc[bo][b] = mfma16(af[0][bo], tf, acc[bo][b]);
+            }
+          }
+        }
+      }
+    }
+  } else if constexpr (MODE != kStreamK) {  // (stream-K launches take R dividing 64 only)
+  if (p.has_lora && w == wl) {
+  // Other ranks: the tile's last contributor loads the operands into
+  // registers.  Items are (run of equal pairs within a 16-row block, 32-wide
+  // kappa step); the loads of up to G items are issued together before their
+  // MFMAs.  When every row of the wave's range that has a pair has the same
+  // one, the B fragments of a kappa step serve all NBR row blocks.
   int upair = kSkip;
-  bool uniform = do_ext;
+  bool uniform = true;
   if (uniform) {
     for (int i = 0; i < WR; ++i) {  // LDS broadcast reads, the same for every lane
       const int q = s_pair[wr * WR + i];
@@ -240,7 +381,7 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
           for (int bo = 0; bo < NBO; ++bo) acc[bo][b] = mfma16(bv[s][bo], tv[s][b], acc[bo][b]);
       }
     }
-  } else if (do_ext) {
+  } else {
     const int R = p.R, nks = 2 * R / 32;
     constexpr int G = NBO <= 2 ? 8 : (NBO <= 4 ? 4 : 1);
     const int myr = lane & 15;
@@ -299,53 +440,7 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
     }
   }
 
-  // Stage st is in LDS for every wave: wait for this wave's DMAs (at most
-  // `younger` stages issued after it may stay in flight), zero the chunks
-  // this wave fetched past the k range, then the barrier.
-  auto landed = [&](int st, int younger) {
-    wait_stages<LPW, (NS > 2 ? NS - 2 : 0)>(younger);
-    const int k0 = kb + st * 64;
-    if (k0 + 64 > ke) {
-#pragma unroll
-      for (int j = 0; j < LPW; ++j)
-        if (k0 + sch[j] >= ke) ring[st % NS][(wave + NW * j) * 64 + lane] = z4();
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    }
-    block_barrier();
-  };
-  // MFMA fragments of one 32-wide half h of a stage: lane l reads row l%16
-  // of the block, chunk 4h + l/16, at its swizzled slot.
-  uint4 af[2][NBO], bf[2][NBR];
-  auto fetch = [&](int st, auto hc) {
-    constexpr int h = decltype(hc)::value;
-    const uint4 *sl = ring[st % NS];
-    const int c = 4 * h + (lane >> 4);
-#pragma unroll
-    for (int bo = 0; bo < NBO; ++bo) {
-      const int r = (wo * NBO + bo) * 16 + (lane & 15);
-      af[h][bo] = sl[r * 8 + (c ^ ((r >> 1) & 7))];
-    }
-#pragma unroll
-    for (int b = 0; b < NBR; ++b) {
-      const int r = BO + (wr * NBR + b) * 16 + (lane & 15);
-      bf[h][b] = sl[r * 8 + (c ^ ((r >> 1) & 7))];
-    }
-  };
-  auto mma = [&](auto hc) {
-    constexpr int h = decltype(hc)::value;
-#pragma unroll
-    for (int bo = 0; bo < NBO; ++bo)
-#pragma unroll
-      for (int b = 0; b < NBR; ++b) acc[bo][b] = mfma16(af[h][bo], bf[h][b], acc[bo][b]);
-  };
-  for (int st = 0; st < nstage; ++st) {
-    landed(st, min(NS - 2, nstage - 1 - st));
-    // every wave is done with stage st - 1: its ring slot takes stage st + NS - 1
-    if (st + NS - 1 < nstage) issue(st + NS - 1);
-    fetch(st, std::integral_constant<int, 0>{});
-    fetch(st, std::integral_constant<int, 1>{});  // read while the first half's MFMAs run
-    mma(std::integral_constant<int, 0>{});
-    mma(std::integral_constant<int, 1>{});
+  }
   }
 
   // ---------------------------------------------------------- split-K fixup

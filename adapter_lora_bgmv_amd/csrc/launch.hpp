@@ -82,25 +82,23 @@ struct DecodeArgs {
   const int32_t *seq_slot;
   int has_lora;
   int R;
-  int S, k_per_split;   // k split of the base contraction
+  int S, k_per_split;   // k split of the base contraction (k_per_split: a multiple of 64)
   int n_tiles;          // ceil(n_out / kDecodeTileOut)
-  int n_chunks, chunk;  // k ranges of the shrink partials: the S splits, k_per_split wide
+  int n_chunks;         // k chunks of the shrink partials: the S k ranges
   float *partials;      // [n_tiles][S][64 rows][kDecodeTileOut] partial tiles
-  float *t_part;        // [n_chunks][n][R] shrink partials, one per k range
+  float *t_part;        // [n_chunks][n][R] shrink partials, one per k chunk
   int *row_q;           // [64] each row's slot or kSkip, for the epilogue
   float *row_sig;       // [64] each row's scale
   const u16 **row_b;    // [64] each row's B
 };
 
-// Largest batch the decode kernels take, their tile width, LDS scratch,
-// largest k split, k steps per wave in flight together, largest shrink chunk
-// count.
+// Largest batch the decode kernels take, their tile width, the most
+// 64-column stages one k range takes, the largest k split (so k_in <=
+// 64 x 8 x 16 = 8192 on this path).
 constexpr int kDecodeMaxRows = 64;
-constexpr int kDecodeTileOut = 64;
-constexpr int kDecodeLds = 128 * 1024;
-constexpr int kDecodeMaxSplit = 8;
-constexpr int kDecodeBatch = 4;
-constexpr int kDecodeMaxChunks = kDecodeMaxSplit;
+constexpr int kDecodeTileOut = 128;
+constexpr int kDecodeMaxStages = 8;
+constexpr int kDecodeMaxSplit = 16;
 
 // Rows per shrink unit.
 constexpr int kShrinkRows = 64;

@@ -81,15 +81,18 @@ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 // order is the same whether a fused projection is applied whole or part by
 // part; larger batches pick it from the tile count to fill the chip.
 Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pairs) {
-  Cfg c;
-  c.decode = op == LORA_OP_APPLY && n <= kDecodeMaxRows;
+  Cfg c{};
+  c.decode = op == LORA_OP_APPLY && n <= kDecodeMaxRows && k_in <= 64 * kDecodeMaxStages * kDecodeMaxSplit;
   c.units = R > 0 ? (n + kShrinkRows - 1) / kShrinkRows + std::min(n, n_pairs) : 0;
   // Shrink k chunks: enough workgroups to cover the chip for small batches,
   // chunks of at least 256 columns.  A function of (n, k_in) only, so the
   // workspace size does not depend on the routing.
   c.t_splits = R > 0 ? clampi(512 / ((n + kShrinkRows - 1) / kShrinkRows), 1, std::min(kMaxShrinkSplits, std::max(1, k_in / 256))) : 1;
   if (c.decode) {
-    c.to = kDecodeTileOut; c.tr = kDecodeMaxRows; c.splits = clampi(k_in / 1024, 1, 8);
+    // k ranges of at most kDecodeMaxStages 64-column stages
+    const int nst = (k_in + 63) / 64;
+    c.to = kDecodeTileOut; c.tr = kDecodeMaxRows;
+    c.splits = (nst + kDecodeMaxStages - 1) / kDecodeMaxStages;
   } else if (op == LORA_OP_MOE_GATHER) {
     c.to = 256; c.tr = 64; c.splits = 1;
   } else if (n <= 64) {
@@ -99,10 +102,16 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
   } else {
     c.to = 256; c.tr = 256; c.splits = 1;
   }
+  // stream-K stages the LoRA term through LDS, which takes ranks dividing 64;
+  // other ranks go to 128 x 128 tiles
   c.stream_k = !c.decode && op != LORA_OP_MOE_GATHER && n > 128;
+  if (c.stream_k && R > 0 && (R > 64 || 64 % R != 0)) {
+    c.stream_k = false;
+    c.to = 128; c.tr = 128; c.splits = clampi(k_in / 1024, 1, 4);
+  }
   if (c.decode) {
-    const int ksteps = (k_in + 31) / 32;
-    c.k_per_split = ((ksteps + c.splits - 1) / c.splits) * 32;
+    const int nst = (k_in + 63) / 64;
+    c.k_per_split = ((nst + c.splits - 1) / c.splits) * 64;
   } else {
     const int kslabs = (k_in + 63) / 64;
     c.k_per_split = ((kslabs + c.splits - 1) / c.splits) * 64;
@@ -131,7 +140,7 @@ WsLayout ws_layout(const Cfg &c, int n, int R, int k_in) {
   WsLayout w{};
   size_t off = 0;
   if (c.decode) {  // partial tiles; shrink partials; per-row routes
-    const size_t nchunks = R > 0 ? (size_t)c.splits : 0;  // the shrink's k ranges are the splits
+    const size_t nchunks = R > 0 ? (size_t)c.splits : 0;  // the shrink's k chunks are the k ranges
     w.partials = off;
     off = up256(off + (c.splits > 1 || R > 0 ? (size_t)c.n_ntiles * c.splits * 64 * kDecodeTileOut * 4 : 0));
     w.t = off; off = up256(off + nchunks * n * R * 4);
@@ -293,7 +302,6 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
     da.S = c.splits;
     da.k_per_split = c.k_per_split;
     da.n_tiles = c.n_ntiles;
-    da.chunk = c.k_per_split;
     da.n_chunks = R > 0 ? c.splits : 0;
     da.partials = (float *)(ws + L.partials);
     da.t_part = (float *)(ws + L.t);

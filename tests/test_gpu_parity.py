@@ -71,6 +71,9 @@ SMALL = [
     (9, "bf16", 3072, 128, 100, 5, 16),   # 100 rows: 128-row tiles, split-K 3
     (13, "bf16", 160, 88, 7, 3, 16),      # second row block of a tile cut at 8 rows
     (14, "bf16", 1536, 56, 33, 20, 64),   # one ragged tile, 20 slots, rank 64
+    (19, "bf16", 3648, 136, 9, 3, 32),    # 57 stages: the last k range is one stage, its second shrink chunk empty
+    (20, "bf16", 8192, 72, 5, 2, 16),     # the largest k_in of the decode kernels: 16 k ranges
+    (21, "bf16", 8200, 40, 6, 2, 16),     # one column block past it: the tiled path
     (6, "f32", 96, 80, 13, 5, 16),
     (7, "f32", 37, 29, 9, 3, 5),          # f32 takes any shape
 ]
@@ -378,15 +381,18 @@ def test_full_config_parity(orc, name):
         assert np.array_equal(bf16_bits(dw.y)[57:], bf16_bits(yb)[57:])
 
 
-@pytest.mark.parametrize("seed,k,n_out,n", [
-    (15, 2112, 1000, 300),   # 264 k stages over 256 workgroups: ranges cross tile edges
-    (16, 128, 8000, 2100),   # 288 tiles of 2 stages: ranges hold whole tiles and pieces
+@pytest.mark.parametrize("seed,k,n_out,n,R", [
+    (15, 2112, 1000, 300, 32),   # 264 k stages over 256 workgroups: ranges cross tile edges
+    (16, 128, 8000, 2100, 32),   # 288 tiles of 2 stages: ranges hold whole tiles and pieces
+    (17, 1024, 2048, 520, 16),   # rank 16: T's columns past 2R are zero in LDS
+    (18, 640, 1000, 300, 128),   # rank 128: 128 x 128 tiles, the register-staged LoRA term
 ])
-def test_stream_k_partition(orc, seed, k, n_out, n):
+def test_stream_k_partition(orc, seed, k, n_out, n, R):
     """Batches over 128 rows share every tile's k stages out evenly over one
     workgroup per CU; a range that starts or ends inside a tile leaves a
-    partial tile, which the tile's last arrival sums in k order."""
-    wl = WL.random_small(seed, dtype="bf16", k=k, n_out=n_out, n=n, n_slots=6, max_rank=32)
+    partial tile, which the tile's last arrival sums in k order.  The tile's
+    contributors share its runs of equal pairs out for the LoRA term."""
+    wl = WL.random_small(seed, dtype="bf16", k=k, n_out=n_out, n=n, n_slots=6, max_rank=R)
     dw = DeviceWorkload(wl)
     first = bf16_bits(dw.run().clone())
     again = bf16_bits(dw.run().clone())
