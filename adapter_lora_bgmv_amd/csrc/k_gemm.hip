@@ -134,33 +134,36 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
   const u16 *Wg = p.W + (size_t)tile.x * (size_t)p.w_group_stride;
   // Each DMA instruction moves 8 whole 128-byte row segments (full cache
   // lines): lane l takes row 8i + l/8 of the stage and the chunk that belongs
-  // at slot l%8 of that row.  This lane's rows are the same in every stage.
-  const u16 *src[LPW];
-  int sch[LPW];  // element offset of this lane's chunk within the 64 columns
+  // at slot l%8 of that row.  This lane's rows are the same in every stage:
+  // instructions j < JW carry W rows, the rest x rows.  The slot of a chunk
+  // depends on (row >> 1) & 7, which is the same for every j (the rows of
+  // instruction j are NW * 8 j apart, a multiple of 16).
+  constexpr int JW = BO / (8 * NW);
+  static_assert(JW * 8 * NW == BO, "a DMA instruction carries W rows or x rows, not both");
+  int rowid[LPW];  // the W row (output feature) or the x row of each instruction
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
     const int rr = (wave + NW * j) * 8 + (lane >> 3);  // row of the stage
-    const u16 *rowp;
-    if (rr < BO) {
-      const int o = min(o0 + rr, p.n_out - 1);
-      rowp = Wg + (size_t)o * p.w_row_stride;
+    if (j < JW) {
+      rowid[j] = min(o0 + rr, p.n_out - 1);
     } else {
       int r = s_row[rr - BO];
       if (r < 0) r = s_row[0];
-      rowp = p.x + (size_t)r * p.x_row_stride;
+      rowid[j] = r;
     }
-    src[j] = rowp;
-    sch[j] = ((lane & 7) ^ ((rr >> 1) & 7)) * 8;
   }
+  const int sch = ((lane & 7) ^ (((wave * 8 + (lane >> 3)) >> 1) & 7)) * 8;  // this lane's chunk
   // Every wave issues exactly LPW DMA instructions per stage, so the vmcnt
   // waits count stages exactly.  Lanes whose chunk lies past the k range read
   // column 0 of their row instead and zero their landed chunk afterwards.
   auto issue = [&](int st) {
     const int k0 = kb + st * 64;
+    const int kk = k0 + sch < ke ? k0 + sch : 0;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
-      const int kk = k0 + sch[j] < ke ? k0 + sch[j] : 0;
-      dma16(src[j] + kk, lds_addr(&ring[st % NS][(wave + NW * j) * 64]));
+      const u16 *g = j < JW ? Wg + (size_t)rowid[j] * p.w_row_stride + kk
+                            : p.x + (size_t)rowid[j] * p.x_row_stride + kk;
+      dma16(g, lds_addr(&ring[st % NS][(wave + NW * j) * 64]));
     }
   };
   for (int st = 0; st < NS - 1 && st < nstage; ++st) issue(st);
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
     if (k0 + 64 > ke) {
 #pragma unroll
       for (int j = 0; j < LPW; ++j)
-        if (k0 + sch[j] >= ke) ring[st % NS][(wave + NW * j) * 64 + lane] = z4();
+        if (k0 + sch >= ke) ring[st % NS][(wave + NW * j) * 64 + lane] = z4();
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     }
     block_barrier();

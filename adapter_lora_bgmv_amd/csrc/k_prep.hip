@@ -74,7 +74,8 @@ __device__ __forceinline__ int segment_lds(const int *ip, int n_seg, int r) {
 // Routes rows row0 + tid + 256 j (j < 8) into pk[]: every load of the batch
 // (the slot inputs, then the three route tables) in flight together.  `seg`
 // is an LDS copy of seg_indptr (segmented calls), or null.
-__device__ __forceinline__ void route_all(const PrepArgs &a, int *pk, const int *seg, int row0) {
+__device__ __forceinline__ void route_all(const PrepArgs &a, int *pk, const int *seg, int row0,
+                                          bool ranked = false) {
   const int ml = a.has_lora ? a.rd.max_loras : 0;
   const RouteDev &rd = a.rd;
   const Routing &rt = a.rt;
@@ -112,6 +113,7 @@ __device__ __forceinline__ void route_all(const PrepArgs &a, int *pk, const int 
       tb[j] = in ? (uint64_t)(uintptr_t)rd.b_table[idx] : 0ull;
       sc[j] = in ? rd.scale_table[slot[j]] : 0.f;
     }
+    int qv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int r = r0 + 256 * j;
@@ -119,6 +121,32 @@ __device__ __forceinline__ void route_all(const PrepArgs &a, int *pk, const int 
       const int q = drop[j] ? kDrop : (ok ? slot[j] * rd.n_experts + expert[j] : kSkip);
       const int key = drop[j] ? -1 : expert[j] * (ml + 1) + (q >= 0 ? slot[j] : ml);
       if (r < a.n) pk[r] = ((key + 1) << 13) | (q + 2);
+      qv[j] = r < a.n ? q : kSkip;
+    }
+    if (ranked) {  // each row's rank within its pair: the pairs many of a wave's rows share take one atomic each
+      const int lane = threadIdx.x & 63;
+      const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        int q = qv[j], rank = -1;
+        uint64_t todo = __ballot(q >= 0);
+        for (int round = 0; round < 2 && todo; ++round) {
+          const int leader = __ffsll((unsigned long long)todo) - 1;
+          const int v = __builtin_amdgcn_readlane(q, leader);
+          const uint64_t m = __ballot(q == v);
+          int base = 0;
+          if (lane == leader) base = (int)atomicAdd(&a.pair_cnt[v], (unsigned)__popcll(m));
+          base = __builtin_amdgcn_readlane(base, leader);
+          if (q == v) {
+            rank = base + (int)__popcll(m & below);
+            q = kSkip;
+          }
+          todo &= ~m;
+        }
+        if (q >= 0) rank = (int)atomicAdd(&a.pair_cnt[q], 1u);
+        const int r = r0 + 256 * j;
+        if (r < a.n) a.ranks[r] = rank;
+      }
     }
   }
 }
@@ -311,23 +339,17 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
   f32x4 *red = (f32x4 *)(lds + ((P + 8 + kShrinkRows + 3) & ~3));  // [3][4][kShrinkRows/16][64]
   int *pk = (int *)(red + 3 * 4 * (kShrinkRows / 16) * 64);  // [n] the rows' packed routes
 
-  for (int p = tid; p < P; p += 256) cnt[p] = 0;
-  if (a.routes) {  // eight loads per thread in flight at a time
-    for (int r0 = tid; r0 < a.n; r0 += 256 * 8) {
-      int v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = r0 + 256 * j < a.n ? a.routes[r0 + 256 * j] : 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (r0 + 256 * j < a.n) pk[r0 + 256 * j] = v[j];
-    }
-  } else {  // no route buffer (the standalone shrink): route here
+  const bool ranked = a.ranks != nullptr;  // the route kernel counted and ranked the rows
+  if (ranked) {
+    for (int p = tid; p < P; p += 256) cnt[p] = ((int)a.pair_cnt[p] + kShrinkRows - 1) / kShrinkRows;
+  } else {  // the standalone shrink: route and count here
+    for (int p = tid; p < P; p += 256) cnt[p] = 0;
     for (int r0 = 0; r0 < a.n; r0 += 256 * 8) route_all(a, pk, nullptr, r0);
+    __syncthreads();
+    count_rows(pk, a.n, cnt, [](int w) { return pk_pair(w); });
+    __syncthreads();
+    for (int p = tid; p < P; p += 256) cnt[p] = (cnt[p] + kShrinkRows - 1) / kShrinkRows;
   }
-  __syncthreads();
-  count_rows(pk, a.n, cnt, [](int w) { return pk_pair(w); });
-  __syncthreads();
-  for (int p = tid; p < P; p += 256) cnt[p] = (cnt[p] + kShrinkRows - 1) / kShrinkRows;
   __syncthreads();
   const int n_units = block_exscan(cnt, P, wsum);
   if (u >= n_units) return;  // uniform: every thread saw the same total
@@ -344,9 +366,23 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
   const int pstar = info[0];
   const int first = info[1] * kShrinkRows;
 
-  // rows of pstar in row order, ranks [first, first + kShrinkRows): thread t
-  // counts them in its 16-row span, an exclusive scan gives its first rank
-  {
+  if (ranked) {  // the rows of pstar whose rank falls in [first, first + kShrinkRows)
+    for (int r0 = tid; r0 < a.n; r0 += 256 * 8) {
+      int rk[8], w[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool in = r0 + 256 * j < a.n;
+        rk[j] = in ? a.ranks[r0 + 256 * j] : -1;
+        w[j] = in ? a.routes[r0 + 256 * j] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (rk[j] >= first && rk[j] < first + kShrinkRows && pk_pair(w[j]) == pstar) rows[rk[j] - first] = r0 + 256 * j;
+    }
+    if (tid == 0) info[3] = (int)a.pair_cnt[pstar];
+  } else {
+    // rows of pstar in row order, ranks [first, first + kShrinkRows): thread t
+    // counts them in its 16-row span, an exclusive scan gives its first rank
     constexpr int SPAN = 16;
     int c = 0;
     // every thread runs the same number of rounds (the barriers inside)
@@ -509,16 +545,26 @@ __global__ __launch_bounds__(256) void route_kernel(PrepArgs a) {
   if (sl)
     for (int g = threadIdx.x; g <= a.rt.n_seg; g += 256) seg[g] = a.rt.seg_indptr[g];
   __syncthreads();
-  route_all(a, a.routes, sl ? seg : nullptr, (int)blockIdx.x * (256 * 8));
+  route_all(a, a.routes, sl ? seg : nullptr, (int)blockIdx.x * (256 * 8), a.ranks != nullptr);
 }
 
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   extern __shared__ int lds[];
-  if (a.do_plan && blockIdx.x == 0) {
+  if (a.do_plan && blockIdx.x == 0)
     plan_block(a, lds);
-    return;
-  }
-  shrink_unit(a, (int)blockIdx.x - a.do_plan, lds);
+  else
+    shrink_unit(a, (int)blockIdx.x - a.do_plan, lds);
+  if (a.ranks == nullptr) return;
+  // every workgroup has read the pair counts once all have arrived: the last
+  // one zeroes them (and the arrival count) for the next call
+  __syncthreads();
+  __shared__ int last;
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(a.prep_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+  __syncthreads();
+  if (!last) return;
+  for (int p = threadIdx.x; p < a.n_pairs; p += 256) a.pair_cnt[p] = 0u;
+  if (threadIdx.x == 0) *a.prep_done = 0u;
 }
 
 size_t prep_lds_bytes(const PrepArgs &a) {

@@ -38,6 +38,13 @@ struct PrepArgs {
   int n_units;    // shrink units (grid = do_plan + n_units * k_splits)
   int *routes;    // [n] every row's packed route (the route kernel writes it)
   int stable;     // rows of one key keep their index order in the plan
+  // With routes: the route kernel also counts the rows of every pair and
+  // gives each row its rank among them (in no particular order), so that a
+  // shrink unit finds its rows without sorting; the last prep workgroup to
+  // finish zeroes the counts again.
+  int *ranks;              // [n] the row's rank within its pair, or -1
+  unsigned *pair_cnt;      // [n_pairs] rows per pair, zero between calls
+  unsigned *prep_done;     // [1] prep workgroups finished, zero between calls
 };
 
 struct GemmArgs {

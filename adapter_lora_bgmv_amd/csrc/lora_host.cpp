@@ -131,7 +131,7 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
 }
 
 struct WsLayout {
-  size_t counters, shrink_counters, pos_row, pos_pair, routes, tiles, n_tiles, t, t_final, tt, partials, rows, total;
+  size_t counters, shrink_counters, pos_row, pos_pair, routes, ranks, pair_cnt, tiles, n_tiles, t, t_final, tt, partials, rows, total;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -154,6 +154,8 @@ WsLayout ws_layout(const Cfg &c, int n, int R, int k_in) {
   w.pos_row = off; off = up256(off + (size_t)n * 4);
   w.pos_pair = off; off = up256(off + (size_t)n * 4);
   w.routes = off; off = up256(off + (size_t)n * 4);
+  w.ranks = off; off = up256(off + (R > 0 ? (size_t)n * 4 : 0));
+  w.pair_cnt = off; off = up256(off + (R > 0 ? (size_t)(kMaxKeys + 1) * 4 : 0));  // any table size
   w.tiles = off; off = up256(off + (size_t)c.max_mtiles * 16);
   w.n_tiles = off; off = up256(off + 16);
   w.t = off; off = up256(off + (c.t_splits > 1 ? (size_t)c.t_splits * n * R * 4 : 0));
@@ -331,6 +333,11 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
   pa.t_final = (float *)(ws + L.t_final);
   pa.tt = R > 0 ? (u16 *)(ws + L.tt) : nullptr;
   pa.routes = (int *)(ws + L.routes);
+  if (R > 0) {
+    pa.ranks = (int *)(ws + L.ranks);
+    pa.pair_cnt = (unsigned *)(ws + L.pair_cnt);
+    pa.prep_done = pa.pair_cnt + n_pairs;
+  }
   pa.counters = (unsigned *)(ws + L.shrink_counters);
   pa.k_splits = c.t_splits;
   pa.n_pairs = n_pairs;
