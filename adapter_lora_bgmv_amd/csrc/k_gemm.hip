@@ -300,29 +300,34 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
         const int i0 = s_run[jc + s * C], i1 = s_rend[jc + s * C];
         if (i0 >= (wr + 1) * WR || i1 <= wr * WR) continue;  // none of this wave's rows
         const uint4 *bs = blds + (s % EB) * BO * 8;
-        // one 32-column half of the B slice at a time: its fragments serve
-        // every row block and T chunk
+        // one 32-column half of the B slice, and at most four of its output
+        // blocks, at a time (few registers beside the accumulators): its
+        // fragments serve every row block and T chunk
+        constexpr int OB = NBO < 4 ? NBO : 4;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int c8 = 4 * h + (lane >> 4);
 #pragma unroll
-          for (int bo = 0; bo < NBO; ++bo) {
-            const int r = (wo * NBO + bo) * 16 + (lane & 15);
-            af[0][bo] = bs[r * 8 + (c8 ^ ((r >> 1) & 7))];
-          }
+          for (int ob = 0; ob < NBO; ob += OB) {
 #pragma unroll
-          for (int b = 0; b < NBR; ++b) {
-            const int rb0 = wr * WR + b * 16;
-            if (i0 >= rb0 + 16 || i1 <= rb0) continue;
-            const int r = rb0 + (lane & 15);
-            const bool in = r >= i0 && r < i1;
+            for (int bo = 0; bo < OB; ++bo) {
+              const int r = (wo * NBO + ob + bo) * 16 + (lane & 15);
+              af[0][bo] = bs[r * 8 + (c8 ^ ((r >> 1) & 7))];
+            }
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-              if (c >= nck) break;
-              const uint4 tv = tlds[c * BR * 8 + r * 8 + (c8 ^ ((r >> 1) & 7))];
-              const uint4 tf = in ? tv : z4();
+            for (int b = 0; b < NBR; ++b) {
+              const int rb0 = wr * WR + b * 16;
+              if (i0 >= rb0 + 16 || i1 <= rb0) continue;
+              const int r = rb0 + (lane & 15);
+              const bool in = r >= i0 && r < i1;
 #pragma unroll
-              for (int bo = 0; bo < NBO; ++bo) acc[bo][b] = mfma16(af[0][bo], tf, acc[bo][b]);
+              for (int c = 0; c < 2; ++c) {
+                if (c >= nck) break;
+                const uint4 tv = tlds[c * BR * 8 + r * 8 + (c8 ^ ((r >> 1) & 7))];
+                const uint4 tf = in ? tv : z4();
+#pragma unroll
+                for (int bo = 0; bo < OB; ++bo) acc[ob + bo][b] = mfma16(af[0][bo], tf, acc[ob + bo][b]);
+              }
             }
           }
         }
@@ -496,18 +501,31 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
   }
 
   // ---------------------------------------------------------- epilogue
+  // The tile goes through LDS as bf16 (16-byte chunk c of tile row r at slot
+  // c ^ (r % CPR), so the fragment-ordered writes spread over the banks) and
+  // leaves in whole 16-byte pieces, each tile row's by consecutive lanes.
+  constexpr int CPR = BO / 8;  // 16-byte chunks per tile row
+  static_assert(BR * CPR <= NS * RS * 8, "the bf16 tile fits the ring");
+  uint4 *const ylds = &ring[0][0];
+  __syncthreads();  // every wave is done with the ring
 #pragma unroll
   for (int bo = 0; bo < NBO; ++bo) {
-    const int o = o0 + wo * WO + bo * 16 + (lane >> 4) * 4;
+    const int oc = wo * WO + bo * 16 + (lane >> 4) * 4;  // four outputs of the tile
 #pragma unroll
     for (int br = 0; br < NBR; ++br) {
-      const int lr = wr * WR + br * 16 + (lane & 15);
-      const int grow = s_row[lr];
-      if (grow < 0 || o >= p.n_out) continue;
+      const int lr = wr * WR + br * 16 + (lane & 15);  // tile row
       const f32x4 v = acc[bo][br];
-      uint2 pk = make_uint2(pack2(f2bf(v[0]), f2bf(v[1])), pack2(f2bf(v[2]), f2bf(v[3])));
-      *(uint2 *)(p.y + (size_t)grow * p.y_row_stride + o) = pk;
+      const uint2 pk = make_uint2(pack2(f2bf(v[0]), f2bf(v[1])), pack2(f2bf(v[2]), f2bf(v[3])));
+      uint2 *dst = (uint2 *)&ylds[lr * CPR + ((oc >> 3) ^ (lr & (CPR - 1)))];
+      dst[(oc >> 2) & 1] = pk;
     }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < BR * CPR; idx += NW * 64) {
+    const int r = idx / CPR, c = idx % CPR;
+    const int grow = s_row[r], o = o0 + c * 8;
+    if (grow >= 0 && o < p.n_out)
+      *(uint4 *)(p.y + (size_t)grow * p.y_row_stride + o) = ylds[r * CPR + (c ^ (r & (CPR - 1)))];
   }
   };  // segment
 
