@@ -71,9 +71,10 @@ __device__ __forceinline__ int segment_lds(const int *ip, int n_seg, int r) {
   return lo;
 }
 
-// Routes rows row0 + tid + 256 j (j < 8) into pk[]: every load of the batch
+// Routes rows row0 + tid + 256 j (j < J) into pk[]: every load of the batch
 // (the slot inputs, then the three route tables) in flight together.  `seg`
 // is an LDS copy of seg_indptr (segmented calls), or null.
+template <int J = 8>
 __device__ __forceinline__ void route_all(const PrepArgs &a, int *pk, const int *seg, int row0,
                                           bool ranked = false) {
   const int ml = a.has_lora ? a.rd.max_loras : 0;
@@ -81,9 +82,9 @@ __device__ __forceinline__ void route_all(const PrepArgs &a, int *pk, const int 
   const Routing &rt = a.rt;
   {
     const int r0 = row0 + (int)threadIdx.x;
-    int slot[8], expert[8], drop[8];
+    int slot[J], expert[J], drop[J];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < J; ++j) {
       const int r = r0 + 256 * j;
       const bool live = r < a.n;
       int sl = -1, ex = 0, dr = !live;
@@ -103,19 +104,19 @@ __device__ __forceinline__ void route_all(const PrepArgs &a, int *pk, const int 
       expert[j] = ex;
       drop[j] = dr;
     }
-    uint64_t ta[8], tb[8];
-    float sc[8];
+    uint64_t ta[J], tb[J];
+    float sc[J];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {  // the three tables, index 0 standing in for rows without a slot
+    for (int j = 0; j < J; ++j) {  // the three tables, index 0 standing in for rows without a slot
       const bool in = a.has_lora && !drop[j] && slot[j] >= 0 && slot[j] < rd.max_loras;
       const int idx = in ? slot[j] * rd.n_experts + expert[j] : 0;
       ta[j] = in ? (uint64_t)(uintptr_t)rd.a_table[idx] : 0ull;
       tb[j] = in ? (uint64_t)(uintptr_t)rd.b_table[idx] : 0ull;
       sc[j] = in ? rd.scale_table[slot[j]] : 0.f;
     }
-    int qv[8];
+    int qv[J];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < J; ++j) {
       const int r = r0 + 256 * j;
       const bool ok = ta[j] != 0ull && tb[j] != 0ull && sc[j] != 0.0f;
       const int q = drop[j] ? kDrop : (ok ? slot[j] * rd.n_experts + expert[j] : kSkip);
@@ -127,7 +128,7 @@ __device__ __forceinline__ void route_all(const PrepArgs &a, int *pk, const int 
       const int lane = threadIdx.x & 63;
       const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < J; ++j) {
         int q = qv[j], rank = -1;
         uint64_t todo = __ballot(q >= 0);
         for (int round = 0; round < 2 && todo; ++round) {
@@ -538,14 +539,16 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
 
 
 // Every row's packed route, once per call (the plan and the shrink units read
-// it instead of routing all rows again in each workgroup).
+// it instead of routing all rows again in each workgroup): one row per
+// thread, so that each thread's chain of dependent loads and rank atomics is
+// as short as it can be.
 __global__ __launch_bounds__(256) void route_kernel(PrepArgs a) {
   __shared__ int seg[kSegLds];
   const bool sl = seg_in_lds(a.rt);
   if (sl)
     for (int g = threadIdx.x; g <= a.rt.n_seg; g += 256) seg[g] = a.rt.seg_indptr[g];
   __syncthreads();
-  route_all(a, a.routes, sl ? seg : nullptr, (int)blockIdx.x * (256 * 8), a.ranks != nullptr);
+  route_all<1>(a, a.routes, sl ? seg : nullptr, (int)blockIdx.x * 256, a.ranks != nullptr);
 }
 
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
@@ -581,7 +584,7 @@ size_t prep_lds_bytes(const PrepArgs &a) {
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st) {
   const int grid = a.do_plan + a.n_units * a.k_splits;
   if (grid == 0) return hipSuccess;
-  if (a.routes) hipLaunchKernelGGL(route_kernel, dim3((a.n + 2047) / 2048), dim3(256), 0, st, a);
+  if (a.routes) hipLaunchKernelGGL(route_kernel, dim3((a.n + 255) / 256), dim3(256), 0, st, a);
   hipLaunchKernelGGL(prep_kernel, dim3(grid), dim3(256), prep_lds_bytes(a), st, a);
   return hipGetLastError();
 }
