@@ -189,16 +189,21 @@ __device__ void shrink_unit(const DecodeArgs &p, const Rows &s, int uidx, int k0
 }  // namespace
 
 // NB: 16-row blocks of the batch that hold rows (n <= 16 NB).  Wave w owns
-// output blocks OBW (w % (8 / OBW)) .. +OBW-1 and row blocks RBW (w / (8 / OBW)) ..
+// output blocks OBW (w % OWAVES) .. +OBW-1 and row blocks RBW (w / OWAVES) ..
 template <int NB>
 __global__ __launch_bounds__(kNW * 64) void decode_main_kernel(DecodeArgs p) {
-  constexpr int OBW = NB == 4 ? 2 : 1;   // output blocks per wave
-  constexpr int RBW = NB == 4 ? 2 : NB;  // row blocks per wave
-  constexpr int OWAVES = kNW / OBW;      // waves across the output blocks
-  static_assert(OWAVES * OBW * 16 == kTO && (kNW / OWAVES) * RBW == NB, "wave tiling");
+  constexpr int RWAVES = NB >= 2 ? 2 : 1;  // waves across the row blocks
+  constexpr int OWAVES = kNW / RWAVES;     // waves across the output blocks
+  constexpr int OBW = kTO / 16 / OWAVES;   // output blocks per wave
+  constexpr int RBW = NB / RWAVES;         // row blocks per wave
+  static_assert(OWAVES * OBW * 16 == kTO && RWAVES * RBW == NB, "wave tiling");
   __shared__ __attribute__((aligned(16))) uint4 ring[kNS][kRS * 8];
   __shared__ Rows s;
 
+  // every argument the first DMAs need comes in with the first batch of
+  // scalar loads (the route pointer too, which the compiler would otherwise
+  // load behind a branch, one more round trip before the first stage)
+  asm volatile("" ::"s"(p.seq_slot), "s"(p.has_lora));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = p.k_in;
   const int tl = blockIdx.x / p.S, z = blockIdx.x % p.S;
