@@ -437,6 +437,7 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
   // partial through device-coherent (sc1) stores and the last of the unit's
   // k_splits workgroups to arrive sums them in chunk order.
   float *tout = KS == 1 ? a.t_final : a.t + (size_t)kz * a.n * R;
+  const auto prs = coherent_rsrc(a.t, (uint32_t)((size_t)KS * a.n * R * 4));  // the k-chunk partials
   constexpr int GR = kShrinkRows / 16;
 
   for (int rb0 = 0; rb0 < nrb; rb0 += 4) {  // four rank blocks x the row groups at a time
@@ -492,11 +493,8 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
               const float vv[4] = {v[0], v[1], v[2], v[3]};
               store_tt(a.tt, R, rows[i], (rb0 + j) * 16 + (lane >> 4) * 4, sig, vv, 4);
             }
-          } else {
-            const uint64_t lo = (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32);
-            const uint64_t hi = (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32);
-            __hip_atomic_store((uint64_t *)dst, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store((uint64_t *)(dst + 2), hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          } else {  // 16-byte device-coherent store into this chunk's partial
+            st16_coherent(prs, (uint32_t)((dst - a.t) * 4), 0, v);
           }
         }
     }
@@ -511,27 +509,23 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
   __syncthreads();
   if (!info[2]) return;
   // the last of the unit's workgroups: t = sum of the k-chunk partials in
-  // chunk order, every chunk's load in flight together (8 bytes at a time)
-  for (int e = tid * 2; e < nrows * R; e += 256 * 2) {
+  // chunk order, every chunk's 16-byte load in flight together
+  for (int e = tid * 4; e < nrows * R; e += 256 * 4) {
     const int i = e / R, r = e - i * R;
     const size_t off = (size_t)rows[i] * R + r;
-    uint64_t v[kMaxShrinkSplits];
+    f32x4 v[kMaxShrinkSplits];
 #pragma unroll
     for (int z = 0; z < kMaxShrinkSplits; ++z)
-      v[z] = z < KS ? __hip_atomic_load((uint64_t *)(a.t + (size_t)z * a.n * R + off), __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT)
-                    : 0ull;
-    float s0 = 0.f, s1 = 0.f;
+      v[z] = z < KS ? ld16_coherent(prs, (uint32_t)(off * 4), (uint32_t)((size_t)z * a.n * R * 4))
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 sum = v[0];
 #pragma unroll
-    for (int z = 0; z < kMaxShrinkSplits; ++z) {
-      if (z >= KS) break;
-      s0 += __uint_as_float((uint32_t)v[z]);
-      s1 += __uint_as_float((uint32_t)(v[z] >> 32));
-    }
-    *(float2 *)(a.t_final + off) = make_float2(s0, s1);
+    for (int z = 1; z < kMaxShrinkSplits; ++z)
+      if (z < KS) sum += v[z];
+    *(f32x4 *)(a.t_final + off) = sum;
     if (a.tt) {
-      const float vv[2] = {s0, s1};
-      store_tt(a.tt, R, rows[i], r, sig, vv, 2);
+      const float vv[4] = {sum[0], sum[1], sum[2], sum[3]};
+      store_tt(a.tt, R, rows[i], r, sig, vv, 4);
     }
   }
   if (tid == 0) __hip_atomic_store(&a.counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
