@@ -337,8 +337,8 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
   int *wsum = cnt + P;        // [4]
   int *info = wsum + 4;       // [4]
   int *rows = info + 4;       // [kShrinkRows]
-  f32x4 *red = (f32x4 *)(lds + ((P + 8 + kShrinkRows + 3) & ~3));  // [3][4][kShrinkRows/16][64]
-  int *pk = (int *)(red + 3 * 4 * (kShrinkRows / 16) * 64);  // [n] the rows' packed routes
+  uint4 *stg = (uint4 *)(lds + ((P + 8 + kShrinkRows + 3) & ~3));  // [kShrinkStages][128 rows][8] stages
+  int *pk = (int *)(stg + kShrinkStages * 128 * 8);  // [n] the rows' packed routes (standalone shrink)
 
   const bool ranked = a.ranks != nullptr;  // the route kernel counted and ranked the rows
   if (ranked) {
@@ -419,86 +419,90 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
   const int nrows = min(kShrinkRows, info[3] - first);
 
   const u16 *A = (const u16 *)a.rd.a_table[pstar];
-  const int R = a.rd.R, nrb = R / 16, K = a.k_in;
+  const int R = a.rd.R, K = a.k_in;
   const float sig = a.rd.scale_table[pstar / a.rd.n_experts];
   const int G = (nrows + 15) / 16;  // row groups of 16 (<= kShrinkRows / 16)
-  const u16 *xr[kShrinkRows / 16];
-#pragma unroll
-  for (int g = 0; g < kShrinkRows / 16; ++g) {
-    const int j = g * 16 + (lane & 15);
-    xr[g] = g < G && j < nrows ? a.x + (size_t)rows[j] * a.x_stride : nullptr;
-  }
-  // this unit's k chunk, cut in 32-wide steps; wave w takes steps w, w+4, ...
+  // this unit's k chunk, in 64-wide stages
   const int chunk = ((K + KS - 1) / KS + 127) / 128 * 128;
   const int kc0 = min(kz * chunk, K), kc1 = min(kc0 + chunk, K);
-  const int nsteps = (kc1 - kc0 + 31) / 32;
-  const int koff = (lane >> 4) * 8;
+  const int nst = (kc1 - kc0 + 63) / 64;
   // k_splits == 1: this unit writes the final t.  Otherwise it writes its
-  // partial through device-coherent (sc1) stores and the last of the unit's
+  // partial through device-coherent stores and the last of the unit's
   // k_splits workgroups to arrive sums them in chunk order.
   float *tout = KS == 1 ? a.t_final : a.t + (size_t)kz * a.n * R;
   const auto prs = coherent_rsrc(a.t, (uint32_t)((size_t)KS * a.n * R * 4));  // the k-chunk partials
-  constexpr int GR = kShrinkRows / 16;
 
-  for (int rb0 = 0; rb0 < nrb; rb0 += 4) {  // four rank blocks x the row groups at a time
-    const int nb = min(4, nrb - rb0);
-    f32x4 acc[4][GR];
+  // 64 ranks at a time.  A stage is 64 k columns of the group's rank rows of
+  // A, then of the unit's x rows (gathered, 16 G of them), in whole 128-byte
+  // lines by LDS-DMA (chunk c of row r at slot c ^ ((r >> 1) & 7)); up to
+  // kShrinkStages stages go out together, then wave w takes rank block w
+  // through them, every row group, in k order.
+  for (int rg = 0; rg * 64 < R; ++rg) {
+    const int RA = min(64, R - rg * 64);  // rank rows of the group
+    const int RU = RA + 16 * G;           // rows of a stage
+    const int per = RU / 8;               // DMA instructions per stage
+    f32x4 acc[kShrinkRows / 16];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int g = 0; g < GR; ++g) acc[j][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const u16 *Ab = A + (size_t)(rb0 * 16 + (lane & 15)) * K;
-    for (int s0 = wave; s0 < nsteps; s0 += 4 * 4) {  // four steps per wave in flight
-      uint4 xv[4][GR], av[4][4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int kk = kc0 + (s0 + 4 * s) * 32 + koff;
-        const bool in = kk < kc1;
-#pragma unroll
-        for (int g = 0; g < GR; ++g) xv[s][g] = (xr[g] && in) ? ldg16(xr[g] + kk) : z4();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) av[s][j] = (in && j < nb) ? ldg16(Ab + (size_t)j * 16 * K + kk) : z4();
+    for (int g = 0; g < kShrinkRows / 16; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sb = 0; sb < nst; sb += kShrinkStages) {
+      const int nsn = min(kShrinkStages, nst - sb), kb0 = kc0 + sb * 64;
+      __syncthreads();  // the previous batch is read
+      for (int ii = wave; ii < nsn * per; ii += 4) {
+        const int st = ii / per, k8 = ii % per;
+        const int rr = k8 * 8 + (lane >> 3);  // row of the stage
+        const u16 *rowp = rr < RA ? A + (size_t)(rg * 64 + rr) * K
+                                  : a.x + (size_t)rows[min(rr - RA, nrows - 1)] * a.x_stride;
+        const int kk = kb0 + st * 64 + ((lane & 7) ^ ((rr >> 1) & 7)) * 8;
+        dma16(rowp + (kk < kc1 ? kk : kc0), lds_addr(stg + (st * RU + k8 * 8) * 8));
       }
+      __builtin_amdgcn_s_waitcnt(0);
+      if (kb0 + nsn * 64 > kc1) {  // zero what the last stage fetched past the chunk
+        for (int ii = wave; ii < nsn * per; ii += 4) {
+          const int st = ii / per, k8 = ii % per;
+          const int rr = k8 * 8 + (lane >> 3);
+          if (kb0 + st * 64 + ((lane & 7) ^ ((rr >> 1) & 7)) * 8 >= kc1) stg[(st * RU + k8 * 8) * 8 + lane] = z4();
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      }
+      __syncthreads();
+      if (wave * 16 < RA) {
+        const int ra = wave * 16 + (lane & 15);
+        for (int st = 0; st < nsn; ++st) {
+          const uint4 *sl = stg + st * RU * 8;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+          for (int h = 0; h < 2; ++h) {
+            const int c = 4 * h + (lane >> 4);
+            const uint4 av = sl[ra * 8 + (c ^ ((ra >> 1) & 7))];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int g = 0; g < GR; ++g)
-            if (j < nb && g < G) acc[j][g] = mfma16(av[s][j], xv[s][g], acc[j][g]);
-    }
-    if (wave > 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int g = 0; g < GR; ++g) red[(((wave - 1) * 4 + j) * GR + g) * 64 + lane] = acc[j][g];
-    }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int g = 0; g < GR; ++g) {
-          const int i = g * 16 + (lane & 15);
-          if (j >= nb || i >= nrows) continue;
-          f32x4 v = acc[j][g];  // fixed order: wave 0, 1, 2, 3
-          v += red[((0 * 4 + j) * GR + g) * 64 + lane];
-          v += red[((1 * 4 + j) * GR + g) * 64 + lane];
-          v += red[((2 * 4 + j) * GR + g) * 64 + lane];
-          // D column = lane%16 (the row), D rows = ranks 4*(lane/16) .. +3 of block rb0+j
-          float *dst = tout + (size_t)rows[i] * R + (rb0 + j) * 16 + (lane >> 4) * 4;
-          if (KS == 1) {
-            *(f32x4 *)dst = v;
-            if (a.tt) {
-              const float vv[4] = {v[0], v[1], v[2], v[3]};
-              store_tt(a.tt, R, rows[i], (rb0 + j) * 16 + (lane >> 4) * 4, sig, vv, 4);
+            for (int g = 0; g < kShrinkRows / 16; ++g) {
+              if (g >= G) break;
+              const int rx = RA + g * 16 + (lane & 15);
+              acc[g] = mfma16(av, sl[rx * 8 + (c ^ ((rx >> 1) & 7))], acc[g]);
             }
-          } else {  // 16-byte device-coherent store into this chunk's partial
-            st16_coherent(prs, (uint32_t)((dst - a.t) * 4), 0, v);
           }
         }
+      }
     }
-    __syncthreads();
+    if (wave * 16 < RA) {
+#pragma unroll
+      for (int g = 0; g < kShrinkRows / 16; ++g) {
+        const int i = g * 16 + (lane & 15);
+        if (g >= G || i >= nrows) continue;
+        // D column = lane%16 (the row), D rows = ranks 4*(lane/16) .. +3 of the wave's block
+        const int rk = rg * 64 + wave * 16 + (lane >> 4) * 4;
+        float *dst = tout + (size_t)rows[i] * R + rk;
+        const f32x4 v = acc[g];
+        if (KS == 1) {
+          *(f32x4 *)dst = v;
+          if (a.tt) {
+            const float vv[4] = {v[0], v[1], v[2], v[3]};
+            store_tt(a.tt, R, rows[i], rk, sig, vv, 4);
+          }
+        } else {  // 16-byte device-coherent store into this chunk's partial
+          st16_coherent(prs, (uint32_t)((dst - a.t) * 4), 0, v);
+        }
+      }
+    }
   }
   if (KS == 1) return;
   __builtin_amdgcn_s_waitcnt(0);
@@ -569,8 +573,8 @@ size_t prep_lds_bytes(const PrepArgs &a) {
   const int NG = a.rt.n_experts;
   const int NK = NG * (ml + 1);
   size_t plan = a.do_plan ? (size_t)(2 * NK + NG + 8 + a.n + (a.stable ? 3 * NK : 0)) * 4 : 0;
-  size_t shr = a.n_units ? (size_t)((a.n_pairs + 8 + kShrinkRows + 3) & ~3) * 4 + 3 * 4 * (kShrinkRows / 16) * 64 * 16 +
-                               (size_t)a.n * 4
+  size_t shr = a.n_units ? (size_t)((a.n_pairs + 8 + kShrinkRows + 3) & ~3) * 4 + (size_t)kShrinkStages * 128 * 128 +
+                               (a.ranks ? 0 : (size_t)a.n * 4)
                          : 0;
   return plan > shr ? plan : shr;
 }

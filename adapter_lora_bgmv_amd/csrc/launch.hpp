@@ -107,8 +107,9 @@ constexpr int kDecodeTileOut = 128;
 constexpr int kDecodeMaxStages = 8;
 constexpr int kDecodeMaxSplit = 16;
 
-// Rows per shrink unit.
+// Rows per shrink unit; its 64-column stages in LDS at a time (16 KB each).
 constexpr int kShrinkRows = 64;
+constexpr int kShrinkStages = 4;
 // Largest k split of the shrink units.
 constexpr int kMaxShrinkSplits = 8;
 // Largest key space the one-workgroup plan handles (LDS histogram).
