@@ -79,7 +79,7 @@ class Workload:
     B: np.ndarray                      # [P][n_out][max_rank], pad cols zero
     x: np.ndarray                      # [n][k_in]
     adapters: List[AdapterSpec]        # one per pool slot (moe: per adapter)
-    kind: str = "decode"               # decode | segmented | moe
+    kind: str = "decode"               # decode | segmented | moe | moe_grouped
     # decode routing (metrale slot_math.rs build_seq_slot_host inputs)
     adapter_slots: Optional[np.ndarray] = None   # [n_real] int32, <0 = active
     padded_n: int = 0
@@ -92,6 +92,9 @@ class Workload:
     top_k: int = 0
     indices: Optional[np.ndarray] = None         # [n_tokens*top_k] int32, slot-major
     token_slot: Optional[np.ndarray] = None      # [n_tokens] int32
+    # moe grouped routing: rows sorted by expert
+    expert_offsets: Optional[np.ndarray] = None  # [n_experts+1] int32, non-decreasing
+    row_slot: Optional[np.ndarray] = None        # [n] int32, each sorted row's adapter slot
     # slots whose table entry is NULL (a base-only slot), by pool index
     null_slots: List[int] = field(default_factory=list)
     # the true-rank (unpadded) pool, for padded == true-rank checks
@@ -226,6 +229,42 @@ def moe_down_gather(seed: int = 0, n_experts: int = 64, n_out: int = 2048, k: in
                     indices=idx.reshape(-1), token_slot=token_slot, A_true=At, B_true=Bt)
 
 
+def group_by_expert(indices: np.ndarray, token_slot: np.ndarray, top_k: int, n_experts: int):
+    """Sorts slot-major routing slots by expert (stable).  Returns the order
+    (sorted position -> routing slot), expert_offsets [E+1] and each sorted
+    row's adapter slot (its token's)."""
+    order = np.argsort(indices, kind="stable").astype(np.int32)
+    counts = np.bincount(indices, minlength=n_experts)
+    offsets = np.zeros(n_experts + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    return order, offsets, token_slot[order // top_k].astype(np.int32)
+
+
+def moe_down_grouped(seed: int = 0, n_experts: int = 64, n_out: int = 2048, k: int = 1408,
+                     n_tokens: int = 2048, top_k: int = 6, n_adapters: int = 4,
+                     rank: int = 16) -> Workload:
+    """MoE down_proj, grouped: the gather workload's expert and pool shapes with
+    a prefill-sized batch (2048 tokens, top-6) whose routing slots come
+    sorted by expert, delimited by expert_offsets."""
+    rng = np.random.default_rng(seed)
+    W = _store(rng.standard_normal((n_experts, n_out, k)) * 0.02, BF16)
+    P = n_adapters * n_experts
+    A, B, At, Bt = _pool(rng, [rank] * P, k, n_out, rank, 0.02, BF16)
+    n = n_tokens * top_k
+    x = _store(rng.standard_normal((n, k)), BF16)  # already in sorted order
+    idx = np.empty((n_tokens, top_k), np.int32)
+    for t in range(n_tokens):
+        idx[t] = rng.choice(n_experts, size=top_k, replace=False)
+    token_slot = rng.integers(0, n_adapters, size=n_tokens).astype(np.int32)
+    order, offsets, row_slot = group_by_expert(idx.reshape(-1), token_slot, top_k, n_experts)
+    return Workload(name=f"moe_down_grouped_{n_experts}x{n_out}x{k}_t{n_tokens}_top{top_k}_r{rank}",
+                    dtype=BF16, k_in=k, n_out=n_out, max_rank=rank, W=W, A=A, B=B, x=x,
+                    adapters=[AdapterSpec(rank, 0.0, 1.0) for _ in range(n_adapters)],
+                    kind="moe_grouped", n_experts=n_experts, top_k=top_k,
+                    expert_offsets=offsets, row_slot=row_slot, A_true=At, B_true=Bt,
+                    meta={"order": order})
+
+
 # the five workloads, full size, seed 0
 CONFIGS = {
     "single_projection_f32": single_projection_f32,
@@ -247,7 +286,7 @@ def random_small(seed: int, dtype: str = BF16, k: int = 96, n_out: int = 80, n: 
     rng = np.random.default_rng(seed)
     if ranks is None:
         ranks = [int(rng.integers(1, max_rank + 1)) for _ in range(n_slots)]
-    if kind == "moe":
+    if kind in ("moe", "moe_grouped"):
         W = _store(rng.standard_normal((n_experts, n_out, k)) * sigma_w, dtype)
         P = n_slots * n_experts
         rk = [ranks[p // n_experts] for p in range(P)]
@@ -288,4 +327,17 @@ def random_small(seed: int, dtype: str = BF16, k: int = 96, n_out: int = 80, n: 
         common["adapters"] = adapters
         return Workload(name=f"small_moe_s{seed}", x=x, kind="moe", n_experts=n_experts,
                         top_k=top_k, indices=idx.reshape(-1), token_slot=token_slot, **common)
+    if kind == "moe_grouped":
+        # n rows inside the expert ranges (some experts empty), a few rows
+        # before the first range and after the last, which are not written
+        counts = rng.multinomial(n, np.full(n_experts, 1.0 / n_experts))
+        lead, tail = (int(v) for v in rng.integers(0, 3, size=2))
+        offsets = np.zeros(n_experts + 1, np.int32)
+        offsets[1:] = np.cumsum(counts)
+        offsets += lead
+        nn = lead + n + tail
+        x = _store(rng.standard_normal((nn, k)), dtype)
+        row_slot = rng.integers(-1, n_slots + 1, size=nn).astype(np.int32)
+        return Workload(name=f"small_moe_grouped_s{seed}", x=x, kind="moe_grouped",
+                        n_experts=n_experts, expert_offsets=offsets, row_slot=row_slot, **common)
     raise ValueError(kind)

@@ -96,6 +96,13 @@ class Oracle:
         L.orc_apply_moe_gather.argtypes = [C.c_void_p, C.c_longlong, C.c_int, RP, C.c_int,
                                            C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_int, _i32p,
                                            C.c_int, _i32p, _i32p, C.c_int, _f64p]
+        L.orc_apply_moe_grouped.argtypes = [C.c_void_p, C.c_longlong, C.c_int, RP, C.c_int,
+                                            C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_int,
+                                            _i32p, _i32p, _i32p, C.c_int, _f64p]
+        L.orc_moe_grouped_shrink.argtypes = [RP, C.c_void_p, C.c_int, _i32p, _i32p, C.c_int,
+                                             _f64p]
+        L.orc_moe_grouped_expand_fold.argtypes = [RP, _f32p, _i32p, _i32p, C.c_int, C.c_void_p,
+                                                  C.c_int, _f64p]
         L.orc_mutant.restype = C.c_int
         L.orc_threads.restype = C.c_int
         self.L = L
@@ -212,6 +219,53 @@ class Oracle:
                                     _p(rr, _i32p), len(rr), _p(y, _f64p))
         return y
 
+    def apply_moe_grouped(self, W, route, x, expert_offsets, seq_slot, dtype, rows=None,
+                          fill=np.nan) -> np.ndarray:
+        """Grouped MoE: rows sorted by expert, expert e's rows in
+        [expert_offsets[e], expert_offsets[e+1]); rows outside every range
+        keep ``fill``."""
+        W = np.ascontiguousarray(W)
+        x = np.ascontiguousarray(x)
+        E, n_out, k_in = W.shape
+        off = np.ascontiguousarray(expert_offsets, np.int32)
+        assert len(off) == E + 1
+        ss = None if seq_slot is None else np.ascontiguousarray(seq_slot, np.int32)
+        rr = np.arange(x.shape[0], dtype=np.int32) if rows is None else \
+            np.ascontiguousarray(rows, np.int32)
+        y = np.full((len(rr), n_out), fill, np.float64)
+        rp = C.byref(route.c) if route is not None else None
+        self.L.orc_apply_moe_grouped(_p(W), n_out * k_in, k_in, rp, dtype, k_in, n_out, E, _p(x),
+                                     x.shape[1], _p(off, _i32p),
+                                     _p(ss, _i32p) if ss is not None else None,
+                                     _p(rr, _i32p), len(rr), _p(y, _f64p))
+        return y
+
+    def moe_grouped_shrink(self, route: Route, x, expert_offsets, seq_slot,
+                           fill: float = np.nan) -> np.ndarray:
+        x = np.ascontiguousarray(x)
+        n = x.shape[0]
+        off = np.ascontiguousarray(expert_offsets, np.int32)
+        assert len(off) == route.c.n_experts + 1
+        ss = np.ascontiguousarray(seq_slot, np.int32)
+        t = np.full((n, route.c.max_rank), fill, np.float64)
+        self.L.orc_moe_grouped_shrink(C.byref(route.c), _p(x), x.shape[1], _p(off, _i32p),
+                                      _p(ss, _i32p), n, _p(t, _f64p))
+        return t
+
+    def moe_grouped_expand_fold(self, route: Route, t, expert_offsets, seq_slot,
+                                y_in) -> np.ndarray:
+        t = np.ascontiguousarray(t, np.float32)
+        y_in = np.ascontiguousarray(y_in)
+        n = y_in.shape[0]
+        off = np.ascontiguousarray(expert_offsets, np.int32)
+        assert len(off) == route.c.n_experts + 1
+        ss = np.ascontiguousarray(seq_slot, np.int32)
+        out = np.empty((n, route.c.n_out), np.float64)
+        self.L.orc_moe_grouped_expand_fold(C.byref(route.c), _p(t, _f32p), _p(off, _i32p),
+                                           _p(ss, _i32p), n, _p(y_in), y_in.shape[1],
+                                           _p(out, _f64p))
+        return out
+
     # -------------------------------------------------------------- workload glue
     def seq_slot_for(self, wl) -> np.ndarray:
         return self.build_seq_slot(wl.adapter_slots, wl.padded_n, wl.active)
@@ -226,6 +280,9 @@ class Oracle:
             return self.apply_segmented(wl.W, r, wl.x, wl.seg_indptr, wl.seg_slot, dt, rows)
         if wl.kind == "moe":
             return self.apply_moe(wl.W, r, wl.x, wl.indices, wl.top_k, wl.token_slot, dt, rows)
+        if wl.kind == "moe_grouped":
+            return self.apply_moe_grouped(wl.W, r, wl.x, wl.expert_offsets, wl.row_slot, dt,
+                                          rows)
         raise ValueError(wl.kind)
 
 

@@ -24,7 +24,8 @@
  *  - atlas "spark_model/layers/ops/lora_delta.rs": LoraRoute, LoraPair
  *    (rank padding, scale alpha/r or alpha/sqrt(r)), apply_lora_bgmv doc
  *    (seq_slot < 0 = base; NULL/0 table entries = base-only slot), the
- *    moe_lora_gather_bgmv field doc (expert keyed through indices).
+ *    moe_lora_gather_bgmv field doc (expert keyed through indices), the
+ *    moe_lora_grouped_down field doc (expert keyed through expert_offsets).
  *  - metrale "lora/slot_math.rs": build_seq_slot_host, scale_table_values.
  *
  * Readings where the pages leave a step open are listed with each function.
@@ -355,6 +356,100 @@ void orc_apply_moe_gather(const void *W, long long expert_stride, int w_stride,
     int a = token_slot[j / top_k];
     apply_row(W, (size_t)e * (size_t)expert_stride, w_stride, r, dtype, k_in, n_out, x,
               xrow((size_t)j, x_stride, k_in), a, e, y + (size_t)jj * n_out);
+  }
+}
+
+/*
+ * MoE grouped layout (atlas lora_delta.rs, the moe_lora_grouped_down field
+ * doc: the expert down_proj delta keyed on expert through device
+ * expert_offsets, the sorted twin of the gather above).  The rows come
+ * sorted by expert: rows expert_offsets[e] .. expert_offsets[e+1]-1 belong
+ * to expert e.  Readings: offsets are non-decreasing, so at most one range
+ * holds a row; a row outside every range is not written; each sorted row
+ * carries its own adapter slot (seq_slot[j], the slot of the token it came
+ * from), resolved by the same rule as the dense path with the pair of
+ * (adapter a, expert e) at table index a * n_experts + e.
+ * Returns the expert of row j, or -1.
+ */
+static int expert_of(const int32_t *offsets, int n_experts, int j) {
+  for (int e = 0; e < n_experts; ++e) {
+#if ORC_MUTANT == 13
+    if (j >= offsets[e] && j <= offsets[e + 1]) return e;
+#else
+    if (j >= offsets[e] && j < offsets[e + 1]) return e;
+#endif
+  }
+  return -1;
+}
+
+/* The slot a grouped row carries. */
+static int grouped_slot(const int32_t *seq_slot, const int32_t *offsets, int e, int j) {
+#if ORC_MUTANT == 14
+  return seq_slot[j - offsets[e]];
+#else
+  (void)offsets;
+  (void)e;
+  return seq_slot[j];
+#endif
+}
+
+/*
+ * Fused grouped apply: y[j] = W_e x[j] + s_a B_{a,e} (A_{a,e} x[j]) for row
+ * j of expert e's range, a = seq_slot[j]; only the listed rows, in order.
+ * Rows outside every range are left untouched.  `r` may be NULL (base only).
+ */
+void orc_apply_moe_grouped(const void *W, long long expert_stride, int w_stride,
+                           const orc_route *r, int dtype, int k_in, int n_out, int n_experts,
+                           const void *x, int x_stride, const int32_t *expert_offsets,
+                           const int32_t *seq_slot, const int32_t *rows, int n_rows,
+                           double *y) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int jj = 0; jj < n_rows; ++jj) {
+    int j = rows[jj];
+    int e = expert_of(expert_offsets, n_experts, j);
+    if (e < 0) continue;
+    int a = seq_slot ? grouped_slot(seq_slot, expert_offsets, e, j) : -1;
+    apply_row(W, (size_t)e * (size_t)expert_stride, w_stride, r, dtype, k_in, n_out, x,
+              xrow((size_t)j, x_stride, k_in), a, e, y + (size_t)jj * n_out);
+  }
+}
+
+/* The grouped shrink: t[j] = A_{a,e} x[j] for rows that resolve; others untouched. */
+void orc_moe_grouped_shrink(const orc_route *r, const void *x, int x_stride,
+                            const int32_t *expert_offsets, const int32_t *seq_slot, int n,
+                            double *t) {
+#pragma omp parallel for schedule(static)
+  for (int j = 0; j < n; ++j) {
+    int e = expert_of(expert_offsets, r->n_experts, j);
+    if (e < 0) continue;
+    int idx = resolve(r, grouped_slot(seq_slot, expert_offsets, e, j), e);
+    if (idx < 0) continue;
+    shrink_row(r, idx, x, xrow((size_t)j, x_stride, r->k_in), t + (size_t)j * r->max_rank);
+  }
+}
+
+/*
+ * The grouped expand-and-fold: y_out[j] = y_in[j] + s_a B_{a,e} t[j] for rows
+ * that resolve; every other row (skipped, or outside every range) copies
+ * y_in exactly.
+ */
+void orc_moe_grouped_expand_fold(const orc_route *r, const float *t,
+                                 const int32_t *expert_offsets, const int32_t *seq_slot, int n,
+                                 const void *y_in, int y_stride, double *y_out) {
+#pragma omp parallel for schedule(static)
+  for (int j = 0; j < n; ++j) {
+    double *yo = y_out + (size_t)j * r->n_out;
+    for (int o = 0; o < r->n_out; ++o) yo[o] = widen(y_in, r->dtype, (size_t)j * y_stride + o);
+    int e = expert_of(expert_offsets, r->n_experts, j);
+    if (e < 0) continue;
+    int a = grouped_slot(seq_slot, expert_offsets, e, j);
+    int idx = resolve(r, a, e);
+    if (idx < 0) continue;
+    double *tt = (double *)malloc(sizeof(double) * (size_t)r->max_rank);
+    for (int k = 0; k < r->max_rank; ++k) tt[k] = (double)t[(size_t)j * r->max_rank + k];
+    double s = (double)r->scale[a];
+    for (int o = 0; o < r->n_out; ++o) yo[o] = yo[o] + delta_sign() * s * expand_one(r, idx, o, tt);
+    free(tt);
   }
 }
 

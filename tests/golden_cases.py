@@ -19,6 +19,12 @@ def _arr(v, dtype):
     return f32_to_bf16_bits(a) if dtype == "bf16" else a
 
 
+def expected_y(case):
+    """The case's y as fp64, NaN for rows that are not written (null)."""
+    n_out = case["n_out"]
+    return np.array([[np.nan] * n_out if r is None else r for r in case["y"]], np.float64)
+
+
 def hand_workload(case, dtype="f32"):
     ad = [AdapterSpec(rank=r, alpha=al, adapter_scale=s, rslora=rs)
           for (s, al, r, rs) in case["adapters"]]
@@ -33,6 +39,10 @@ def hand_workload(case, dtype="f32"):
     elif case["kind"] == "segmented":
         kw.update(seg_indptr=np.array(case["seg_indptr"], np.int32),
                   seg_slot=np.array(case["seg_slot"], np.int32))
+    elif case["kind"] == "moe_grouped":
+        kw.update(n_experts=case["n_experts"],
+                  expert_offsets=np.array(case["expert_offsets"], np.int32),
+                  row_slot=np.array(case["seq_slot"], np.int32))
     else:
         kw.update(n_experts=case["n_experts"], top_k=case["top_k"],
                   indices=np.array(case["indices"], np.int32),

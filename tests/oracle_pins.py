@@ -81,6 +81,8 @@ def _hand_run(o, wl, case):
         return o.apply(wl.W, r, wl.x, wl.meta["seq_slot"], dt)
     if wl.kind == "segmented":
         return o.apply_segmented(wl.W, r, wl.x, wl.seg_indptr, wl.seg_slot, dt)
+    if wl.kind == "moe_grouped":
+        return o.apply_moe_grouped(wl.W, r, wl.x, wl.expert_offsets, wl.row_slot, dt)
     return o.apply_moe(wl.W, r, wl.x, wl.indices, wl.top_k, wl.token_slot, dt)
 
 
@@ -90,7 +92,8 @@ def hand_cases(o):
         for dtype in ("f32", "bf16"):
             wl = golden_cases.hand_workload(case, dtype)
             y = _hand_run(o, wl, case)
-            assert np.array_equal(y, np.array(case["y"], np.float64)), (case["name"], dtype, y)
+            want = golden_cases.expected_y(case)
+            assert np.array_equal(y, want, equal_nan=True), (case["name"], dtype, y)
 
 
 @pin
@@ -165,6 +168,75 @@ def brute_force_tiny_moe(o):
         want = brute.dense_rows(wl.W, wl.A, wl.B, wl.x, "bf16", slots, st, (),
                                 n_experts=wl.n_experts, experts=wl.indices)
         _close(y, want, 1e-12, f"moe seed {seed}")
+
+
+def _grouped_experts(offsets, n):
+    """Each row's expert from the ranges, -1 outside: numpy's searchsorted, not
+    the oracle's scan."""
+    off = np.asarray(offsets, np.int64)
+    e = np.searchsorted(off, np.arange(n), side="right") - 1
+    e[(np.arange(n) < off[0]) | (np.arange(n) >= off[-1])] = -1
+    return e
+
+
+@pin
+def brute_force_tiny_moe_grouped(o):
+    for seed in range(5):
+        dtype = "bf16" if seed % 2 == 0 else "f32"
+        wl = WL.random_small(300 + seed, dtype=dtype, k=10, n_out=7, n=9, n_slots=3,
+                             max_rank=4, kind="moe_grouped", n_experts=4)
+        st = o.scale_table(wl.adapters)
+        y = o.apply_moe_grouped(wl.W, o.route_for(wl, st), wl.x, wl.expert_offsets,
+                                wl.row_slot, _dt(wl))
+        ex = _grouped_experts(wl.expert_offsets, wl.n_rows)
+        inside = ex >= 0
+        assert np.all(np.isnan(y[~inside])), "a row outside every range was written"
+        want = brute.dense_rows(wl.W, wl.A, wl.B, wl.x[inside], dtype, wl.row_slot[inside], st,
+                                (), n_experts=wl.n_experts, experts=ex[inside])
+        _close(y[inside], want, 1e-12, f"moe grouped seed {seed}")
+
+
+@pin
+def grouped_equals_gather_sorted(o):
+    """The grouped layout is the gather's routing slots sorted by expert: the same
+    rows give the same outputs, bit for bit, in the sorted order."""
+    wl = WL.random_small(400, dtype="bf16", k=12, n_out=8, n=6, n_slots=3, max_rank=4,
+                         kind="moe", n_experts=5, top_k=3)
+    st = o.scale_table(wl.adapters)
+    r = o.route_for(wl, st)
+    yg = o.apply_moe(wl.W, r, wl.x, wl.indices, wl.top_k, wl.token_slot, 1)
+    order, off, rs = WL.group_by_expert(wl.indices, wl.token_slot, wl.top_k, wl.n_experts)
+    ys = o.apply_moe_grouped(wl.W, r, wl.x[order], off, rs, 1)
+    assert np.array_equal(ys, yg[order])
+
+
+@pin
+def grouped_shrink_and_expand_match_matmul(o):
+    wl = WL.random_small(401, dtype="bf16", k=24, n_out=10, n=12, n_slots=3, max_rank=8,
+                         kind="moe_grouped", n_experts=3)
+    wl.null_slots = [4]  # adapter 1, expert 1
+    st = o.scale_table(wl.adapters)
+    r = o.route_for(wl, st)
+    t = o.moe_grouped_shrink(r, wl.x, wl.expert_offsets, wl.row_slot)
+    rng = np.random.default_rng(2)
+    tin = rng.standard_normal((wl.n_rows, wl.max_rank)).astype(np.float32)
+    yin = WL.f32_to_bf16_bits(rng.standard_normal((wl.n_rows, wl.n_out)).astype(np.float32))
+    yo = o.moe_grouped_expand_fold(r, tin, wl.expert_offsets, wl.row_slot, yin)
+    Ad, Bd, xd = (brute.widen(v, "bf16") for v in (wl.A, wl.B, wl.x))
+    ex = _grouped_experts(wl.expert_offsets, wl.n_rows)
+    live = 0
+    for j in range(wl.n_rows):
+        s, e = int(wl.row_slot[j]), int(ex[j])
+        p = s * wl.n_experts + e
+        if e >= 0 and brute.resolved(s, len(st), set(), st) and p not in wl.null_slots:
+            live += 1
+            _close(t[j], Ad[p] @ xd[j], 1e-12, f"grouped shrink row {j}")
+            _close(yo[j], brute.widen(yin[j], "bf16") + float(st[s]) * (Bd[p] @ tin[j].astype(np.float64)),
+                   1e-12, f"grouped expand row {j}")
+        else:
+            assert np.all(np.isnan(t[j])), f"skipped row {j} written"
+            assert np.array_equal(yo[j], brute.widen(yin[j], "bf16")), f"skipped row {j} changed"
+    assert live >= 4
 
 
 @pin

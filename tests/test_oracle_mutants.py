@@ -7,6 +7,8 @@ Each mutant is a build of oracle/lora_oracle.c with ORC_MUTANT=k (CPU only):
  4 B read transposed                           10 MoE pair index e*max_loras + a
  5 delta subtracted                            11 segment end treated as inclusive
  6 padding rows take the active slot           12 base drops the first input column
+13 grouped expert range end treated as inclusive
+14 grouped row slot read relative to its expert's first row
 """
 import shutil
 
@@ -16,7 +18,7 @@ import oracle
 import oracle_pins
 from oracle import build as obuild
 
-MUTANTS = list(range(1, 13))
+MUTANTS = list(range(1, 15))
 
 
 @pytest.fixture(scope="module")
