@@ -17,7 +17,7 @@ import numpy as np
 LIB_PATH = Path(__file__).resolve().parent / "_lib" / "liblora_mi355x.so"
 
 LORA_F32, LORA_BF16 = 0, 1
-LORA_OP_APPLY, LORA_OP_SEGMENTED, LORA_OP_MOE_GATHER = 0, 1, 2
+LORA_OP_APPLY, LORA_OP_SEGMENTED, LORA_OP_MOE_GATHER, LORA_OP_MOE_GROUPED = 0, 1, 2, 3
 STATUS = {0: "LORA_OK", -1: "LORA_ERR_SHAPE", -2: "LORA_ERR_NULL_PTR", -3: "LORA_ERR_STRIDE",
           -4: "LORA_ERR_DTYPE", -5: "LORA_ERR_UNSUPPORTED", -6: "LORA_ERR_LAUNCH",
           -7: "LORA_ERR_WORKSPACE"}
@@ -26,7 +26,8 @@ STATUS = {0: "LORA_OK", -1: "LORA_ERR_SHAPE", -2: "LORA_ERR_NULL_PTR", -3: "LORA
 EXPORTS = ("lora_last_error", "lora_version", "lora_init", "lora_scale", "lora_scale_table",
            "lora_build_seq_slot", "lora_workspace_bytes", "lora_shrink", "lora_expand_fold",
            "lora_apply", "lora_apply_segmented", "lora_apply_moe_gather",
-           "lora_set_profile_events")
+           "lora_set_profile_events", "lora_moe_grouped_shrink", "lora_moe_grouped_expand_fold",
+           "lora_apply_moe_grouped")
 
 
 class LoraError(RuntimeError):
@@ -80,6 +81,11 @@ def lib() -> C.CDLL:
     L.lora_apply_moe_gather.argtypes = [i32, u32, u32, u32, vp, C.c_uint64, u32,
                                         C.POINTER(lora_route_moe), vp, u32, vp, u32, vp, u32, vp,
                                         u32, vp, sz, vp]
+    RM = C.POINTER(lora_route_moe)
+    L.lora_moe_grouped_shrink.argtypes = [RM, vp, u32, vp, vp, u32, vp, vp]
+    L.lora_moe_grouped_expand_fold.argtypes = [RM, vp, vp, vp, u32, vp, u32, vp]
+    L.lora_apply_moe_grouped.argtypes = [i32, u32, u32, u32, vp, C.c_uint64, u32, RM, vp, u32, vp,
+                                         vp, u32, vp, u32, vp, sz, vp]
     _lib = L
     return L
 
@@ -243,3 +249,28 @@ def lora_apply_moe_gather(dtype: int, n_experts: int, n_out: int, k_in: int, W_e
                                        x_row_stride, _ptr(indices), top_k, _ptr(token_slot),
                                        n_tokens, _ptr(y), y_row_stride, _ptr(workspace),
                                        workspace_bytes, _stream(stream)))
+
+
+def lora_moe_grouped_shrink(route: DeviceRoute, x, x_row_stride: int, expert_offsets, seq_slot,
+                            n: int, t, stream=None):
+    _check(lib().lora_moe_grouped_shrink(C.byref(route.c), _ptr(x), x_row_stride,
+                                         _ptr(expert_offsets), _ptr(seq_slot), n, _ptr(t),
+                                         _stream(stream)))
+
+
+def lora_moe_grouped_expand_fold(route: DeviceRoute, t, expert_offsets, seq_slot, n: int, y,
+                                 y_row_stride: int, stream=None):
+    _check(lib().lora_moe_grouped_expand_fold(C.byref(route.c), _ptr(t), _ptr(expert_offsets),
+                                              _ptr(seq_slot), n, _ptr(y), y_row_stride,
+                                              _stream(stream)))
+
+
+def lora_apply_moe_grouped(dtype: int, n_experts: int, n_out: int, k_in: int, W_experts,
+                           expert_stride: int, w_row_stride: int, route, x, x_row_stride: int,
+                           expert_offsets, seq_slot, n: int, y, y_row_stride: int, workspace,
+                           workspace_bytes: int, stream=None):
+    _check(lib().lora_apply_moe_grouped(dtype, n_experts, n_out, k_in, _ptr(W_experts),
+                                        expert_stride, w_row_stride, _route_ref(route), _ptr(x),
+                                        x_row_stride, _ptr(expert_offsets), _ptr(seq_slot), n,
+                                        _ptr(y), y_row_stride, _ptr(workspace), workspace_bytes,
+                                        _stream(stream)))

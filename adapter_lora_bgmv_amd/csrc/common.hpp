@@ -15,7 +15,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kSkip = -1;
 constexpr int kDrop = -2;
 
-enum Mode : int { kModeDecode = 0, kModeSegmented = 1, kModeMoe = 2 };
+enum Mode : int { kModeDecode = 0, kModeSegmented = 1, kModeMoe = 2, kModeMoeGrouped = 3 };
 
 __device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float((uint32_t)b << 16); }
 
@@ -130,7 +130,7 @@ __device__ __forceinline__ int resolve_slot(int slot, int expert, int max_loras,
 // Routing inputs of one call, in the form the caller handed them over.
 struct Routing {
   int mode;                 // Mode
-  const int32_t *seq_slot;  // decode: [n]
+  const int32_t *seq_slot;  // decode, moe grouped: [n]
   const int32_t *seg_indptr;  // segmented: [n_seg+1]
   const int32_t *seg_slot;    // segmented: [n_seg]
   int n_seg;
@@ -138,6 +138,7 @@ struct Routing {
   const int32_t *token_slot;  // moe: [n / top_k]
   int top_k;
   int n_experts;              // 1 unless moe
+  const int32_t *expert_offsets;  // moe grouped: [n_experts+1], rows sorted by expert
 };
 
 struct RouteDev {
@@ -176,6 +177,12 @@ __device__ __forceinline__ int row_route(const Routing &rt, const RouteDev &rd, 
     int g = segment_of(rt.seg_indptr, rt.n_seg, r);
     if (g < 0) return kDrop;
     slot = rt.seg_slot[g];
+  } else if (rt.mode == kModeMoeGrouped) {
+    expert = segment_of(rt.expert_offsets, rt.n_experts, r);
+    if (expert < 0) return kDrop;
+    *group = expert;
+    if (!has_lora) return kSkip;  // seq_slot may be NULL for a base-only call
+    slot = rt.seq_slot[r];
   } else {
     expert = rt.indices[r];
     if (expert < 0 || expert >= rt.n_experts) return kDrop;

@@ -54,10 +54,21 @@ __device__ int block_exscan(int *a, int L, int *wsum) {
 __device__ __forceinline__ int pk_key(int w) { return (w >> 13) - 1; }
 __device__ __forceinline__ int pk_pair(int w) { return (w & 0x1fff) - 2; }
 
-// Segment tables up to this many entries are copied to LDS for the routing.
+// Row ranges of a call: the segments of a segmented call, the experts of a
+// grouped MoE call ([n+1] non-decreasing starts); tables up to kSegLds
+// entries are copied to LDS for the routing.
 constexpr int kSegLds = 4096;
+__device__ __forceinline__ bool has_ranges(const Routing &rt) {
+  return rt.mode == kModeSegmented || rt.mode == kModeMoeGrouped;
+}
+__device__ __forceinline__ const int32_t *range_starts(const Routing &rt) {
+  return rt.mode == kModeSegmented ? rt.seg_indptr : rt.expert_offsets;
+}
+__device__ __forceinline__ int range_count(const Routing &rt) {
+  return rt.mode == kModeSegmented ? rt.n_seg : rt.n_experts;
+}
 __device__ __forceinline__ bool seg_in_lds(const Routing &rt) {
-  return rt.mode == kModeSegmented && rt.n_seg + 1 <= kSegLds;
+  return has_ranges(rt) && range_count(rt) + 1 <= kSegLds;
 }
 
 // The segment of row r from an LDS copy of seg_indptr (binary search).
@@ -73,7 +84,7 @@ __device__ __forceinline__ int segment_lds(const int *ip, int n_seg, int r) {
 
 // Routes rows row0 + tid + 256 j (j < J) into pk[]: every load of the batch
 // (the slot inputs, then the three route tables) in flight together.  `seg`
-// is an LDS copy of seg_indptr (segmented calls), or null.
+// is an LDS copy of the row ranges (segmented and grouped MoE calls), or null.
 template <int J = 8>
 __device__ __forceinline__ void route_all(const PrepArgs &a, int *pk, const int *seg, int row0,
                                           bool ranked = false) {
@@ -94,6 +105,11 @@ __device__ __forceinline__ void route_all(const PrepArgs &a, int *pk, const int 
         const int g = seg ? segment_lds(seg, rt.n_seg, r) : segment_of(rt.seg_indptr, rt.n_seg, r);
         dr = g < 0;
         sl = g < 0 ? -1 : rt.seg_slot[g];
+      } else if (live && rt.mode == kModeMoeGrouped) {
+        const int e = seg ? segment_lds(seg, rt.n_experts, r) : segment_of(rt.expert_offsets, rt.n_experts, r);
+        dr = e < 0;
+        ex = dr ? 0 : e;
+        sl = a.has_lora && !dr ? rt.seq_slot[r] : -1;
       } else if (live) {
         const int e = rt.indices[r];
         dr = e < 0 || e >= rt.n_experts;
@@ -543,8 +559,10 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
 __global__ __launch_bounds__(256) void route_kernel(PrepArgs a) {
   __shared__ int seg[kSegLds];
   const bool sl = seg_in_lds(a.rt);
-  if (sl)
-    for (int g = threadIdx.x; g <= a.rt.n_seg; g += 256) seg[g] = a.rt.seg_indptr[g];
+  if (sl) {
+    const int32_t *starts = range_starts(a.rt);
+    for (int g = threadIdx.x; g <= range_count(a.rt); g += 256) seg[g] = starts[g];
+  }
   __syncthreads();
   route_all<1>(a, a.routes, sl ? seg : nullptr, (int)blockIdx.x * 256, a.ranks != nullptr);
 }

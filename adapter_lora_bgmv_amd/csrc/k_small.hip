@@ -84,16 +84,16 @@ __global__ __launch_bounds__(256) void apply_f32_kernel(RouteDev rd, Routing rt,
 }
 
 // ---------------------------------------------------------------- expand + fold
-// y[i, o] = y[i, o] + s * (B_s t_i)[o] for rows that resolve; others untouched.
-// One thread per output; t_i staged in LDS; the rank sum runs k ascending.
+// y[i, o] = y[i, o] + s * (B_pair t_i)[o] for rows that resolve; others untouched
+// (rows outside every range too).  One thread per output; t_i staged in LDS;
+// the rank sum runs k ascending.
 template <typename T>
-__global__ __launch_bounds__(256) void expand_fold_kernel(RouteDev rd, const int32_t *seq_slot,
-                                                          const float *t, T *y, int y_stride,
-                                                          int n_out) {
+__global__ __launch_bounds__(256) void expand_fold_kernel(RouteDev rd, Routing rt, const float *t,
+                                                          T *y, int y_stride, int n_out) {
   __shared__ float tsh[256];
   const int i = blockIdx.y;
-  const int s = seq_slot[i];
-  const int q = resolve_slot(s, 0, rd.max_loras, 1, rd.a_table, rd.b_table, rd.scale_table);
+  int group, sidx;
+  const int q = row_route(rt, rd, true, i, &group, &sidx);
   if (q < 0) return;
   for (int k = threadIdx.x; k < rd.R; k += 256) tsh[k] = t[(size_t)i * rd.R + k];
   __syncthreads();
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void expand_fold_kernel(RouteDev rd, const int
   float d = 0.f;
   for (int k = 0; k < rd.R; ++k) d += ld(B, (size_t)o * rd.R + k) * tsh[k];
   const size_t yi = (size_t)i * y_stride + o;
-  st(y, yi, ld((const T *)y, yi) + rd.scale_table[s] * d);
+  st(y, yi, ld((const T *)y, yi) + rd.scale_table[sidx] * d);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -122,16 +122,15 @@ hipError_t launch_apply_f32(const RouteDev &rd, const Routing &rt, bool has_lora
   return hipGetLastError();
 }
 
-hipError_t launch_expand_fold(const RouteDev &rd, int dtype, const int32_t *seq_slot,
-                              const float *t, void *y, int y_stride, int n_out, int n,
-                              hipStream_t st) {
+hipError_t launch_expand_fold(const RouteDev &rd, int dtype, const Routing &rt, const float *t,
+                              void *y, int y_stride, int n_out, int n, hipStream_t st) {
   dim3 grid((n_out + 255) / 256, n);
   if (dtype == 0)
-    hipLaunchKernelGGL(expand_fold_kernel<float>, grid, dim3(256), 0, st, rd, seq_slot, t,
-                       (float *)y, y_stride, n_out);
+    hipLaunchKernelGGL(expand_fold_kernel<float>, grid, dim3(256), 0, st, rd, rt, t, (float *)y,
+                       y_stride, n_out);
   else
-    hipLaunchKernelGGL(expand_fold_kernel<u16>, grid, dim3(256), 0, st, rd, seq_slot, t,
-                       (u16 *)y, y_stride, n_out);
+    hipLaunchKernelGGL(expand_fold_kernel<u16>, grid, dim3(256), 0, st, rd, rt, t, (u16 *)y,
+                       y_stride, n_out);
   return hipGetLastError();
 }
 

@@ -122,9 +122,8 @@ hipError_t launch_shrink_f32(const RouteDev &rd, const Routing &rt, const float 
 hipError_t launch_apply_f32(const RouteDev &rd, const Routing &rt, bool has_lora, const float *W,
                             long long w_group_stride, int w_stride, const float *x, int x_stride,
                             int k_in, int n_out, int n, float *y, int y_stride, hipStream_t st);
-hipError_t launch_expand_fold(const RouteDev &rd, int dtype, const int32_t *seq_slot,
-                              const float *t, void *y, int y_stride, int n_out, int n,
-                              hipStream_t st);
+hipError_t launch_expand_fold(const RouteDev &rd, int dtype, const Routing &rt, const float *t,
+                              void *y, int y_stride, int n_out, int n, hipStream_t st);
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &a, int to, int tr, hipStream_t st);
 hipError_t launch_decode_main(const DecodeArgs &a, hipStream_t st);

@@ -82,6 +82,7 @@ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 // part; larger batches pick it from the tile count to fill the chip.
 Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pairs) {
   Cfg c{};
+  const bool moe = op == LORA_OP_MOE_GATHER || op == LORA_OP_MOE_GROUPED;
   c.decode = op == LORA_OP_APPLY && n <= kDecodeMaxRows && k_in <= 64 * kDecodeMaxStages * kDecodeMaxSplit;
   c.units = R > 0 ? (n + kShrinkRows - 1) / kShrinkRows + std::min(n, n_pairs) : 0;
   // Shrink k chunks: enough workgroups to cover the chip for small batches,
@@ -93,7 +94,7 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
     const int nst = (k_in + 63) / 64;
     c.to = kDecodeTileOut; c.tr = kDecodeMaxRows;
     c.splits = (nst + kDecodeMaxStages - 1) / kDecodeMaxStages;
-  } else if (op == LORA_OP_MOE_GATHER) {
+  } else if (moe) {
     c.to = 256; c.tr = 64; c.splits = 1;
   } else if (n <= 64) {
     c.to = 64; c.tr = 64; c.splits = clampi(k_in / 1024, 1, 8);
@@ -104,7 +105,7 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
   }
   // stream-K stages the LoRA term through LDS, which takes ranks dividing 64;
   // other ranks go to 128 x 128 tiles
-  c.stream_k = !c.decode && op != LORA_OP_MOE_GATHER && n > 128;
+  c.stream_k = !c.decode && !moe && n > 128;
   if (c.stream_k && R > 0 && (R > 64 || 64 % R != 0)) {
     c.stream_k = false;
     c.to = 128; c.tr = 128; c.splits = clampi(k_in / 1024, 1, 4);
@@ -116,7 +117,7 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
     const int kslabs = (k_in + 63) / 64;
     c.k_per_split = ((kslabs + c.splits - 1) / c.splits) * 64;
   }
-  c.max_mtiles = (n + c.tr - 1) / c.tr + (op == LORA_OP_MOE_GATHER ? groups : 0);
+  c.max_mtiles = (n + c.tr - 1) / c.tr + (moe ? groups : 0);
   c.n_ntiles = (n_out + c.to - 1) / c.to;
   const long long tiles = (long long)c.max_mtiles * c.n_ntiles;
   c.partial_slots = c.splits > 1 ? (int)(tiles * c.splits) : 0;
@@ -246,6 +247,82 @@ RouteDev route_dev(const lora_route *r) {
     d.R = (int)r->max_rank;
   }
   return d;
+}
+
+// A MoE route against the call's shape; fills *rd (all zero for a NULL
+// route, a base-only call).
+int check_route_moe(const char *what, const lora_route_moe *route, int32_t dtype, uint32_t n_experts,
+                    uint32_t n_out, uint32_t k_in, RouteDev *rd) {
+  *rd = RouteDev{};
+  if (!route) return LORA_OK;
+  if (!route->a_table || !route->b_table || !route->scale_table)
+    return fail(LORA_ERR_NULL_PTR, "%s: route tables must be non-NULL (a_table %p, b_table %p, scale_table %p)",
+                what, (const void *)route->a_table, (const void *)route->b_table,
+                (const void *)route->scale_table);
+  if (route->dtype != dtype)
+    return fail(LORA_ERR_DTYPE, "%s: route dtype %d differs from the call's dtype %d", what, route->dtype, dtype);
+  if (route->k_in != k_in || route->n_out != n_out || route->n_experts != n_experts)
+    return fail(LORA_ERR_SHAPE,
+                "%s: route is [n_out %u x k_in %u] over %u experts but the call is [n_out %u x k_in %u] over %u",
+                what, route->n_out, route->k_in, route->n_experts, n_out, k_in, n_experts);
+  if (n_experts == 0 || route->max_loras == 0 || (uint64_t)n_experts * (route->max_loras + 1) > (uint64_t)kMaxKeys)
+    return fail(LORA_ERR_SHAPE, "%s: [n_out %u x k_in %u]: n_experts %u x (max_loras %u + 1) must be in 1..%d", what,
+                n_out, k_in, n_experts, route->max_loras, kMaxKeys);
+  if (int e = check_rank(what, dtype, n_out, k_in, route->max_rank)) return e;
+  rd->a_table = route->a_table;
+  rd->b_table = route->b_table;
+  rd->scale_table = route->scale_table;
+  rd->max_loras = (int)route->max_loras;
+  rd->n_experts = (int)n_experts;
+  rd->R = (int)route->max_rank;
+  return LORA_OK;
+}
+
+// Checks of a W_experts operand: expert_stride covers one expert's matrix.
+int check_experts(const char *what, int32_t dtype, uint32_t n_experts, uint32_t n_out, uint32_t k_in,
+                  uint64_t expert_stride, uint32_t w_row_stride) {
+  if (n_experts == 0 || (uint64_t)n_experts > (uint64_t)kMaxKeys)
+    return fail(LORA_ERR_SHAPE, "%s: [n_out %u x k_in %u]: n_experts %u must be in 1..%d", what, n_out, k_in,
+                n_experts, kMaxKeys);
+  if (expert_stride < (uint64_t)(n_out - 1) * w_row_stride + k_in && n_experts > 1)
+    return fail(LORA_ERR_STRIDE, "%s: [n_out %u x k_in %u]: expert_stride %llu is smaller than one expert", what,
+                n_out, k_in, (unsigned long long)expert_stride);
+  if (dtype == LORA_BF16 && expert_stride % 8)
+    return fail(LORA_ERR_UNSUPPORTED, "%s: bf16 needs expert_stride %llu to be a multiple of 8", what,
+                (unsigned long long)expert_stride);
+  return LORA_OK;
+}
+
+// Shared by the grouped shrink and expand-fold: the route, the row count
+// and the pointers (the input rows `in`, the output `out`).
+int check_grouped_call(const char *what, const lora_route_moe *route, uint32_t n, const void *in,
+                       const int32_t *expert_offsets, const int32_t *seq_slot, const void *out,
+                       uint32_t x_row_stride, uint32_t y_row_stride, bool shrink, RouteDev *rd) {
+  if (!route) return fail(LORA_ERR_NULL_PTR, "%s: route is NULL", what);
+  const uint32_t k_in = route->k_in, n_out = route->n_out;
+  if (int e = check_proj(what, route->dtype, n_out, k_in, n, shrink ? x_row_stride : k_in,
+                         shrink ? n_out : y_row_stride, k_in))
+    return e;
+  if (route->n_experts == 0)
+    return fail(LORA_ERR_SHAPE, "%s: [n_out %u x k_in %u]: route n_experts must be >= 1", what, n_out, k_in);
+  if (int e = check_route_moe(what, route, route->dtype, route->n_experts, n_out, k_in, rd)) return e;
+  if (n == 0) return LORA_OK;
+  if (!in || !expert_offsets || !seq_slot || !out)
+    return fail(LORA_ERR_NULL_PTR,
+                "%s: [n_out %u x k_in %u]: %s %p, expert_offsets %p, seq_slot %p, %s %p must be non-NULL", what,
+                n_out, k_in, shrink ? "x" : "t", in, (const void *)expert_offsets, (const void *)seq_slot,
+                shrink ? "t" : "y", out);
+  return LORA_OK;
+}
+
+Routing routing_grouped(const int32_t *expert_offsets, const int32_t *seq_slot, uint32_t n_experts) {
+  Routing rt{};
+  rt.mode = kModeMoeGrouped;
+  rt.expert_offsets = expert_offsets;
+  rt.seq_slot = seq_slot;
+  rt.n_experts = (int)n_experts;
+  rt.top_k = 1;
+  return rt;
 }
 
 Routing routing_decode(const int32_t *seq_slot) {
@@ -501,8 +578,8 @@ int lora_expand_fold(const lora_route *route, const float *t, const int32_t *seq
     return fail(LORA_ERR_NULL_PTR, "%s: [n_out %u x k_in %u]: t %p, seq_slot %p, y %p must be non-NULL", what,
                 route->n_out, route->k_in, (const void *)t, (const void *)seq_slot, y);
   if (int e = check_device(what)) return e;
-  return launch_status(launch_expand_fold(route_dev(route), route->dtype, seq_slot, t, y, (int)y_row_stride,
-                                          (int)route->n_out, (int)n, (hipStream_t)stream),
+  return launch_status(launch_expand_fold(route_dev(route), route->dtype, routing_decode(seq_slot), t, y,
+                                          (int)y_row_stride, (int)route->n_out, (int)n, (hipStream_t)stream),
                        what);
 }
 
@@ -586,35 +663,9 @@ int lora_apply_moe_gather(int32_t dtype, uint32_t n_experts, uint32_t n_out, uin
                 n_out, k_in, n_tokens, top_k, kMaxRows);
   const uint32_t n = (uint32_t)rows64;
   if (int e = check_proj(what, dtype, n_out, k_in, n, x_row_stride, y_row_stride, w_row_stride)) return e;
-  if (expert_stride < (uint64_t)(n_out - 1) * w_row_stride + k_in && n_experts > 1)
-    return fail(LORA_ERR_STRIDE, "%s: [n_out %u x k_in %u]: expert_stride %llu is smaller than one expert", what,
-                n_out, k_in, (unsigned long long)expert_stride);
-  if (dtype == LORA_BF16 && expert_stride % 8)
-    return fail(LORA_ERR_UNSUPPORTED, "%s: bf16 needs expert_stride %llu to be a multiple of 8", what,
-                (unsigned long long)expert_stride);
-  if ((uint64_t)n_experts > (uint64_t)kMaxKeys)
-    return fail(LORA_ERR_SHAPE, "%s: n_experts %u exceeds %d", what, n_experts, kMaxKeys);
+  if (int e = check_experts(what, dtype, n_experts, n_out, k_in, expert_stride, w_row_stride)) return e;
   RouteDev rd{};
-  if (route) {
-    if (!route->a_table || !route->b_table || !route->scale_table)
-      return fail(LORA_ERR_NULL_PTR, "%s: route tables must be non-NULL", what);
-    if (route->dtype != dtype)
-      return fail(LORA_ERR_DTYPE, "%s: route dtype %d differs from the call's dtype %d", what, route->dtype, dtype);
-    if (route->k_in != k_in || route->n_out != n_out || route->n_experts != n_experts)
-      return fail(LORA_ERR_SHAPE,
-                  "%s: route is [n_out %u x k_in %u] over %u experts but the call is [n_out %u x k_in %u] over %u",
-                  what, route->n_out, route->k_in, route->n_experts, n_out, k_in, n_experts);
-    if (route->max_loras == 0 || (uint64_t)n_experts * (route->max_loras + 1) > (uint64_t)kMaxKeys)
-      return fail(LORA_ERR_SHAPE, "%s: n_experts %u x (max_loras %u + 1) must be at most %d", what, n_experts,
-                  route->max_loras, kMaxKeys);
-    if (int e = check_rank(what, dtype, n_out, k_in, route->max_rank)) return e;
-    rd.a_table = route->a_table;
-    rd.b_table = route->b_table;
-    rd.scale_table = route->scale_table;
-    rd.max_loras = (int)route->max_loras;
-    rd.n_experts = (int)n_experts;
-    rd.R = (int)route->max_rank;
-  }
+  if (int e = check_route_moe(what, route, dtype, n_experts, n_out, k_in, &rd)) return e;
   if (n == 0) return LORA_OK;
   if (!W_experts || !x || !y || !indices || (route && !token_slot))
     return fail(LORA_ERR_NULL_PTR, "%s: [n_out %u x k_in %u]: W_experts, x, y, indices%s must be non-NULL", what,
@@ -636,6 +687,88 @@ int lora_apply_moe_gather(int32_t dtype, uint32_t n_experts, uint32_t n_out, uin
                                           (int)x_row_stride, (int)k_in, (int)n_out, (int)n, (float *)y,
                                           (int)y_row_stride, st); }, st);
   return run_fused(what, LORA_OP_MOE_GATHER, rt, rd, route != nullptr, n_out, k_in, W_experts,
+                   (long long)expert_stride, w_row_stride, x, x_row_stride, n, y, y_row_stride, workspace,
+                   workspace_bytes, (int)n_experts, st);
+}
+
+int lora_moe_grouped_shrink(const lora_route_moe *route, const void *x, uint32_t x_row_stride,
+                            const int32_t *expert_offsets, const int32_t *seq_slot, uint32_t n, float *t,
+                            void *stream) {
+  clear_err();
+  const char *what = "lora_moe_grouped_shrink";
+  RouteDev rd{};
+  if (int e = check_grouped_call(what, route, n, x, expert_offsets, seq_slot, t, x_row_stride, 0, true, &rd))
+    return e;
+  if (n == 0) return LORA_OK;
+  if (route->dtype == LORA_BF16 && (!aligned16(x) || !aligned16(t)))
+    return fail(LORA_ERR_UNSUPPORTED, "%s: bf16 needs 16-byte aligned x %p and t %p", what, x, (void *)t);
+  if (int e = check_device(what)) return e;
+  const Routing rt = routing_grouped(expert_offsets, seq_slot, route->n_experts);
+  hipStream_t st = (hipStream_t)stream;
+  if (route->dtype == LORA_F32)
+    return launch_status(launch_shrink_f32(rd, rt, (const float *)x, (int)x_row_stride, (int)route->k_in, (int)n,
+                                           t, st),
+                         what);
+  const int n_pairs = rd.max_loras * rd.n_experts;
+  PrepArgs pa{};
+  pa.rd = rd;
+  pa.rt = rt;
+  pa.has_lora = true;
+  pa.x = (const u16 *)x;
+  pa.x_stride = (int)x_row_stride;
+  pa.k_in = (int)route->k_in;
+  pa.n = (int)n;
+  pa.t = t;
+  pa.t_final = t;
+  pa.k_splits = 1;  // t is the caller's [n][max_rank] output: whole k per unit
+  pa.n_pairs = n_pairs;
+  pa.do_plan = 0;
+  pa.n_units = (int)((n + kShrinkRows - 1) / kShrinkRows) + (int)std::min<uint32_t>(n, (uint32_t)n_pairs);
+  return launch_status(launch_prep(pa, st), what);
+}
+
+int lora_moe_grouped_expand_fold(const lora_route_moe *route, const float *t, const int32_t *expert_offsets,
+                                 const int32_t *seq_slot, uint32_t n, void *y, uint32_t y_row_stride,
+                                 void *stream) {
+  clear_err();
+  const char *what = "lora_moe_grouped_expand_fold";
+  RouteDev rd{};
+  if (int e = check_grouped_call(what, route, n, t, expert_offsets, seq_slot, y, 0, y_row_stride, false, &rd))
+    return e;
+  if (n == 0) return LORA_OK;
+  if (int e = check_device(what)) return e;
+  return launch_status(launch_expand_fold(rd, route->dtype, routing_grouped(expert_offsets, seq_slot, route->n_experts),
+                                          t, y, (int)y_row_stride, (int)route->n_out, (int)n, (hipStream_t)stream),
+                       what);
+}
+
+int lora_apply_moe_grouped(int32_t dtype, uint32_t n_experts, uint32_t n_out, uint32_t k_in,
+                           const void *W_experts, uint64_t expert_stride, uint32_t w_row_stride,
+                           const lora_route_moe *route, const void *x, uint32_t x_row_stride,
+                           const int32_t *expert_offsets, const int32_t *seq_slot, uint32_t n, void *y,
+                           uint32_t y_row_stride, void *workspace, size_t workspace_bytes, void *stream) {
+  clear_err();
+  const char *what = "lora_apply_moe_grouped";
+  if (int e = check_proj(what, dtype, n_out, k_in, n, x_row_stride, y_row_stride, w_row_stride)) return e;
+  if (int e = check_experts(what, dtype, n_experts, n_out, k_in, expert_stride, w_row_stride)) return e;
+  RouteDev rd{};
+  if (int e = check_route_moe(what, route, dtype, n_experts, n_out, k_in, &rd)) return e;
+  if (n == 0) return LORA_OK;
+  if (!W_experts || !x || !y || !expert_offsets || (route && !seq_slot))
+    return fail(LORA_ERR_NULL_PTR, "%s: [n_out %u x k_in %u]: W_experts, x, y, expert_offsets%s must be non-NULL",
+                what, n_out, k_in, route ? ", seq_slot" : "");
+  if (dtype == LORA_BF16 && (!aligned16(W_experts) || !aligned16(x) || !aligned16(y)))
+    return fail(LORA_ERR_UNSUPPORTED, "%s: bf16 needs 16-byte aligned W_experts %p, x %p, y %p", what, W_experts,
+                x, y);
+  if (int e = check_device(what)) return e;
+  const Routing rt = routing_grouped(expert_offsets, route ? seq_slot : nullptr, n_experts);
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == LORA_F32)
+    return run_f32_timed(what, [&] { return launch_apply_f32(rd, rt, route != nullptr, (const float *)W_experts,
+                                          (long long)expert_stride, (int)w_row_stride, (const float *)x,
+                                          (int)x_row_stride, (int)k_in, (int)n_out, (int)n, (float *)y,
+                                          (int)y_row_stride, st); }, st);
+  return run_fused(what, LORA_OP_MOE_GROUPED, rt, rd, route != nullptr, n_out, k_in, W_experts,
                    (long long)expert_stride, w_row_stride, x, x_row_stride, n, y, y_row_stride, workspace,
                    workspace_bytes, (int)n_experts, st);
 }

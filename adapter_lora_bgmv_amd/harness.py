@@ -65,6 +65,13 @@ class DeviceWorkload:
             self.indices = to_device(wl.indices.astype(np.int32), device)
             self.token_slot = to_device(wl.token_slot.astype(np.int32), device)
             op, groups = B.LORA_OP_MOE_GATHER, wl.n_experts
+        elif wl.kind == "moe_grouped":
+            self.route = B.DeviceRoute(self.A, self.Bp, self.scale_table_host, null_slots=ns,
+                                       n_experts=wl.n_experts)
+            self.expert_offsets = to_device(wl.expert_offsets.astype(np.int32), device)
+            self.seq_slot_host = np.asarray(wl.row_slot, np.int32)
+            self.seq_slot = to_device(self.seq_slot_host, device)
+            op, groups = B.LORA_OP_MOE_GROUPED, wl.n_experts
         else:
             self.route = B.DeviceRoute(self.A, self.Bp, self.scale_table_host, null_slots=ns)
             groups = 1
@@ -102,6 +109,12 @@ class DeviceWorkload:
                                    self.x_row_stride, self.seg_indptr, self.seg_slot,
                                    len(wl.seg_slot), self.n, y, self.y_row_stride,
                                    self.workspace, self.ws_bytes, stream)
+        elif wl.kind == "moe_grouped":
+            B.lora_apply_moe_grouped(self.dtype, wl.n_experts, wl.n_out, wl.k_in, self.W,
+                                     wl.n_out * wl.k_in, wl.k_in, r, self.x, self.x_row_stride,
+                                     self.expert_offsets, self.seq_slot if route else None,
+                                     self.n, y, self.y_row_stride, self.workspace, self.ws_bytes,
+                                     stream)
         else:
             B.lora_apply_moe_gather(self.dtype, wl.n_experts, wl.n_out, wl.k_in, self.W,
                                     wl.n_out * wl.k_in, wl.k_in, r, self.x, self.x_row_stride,

@@ -29,11 +29,10 @@ BF16 = "bf16"
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round f32 values to bf16 (round to nearest, ties to even); uint16 bits."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = (u + 0x7FFF + lsb) >> 16
+    u = a.view(np.uint32)
+    # in 32 bits: only NaN patterns can wrap, and they are replaced below
+    out = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(a)
-    out = r.astype(np.uint16)
     out[nan] = 0x7FC0
     return out
 
@@ -272,6 +271,12 @@ CONFIGS = {
     "fused_gate_up": fused_gate_up,
     "prefill_segmented": prefill_segmented,
     "moe_down_gather": moe_down_gather,
+}
+
+
+# workloads of the variants built beyond the five: the grouped MoE layout
+NEXT_WORKLOADS = {
+    "moe_down_grouped": moe_down_grouped,
 }
 
 

@@ -43,11 +43,20 @@ WORKLOAD_TEXT = {
     "fused_gate_up": "fused gate/up: W 22016x4096 bf16, 32 slots r in {8,16,32,64} padded to 64, rsLoRA alpha 16, 8 slots at scale 0, 256 rows",
     "prefill_segmented": "prefill segmented: o_proj W 4096x4096 bf16, 8 segments x 512 tokens, one rank-64 adapter each",
     "moe_down_gather": "MoE down_proj gather: 64 experts W_e 2048x1408 bf16, 512 tokens top-6, rank-16 pair per (adapter, expert), 4 adapters",
+    "moe_down_grouped": "MoE down_proj grouped: 64 experts W_e 2048x1408 bf16, 2048 tokens top-6 = 12288 rows sorted by expert (expert_offsets), rank-16 pair per (adapter, expert), 4 adapters",
 }
 ROTATE = {"single_projection_f32": 4, "decode_bgmv": 16, "fused_gate_up": 4,
-          "prefill_segmented": 8, "moe_down_gather": 2}
+          "prefill_segmented": 8, "moe_down_gather": 2, "moe_down_grouped": 2}
 BOUND = {"single_projection_f32": "latency", "decode_bgmv": "hbm", "fused_gate_up": "hbm",
-         "prefill_segmented": "mfma", "moe_down_gather": "hbm"}
+         "prefill_segmented": "mfma", "moe_down_gather": "hbm", "moe_down_grouped": "hbm"}
+# the five workloads of the path, then the variants built beyond them
+OTHERS = ("single_projection_f32", "fused_gate_up", "prefill_segmented", "moe_down_gather",
+          "moe_down_grouped")
+
+
+def workload(name):
+    from adapter_lora_bgmv_amd import workloads as WL
+    return {**WL.CONFIGS, **WL.NEXT_WORKLOADS}[name]()
 
 
 def parse():
@@ -86,6 +95,18 @@ def resolve_rows(wl, scale_table):
         return pairs, np.zeros(wl.n_rows, int)
     E = wl.n_experts
     pairs, groups = [], []
+    if wl.kind == "moe_grouped":
+        off = wl.expert_offsets
+        for j in range(wl.n_rows):
+            e = int(np.searchsorted(off, j, side="right")) - 1
+            if j < off[0] or j >= off[-1]:
+                pairs.append(-2)
+                groups.append(0)
+                continue
+            a = int(wl.row_slot[j])
+            groups.append(e)
+            pairs.append(a * E + e if 0 <= a < P and scale_table[a] != 0 else -1)
+        return np.array(pairs), np.array(groups)
     for j in range(wl.n_rows):
         e = int(wl.indices[j])
         a = int(wl.token_slot[j // wl.top_k])
@@ -104,7 +125,7 @@ def algorithmic_counts(wl, scale_table):
     active = int((pairs >= 0).sum())
     touched = len(set(int(p) for p in pairs if p >= 0))
     R, k, o = wl.max_rank, wl.k_in, wl.n_out
-    w_bytes = (len(set(groups[pairs >= -1].tolist())) if wl.kind == "moe" else 1) * o * k * esz
+    w_bytes = (len(set(groups[pairs >= -1].tolist())) if wl.kind in ("moe", "moe_grouped") else 1) * o * k * esz
     a_bytes = touched * R * k * esz
     b_bytes = touched * o * R * esz
     x_bytes = n * k * esz
@@ -173,7 +194,7 @@ def time_workload(name, steps, warmup, apply=True):
     from adapter_lora_bgmv_amd import workloads as WL
     from adapter_lora_bgmv_amd.harness import DeviceWorkload
 
-    wl = WL.CONFIGS[name]()
+    wl = workload(name)
     R = ROTATE[name]
     dws = [DeviceWorkload(wl) for _ in range(R)]
     counts = algorithmic_counts(wl, dws[0].scale_table_host)
@@ -278,7 +299,7 @@ def measured_traffic(kernel, workload):
 def cpu_baseline(name, seconds):
     import oracle
     from adapter_lora_bgmv_amd import workloads as WL
-    wl = WL.CONFIGS[name]()
+    wl = workload(name)
     orc = oracle.get()
     st = orc.scale_table(wl.adapters)
     counts = algorithmic_counts(wl, st)
@@ -323,7 +344,7 @@ def main():
 
     others = {}
     if not a.no_others:
-        for other in ("single_projection_f32", "fused_gate_up", "prefill_segmented", "moe_down_gather"):
+        for other in OTHERS:
             if other == name:
                 continue
             _, c2, t2 = time_workload(other, min(a.steps, 64), 8)

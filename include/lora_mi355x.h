@@ -75,7 +75,7 @@ enum lora_status {
   LORA_ERR_WORKSPACE = -7    /* workspace missing or smaller than required */
 };
 
-enum lora_op { LORA_OP_APPLY = 0, LORA_OP_SEGMENTED = 1, LORA_OP_MOE_GATHER = 2 };
+enum lora_op { LORA_OP_APPLY = 0, LORA_OP_SEGMENTED = 1, LORA_OP_MOE_GATHER = 2, LORA_OP_MOE_GROUPED = 3 };
 
 /*
  * A module's routing tables (atlas lora_delta.rs LoraRoute): load-time-fixed
@@ -100,9 +100,10 @@ typedef struct lora_route {
 
 /*
  * MoE routing tables (atlas lora_delta.rs moe_lora_gather_bgmv field doc:
- * the expert is keyed through the per-slot indices array).  The pair of
- * (adapter a, expert e) sits at table index a * n_experts + e; the scale is
- * the adapter's, scale_table[a].
+ * the expert is keyed through the per-slot indices array; the
+ * moe_lora_grouped_down field doc: keyed through expert_offsets).  The pair
+ * of (adapter a, expert e) sits at table index a * n_experts + e; the scale
+ * is the adapter's, scale_table[a].
  */
 typedef struct lora_route_moe {
   const void *const *a_table;   /* [dev] [max_loras * n_experts] */
@@ -162,8 +163,9 @@ int lora_build_seq_slot(const int32_t *adapter_slots, uint32_t n, uint32_t padde
 /*
  * Workspace bytes a fused entry point needs for this problem (0 for
  * LORA_F32, which needs none).  op is a lora_op; n_rows is n (apply,
- * segmented) or n_tokens * top_k (MoE); n_groups is n_experts for the MoE
- * gather and 1 otherwise; max_rank is 0 for a base-only call.
+ * segmented, MoE grouped) or n_tokens * top_k (MoE gather); n_groups is
+ * n_experts for the two MoE ops and 1 otherwise; max_rank is 0 for a
+ * base-only call.
  */
 size_t lora_workspace_bytes(int32_t op, int32_t dtype, uint32_t n_rows, uint32_t n_out,
                             uint32_t k_in, uint32_t max_rank, uint32_t n_groups);
@@ -172,11 +174,11 @@ size_t lora_workspace_bytes(int32_t op, int32_t dtype, uint32_t n_rows, uint32_t
  * Measurement aid (atlas lora_delta.rs lora_no_apply doc: apply cost is
  * measured apart from everything else).  With n >= 4 HIP events set, every
  * later fused call on the calling thread (lora_apply, lora_apply_segmented,
- * lora_apply_moe_gather) records on its stream events[0] before its first
- * kernel, events[1] right before its main kernel (after the route plan and
- * shrink kernel where there is one), events[2] right after the main kernel,
- * and events[3] after its last kernel (the decode epilogue where there is
- * one).  n == 0 switches it off.  events is [host]; the events themselves are
+ * lora_apply_moe_gather, lora_apply_moe_grouped) records on its stream
+ * events[0] before its first kernel, events[1] right before its main kernel
+ * (after the route plan and shrink kernel where there is one), events[2]
+ * right after the main kernel, and events[3] after its last kernel (the
+ * decode epilogue where there is one).  n == 0 switches it off.  events is [host]; the events themselves are
  * the caller's hipEvent_t.  Returns LORA_ERR_NULL_PTR for 0 < n < 4 or a NULL
  * event.
  */
@@ -253,6 +255,51 @@ int lora_apply_moe_gather(int32_t dtype, uint32_t n_experts, uint32_t n_out, uin
                           const int32_t *token_slot, uint32_t n_tokens, void *y,
                           uint32_t y_row_stride, void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/*
+ * Grouped MoE layout (atlas lora_delta.rs moe_lora_grouped_down field doc:
+ * the MoE expert down_proj delta keyed on expert through device
+ * expert_offsets; the sorted twin of the gather above).  The n rows come
+ * sorted by expert: rows expert_offsets[e] .. expert_offsets[e+1]-1 belong
+ * to expert e.  Each sorted row carries its own adapter slot, seq_slot[j]
+ * (the slot of the token it was routed from), resolved by the rule of the
+ * conventions above with the pair (a = seq_slot[j], e) at table index
+ * a * n_experts + e.  expert_offsets [dev] int32 [n_experts+1] must be
+ * non-decreasing; it lives in device memory and is not validated on the
+ * host.  A row outside [expert_offsets[0], expert_offsets[n_experts]) is
+ * not written (and its x row is not read).  With offsets that decrease,
+ * every access still stays inside the operands (each row maps to at most
+ * one expert by a binary search) but which expert a row gets is
+ * unspecified.  seq_slot [dev] int32 [n].
+ */
+
+/* Grouped shrink: t[j, 0:max_rank] = A_{a,e} x[j] for rows that resolve;
+ * other rows of t are not written.  x [dev] [n][x_row_stride]; t [dev] f32
+ * [n][max_rank]. */
+int lora_moe_grouped_shrink(const lora_route_moe *route, const void *x, uint32_t x_row_stride,
+                            const int32_t *expert_offsets, const int32_t *seq_slot, uint32_t n,
+                            float *t, void *stream);
+
+/* Grouped expand and fold: y[j, o] += scale_table[a] * (B_{a,e} t[j])[o] in
+ * place for rows that resolve; every other row is untouched.  The rank sum
+ * runs in f32; a bf16 y is rounded once.  t [dev] f32 [n][max_rank]; y
+ * [dev] [n][y_row_stride]. */
+int lora_moe_grouped_expand_fold(const lora_route_moe *route, const float *t,
+                                 const int32_t *expert_offsets, const int32_t *seq_slot,
+                                 uint32_t n, void *y, uint32_t y_row_stride, void *stream);
+
+/* Fused grouped apply: y[j] = W_e x[j] + scale_table[a] B_{a,e} (A_{a,e} x[j])
+ * written with one rounding, e the expert whose range holds j.  W_experts
+ * as in lora_apply_moe_gather; x [dev] [n][x_row_stride]; y [dev]
+ * [n][y_row_stride]; workspace [dev] (op LORA_OP_MOE_GROUPED, n_rows n,
+ * n_groups n_experts).  route may be NULL (base only; seq_slot may then be
+ * NULL).  n is limited to 16384 rows. */
+int lora_apply_moe_grouped(int32_t dtype, uint32_t n_experts, uint32_t n_out, uint32_t k_in,
+                           const void *W_experts, uint64_t expert_stride, uint32_t w_row_stride,
+                           const lora_route_moe *route, const void *x, uint32_t x_row_stride,
+                           const int32_t *expert_offsets, const int32_t *seq_slot, uint32_t n,
+                           void *y, uint32_t y_row_stride, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

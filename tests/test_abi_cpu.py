@@ -182,3 +182,51 @@ def test_moe_refuses_zero_top_k(L):
 def test_shrink_and_expand_refuse_null_route(L):
     assert L.lora_shrink(None, FAKE, 64, FAKE, 4, FAKE, None) == -2
     assert L.lora_expand_fold(None, FAKE, FAKE, 4, FAKE, 64, None) == -2
+
+
+def _moe_route(E=4, max_loras=2, n_out=64, k_in=64, R=16, dtype=B.LORA_BF16):
+    return B.lora_route_moe(FAKE, FAKE, FAKE, max_loras, E, k_in, n_out, R, dtype)
+
+
+def test_grouped_refuses_null_route_and_null_offsets(L):
+    r = _moe_route()
+    assert L.lora_moe_grouped_shrink(None, FAKE, 64, FAKE, FAKE, 4, FAKE, None) == -2
+    assert L.lora_moe_grouped_expand_fold(None, FAKE, FAKE, FAKE, 4, FAKE, 64, None) == -2
+    assert L.lora_moe_grouped_shrink(C.byref(r), FAKE, 64, None, FAKE, 4, FAKE, None) == -2
+    assert "expert_offsets" in L.lora_last_error().decode()
+    rc = L.lora_apply_moe_grouped(B.LORA_BF16, 4, 64, 64, FAKE, 64 * 64, 64, C.byref(r), FAKE, 64,
+                                  None, FAKE, 8, FAKE, 64, FAKE, 1 << 20, None)
+    assert rc == -2 and "expert_offsets" in L.lora_last_error().decode()
+
+
+def test_grouped_refuses_route_over_other_experts(L):
+    r = _moe_route(E=8)
+    rc = L.lora_apply_moe_grouped(B.LORA_BF16, 4, 64, 64, FAKE, 64 * 64, 64, C.byref(r), FAKE, 64,
+                                  FAKE, FAKE, 8, FAKE, 64, FAKE, 1 << 20, None)
+    msg = L.lora_last_error().decode()
+    assert rc == -1 and "over 8 experts" in msg and "over 4" in msg
+
+
+def test_grouped_refuses_small_expert_stride_and_bad_strides(L):
+    rc = L.lora_apply_moe_grouped(B.LORA_BF16, 4, 64, 64, FAKE, 64 * 63, 64, None, FAKE, 64,
+                                  FAKE, None, 8, FAKE, 64, FAKE, 1 << 20, None)
+    assert rc == -3 and "expert_stride" in L.lora_last_error().decode()
+    r = _moe_route()
+    assert L.lora_moe_grouped_shrink(C.byref(r), FAKE, 32, FAKE, FAKE, 4, FAKE, None) == -3
+    assert "x_row_stride 32 < k_in 64" in L.lora_last_error().decode()
+    assert L.lora_moe_grouped_expand_fold(C.byref(r), FAKE, FAKE, FAKE, 4, FAKE, 16, None) == -3
+    assert "y_row_stride 16 < n_out 64" in L.lora_last_error().decode()
+
+
+def test_grouped_empty_batch_launches_nothing(L):
+    r = _moe_route()
+    assert L.lora_moe_grouped_shrink(C.byref(r), None, 64, None, None, 0, None, None) == 0
+    assert L.lora_moe_grouped_expand_fold(C.byref(r), None, None, None, 0, None, 64, None) == 0
+    assert L.lora_apply_moe_grouped(B.LORA_BF16, 4, 64, 64, None, 64 * 64, 64, C.byref(r), None,
+                                    64, None, None, 0, None, 64, None, 0, None) == 0
+
+
+def test_grouped_workspace_counts_expert_tiles(L):
+    a = L.lora_workspace_bytes(B.LORA_OP_MOE_GROUPED, B.LORA_BF16, 3072, 2048, 1408, 16, 64)
+    g = L.lora_workspace_bytes(B.LORA_OP_MOE_GATHER, B.LORA_BF16, 3072, 2048, 1408, 16, 64)
+    assert a == g > 0

@@ -135,6 +135,77 @@ def test_moe_invalid_expert_rows_not_written(orc):
     check(got[keep], ref[keep], "bf16", "moe valid rows")
 
 
+@pytest.mark.parametrize("seed,dtype,E,n,k,n_out", [
+    (24, "bf16", 5, 90, 72, 48),
+    (25, "bf16", 9, 300, 136, 264),    # 300 rows over 9 experts: several row tiles per expert
+    (26, "bf16", 64, 200, 64, 32),     # more experts than rows per expert, many empty
+    (27, "f32", 4, 23, 37, 29),
+])
+def test_moe_grouped_small(orc, seed, dtype, E, n, k, n_out):
+    """atlas moe_lora_grouped_down: rows sorted by expert, ranges from
+    expert_offsets; rows outside every range keep their sentinel."""
+    wl = WL.random_small(seed, dtype=dtype, k=k, n_out=n_out, n=n, n_slots=3, max_rank=16,
+                         kind="moe_grouped", n_experts=E)
+    dw = DeviceWorkload(wl)
+    dw.y.fill_(float("nan"))
+    dw.run()
+    torch.cuda.synchronize()
+    ref = orc.run(wl, scale_table=dw.scale_table_host)
+    got = dw.y_host()
+    outside = np.isnan(ref[:, 0])
+    assert np.all(np.isnan(got[outside])), "a row outside every expert range was written"
+    check(got[~outside], ref[~outside], dtype, wl.name)
+
+
+def test_moe_grouped_equals_gather_sorted():
+    """The grouped call on the gather's routing slots sorted by expert gives the
+    gather's rows, bit for bit: each output is reduced row-locally in the same order."""
+    wl = WL.random_small(28, dtype="bf16", k=200, n_out=96, n=40, n_slots=3, max_rank=16,
+                         kind="moe", n_experts=6, top_k=3)
+    dg = DeviceWorkload(wl)
+    yg = bf16_bits(dg.run().clone())
+    order, off, rs = WL.group_by_expert(wl.indices, wl.token_slot, wl.top_k, wl.n_experts)
+    ws = WL.Workload(name="sorted", dtype="bf16", k_in=wl.k_in, n_out=wl.n_out,
+                     max_rank=wl.max_rank, W=wl.W, A=wl.A, B=wl.B, x=wl.x[order],
+                     adapters=wl.adapters, kind="moe_grouped", n_experts=wl.n_experts,
+                     expert_offsets=off, row_slot=rs)
+    ds = DeviceWorkload(ws)
+    ys = bf16_bits(ds.run().clone())
+    torch.cuda.synchronize()
+    assert np.array_equal(ys, yg[order])
+
+
+@pytest.mark.parametrize("dtype,R", [("bf16", 32), ("f32", 8)])
+def test_moe_grouped_shrink_and_expand_fold(orc, dtype, R):
+    wl = WL.random_small(29, dtype=dtype, k=520, n_out=136 if dtype == "bf16" else 50, n=80,
+                         n_slots=3, max_rank=R, kind="moe_grouped", n_experts=5)
+    dw = DeviceWorkload(wl, null_slots=[7])  # adapter 1, expert 2
+    oroute = orc.route_for(wl, dw.scale_table_host, null_slots=[7])
+    t = torch.full((dw.n, R), float("nan"), dtype=torch.float32, device="cuda")
+    B.lora_moe_grouped_shrink(dw.route, dw.x, dw.x_row_stride, dw.expert_offsets, dw.seq_slot,
+                              dw.n, t)
+    rng = np.random.default_rng(4)
+    th = rng.standard_normal((dw.n, R)).astype(np.float32)
+    yh = rng.standard_normal((dw.n, wl.n_out)).astype(np.float32)
+    yh = WL.f32_to_bf16_bits(yh) if dtype == "bf16" else yh
+    y = to_device(yh)
+    B.lora_moe_grouped_expand_fold(dw.route, to_device(th), dw.expert_offsets, dw.seq_slot, dw.n,
+                                   y, wl.n_out)
+    torch.cuda.synchronize()
+    got_t = t.cpu().numpy().astype(np.float64)
+    ref_t = orc.moe_grouped_shrink(oroute, wl.x, wl.expert_offsets, wl.row_slot)
+    written = ~np.isnan(ref_t[:, 0])
+    assert written.sum() >= 20
+    assert np.array_equal(~np.isnan(got_t[:, 0]), written), "rows written differ from rows routed"
+    check(got_t[written], ref_t[written], "f32", "grouped shrink")
+    ref_y = orc.moe_grouped_expand_fold(oroute, th, wl.expert_offsets, wl.row_slot, yh)
+    got = bf16_bits(y)
+    if dtype == "bf16":
+        assert np.array_equal(got[~written], yh[~written])  # untouched bit for bit
+        got = (got.astype(np.uint32) << 16).view(np.float32)
+    check(got, ref_y, dtype, "grouped expand_fold")
+
+
 # ------------------------------------------------------------------ hand cases, bit exact
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_hand_cases_bit_exact(dtype):
@@ -143,9 +214,10 @@ def test_hand_cases_bit_exact(dtype):
             continue  # the bf16 path takes padded shapes only; see the padded variant below
         wl = golden_cases.hand_workload(case, dtype)
         dw = DeviceWorkload(wl)
+        dw.y.fill_(float("nan"))
         dw.run()
         torch.cuda.synchronize()
-        assert np.array_equal(dw.y_host(), np.array(case["y"], np.float64)), case["name"]
+        assert np.array_equal(dw.y_host(), golden_cases.expected_y(case), equal_nan=True), case["name"]
 
 
 def _pad_case(case, k_to=8, o_to=8, r_to=16):
@@ -159,7 +231,7 @@ def _pad_case(case, k_to=8, o_to=8, r_to=16):
         sl = tuple(slice(0, s) for s in a.shape)
         out[sl] = a
         return out
-    if case["kind"] == "moe":
+    if case["kind"] in ("moe", "moe_grouped"):
         c["W"] = pad(case["W"], (len(case["W"]), O, K)).tolist()
     else:
         c["W"] = pad(case["W"], (O, K)).tolist()
@@ -168,7 +240,8 @@ def _pad_case(case, k_to=8, o_to=8, r_to=16):
     c["x"] = pad(case["x"], (len(case["x"]), K)).tolist()
     c["k_in"], c["n_out"], c["max_rank"] = K, O, R
     y = np.zeros((len(case["y"]), O))
-    y[:, :o] = case["y"]
+    y[:, :o] = golden_cases.expected_y(case)
+    y[np.isnan(y[:, 0])] = np.nan  # a row that is not written stays NaN in every column
     return c, y
 
 
@@ -177,9 +250,10 @@ def test_hand_cases_padded_bf16_bit_exact():
         c, want = _pad_case(case)
         wl = golden_cases.hand_workload(c, "bf16")
         dw = DeviceWorkload(wl)
+        dw.y.fill_(float("nan"))
         dw.run()
         torch.cuda.synchronize()
-        assert np.array_equal(dw.y_host(), want), case["name"]
+        assert np.array_equal(dw.y_host(), want, equal_nan=True), case["name"]
 
 
 # ------------------------------------------------------------------ exact-integer routing
@@ -190,14 +264,15 @@ def _int_pool(rng, S, R, k, n_out, E=1):
     return A, Bp
 
 
-@pytest.mark.parametrize("kind", ["decode", "segmented", "moe"])
+@pytest.mark.parametrize("kind", ["decode", "segmented", "moe", "moe_grouped"])
 def test_integer_routing_bit_exact(orc, kind):
     """Small integers, power-of-two scales: every partial sum is exact in f32 and
     every output is a multiple of 1/2 below 128, so the GPU must equal the oracle exactly."""
     rng = np.random.default_rng(42)
     k, n_out, R, S = 16, 24, 16, 4
-    E = 3 if kind == "moe" else 1
-    W = rng.integers(-1, 2, (E, n_out, k) if kind == "moe" else (n_out, k)).astype(np.float32)
+    moe = kind in ("moe", "moe_grouped")
+    E = 3 if moe else 1
+    W = rng.integers(-1, 2, (E, n_out, k) if moe else (n_out, k)).astype(np.float32)
     A, Bp = _int_pool(rng, S, R, k, n_out, E)
     A[:, 2:, :] = 0    # rank 2 in a rank-16 pool keeps the sums small
     Bp[:, :, 2:] = 0
@@ -214,20 +289,30 @@ def test_integer_routing_bit_exact(orc, kind):
         x = rng.integers(-1, 2, (30, k)).astype(np.float32)
         wl = WL.Workload(x=WL.f32_to_bf16_bits(x), seg_indptr=np.array([0, 7, 7, 19, 30], np.int32),
                          seg_slot=np.array([2, 0, -1, 1], np.int32), **kw)
+    elif kind == "moe_grouped":  # rows 0-1 and 27-28 outside every range; expert 1 empty
+        x = rng.integers(-1, 2, (29, k)).astype(np.float32)
+        rs = np.array([0, 1, 2, 3, -1, 7, 0, 1, 2, 3, 1, 0, 3, 2, 1, 0] + list(rng.integers(-1, 5, 13)),
+                      np.int32)
+        wl = WL.Workload(x=WL.f32_to_bf16_bits(x), n_experts=E,
+                         expert_offsets=np.array([2, 15, 15, 27], np.int32), row_slot=rs, **kw)
     else:
         x = rng.integers(-1, 2, (24, k)).astype(np.float32)
         idx = np.array([rng.choice(E, 2, replace=False) for _ in range(12)], np.int32).reshape(-1)
         wl = WL.Workload(x=WL.f32_to_bf16_bits(x), n_experts=E, top_k=2, indices=idx,
                          token_slot=np.array([0, 1, 2, 3, -1, 7, 0, 1, 2, 3, 1, 0], np.int32), **kw)
     dw = DeviceWorkload(wl)
+    dw.y.fill_(float("nan"))
     dw.run()
     torch.cuda.synchronize()
     if kind == "decode":
         ref = orc.apply(wl.W, orc.route_for(wl, dw.scale_table_host), wl.x, ss, 1)
     else:
         ref = orc.run(wl, scale_table=dw.scale_table_host)
-    assert np.all(np.abs(ref) < 128) and np.array_equal(2 * ref, np.round(2 * ref))  # halves: exact in bf16
-    assert np.array_equal(dw.y_host(), ref)
+    done = ~np.isnan(ref[:, 0])
+    assert done.sum() >= 20
+    r = ref[done]
+    assert np.all(np.abs(r) < 128) and np.array_equal(2 * r, np.round(2 * r))  # halves: exact in bf16
+    assert np.array_equal(dw.y_host(), ref, equal_nan=True)
 
 
 # ------------------------------------------------------------------ byte identity
@@ -360,6 +445,21 @@ def _sample_rows(n, extra=(), k=24, seed=0):
     rng = np.random.default_rng(seed)
     rows = set(int(v) for v in rng.choice(n, size=min(k, n), replace=False)) | set(extra)
     return np.array(sorted(r for r in rows if 0 <= r < n), np.int32)
+
+
+def test_moe_grouped_full_size(orc):
+    """The grouped workload at full size (2048 tokens x top-6 over 64 experts
+    [2048 x 1408], rank 16): sampled rows, the first and last row of every
+    tenth expert range among them."""
+    wl = WL.moe_down_grouped()
+    dw = DeviceWorkload(wl)
+    dw.run()
+    torch.cuda.synchronize()
+    off = wl.expert_offsets
+    edges = [int(v) for e in range(0, wl.n_experts, 10) for v in (off[e], off[e + 1] - 1)]
+    rows = _sample_rows(dw.n, extra=edges + [0, dw.n - 1], k=64)
+    ref = orc.run(wl, rows=rows, scale_table=dw.scale_table_host)
+    check(dw.y_host()[rows], ref, "bf16", wl.name)
 
 
 @pytest.mark.parametrize("name", list(WL.CONFIGS))
