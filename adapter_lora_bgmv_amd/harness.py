@@ -38,7 +38,7 @@ class DeviceWorkload:
 
     def __init__(self, wl: Workload, device="cuda", scale_table=None,
                  null_slots: Optional[Sequence[int]] = None, x_extra_cols: int = 0,
-                 y_extra_cols: int = 0):
+                 y_extra_cols: int = 0, y_col_offset: int = 0):
         import torch
         self.wl = wl
         self.device = device
@@ -52,9 +52,13 @@ class DeviceWorkload:
         xh[:, :k] = wl.x
         self.x = to_device(xh, device)
         self.x_row_stride = xs
-        self.y_row_stride = wl.n_out + y_extra_cols
+        # y's rows may be wider than n_out, with the projection's columns at
+        # y_col_offset inside them (an interleaved [Q|K|V] row, say)
+        self.y_row_stride = y_col_offset + wl.n_out + y_extra_cols
+        self.y_col_offset = y_col_offset
         tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-        self.y = torch.empty((n, self.y_row_stride), dtype=tdt, device=device)
+        self.y_full = torch.empty((n, self.y_row_stride), dtype=tdt, device=device)
+        self.y = self.y_full[:, y_col_offset:]
         self.scale_table_host = (B.lora_scale_table(wl.adapters) if scale_table is None
                                  else np.asarray(scale_table, np.float32))
         ns = wl.null_slots if null_slots is None else null_slots

@@ -274,9 +274,33 @@ CONFIGS = {
 }
 
 
-# workloads of the variants built beyond the five: the grouped MoE layout
+def spec_verify_kv(seed: int = 0, n_seqs: int = 4, draft: int = 9, k: int = 4096,
+                   kv_dim: int = 1024, q_dim: int = 4096, n_slots: int = 16, rank: int = 16,
+                   alpha: float = 32.0, dtype: str = BF16) -> Workload:
+    """Speculative verify on the K projection: n_seqs sequences x `draft` tokens
+    = 36 rows, each sequence's rows on its sequence's adapter; W_k [1024 x 4096]
+    writing into the K columns of an interleaved [Q|K|V] row (q_dim + 2 kv_dim
+    elements)."""
+    rng = np.random.default_rng(seed)
+    W = _store(rng.standard_normal((kv_dim, k)) * 0.02, dtype)
+    A, B, At, Bt = _pool(rng, [rank] * n_slots, k, kv_dim, rank, 0.02, dtype)
+    n = n_seqs * draft
+    x = _store(rng.standard_normal((n, k)), dtype)
+    seq_slots = rng.integers(0, n_slots, size=n_seqs).astype(np.int32)
+    slots = np.repeat(seq_slots, draft).astype(np.int32)
+    return Workload(name=f"spec_verify_kv_{kv_dim}x{k}_s{n_slots}_r{rank}_{n_seqs}x{draft}",
+                    dtype=dtype, k_in=k, n_out=kv_dim, max_rank=rank, W=W, A=A, B=B, x=x,
+                    adapters=[AdapterSpec(rank, alpha, 1.0) for _ in range(n_slots)],
+                    adapter_slots=slots, padded_n=n, active=0, A_true=At, B_true=Bt,
+                    meta={"q_dim": q_dim, "kv_dim": kv_dim, "qkv_row": q_dim + 2 * kv_dim,
+                          "n_seqs": n_seqs, "draft": draft, "seq_slots": seq_slots})
+
+
+# workloads of the variants built beyond the five: the grouped MoE layout and
+# the speculative-verify K fold
 NEXT_WORKLOADS = {
     "moe_down_grouped": moe_down_grouped,
+    "spec_verify_kv": spec_verify_kv,
 }
 
 

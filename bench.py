@@ -44,14 +44,24 @@ WORKLOAD_TEXT = {
     "prefill_segmented": "prefill segmented: o_proj W 4096x4096 bf16, 8 segments x 512 tokens, one rank-64 adapter each",
     "moe_down_gather": "MoE down_proj gather: 64 experts W_e 2048x1408 bf16, 512 tokens top-6, rank-16 pair per (adapter, expert), 4 adapters",
     "moe_down_grouped": "MoE down_proj grouped: 64 experts W_e 2048x1408 bf16, 2048 tokens top-6 = 12288 rows sorted by expert (expert_offsets), rank-16 pair per (adapter, expert), 4 adapters",
+    "spec_verify_kv": "speculative verify, K projection: W_k 1024x4096 bf16, 16 slots r=16 alpha 32, 4 sequences x 9 draft tokens = 36 rows, output into the K columns of interleaved [Q|K|V] rows (6144 elements)",
 }
 ROTATE = {"single_projection_f32": 4, "decode_bgmv": 16, "fused_gate_up": 4,
-          "prefill_segmented": 8, "moe_down_gather": 2, "moe_down_grouped": 2}
+          "prefill_segmented": 8, "moe_down_gather": 2, "moe_down_grouped": 2,
+          "spec_verify_kv": 64}
 BOUND = {"single_projection_f32": "latency", "decode_bgmv": "hbm", "fused_gate_up": "hbm",
-         "prefill_segmented": "mfma", "moe_down_gather": "hbm", "moe_down_grouped": "hbm"}
+         "prefill_segmented": "mfma", "moe_down_gather": "hbm", "moe_down_grouped": "hbm",
+         "spec_verify_kv": "latency"}
 # the five workloads of the path, then the variants built beyond them
 OTHERS = ("single_projection_f32", "fused_gate_up", "prefill_segmented", "moe_down_gather",
-          "moe_down_grouped")
+          "moe_down_grouped", "spec_verify_kv")
+
+
+def device_kwargs(wl):
+    """Output placement of a workload: the verify K fold writes into [Q|K|V] rows."""
+    if wl.name.startswith("spec_verify_kv"):
+        return {"y_col_offset": wl.meta["q_dim"], "y_extra_cols": wl.meta["kv_dim"]}
+    return {}
 
 
 def workload(name):
@@ -196,7 +206,7 @@ def time_workload(name, steps, warmup, apply=True):
 
     wl = workload(name)
     R = ROTATE[name]
-    dws = [DeviceWorkload(wl) for _ in range(R)]
+    dws = [DeviceWorkload(wl, **device_kwargs(wl)) for _ in range(R)]
     counts = algorithmic_counts(wl, dws[0].scale_table_host)
     steps = max(R, (steps + R - 1) // R * R)
 

@@ -503,6 +503,69 @@ def test_stream_k_partition(orc, seed, k, n_out, n, R):
     check(dw.y_host()[rows], ref, "bf16", wl.name)
 
 
+# ------------------------------------------------------------------ speculative verify, strided folds
+def _qkv_regions(dw):
+    """Bits of the Q, K and V column blocks of the interleaved rows."""
+    m = dw.wl.meta
+    full = bf16_bits(dw.y_full)
+    q, kv = m["q_dim"], m["kv_dim"]
+    return full[:, :q], full[:, q:q + kv], full[:, q + kv:q + 2 * kv]
+
+
+@pytest.mark.parametrize("n_seqs,draft", [(4, 9), (1, 9), (3, 5), (2, 1)])
+def test_spec_verify_k_fold_into_qkv(orc, n_seqs, draft):
+    """atlas lora_gemv_max_m doc: speculative verify presents n_seqs x draft rows
+    (up to 4 x 9 = 36), every row of a sequence on the sequence's adapter; the
+    apply_lora_bgmv doc: the K projection's output row stride is the interleaved
+    [Q|K|V] row, so the result lands in the K columns and Q and V stay as they were."""
+    wl = WL.spec_verify_kv(seed=80 + n_seqs * 10 + draft, n_seqs=n_seqs, draft=draft)
+    m = wl.meta
+    dw = DeviceWorkload(wl, y_col_offset=m["q_dim"], y_extra_cols=m["kv_dim"])
+    dw.y_full.fill_(float("nan"))
+    dw.run()
+    torch.cuda.synchronize()
+    q, k, v = _qkv_regions(dw)
+    assert np.all(q == 0x7FC0) and np.all(v == 0x7FC0), "a Q or V column was written"
+    ref = orc.run(wl, scale_table=dw.scale_table_host)
+    check(dw.y_host(), ref, "bf16", wl.name)
+    # the batched verify equals each sequence verified on its own, bit for bit
+    for s in range(n_seqs):
+        rows = slice(s * draft, (s + 1) * draft)
+        one = WL.Workload(name="seq", dtype="bf16", k_in=wl.k_in, n_out=wl.n_out,
+                          max_rank=wl.max_rank, W=wl.W, A=wl.A, B=wl.B, x=wl.x[rows],
+                          adapters=wl.adapters, adapter_slots=wl.adapter_slots[rows],
+                          padded_n=draft, meta=dict(m))
+        d1 = DeviceWorkload(one, y_col_offset=m["q_dim"], y_extra_cols=m["kv_dim"])
+        d1.run()
+        torch.cuda.synchronize()
+        assert np.array_equal(d1.y_bits(), k[rows]), s
+
+
+def test_strided_expand_fold_into_v(orc):
+    """atlas apply_lora_bgmv doc (STRIDES): the V delta folds into the V columns
+    of the interleaved [Q|K|V] rows; rows that skip, and the Q and K columns,
+    keep their bits."""
+    wl = WL.spec_verify_kv(seed=90, n_seqs=4, draft=9)
+    m = wl.meta
+    q, kv, row = m["q_dim"], m["kv_dim"], m["qkv_row"]
+    dw = DeviceWorkload(wl)
+    ss = dw.seq_slot_host.copy()
+    ss[[0, 10, 20]] = [-1, 99, -3]
+    dw.seq_slot.copy_(torch.from_numpy(ss))
+    rng = np.random.default_rng(5)
+    full = WL.f32_to_bf16_bits(rng.standard_normal((dw.n, row)).astype(np.float32))
+    qkv = to_device(full)
+    th = rng.standard_normal((dw.n, wl.max_rank)).astype(np.float32)
+    B.lora_expand_fold(dw.route, to_device(th), dw.seq_slot, dw.n, qkv[:, q + kv:], row)
+    torch.cuda.synchronize()
+    got = bf16_bits(qkv)
+    assert np.array_equal(got[:, :q + kv], full[:, :q + kv]), "a Q or K column changed"
+    vin = full[:, q + kv:]
+    ref = orc.expand_fold(orc.route_for(wl, dw.scale_table_host), th, ss, vin)
+    assert np.array_equal(got[[0, 10, 20], q + kv:], vin[[0, 10, 20]])
+    check((got[:, q + kv:].astype(np.uint32) << 16).view(np.float32), ref, "bf16", "V fold")
+
+
 def test_decode_batch_equals_per_row_calls():
     """atlas apply_lora_bgmv doc: the batched call equals n one-row calls.  On the
     decode path every output element is reduced in the same order whatever the
