@@ -78,7 +78,7 @@ class Workload:
     B: np.ndarray                      # [P][n_out][max_rank], pad cols zero
     x: np.ndarray                      # [n][k_in]
     adapters: List[AdapterSpec]        # one per pool slot (moe: per adapter)
-    kind: str = "decode"               # decode | segmented | moe | moe_grouped
+    kind: str = "decode"               # decode | segmented | moe | moe_grouped | stack
     # decode routing (metrale slot_math.rs build_seq_slot_host inputs)
     adapter_slots: Optional[np.ndarray] = None   # [n_real] int32, <0 = active
     padded_n: int = 0
@@ -296,11 +296,56 @@ def spec_verify_kv(seed: int = 0, n_seqs: int = 4, draft: int = 9, k: int = 4096
                           "n_seqs": n_seqs, "draft": draft, "seq_slots": seq_slots})
 
 
-# workloads of the variants built beyond the five: the grouped MoE layout and
-# the speculative-verify K fold
+def adapter_stack(seed: int = 0, k: int = 4096, n_out: int = 4096, n_levels: int = 3,
+                  n_slots: int = 8, rank: int = 16, alpha: float = 32.0, n: int = 64,
+                  dtype: str = BF16) -> Workload:
+    """Adapter stack on q_proj (W [4096 x 4096]): three levels, each a pool of 8
+    rank-16 adapters (alpha 32) with its own per-row slot; 64 rows, every level
+    drawing its rows' slots uniformly from [-1, 8) (-1: the level adds nothing)."""
+    rng = np.random.default_rng(seed)
+    W = _store(rng.standard_normal((n_out, k)) * 0.02, dtype)
+    levels = []
+    for _ in range(n_levels):
+        A, B, At, Bt = _pool(rng, [rank] * n_slots, k, n_out, rank, 0.02, dtype)
+        levels.append({"A": A, "B": B, "adapters": [AdapterSpec(rank, alpha, 1.0)] * n_slots})
+    x = _store(rng.standard_normal((n, k)), dtype)
+    for lv in levels:
+        lv["seq_slot"] = rng.integers(-1, n_slots, size=n).astype(np.int32)
+    l0 = levels[0]
+    return Workload(name=f"adapter_stack_{n_out}x{k}_{n_levels}lv_s{n_slots}_r{rank}_n{n}",
+                    dtype=dtype, k_in=k, n_out=n_out, max_rank=rank, W=W, A=l0["A"], B=l0["B"],
+                    x=x, adapters=l0["adapters"], kind="stack", adapter_slots=l0["seq_slot"],
+                    padded_n=n, active=0, meta={"levels": levels, "seq_slot": l0["seq_slot"]})
+
+
+def random_stack(seed: int, dtype: str = BF16, k: int = 96, n_out: int = 80, n: int = 13,
+                 n_levels: int = 2, n_slots: int = 3, max_rank: int = 16) -> Workload:
+    """Small stack with ragged sizes, mixed ranks and -1 / out-of-range slots per level."""
+    rng = np.random.default_rng(seed)
+    W = _store(rng.standard_normal((n_out, k)) * 0.05, dtype)
+    levels = []
+    for _ in range(n_levels):
+        ranks = [int(rng.integers(1, max_rank + 1)) for _ in range(n_slots)]
+        A, B, At, Bt = _pool(rng, ranks, k, n_out, max_rank, 0.1, dtype)
+        ad = [AdapterSpec(ranks[s], float(rng.choice([0.0, 8.0])), float(rng.choice([0.5, 1.0])),
+                          bool(rng.integers(0, 2))) for s in range(n_slots)]
+        levels.append({"A": A, "B": B, "adapters": ad})
+    x = _store(rng.standard_normal((n, k)), dtype)
+    for lv in levels:
+        lv["seq_slot"] = rng.integers(-1, n_slots + 1, size=n).astype(np.int32)
+    l0 = levels[0]
+    return Workload(name=f"small_stack_s{seed}", dtype=dtype, k_in=k, n_out=n_out,
+                    max_rank=max_rank, W=W, A=l0["A"], B=l0["B"], x=x, adapters=l0["adapters"],
+                    kind="stack", adapter_slots=l0["seq_slot"], padded_n=n, active=0,
+                    meta={"levels": levels, "seq_slot": l0["seq_slot"]})
+
+
+# workloads of the variants built beyond the five: the grouped MoE layout,
+# the speculative-verify K fold and the adapter stack
 NEXT_WORKLOADS = {
     "moe_down_grouped": moe_down_grouped,
     "spec_verify_kv": spec_verify_kv,
+    "adapter_stack": adapter_stack,
 }
 
 

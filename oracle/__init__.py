@@ -103,6 +103,9 @@ class Oracle:
                                              _f64p]
         L.orc_moe_grouped_expand_fold.argtypes = [RP, _f32p, _i32p, _i32p, C.c_int, C.c_void_p,
                                                   C.c_int, _f64p]
+        L.orc_apply_stack.argtypes = [C.c_void_p, C.c_int, C.POINTER(RP), C.POINTER(_i32p),
+                                      C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_int,
+                                      _i32p, C.c_int, _f64p]
         L.orc_mutant.restype = C.c_int
         L.orc_threads.restype = C.c_int
         self.L = L
@@ -266,6 +269,23 @@ class Oracle:
                                            _p(out, _f64p))
         return out
 
+    def apply_stack(self, W, routes, x, seq_slots, dtype, rows=None) -> np.ndarray:
+        """y = W x + the deltas of every level in order; routes[l] / seq_slots[l] per level."""
+        W = np.ascontiguousarray(W)
+        x = np.ascontiguousarray(x)
+        n_out, k_in = W.shape
+        L = len(routes)
+        assert L == len(seq_slots)
+        ss = [np.ascontiguousarray(v, np.int32) for v in seq_slots]
+        rarr = (C.POINTER(_Route) * max(L, 1))(*[C.pointer(r.c) for r in routes])
+        sarr = (_i32p * max(L, 1))(*[_p(v, _i32p) for v in ss])
+        rr = np.arange(x.shape[0], dtype=np.int32) if rows is None else \
+            np.ascontiguousarray(rows, np.int32)
+        y = np.empty((len(rr), n_out), np.float64)
+        self.L.orc_apply_stack(_p(W), W.shape[1], rarr, sarr, L, dtype, k_in, n_out, _p(x),
+                               x.shape[1], _p(rr, _i32p), len(rr), _p(y, _f64p))
+        return y
+
     # -------------------------------------------------------------- workload glue
     def seq_slot_for(self, wl) -> np.ndarray:
         return self.build_seq_slot(wl.adapter_slots, wl.padded_n, wl.active)
@@ -280,6 +300,14 @@ class Oracle:
             return self.apply_segmented(wl.W, r, wl.x, wl.seg_indptr, wl.seg_slot, dt, rows)
         if wl.kind == "moe":
             return self.apply_moe(wl.W, r, wl.x, wl.indices, wl.top_k, wl.token_slot, dt, rows)
+        if wl.kind == "stack":
+            levels = wl.meta["levels"]
+            sts = [self.scale_table(lv["adapters"]) for lv in levels] if scale_table is None \
+                else scale_table
+            routes = [Route(lv["A"], lv["B"], st, dt, wl.k_in, wl.n_out, wl.max_rank)
+                      for lv, st in zip(levels, sts)] if route else []
+            return self.apply_stack(wl.W, routes, wl.x,
+                                    [lv["seq_slot"] for lv in levels] if route else [], dt, rows)
         if wl.kind == "moe_grouped":
             return self.apply_moe_grouped(wl.W, r, wl.x, wl.expert_offsets, wl.row_slot, dt,
                                           rows)

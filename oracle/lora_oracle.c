@@ -18,7 +18,7 @@
  * Sources (page title, then the item):
  *  - ferrox-core "weight_matrix/lora.rs": module doc (the formula, layouts,
  *    scale, "cost when absent"), LoraDelta::new / effective_scale / project /
- *    accumulate / add_to / add_batch_to.
+ *    accumulate / add_to / add_batch_to, LoraStack (adapters applied in order).
  *  - frink-models "lora_attach.rs": module doc (fused-tensor split: one copy
  *    of A per part, B rows split in order).
  *  - atlas "spark_model/layers/ops/lora_delta.rs": LoraRoute, LoraPair
@@ -450,6 +450,41 @@ void orc_moe_grouped_expand_fold(const orc_route *r, const float *t,
     double s = (double)r->scale[a];
     for (int o = 0; o < r->n_out; ++o) yo[o] = yo[o] + delta_sign() * s * expand_one(r, idx, o, tt);
     free(tt);
+  }
+}
+
+/*
+ * Adapter stack (ferrox lora.rs LoraStack: every adapter attached to one
+ * base matrix, applied in order, each a term of the sum W x + sum_i s_i
+ * B_i (A_i x)).  Level l has its own route and per-row slot buffer;
+ * y[i] = W x_i + sum over levels, in level order, of the level's delta
+ * (each level skips by the usual rule).  Only the listed rows.
+ */
+void orc_apply_stack(const void *W, int w_stride, const orc_route *const *routes,
+                     const int32_t *const *seq_slots, int n_levels, int dtype, int k_in,
+                     int n_out, const void *x, int x_stride, const int32_t *rows, int n_rows,
+                     double *y) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int jj = 0; jj < n_rows; ++jj) {
+    size_t i = (size_t)rows[jj];
+    size_t x_off = xrow(i, x_stride, k_in);
+    double *yo = y + (size_t)jj * n_out;
+    for (int o = 0; o < n_out; ++o) yo[o] = base_one(W, 0, w_stride, dtype, o, x, x_off, k_in);
+#if ORC_MUTANT == 15
+    for (int l = 0; l < n_levels && l < 1; ++l) {
+#else
+    for (int l = 0; l < n_levels; ++l) {
+#endif
+      const orc_route *r = routes[l];
+      int slot = seq_slots[l][i];
+      int idx = resolve(r, slot, 0);
+      if (idx < 0) continue; /* this level adds nothing to the row */
+      double *t = (double *)malloc(sizeof(double) * (size_t)r->max_rank);
+      shrink_row(r, idx, x, x_off, t);
+      double s = (double)r->scale[slot];
+      for (int o = 0; o < n_out; ++o) yo[o] = yo[o] + delta_sign() * s * expand_one(r, idx, o, t);
+      free(t);
+    }
   }
 }
 

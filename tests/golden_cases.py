@@ -25,9 +25,22 @@ def expected_y(case):
     return np.array([[np.nan] * n_out if r is None else r for r in case["y"]], np.float64)
 
 
+def _adapters(rows):
+    return [AdapterSpec(rank=r, alpha=al, adapter_scale=s, rslora=rs) for (s, al, r, rs) in rows]
+
+
 def hand_workload(case, dtype="f32"):
-    ad = [AdapterSpec(rank=r, alpha=al, adapter_scale=s, rslora=rs)
-          for (s, al, r, rs) in case["adapters"]]
+    if case["kind"] == "stack":
+        levels = [{"A": _arr(lv["A"], dtype), "B": _arr(lv["B"], dtype),
+                   "adapters": _adapters(lv["adapters"]),
+                   "seq_slot": np.array(lv["seq_slot"], np.int32)} for lv in case["levels"]]
+        l0 = levels[0]
+        return Workload(name=case["name"], dtype=dtype, k_in=case["k_in"], n_out=case["n_out"],
+                        max_rank=case["max_rank"], W=_arr(case["W"], dtype), A=l0["A"], B=l0["B"],
+                        x=_arr(case["x"], dtype), adapters=l0["adapters"], kind="stack",
+                        adapter_slots=l0["seq_slot"], padded_n=len(l0["seq_slot"]),
+                        meta={"levels": levels, "seq_slot": l0["seq_slot"]})
+    ad = _adapters(case["adapters"])
     kw = dict(name=case["name"], dtype=dtype, k_in=case["k_in"], n_out=case["n_out"],
               max_rank=case["max_rank"], W=_arr(case["W"], dtype), A=_arr(case["A"], dtype),
               B=_arr(case["B"], dtype), x=_arr(case["x"], dtype), adapters=ad, kind=case["kind"])

@@ -20,6 +20,7 @@ import numpy as np
 
 import brute
 import golden_cases
+import oracle
 from adapter_lora_bgmv_amd import workloads as WL
 
 PINS = []
@@ -83,6 +84,8 @@ def _hand_run(o, wl, case):
         return o.apply_segmented(wl.W, r, wl.x, wl.seg_indptr, wl.seg_slot, dt)
     if wl.kind == "moe_grouped":
         return o.apply_moe_grouped(wl.W, r, wl.x, wl.expert_offsets, wl.row_slot, dt)
+    if wl.kind == "stack":
+        return o.run(wl)
     return o.apply_moe(wl.W, r, wl.x, wl.indices, wl.top_k, wl.token_slot, dt)
 
 
@@ -237,6 +240,50 @@ def grouped_shrink_and_expand_match_matmul(o):
             assert np.all(np.isnan(t[j])), f"skipped row {j} written"
             assert np.array_equal(yo[j], brute.widen(yin[j], "bf16")), f"skipped row {j} changed"
     assert live >= 4
+
+
+def _stack_routes(o, wl, sts=None):
+    levels = wl.meta["levels"]
+    sts = sts or [o.scale_table(lv["adapters"]) for lv in levels]
+    dt = _dt(wl)
+    return [oracle.Route(lv["A"], lv["B"], st, dt, wl.k_in, wl.n_out, wl.max_rank)
+            for lv, st in zip(levels, sts)], sts
+
+
+@pin
+def brute_force_tiny_stack(o):
+    """ferrox LoraStack: W x + sum over levels of s_l B_l (A_l x), each level routed
+    on its own; the brute force materialises W + sum_l s_l B_l A_l per row."""
+    for seed in range(4):
+        dtype = "bf16" if seed % 2 == 0 else "f32"
+        wl = WL.random_stack(500 + seed, dtype=dtype, k=9, n_out=6, n=7, n_levels=2 + seed % 2,
+                             n_slots=3, max_rank=4)
+        routes, sts = _stack_routes(o, wl)
+        levels = wl.meta["levels"]
+        y = o.apply_stack(wl.W, routes, wl.x, [lv["seq_slot"] for lv in levels], _dt(wl))
+        Wd, xd = brute.widen(wl.W, dtype), brute.widen(wl.x, dtype)
+        for i in range(wl.n_rows):
+            M = Wd.copy()
+            for lv, st in zip(levels, sts):
+                s = int(lv["seq_slot"][i])
+                if brute.resolved(s, len(st), set(), st):
+                    M = M + float(st[s]) * (brute.widen(lv["B"][s], dtype) @ brute.widen(lv["A"][s], dtype))
+            _close(y[i], M @ xd[i], 1e-12, f"stack seed {seed} row {i}")
+
+
+@pin
+def stack_of_one_is_the_apply(o):
+    """A stack with one adapter is that adapter's apply, bit for bit; a level whose
+    rows all skip adds nothing, bit for bit (ferrox: a zero scale is skipped
+    before any arithmetic)."""
+    wl = WL.random_stack(510, dtype="bf16", k=20, n_out=12, n=9, n_levels=2, n_slots=3, max_rank=8)
+    routes, sts = _stack_routes(o, wl)
+    lv = wl.meta["levels"]
+    one = o.apply_stack(wl.W, routes[:1], wl.x, [lv[0]["seq_slot"]], 1)
+    assert np.array_equal(one, o.apply(wl.W, routes[0], wl.x, lv[0]["seq_slot"], 1))
+    off = np.full(wl.n_rows, -1, np.int32)
+    two = o.apply_stack(wl.W, routes, wl.x, [lv[0]["seq_slot"], off], 1)
+    assert np.array_equal(two, one)
 
 
 @pin

@@ -9,6 +9,7 @@ Each mutant is a build of oracle/lora_oracle.c with ORC_MUTANT=k (CPU only):
  6 padding rows take the active slot           12 base drops the first input column
 13 grouped expert range end treated as inclusive
 14 grouped row slot read relative to its expert's first row
+15 a stack applies its first adapter only
 """
 import shutil
 
@@ -18,7 +19,7 @@ import oracle
 import oracle_pins
 from oracle import build as obuild
 
-MUTANTS = list(range(1, 15))
+MUTANTS = list(range(1, 16))
 
 
 @pytest.fixture(scope="module")
