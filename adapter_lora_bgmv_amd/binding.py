@@ -17,7 +17,7 @@ import numpy as np
 LIB_PATH = Path(__file__).resolve().parent / "_lib" / "liblora_mi355x.so"
 
 LORA_F32, LORA_BF16 = 0, 1
-LORA_OP_APPLY, LORA_OP_SEGMENTED, LORA_OP_MOE_GATHER, LORA_OP_MOE_GROUPED = 0, 1, 2, 3
+LORA_OP_APPLY, LORA_OP_SEGMENTED, LORA_OP_MOE_GATHER, LORA_OP_MOE_GROUPED, LORA_OP_STACK = 0, 1, 2, 3, 4
 STATUS = {0: "LORA_OK", -1: "LORA_ERR_SHAPE", -2: "LORA_ERR_NULL_PTR", -3: "LORA_ERR_STRIDE",
           -4: "LORA_ERR_DTYPE", -5: "LORA_ERR_UNSUPPORTED", -6: "LORA_ERR_LAUNCH",
           -7: "LORA_ERR_WORKSPACE"}
@@ -27,7 +27,7 @@ EXPORTS = ("lora_last_error", "lora_version", "lora_init", "lora_scale", "lora_s
            "lora_build_seq_slot", "lora_workspace_bytes", "lora_shrink", "lora_expand_fold",
            "lora_apply", "lora_apply_segmented", "lora_apply_moe_gather",
            "lora_set_profile_events", "lora_moe_grouped_shrink", "lora_moe_grouped_expand_fold",
-           "lora_apply_moe_grouped")
+           "lora_apply_moe_grouped", "lora_apply_stack")
 
 
 class LoraError(RuntimeError):
@@ -86,6 +86,8 @@ def lib() -> C.CDLL:
     L.lora_moe_grouped_expand_fold.argtypes = [RM, vp, vp, vp, u32, vp, u32, vp]
     L.lora_apply_moe_grouped.argtypes = [i32, u32, u32, u32, vp, C.c_uint64, u32, RM, vp, u32, vp,
                                          vp, u32, vp, u32, vp, sz, vp]
+    L.lora_apply_stack.argtypes = [i32, u32, u32, vp, u32, C.POINTER(lora_route), C.POINTER(vp),
+                                   u32, vp, u32, u32, vp, u32, vp, sz, vp]
     _lib = L
     return L
 
@@ -274,3 +276,17 @@ def lora_apply_moe_grouped(dtype: int, n_experts: int, n_out: int, k_in: int, W_
                                         x_row_stride, _ptr(expert_offsets), _ptr(seq_slot), n,
                                         _ptr(y), y_row_stride, _ptr(workspace), workspace_bytes,
                                         _stream(stream)))
+
+
+def lora_apply_stack(dtype: int, n_out: int, k_in: int, W, w_row_stride: int, routes, x,
+                     x_row_stride: int, seq_slots, n: int, y, y_row_stride: int, workspace,
+                     workspace_bytes: int, stream=None):
+    """routes: DeviceRoutes, one per level; seq_slots: device int32 [n] tensors, one per level."""
+    L = len(routes)
+    assert L == len(seq_slots)
+    rarr = (lora_route * max(L, 1))(*[r.c for r in routes])
+    sarr = (C.c_void_p * max(L, 1))(*[_ptr(v) for v in seq_slots])
+    _check(lib().lora_apply_stack(dtype, n_out, k_in, _ptr(W), w_row_stride,
+                                  rarr if L else None, sarr if L else None, L, _ptr(x),
+                                  x_row_stride, n, _ptr(y), y_row_stride, _ptr(workspace),
+                                  workspace_bytes, _stream(stream)))

@@ -106,6 +106,46 @@ __global__ __launch_bounds__(256) void expand_fold_kernel(RouteDev rd, Routing r
   st(y, yi, ld((const T *)y, yi) + rd.scale_table[sidx] * d);
 }
 
+// ---------------------------------------------------------------- stack fold
+// The extra levels of an adapter stack (ferrox LoraStack: every adapter a
+// term of the sum, in order): y[i, o] = y[i, o] + sum over levels of
+// s_l * (B_l t_l[i])[o], the level sum in f32 and y rounded once.  A row no
+// level resolves is untouched.  One thread per output; each resolved
+// level's t row staged in LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void expand_fold_stack_kernel(StackFold f, T *y, int y_stride, int n_out) {
+  __shared__ float tsh[kMaxStackLevels][256];
+  __shared__ int q_of[kMaxStackLevels];
+  const int i = blockIdx.y;
+  if (threadIdx.x < f.n_levels) {
+    const StackLevel &L = f.lv[threadIdx.x];
+    q_of[threadIdx.x] = resolve_slot(L.seq_slot[i], 0, L.max_loras, 1, L.a_table, L.b_table, L.scale_table);
+  }
+  __syncthreads();
+  bool any = false;
+  for (int l = 0; l < f.n_levels; ++l) {
+    if (q_of[l] < 0) continue;
+    any = true;
+    for (int k = threadIdx.x; k < f.lv[l].R; k += 256) tsh[l][k] = f.lv[l].t[(size_t)i * f.lv[l].R + k];
+  }
+  if (!any) return;  // uniform: q_of is the same for every thread
+  __syncthreads();
+  const int o = blockIdx.x * 256 + threadIdx.x;
+  if (o >= n_out) return;
+  float acc = 0.f;
+  for (int l = 0; l < f.n_levels; ++l) {
+    const int q = q_of[l];
+    if (q < 0) continue;
+    const StackLevel &L = f.lv[l];
+    const T *B = (const T *)L.b_table[q];
+    float d = 0.f;
+    for (int k = 0; k < L.R; ++k) d += ld(B, (size_t)o * L.R + k) * tsh[l][k];
+    acc += L.scale_table[L.seq_slot[i]] * d;
+  }
+  const size_t yi = (size_t)i * y_stride + o;
+  st(y, yi, ld((const T *)y, yi) + acc);
+}
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_shrink_f32(const RouteDev &rd, const Routing &rt, const float *x, int x_stride,
                              int k_in, int n, float *t, hipStream_t st) {
@@ -131,6 +171,16 @@ hipError_t launch_expand_fold(const RouteDev &rd, int dtype, const Routing &rt, 
   else
     hipLaunchKernelGGL(expand_fold_kernel<u16>, grid, dim3(256), 0, st, rd, rt, t, (u16 *)y,
                        y_stride, n_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_expand_fold_stack(const StackFold &f, int dtype, void *y, int y_stride, int n_out, int n,
+                                    hipStream_t st) {
+  dim3 grid((n_out + 255) / 256, n);
+  if (dtype == 0)
+    hipLaunchKernelGGL(expand_fold_stack_kernel<float>, grid, dim3(256), 0, st, f, (float *)y, y_stride, n_out);
+  else
+    hipLaunchKernelGGL(expand_fold_stack_kernel<u16>, grid, dim3(256), 0, st, f, (u16 *)y, y_stride, n_out);
   return hipGetLastError();
 }
 

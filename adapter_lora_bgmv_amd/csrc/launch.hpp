@@ -115,6 +115,24 @@ constexpr int kMaxShrinkSplits = 8;
 // Largest key space the one-workgroup plan handles (LDS histogram).
 constexpr int kMaxKeys = 4096;
 
+// The extra levels of an adapter stack (every level but the first, which the
+// fused apply takes): each level's route tables, per-row slots and shrink
+// output t [n][R].
+constexpr int kMaxStackLevels = 8;
+struct StackLevel {
+  const void *const *a_table;
+  const void *const *b_table;
+  const float *scale_table;
+  const int32_t *seq_slot;
+  const float *t;
+  int max_loras;
+  int R;
+};
+struct StackFold {
+  StackLevel lv[kMaxStackLevels];
+  int n_levels;
+};
+
 size_t prep_lds_bytes(const PrepArgs &a);
 
 hipError_t launch_shrink_f32(const RouteDev &rd, const Routing &rt, const float *x, int x_stride,
@@ -124,6 +142,8 @@ hipError_t launch_apply_f32(const RouteDev &rd, const Routing &rt, bool has_lora
                             int k_in, int n_out, int n, float *y, int y_stride, hipStream_t st);
 hipError_t launch_expand_fold(const RouteDev &rd, int dtype, const Routing &rt, const float *t,
                               void *y, int y_stride, int n_out, int n, hipStream_t st);
+hipError_t launch_expand_fold_stack(const StackFold &f, int dtype, void *y, int y_stride, int n_out, int n,
+                                    hipStream_t st);
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &a, int to, int tr, hipStream_t st);
 hipError_t launch_decode_main(const DecodeArgs &a, hipStream_t st);

@@ -325,6 +325,41 @@ Routing routing_grouped(const int32_t *expert_offsets, const int32_t *seq_slot, 
   return rt;
 }
 
+// A further stack level's shrink: k split like the fused paths' shrink (a
+// function of n and k_in only), its partials summed by the last arrival.
+int stack_shrink_splits(int n, int k_in) {
+  return clampi(512 / ((n + kShrinkRows - 1) / kShrinkRows), 1, std::min(kMaxShrinkSplits, std::max(1, k_in / 256)));
+}
+
+// Workspace of one further stack level: arrival counters (zero between
+// calls), k-split partials, and t [n][R].  Sized for any pool of up to n
+// slots, so the offsets depend on (n, R, k_in) only.
+struct StackLevelLayout {
+  size_t counters, partials, t, total;
+};
+StackLevelLayout stack_level_layout(int32_t dtype, int n, int R, int k_in) {
+  StackLevelLayout w{};
+  size_t off = 0;
+  const int ks = dtype == LORA_BF16 ? stack_shrink_splits(n, k_in) : 1;
+  w.counters = off; off = up256(off + (ks > 1 ? (size_t)((n + kShrinkRows - 1) / kShrinkRows + n) * 4 : 0));
+  w.partials = off; off = up256(off + (ks > 1 ? (size_t)ks * n * R * 4 : 0));
+  w.t = off; off = up256(off + (size_t)n * R * 4);
+  w.total = off;
+  return w;
+}
+
+// The workspace the first level of a stack takes: the fused apply's, for any
+// first-level rank up to max_rank (bf16 ranks are multiples of 16).
+size_t stack_apply_bytes(int32_t dtype, int n, int n_out, int k_in, int max_rank) {
+  if (dtype != LORA_BF16) return 0;
+  size_t most = 0;
+  for (int R = 0; R <= max_rank; R += 16) {
+    const Cfg c = choose_cfg(LORA_OP_APPLY, n, n_out, k_in, 1, R, R ? n : 0);
+    most = std::max(most, ws_layout(c, n, R, k_in).total);
+  }
+  return up256(most);
+}
+
 Routing routing_decode(const int32_t *seq_slot) {
   Routing rt{};
   rt.mode = kModeDecode;
@@ -516,6 +551,12 @@ int lora_build_seq_slot(const int32_t *adapter_slots, uint32_t n, uint32_t padde
 
 size_t lora_workspace_bytes(int32_t op, int32_t dtype, uint32_t n_rows, uint32_t n_out, uint32_t k_in,
                             uint32_t max_rank, uint32_t n_groups) {
+  if (op == LORA_OP_STACK) {
+    if (n_rows == 0) return 0;
+    const size_t levels = n_groups ? n_groups : 1;
+    return stack_apply_bytes(dtype, (int)n_rows, (int)n_out, (int)k_in, (int)max_rank) +
+           (levels - 1) * stack_level_layout(dtype, (int)n_rows, (int)max_rank, (int)k_in).total;
+  }
   if (dtype != LORA_BF16 || n_rows == 0) return 0;
   // pairs are counted generously: any table size the call may use
   const int groups = (int)(n_groups ? n_groups : 1);
@@ -771,6 +812,97 @@ int lora_apply_moe_grouped(int32_t dtype, uint32_t n_experts, uint32_t n_out, ui
   return run_fused(what, LORA_OP_MOE_GROUPED, rt, rd, route != nullptr, n_out, k_in, W_experts,
                    (long long)expert_stride, w_row_stride, x, x_row_stride, n, y, y_row_stride, workspace,
                    workspace_bytes, (int)n_experts, st);
+}
+
+int lora_apply_stack(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W, uint32_t w_row_stride,
+                     const lora_route *routes, const int32_t *const *seq_slots, uint32_t n_levels,
+                     const void *x, uint32_t x_row_stride, uint32_t n, void *y, uint32_t y_row_stride,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+  clear_err();
+  const char *what = "lora_apply_stack";
+  if (int e = check_proj(what, dtype, n_out, k_in, n, x_row_stride, y_row_stride, w_row_stride)) return e;
+  if (n_levels > (uint32_t)kMaxStackLevels)
+    return fail(LORA_ERR_SHAPE, "%s: [n_out %u x k_in %u]: %u levels exceed the limit %d", what, n_out, k_in,
+                n_levels, kMaxStackLevels);
+  if (n_levels && (!routes || !seq_slots))
+    return fail(LORA_ERR_NULL_PTR, "%s: [n_out %u x k_in %u]: routes %p and seq_slots %p must be non-NULL for %u levels",
+                what, n_out, k_in, (const void *)routes, (const void *)seq_slots, n_levels);
+  int r_max = 0;
+  for (uint32_t l = 0; l < n_levels; ++l) {
+    if (int e = check_route(what, &routes[l], dtype, n_out, k_in)) return e;
+    r_max = std::max(r_max, (int)routes[l].max_rank);
+  }
+  if (n == 0) return LORA_OK;
+  if (!W || !x || !y)
+    return fail(LORA_ERR_NULL_PTR, "%s: [n_out %u x k_in %u]: W %p, x %p, y %p must be non-NULL", what, n_out, k_in,
+                W, x, y);
+  for (uint32_t l = 0; l < n_levels; ++l)
+    if (!seq_slots[l])
+      return fail(LORA_ERR_NULL_PTR, "%s: [n_out %u x k_in %u]: seq_slots[%u] is NULL", what, n_out, k_in, l);
+  if (dtype == LORA_BF16 && (!aligned16(W) || !aligned16(x) || !aligned16(y)))
+    return fail(LORA_ERR_UNSUPPORTED, "%s: bf16 needs 16-byte aligned W %p, x %p, y %p", what, W, x, y);
+  // layout: the first level's fused-apply workspace, then t [n][R_l] of every further level
+  const size_t apply_bytes = stack_apply_bytes(dtype, (int)n, (int)n_out, (int)k_in, r_max);
+  size_t need = apply_bytes;
+  for (uint32_t l = 1; l < n_levels; ++l)
+    need += stack_level_layout(dtype, (int)n, (int)routes[l].max_rank, (int)k_in).total;
+  if ((need && !workspace) || workspace_bytes < need)
+    return fail(LORA_ERR_WORKSPACE, "%s: [n_out %u x k_in %u] with %u levels up to max_rank %d, n %u: workspace %p of %zu bytes, %zu needed",
+                what, n_out, k_in, n_levels, r_max, n, workspace, workspace_bytes, need);
+  if (workspace && !aligned16(workspace))
+    return fail(LORA_ERR_UNSUPPORTED, "%s: workspace %p is not 16-byte aligned", what, workspace);
+  if (int e = check_device(what)) return e;
+  hipStream_t st = (hipStream_t)stream;
+  const lora_route *r0 = n_levels ? &routes[0] : nullptr;
+  const RouteDev rd0 = route_dev(r0);
+  const Routing rt0 = routing_decode(r0 ? seq_slots[0] : nullptr);
+  int e;
+  if (dtype == LORA_F32)
+    e = run_f32_timed(what, [&] { return launch_apply_f32(rd0, rt0, r0 != nullptr, (const float *)W, 0,
+                                                          (int)w_row_stride, (const float *)x, (int)x_row_stride,
+                                                          (int)k_in, (int)n_out, (int)n, (float *)y,
+                                                          (int)y_row_stride, st); }, st);
+  else
+    e = run_fused(what, LORA_OP_APPLY, rt0, rd0, r0 != nullptr, n_out, k_in, W, 0, w_row_stride, x, x_row_stride,
+                  n, y, y_row_stride, workspace, apply_bytes, 1, st);
+  if (e || n_levels <= 1) return e;
+  // every further level: its shrink into its own t, then one fold of all of them
+  StackFold f{};
+  f.n_levels = (int)n_levels - 1;
+  char *tp = (char *)workspace + apply_bytes;
+  for (uint32_t l = 1; l < n_levels; ++l) {
+    const RouteDev rd = route_dev(&routes[l]);
+    const Routing rt = routing_decode(seq_slots[l]);
+    const StackLevelLayout lay = stack_level_layout(dtype, (int)n, (int)routes[l].max_rank, (int)k_in);
+    float *t = (float *)(tp + lay.t);
+    if (dtype == LORA_F32) {
+      e = launch_status(launch_shrink_f32(rd, rt, (const float *)x, (int)x_row_stride, (int)k_in, (int)n, t, st),
+                        what);
+    } else {
+      PrepArgs pa{};
+      pa.rd = rd;
+      pa.rt = rt;
+      pa.has_lora = true;
+      pa.x = (const u16 *)x;
+      pa.x_stride = (int)x_row_stride;
+      pa.k_in = (int)k_in;
+      pa.n = (int)n;
+      pa.k_splits = stack_shrink_splits((int)n, (int)k_in);
+      pa.t = pa.k_splits > 1 ? (float *)(tp + lay.partials) : t;
+      pa.t_final = t;
+      pa.counters = (unsigned *)(tp + lay.counters);
+      pa.n_pairs = (int)routes[l].max_loras;
+      pa.do_plan = 0;
+      pa.n_units = (int)((n + kShrinkRows - 1) / kShrinkRows) + (int)std::min<uint32_t>(n, routes[l].max_loras);
+      e = launch_status(launch_prep(pa, st), what);
+    }
+    tp += lay.total;
+    if (e) return e;
+    f.lv[l - 1] = StackLevel{rd.a_table, rd.b_table, rd.scale_table, seq_slots[l], t, rd.max_loras, rd.R};
+  }
+  e = launch_status(launch_expand_fold_stack(f, dtype, y, (int)y_row_stride, (int)n_out, (int)n, st), what);
+  prof_record(3, st);
+  return e;
 }
 
 }  // extern "C"

@@ -69,6 +69,18 @@ class DeviceWorkload:
             self.indices = to_device(wl.indices.astype(np.int32), device)
             self.token_slot = to_device(wl.token_slot.astype(np.int32), device)
             op, groups = B.LORA_OP_MOE_GATHER, wl.n_experts
+        elif wl.kind == "stack":
+            # one route and one per-row slot buffer per level, in order
+            self.levels = []
+            for lv in wl.meta["levels"]:
+                A, Bp = to_device(lv["A"], device), to_device(lv["B"], device)
+                st = B.lora_scale_table(lv["adapters"])
+                self.levels.append({"A": A, "B": Bp, "scale_table_host": st,
+                                    "route": B.DeviceRoute(A, Bp, st),
+                                    "seq_slot": to_device(lv["seq_slot"].astype(np.int32), device)})
+            self.route = self.levels[0]["route"] if self.levels else None
+            self.scale_table_host = [lv["scale_table_host"] for lv in self.levels]
+            op, groups = B.LORA_OP_STACK, max(1, len(self.levels))
         elif wl.kind == "moe_grouped":
             self.route = B.DeviceRoute(self.A, self.Bp, self.scale_table_host, null_slots=ns,
                                        n_experts=wl.n_experts)
@@ -113,6 +125,12 @@ class DeviceWorkload:
                                    self.x_row_stride, self.seg_indptr, self.seg_slot,
                                    len(wl.seg_slot), self.n, y, self.y_row_stride,
                                    self.workspace, self.ws_bytes, stream)
+        elif wl.kind == "stack":
+            lv = self.levels if route else []
+            B.lora_apply_stack(self.dtype, wl.n_out, wl.k_in, self.W, wl.k_in,
+                               [v["route"] for v in lv], self.x, self.x_row_stride,
+                               [v["seq_slot"] for v in lv], self.n, y, self.y_row_stride,
+                               self.workspace, self.ws_bytes, stream)
         elif wl.kind == "moe_grouped":
             B.lora_apply_moe_grouped(self.dtype, wl.n_experts, wl.n_out, wl.k_in, self.W,
                                      wl.n_out * wl.k_in, wl.k_in, r, self.x, self.x_row_stride,

@@ -44,17 +44,18 @@ WORKLOAD_TEXT = {
     "prefill_segmented": "prefill segmented: o_proj W 4096x4096 bf16, 8 segments x 512 tokens, one rank-64 adapter each",
     "moe_down_gather": "MoE down_proj gather: 64 experts W_e 2048x1408 bf16, 512 tokens top-6, rank-16 pair per (adapter, expert), 4 adapters",
     "moe_down_grouped": "MoE down_proj grouped: 64 experts W_e 2048x1408 bf16, 2048 tokens top-6 = 12288 rows sorted by expert (expert_offsets), rank-16 pair per (adapter, expert), 4 adapters",
+    "adapter_stack": "adapter stack: q_proj W 4096x4096 bf16, 3 levels x 8 slots r=16 alpha 32, 64 rows, each level's slot per row uniform in [-1, 8)",
     "spec_verify_kv": "speculative verify, K projection: W_k 1024x4096 bf16, 16 slots r=16 alpha 32, 4 sequences x 9 draft tokens = 36 rows, output into the K columns of interleaved [Q|K|V] rows (6144 elements)",
 }
 ROTATE = {"single_projection_f32": 4, "decode_bgmv": 16, "fused_gate_up": 4,
           "prefill_segmented": 8, "moe_down_gather": 2, "moe_down_grouped": 2,
-          "spec_verify_kv": 64}
+          "spec_verify_kv": 64, "adapter_stack": 16}
 BOUND = {"single_projection_f32": "latency", "decode_bgmv": "hbm", "fused_gate_up": "hbm",
          "prefill_segmented": "mfma", "moe_down_gather": "hbm", "moe_down_grouped": "hbm",
-         "spec_verify_kv": "latency"}
+         "spec_verify_kv": "latency", "adapter_stack": "hbm"}
 # the five workloads of the path, then the variants built beyond them
 OTHERS = ("single_projection_f32", "fused_gate_up", "prefill_segmented", "moe_down_gather",
-          "moe_down_grouped", "spec_verify_kv")
+          "moe_down_grouped", "spec_verify_kv", "adapter_stack")
 
 
 def device_kwargs(wl):
@@ -125,9 +126,39 @@ def resolve_rows(wl, scale_table):
     return np.array(pairs), np.array(groups)
 
 
+def stack_counts(wl, scale_tables):
+    """An adapter stack: W, x and y once; every level's touched slots' A and B once."""
+    esz = 2 if wl.dtype == "bf16" else 4
+    R, k, o, n = wl.max_rank, wl.k_in, wl.n_out, wl.n_rows
+    live = np.zeros(n, bool)
+    a_bytes = b_bytes = 0
+    lora_flops = 0.0
+    first = None
+    for lv, st in zip(wl.meta["levels"], scale_tables):
+        ss = lv["seq_slot"]
+        ok = np.array([0 <= s < len(st) and st[s] != 0 for s in ss])
+        touched = len(set(int(s) for s, g in zip(ss, ok) if g))
+        a_bytes += touched * R * k * esz
+        b_bytes += touched * o * R * esz
+        lora_flops += 2.0 * ok.sum() * R * (k + o)
+        live |= ok
+        if first is None:
+            first = (touched * R * k * esz, int(ok.sum()))
+    w_bytes, x_bytes, y_bytes = o * k * esz, n * k * esz, n * o * esz
+    return {"rows": n, "adapted_rows": int(live.sum()), "touched_pairs": None,
+            "path_bytes": w_bytes + a_bytes + b_bytes + x_bytes + y_bytes,
+            "path_flops": 2.0 * n * o * k + lora_flops,
+            # the first level's decode main launch: W and x once, its touched A, its t
+            "main_bytes": w_bytes + x_bytes + first[0] + first[1] * R * 4,
+            "main_flops": 2.0 * n * o * k + 2.0 * first[1] * R * k,
+            "main_kernel": "decode_main_kernel (base partial tiles + first level's shrink)"}
+
+
 def algorithmic_counts(wl, scale_table):
     """Algorithmic bytes and flops: W once (each expert that has rows), each touched
     nonzero-scale pair's A and B once at max_rank, x once, y once."""
+    if wl.kind == "stack":
+        return stack_counts(wl, scale_table)
     esz = 2 if wl.dtype == "bf16" else 4
     pairs, groups = resolve_rows(wl, scale_table)
     live = pairs[pairs >= -1]
@@ -163,7 +194,7 @@ def algorithmic_counts(wl, scale_table):
 
 def decode_path(wl):
     """The decode kernels take lora_apply batches of at most 64 rows in bf16."""
-    return wl.kind == "decode" and wl.dtype == "bf16" and len(wl.x) <= 64
+    return wl.kind in ("decode", "stack") and wl.dtype == "bf16" and len(wl.x) <= 64
 
 
 # ------------------------------------------------------------------ GPU timing

@@ -75,7 +75,13 @@ enum lora_status {
   LORA_ERR_WORKSPACE = -7    /* workspace missing or smaller than required */
 };
 
-enum lora_op { LORA_OP_APPLY = 0, LORA_OP_SEGMENTED = 1, LORA_OP_MOE_GATHER = 2, LORA_OP_MOE_GROUPED = 3 };
+enum lora_op {
+  LORA_OP_APPLY = 0,
+  LORA_OP_SEGMENTED = 1,
+  LORA_OP_MOE_GATHER = 2,
+  LORA_OP_MOE_GROUPED = 3,
+  LORA_OP_STACK = 4
+};
 
 /*
  * A module's routing tables (atlas lora_delta.rs LoraRoute): load-time-fixed
@@ -163,9 +169,11 @@ int lora_build_seq_slot(const int32_t *adapter_slots, uint32_t n, uint32_t padde
 /*
  * Workspace bytes a fused entry point needs for this problem (0 for
  * LORA_F32, which needs none).  op is a lora_op; n_rows is n (apply,
- * segmented, MoE grouped) or n_tokens * top_k (MoE gather); n_groups is
- * n_experts for the two MoE ops and 1 otherwise; max_rank is 0 for a
- * base-only call.
+ * segmented, MoE grouped, stack) or n_tokens * top_k (MoE gather);
+ * n_groups is n_experts for the two MoE ops, the number of levels for a
+ * stack and 1 otherwise; max_rank is 0 for a base-only call (for a stack,
+ * the largest max_rank over its levels).  A stack needs workspace in
+ * LORA_F32 too (the further levels' t).
  */
 size_t lora_workspace_bytes(int32_t op, int32_t dtype, uint32_t n_rows, uint32_t n_out,
                             uint32_t k_in, uint32_t max_rank, uint32_t n_groups);
@@ -174,13 +182,14 @@ size_t lora_workspace_bytes(int32_t op, int32_t dtype, uint32_t n_rows, uint32_t
  * Measurement aid (atlas lora_delta.rs lora_no_apply doc: apply cost is
  * measured apart from everything else).  With n >= 4 HIP events set, every
  * later fused call on the calling thread (lora_apply, lora_apply_segmented,
- * lora_apply_moe_gather, lora_apply_moe_grouped) records on its stream
- * events[0] before its first kernel, events[1] right before its main kernel
- * (after the route plan and shrink kernel where there is one), events[2]
- * right after the main kernel, and events[3] after its last kernel (the
- * decode epilogue where there is one).  n == 0 switches it off.  events is [host]; the events themselves are
- * the caller's hipEvent_t.  Returns LORA_ERR_NULL_PTR for 0 < n < 4 or a NULL
- * event.
+ * lora_apply_moe_gather, lora_apply_moe_grouped, lora_apply_stack) records
+ * on its stream events[0] before its first kernel, events[1] right before
+ * its main kernel (after the route plan and shrink kernel where there is
+ * one), events[2] right after the main kernel, and events[3] after its last
+ * kernel (the decode epilogue, or a stack's further levels, where there are
+ * any).  n == 0 switches it off.  events is [host]; the events themselves
+ * are the caller's hipEvent_t.  Returns LORA_ERR_NULL_PTR for 0 < n < 4 or
+ * a NULL event.
  */
 int lora_set_profile_events(void *const *events, uint32_t n);
 
@@ -300,6 +309,30 @@ int lora_apply_moe_grouped(int32_t dtype, uint32_t n_experts, uint32_t n_out, ui
                            const int32_t *expert_offsets, const int32_t *seq_slot, uint32_t n,
                            void *y, uint32_t y_row_stride, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/*
+ * Adapter stack (ferrox lora.rs LoraStack and module doc: every adapter
+ * attached to one base matrix is a term of W x + sum_i s_i B_i (A_i x),
+ * applied in order):
+ *   y_i = W x_i + sum over levels l = 0 .. n_levels-1 of
+ *         scale_l[s] B_{l,s} (A_{l,s} x_i),   s = seq_slots[l][i],
+ * each level resolved by the rule of the conventions above (a level whose
+ * slot skips adds nothing to the row).  routes is a [host] array of
+ * n_levels route descriptors, all of shape [n_out x k_in] and dtype;
+ * seq_slots is a [host] array of n_levels [dev] int32 [n] buffers.  At most
+ * 8 levels; n_levels == 0 is the base-only output.  Rounding: the first
+ * level runs through the fused apply (y rounded once); the further levels'
+ * terms are summed in f32 and added to y with one more rounding, so a bf16
+ * y is rounded at most twice whatever the depth.  workspace [dev] of at
+ * least lora_workspace_bytes(LORA_OP_STACK, dtype, n, n_out, k_in, largest
+ * max_rank, n_levels) bytes, zero-filled before its first use with a shape.
+ * Decode-shaped batches (n up to 8192).
+ */
+int lora_apply_stack(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W,
+                     uint32_t w_row_stride, const lora_route *routes,
+                     const int32_t *const *seq_slots, uint32_t n_levels, const void *x,
+                     uint32_t x_row_stride, uint32_t n, void *y, uint32_t y_row_stride,
+                     void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

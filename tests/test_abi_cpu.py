@@ -230,3 +230,41 @@ def test_grouped_workspace_counts_expert_tiles(L):
     a = L.lora_workspace_bytes(B.LORA_OP_MOE_GROUPED, B.LORA_BF16, 3072, 2048, 1408, 16, 64)
     g = L.lora_workspace_bytes(B.LORA_OP_MOE_GATHER, B.LORA_BF16, 3072, 2048, 1408, 16, 64)
     assert a == g > 0
+
+
+def _stack_call(L, routes, n_levels, seq=None, ws_bytes=1 << 30, dtype=B.LORA_BF16, n=8):
+    arr = (B.lora_route * max(1, len(routes)))(*routes) if routes else None
+    sarr = (C.c_void_p * max(1, n_levels))(*([FAKE] * n_levels)) if seq is None else seq
+    return L.lora_apply_stack(dtype, 64, 64, FAKE, 64, arr, sarr if n_levels else None, n_levels,
+                              FAKE, 64, n, FAKE, 64, FAKE, ws_bytes, None)
+
+
+def test_stack_refuses_too_many_levels_and_misfit_levels(L):
+    rs = [_route() for _ in range(9)]
+    assert _stack_call(L, rs, 9) == -1 and "9 levels" in L.lora_last_error().decode()
+    rs = [_route(), _route(n_out=32)]
+    rc = _stack_call(L, rs, 2)
+    assert rc == -1 and "[n_out 32 x k_in 64]" in L.lora_last_error().decode()
+    rs = [_route(), _route(dtype=B.LORA_F32)]
+    assert _stack_call(L, rs, 2) == -4
+
+
+def test_stack_refuses_null_slot_buffers_and_small_workspace(L):
+    rs = [_route(), _route()]
+    sarr = (C.c_void_p * 2)(FAKE, None)
+    assert _stack_call(L, rs, 2, seq=sarr) == -2 and "seq_slots[1]" in L.lora_last_error().decode()
+    assert _stack_call(L, rs, 2, ws_bytes=64) == -7
+    assert "2 levels" in L.lora_last_error().decode()
+
+
+def test_stack_workspace_grows_with_levels(L):
+    one = L.lora_workspace_bytes(B.LORA_OP_STACK, B.LORA_BF16, 64, 4096, 4096, 16, 1)
+    three = L.lora_workspace_bytes(B.LORA_OP_STACK, B.LORA_BF16, 64, 4096, 4096, 16, 3)
+    two = L.lora_workspace_bytes(B.LORA_OP_STACK, B.LORA_BF16, 64, 4096, 4096, 16, 2)
+    assert three - two == two - one >= 64 * 16 * 4  # a further level: at least its t [n][R]
+    assert L.lora_workspace_bytes(B.LORA_OP_STACK, B.LORA_F32, 4, 256, 256, 8, 2) == 256
+    assert one >= L.lora_workspace_bytes(B.LORA_OP_APPLY, B.LORA_BF16, 64, 4096, 4096, 16, 1)
+
+
+def test_stack_empty_batch_launches_nothing(L):
+    assert _stack_call(L, [_route(), _route()], 2, n=0) == 0

@@ -235,8 +235,12 @@ def _pad_case(case, k_to=8, o_to=8, r_to=16):
         c["W"] = pad(case["W"], (len(case["W"]), O, K)).tolist()
     else:
         c["W"] = pad(case["W"], (O, K)).tolist()
-    c["A"] = pad(case["A"], (len(case["A"]), R, K)).tolist()
-    c["B"] = pad(case["B"], (len(case["B"]), O, R)).tolist()
+    if case["kind"] == "stack":
+        c["levels"] = [dict(lv, A=pad(lv["A"], (len(lv["A"]), R, K)).tolist(),
+                            B=pad(lv["B"], (len(lv["B"]), O, R)).tolist()) for lv in case["levels"]]
+    else:
+        c["A"] = pad(case["A"], (len(case["A"]), R, K)).tolist()
+        c["B"] = pad(case["B"], (len(case["B"]), O, R)).tolist()
     c["x"] = pad(case["x"], (len(case["x"]), K)).tolist()
     c["k_in"], c["n_out"], c["max_rank"] = K, O, R
     y = np.zeros((len(case["y"]), O))
@@ -501,6 +505,62 @@ def test_stream_k_partition(orc, seed, k, n_out, n, R):
     rows = _sample_rows(n, extra=(0, n - 1), k=48, seed=seed)
     ref = orc.run(wl, rows=rows, scale_table=dw.scale_table_host)
     check(dw.y_host()[rows], ref, "bf16", wl.name)
+
+
+# ------------------------------------------------------------------ adapter stack
+@pytest.mark.parametrize("seed,dtype,k,n_out,n,levels,R", [
+    (100, "bf16", 136, 96, 37, 2, 16),
+    (101, "bf16", 520, 264, 64, 3, 32),
+    (102, "bf16", 264, 136, 150, 3, 16),   # over 64 rows: the first level on the tiled path
+    (103, "bf16", 1032, 72, 5, 8, 48),     # eight levels
+    (104, "f32", 37, 29, 9, 3, 5),
+])
+def test_stack_small(orc, seed, dtype, k, n_out, n, levels, R):
+    """ferrox LoraStack: W x plus every level's delta in order, each level routed
+    by its own slot buffer (-1 and past-the-pool slots add nothing)."""
+    wl = WL.random_stack(seed, dtype=dtype, k=k, n_out=n_out, n=n, n_levels=levels, n_slots=3,
+                         max_rank=R)
+    dw = DeviceWorkload(wl)
+    dw.run()
+    torch.cuda.synchronize()
+    ref = orc.run(wl, scale_table=dw.scale_table_host)
+    check(dw.y_host(), ref, dtype, wl.name)
+
+
+def test_stack_of_one_and_skipping_levels_are_the_apply():
+    """A one-level stack is that level's apply, and further levels whose rows all
+    skip leave it unchanged -- bit for bit."""
+    wl = WL.random_stack(105, dtype="bf16", k=512, n_out=128, n=40, n_levels=3, n_slots=3,
+                         max_rank=16)
+    dw = DeviceWorkload(wl)
+    lv = dw.levels
+    ws, wsb = dw.workspace, dw.ws_bytes
+    one = torch.empty_like(dw.y)
+    B.lora_apply_stack(B.LORA_BF16, wl.n_out, wl.k_in, dw.W, wl.k_in, [lv[0]["route"]], dw.x,
+                       dw.x_row_stride, [lv[0]["seq_slot"]], dw.n, one, dw.y_row_stride, ws, wsb)
+    ap = torch.empty_like(dw.y)
+    aws = torch.zeros(B.lora_workspace_bytes(0, B.LORA_BF16, dw.n, wl.n_out, wl.k_in, 16),
+                      dtype=torch.uint8, device="cuda")
+    B.lora_apply(B.LORA_BF16, wl.n_out, wl.k_in, dw.W, wl.k_in, lv[0]["route"], dw.x,
+                 dw.x_row_stride, lv[0]["seq_slot"], dw.n, ap, dw.y_row_stride, aws, aws.numel())
+    off = torch.full((dw.n,), -1, dtype=torch.int32, device="cuda")
+    three = torch.empty_like(dw.y)
+    B.lora_apply_stack(B.LORA_BF16, wl.n_out, wl.k_in, dw.W, wl.k_in, [v["route"] for v in lv],
+                       dw.x, dw.x_row_stride, [lv[0]["seq_slot"], off, off], dw.n, three,
+                       dw.y_row_stride, ws, wsb)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(one), bf16_bits(ap))
+    assert np.array_equal(bf16_bits(three), bf16_bits(ap))
+
+
+def test_stack_full_size(orc):
+    """Three levels of eight rank-16 adapters on W [4096 x 4096], 64 rows."""
+    wl = WL.adapter_stack()
+    dw = DeviceWorkload(wl)
+    dw.run()
+    torch.cuda.synchronize()
+    ref = orc.run(wl, scale_table=dw.scale_table_host)
+    check(dw.y_host(), ref, "bf16", wl.name)
 
 
 # ------------------------------------------------------------------ speculative verify, strided folds
