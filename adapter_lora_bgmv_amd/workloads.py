@@ -78,7 +78,7 @@ class Workload:
     B: np.ndarray                      # [P][n_out][max_rank], pad cols zero
     x: np.ndarray                      # [n][k_in]
     adapters: List[AdapterSpec]        # one per pool slot (moe: per adapter)
-    kind: str = "decode"               # decode | segmented | moe | moe_grouped | stack
+    kind: str = "decode"               # decode | segmented | moe | moe_grouped | stack | embed
     # decode routing (metrale slot_math.rs build_seq_slot_host inputs)
     adapter_slots: Optional[np.ndarray] = None   # [n_real] int32, <0 = active
     padded_n: int = 0
@@ -340,12 +340,43 @@ def random_stack(seed: int, dtype: str = BF16, k: int = 96, n_out: int = 80, n: 
                     meta={"levels": levels, "seq_slot": l0["seq_slot"]})
 
 
+def token_embedding(seed: int = 0, n_vocab: int = 32000, n_embd: int = 4096, n: int = 4096,
+                    n_slots: int = 8, rank: int = 16, alpha: float = 32.0,
+                    dtype: str = BF16, max_rank: Optional[int] = None, ranks=None) -> Workload:
+    """Token-embedding gather: E [32000 x 4096] bf16, 8 adapters at rank 16
+    (alpha 32) stored the way an adapter file stores an embedding pair --
+    A_file [n_vocab][rank], B_file [n_embd][rank] (ferrox lora.rs module doc:
+    flipped upstream) -- 4096 tokens uniform over the vocabulary, each row's
+    slot uniform in [-1, 8).  W holds E; A and B hold the file layout (the
+    consumers bring it into the one layout themselves)."""
+    rng = np.random.default_rng(seed)
+    R = rank if max_rank is None else max_rank
+    rk = [rank] * n_slots if ranks is None else list(ranks)
+    E = _store(rng.standard_normal((n_vocab, n_embd)) * 0.02, dtype)
+    a_file = np.zeros((n_slots, n_vocab, R), np.uint16 if dtype == BF16 else np.float32)
+    b_file = np.zeros((n_slots, n_embd, R), a_file.dtype)
+    for p in range(n_slots):  # every A_file, then every B_file, at true rank; pads after
+        a_file[p, :, :rk[p]] = _store(rng.standard_normal((n_vocab, rk[p])) * 0.02, dtype)
+    for p in range(n_slots):
+        b_file[p, :, :rk[p]] = _store(rng.standard_normal((n_embd, rk[p])) * 0.02, dtype)
+    tokens = rng.integers(0, n_vocab, size=n).astype(np.int32)
+    slots = rng.integers(-1, n_slots, size=n).astype(np.int32)
+    return Workload(name=f"token_embedding_{n_vocab}x{n_embd}_s{n_slots}_r{rank}_n{n}",
+                    dtype=dtype, k_in=n_embd, n_out=n_vocab, max_rank=R, W=E, A=a_file,
+                    B=b_file, x=np.zeros((n, 0), E.dtype),
+                    adapters=[AdapterSpec(rk[p], alpha, 1.0) for p in range(n_slots)],
+                    kind="embed", adapter_slots=slots, padded_n=n, active=0,
+                    meta={"token_ids": tokens, "seq_slot": slots, "a_file": a_file,
+                          "b_file": b_file})
+
+
 # workloads of the variants built beyond the five: the grouped MoE layout,
-# the speculative-verify K fold and the adapter stack
+# the speculative-verify K fold, the adapter stack and the token embedding
 NEXT_WORKLOADS = {
     "moe_down_grouped": moe_down_grouped,
     "spec_verify_kv": spec_verify_kv,
     "adapter_stack": adapter_stack,
+    "token_embedding": token_embedding,
 }
 
 

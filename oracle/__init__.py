@@ -106,6 +106,9 @@ class Oracle:
         L.orc_apply_stack.argtypes = [C.c_void_p, C.c_int, C.POINTER(RP), C.POINTER(_i32p),
                                       C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_int,
                                       _i32p, C.c_int, _f64p]
+        L.orc_embed_rows.argtypes = [C.c_void_p, C.c_int, RP, C.c_int, C.c_int, C.c_int, _i32p,
+                                     _i32p, _i32p, C.c_int, _f64p]
+        L.orc_embedding_pair.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p]
         L.orc_mutant.restype = C.c_int
         L.orc_threads.restype = C.c_int
         self.L = L
@@ -286,6 +289,38 @@ class Oracle:
                                x.shape[1], _p(rr, _i32p), len(rr), _p(y, _f64p))
         return y
 
+    def embed_rows(self, E, route: Optional[Route], token_ids, seq_slot, dtype, rows=None,
+                   fill=np.nan) -> np.ndarray:
+        """y[i] = E[token_ids[i]] (+ s * B[token] A); route k_in = n_embd, n_out = n_vocab."""
+        E = np.ascontiguousarray(E)
+        n_vocab, n_embd = E.shape
+        tok = np.ascontiguousarray(token_ids, np.int32)
+        ss = None if seq_slot is None else np.ascontiguousarray(seq_slot, np.int32)
+        rr = np.arange(len(tok), dtype=np.int32) if rows is None else \
+            np.ascontiguousarray(rows, np.int32)
+        y = np.full((len(rr), n_embd), fill, np.float64)
+        rp = C.byref(route.c) if route is not None else None
+        self.L.orc_embed_rows(_p(E), n_embd, rp, dtype, n_vocab, n_embd, _p(tok, _i32p),
+                              _p(ss, _i32p) if ss is not None else None, _p(rr, _i32p), len(rr),
+                              _p(y, _f64p))
+        return y
+
+    def embedding_pair(self, b_file, dtype: int) -> np.ndarray:
+        """A [rank][n_embd] from one pair's B_file [n_embd][rank]."""
+        b = np.ascontiguousarray(b_file)
+        n_embd, rank = b.shape
+        out = np.empty((rank, n_embd), b.dtype)
+        self.L.orc_embedding_pair(_p(b), dtype, n_embd, rank, _p(out))
+        return out
+
+    def embed_route(self, wl, scale_table=None) -> Route:
+        """The route of an embedding workload: its file-layout pool in the one layout."""
+        dt = BF16 if wl.dtype == "bf16" else F32
+        st = self.scale_table(wl.adapters) if scale_table is None else scale_table
+        A = np.stack([self.embedding_pair(b, dt) for b in wl.meta["b_file"]])
+        return Route(A, wl.meta["a_file"], st, dt, wl.k_in, wl.n_out, wl.max_rank,
+                     null_slots=wl.null_slots)
+
     # -------------------------------------------------------------- workload glue
     def seq_slot_for(self, wl) -> np.ndarray:
         return self.build_seq_slot(wl.adapter_slots, wl.padded_n, wl.active)
@@ -293,13 +328,17 @@ class Oracle:
     def run(self, wl, rows=None, route: bool = True, scale_table=None) -> np.ndarray:
         """The whole path for a workload: y (fp64) for all rows or the given ones."""
         dt = BF16 if wl.dtype == "bf16" else F32
-        r = self.route_for(wl, scale_table) if route else None
+        r = self.route_for(wl, scale_table) if route and wl.kind not in ("embed", "stack") else None
         if wl.kind == "decode":
             return self.apply(wl.W, r, wl.x, self.seq_slot_for(wl), dt, rows)
         if wl.kind == "segmented":
             return self.apply_segmented(wl.W, r, wl.x, wl.seg_indptr, wl.seg_slot, dt, rows)
         if wl.kind == "moe":
             return self.apply_moe(wl.W, r, wl.x, wl.indices, wl.top_k, wl.token_slot, dt, rows)
+        if wl.kind == "embed":
+            r = self.embed_route(wl, scale_table) if route else None
+            return self.embed_rows(wl.W, r, wl.meta["token_ids"], wl.meta["seq_slot"] if route
+                                   else None, dt, rows)
         if wl.kind == "stack":
             levels = wl.meta["levels"]
             sts = [self.scale_table(lv["adapters"]) for lv in levels] if scale_table is None \

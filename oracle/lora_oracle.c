@@ -18,7 +18,8 @@
  * Sources (page title, then the item):
  *  - ferrox-core "weight_matrix/lora.rs": module doc (the formula, layouts,
  *    scale, "cost when absent"), LoraDelta::new / effective_scale / project /
- *    accumulate / add_to / add_batch_to, LoraStack (adapters applied in order).
+ *    accumulate / add_to / add_batch_to / add_row_to (the token-embedding
+ *    row gather), LoraStack (adapters applied in order).
  *  - frink-models "lora_attach.rs": module doc (fused-tensor split: one copy
  *    of A per part, B rows split in order).
  *  - atlas "spark_model/layers/ops/lora_delta.rs": LoraRoute, LoraPair
@@ -486,6 +487,66 @@ void orc_apply_stack(const void *W, int w_stride, const orc_route *const *routes
       free(t);
     }
   }
+}
+
+/*
+ * Token-embedding row gather (ferrox lora.rs LoraDelta::add_row_to: the delta
+ * of ONE row of the adapted matrix, s * (B[r] A), which a row gather needs;
+ * module doc "Layouts": the embedding pair is brought into the one layout,
+ * A [rank][n_embd], B [n_vocab][rank]).  The route's k_in is n_embd (A's
+ * columns) and its n_out is n_vocab (B's rows).  Row i takes token
+ * t = token_ids[i]:
+ *   y[i, c] = E[t, c] + s * sum_k B[t, k] A[k, c]     (k ascending)
+ * for rows whose slot resolves; E[t, :] alone otherwise.  Reading: a token
+ * outside [0, n_vocab) leaves the row unwritten.  Only the listed rows.
+ */
+void orc_embed_rows(const void *E, int e_stride, const orc_route *r, int dtype, int n_vocab,
+                    int n_embd, const int32_t *token_ids, const int32_t *seq_slot,
+                    const int32_t *rows, int n_rows, double *y) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int jj = 0; jj < n_rows; ++jj) {
+    int i = rows[jj];
+    int tok = token_ids[i];
+    if (tok < 0 || tok >= n_vocab) continue;
+    double *yo = y + (size_t)jj * n_embd;
+    for (int c = 0; c < n_embd; ++c) yo[c] = widen(E, dtype, (size_t)tok * e_stride + c);
+    int slot = seq_slot ? seq_slot[i] : -1;
+    int idx = resolve(r, slot, 0);
+    if (idx < 0) continue;
+    double s = (double)r->scale[slot];
+    for (int c = 0; c < n_embd; ++c) {
+      double acc = 0.0;
+      for (int k = 0; k < r->max_rank; ++k) {
+#if ORC_MUTANT == 16
+        double b = widen(r->b[idx], dtype, (size_t)k * n_vocab + tok);
+#else
+        double b = widen(r->b[idx], dtype, (size_t)tok * r->max_rank + k);
+#endif
+        acc += b * widen(r->a[idx], dtype, (size_t)k * n_embd + c);
+      }
+      yo[c] = yo[c] + delta_sign() * s * acc;
+    }
+  }
+}
+
+/*
+ * The token-embedding pair brought into the one layout (ferrox lora.rs
+ * module doc "Layouts"; frink lora_attach.rs checked_pair, embedding
+ * branch): the file stores A_file [n_vocab][rank] and B_file [n_embd][rank];
+ * in the one layout B is A_file as it is and A [rank][n_embd] is B_file
+ * transposed, A[k][e] = B_file[e][k].  Copies elements of the storage type.
+ */
+void orc_embedding_pair(const void *b_file, int dtype, int n_embd, int rank, void *a_out) {
+  size_t esz = dtype == ORC_F32 ? 4 : 2;
+  for (int k = 0; k < rank; ++k)
+    for (int e = 0; e < n_embd; ++e) {
+#if ORC_MUTANT == 17
+      size_t src = (size_t)k * n_embd + e;
+#else
+      size_t src = (size_t)e * rank + k;
+#endif
+      memcpy((char *)a_out + ((size_t)k * n_embd + e) * esz, (const char *)b_file + src * esz, esz);
+    }
 }
 
 int orc_mutant(void) { return ORC_MUTANT; }

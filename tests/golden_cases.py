@@ -21,7 +21,7 @@ def _arr(v, dtype):
 
 def expected_y(case):
     """The case's y as fp64, NaN for rows that are not written (null)."""
-    n_out = case["n_out"]
+    n_out = case["k_in"] if case["kind"] == "embed" else case["n_out"]  # a gathered row is n_embd wide
     return np.array([[np.nan] * n_out if r is None else r for r in case["y"]], np.float64)
 
 
@@ -30,6 +30,15 @@ def _adapters(rows):
 
 
 def hand_workload(case, dtype="f32"):
+    if case["kind"] == "embed":
+        a_file, b_file = _arr(case["a_file"], dtype), _arr(case["b_file"], dtype)
+        tok = np.array(case["token_ids"], np.int32)
+        ss = np.array(case["seq_slot"], np.int32)
+        return Workload(name=case["name"], dtype=dtype, k_in=case["k_in"], n_out=case["n_out"],
+                        max_rank=case["max_rank"], W=_arr(case["E"], dtype), A=a_file, B=b_file,
+                        x=np.zeros((len(tok), 0), np.float32), adapters=_adapters(case["adapters"]),
+                        kind="embed", adapter_slots=ss, padded_n=len(tok),
+                        meta={"token_ids": tok, "seq_slot": ss, "a_file": a_file, "b_file": b_file})
     if case["kind"] == "stack":
         levels = [{"A": _arr(lv["A"], dtype), "B": _arr(lv["B"], dtype),
                    "adapters": _adapters(lv["adapters"]),

@@ -84,7 +84,7 @@ def _hand_run(o, wl, case):
         return o.apply_segmented(wl.W, r, wl.x, wl.seg_indptr, wl.seg_slot, dt)
     if wl.kind == "moe_grouped":
         return o.apply_moe_grouped(wl.W, r, wl.x, wl.expert_offsets, wl.row_slot, dt)
-    if wl.kind == "stack":
+    if wl.kind in ("stack", "embed"):
         return o.run(wl)
     return o.apply_moe(wl.W, r, wl.x, wl.indices, wl.top_k, wl.token_slot, dt)
 
@@ -284,6 +284,57 @@ def stack_of_one_is_the_apply(o):
     off = np.full(wl.n_rows, -1, np.int32)
     two = o.apply_stack(wl.W, routes, wl.x, [lv[0]["seq_slot"], off], 1)
     assert np.array_equal(two, one)
+
+
+def _small_embed(seed, dtype, n_vocab=11, n_embd=9, n=8, max_rank=4, n_slots=3):
+    rng = np.random.default_rng(seed)
+    ranks = [int(v) for v in rng.integers(1, max_rank + 1, size=n_slots)]
+    wl = WL.token_embedding(seed, n_vocab=n_vocab, n_embd=n_embd, n=n, n_slots=n_slots,
+                            rank=max_rank, alpha=8.0, dtype=dtype, max_rank=max_rank, ranks=ranks)
+    wl.meta["token_ids"] = wl.meta["token_ids"].copy()
+    wl.meta["token_ids"][[1, n - 1]] = [n_vocab, -1]  # past the vocabulary: not written
+    return wl
+
+
+@pin
+def brute_force_tiny_embed(o):
+    """The row gather through the one-layout pair equals the row of the dense
+    E + s A_file B_file^T formed straight from the file layout (the graph gathers
+    a row of A_file per token and multiplies it by B_file)."""
+    for seed in range(4):
+        dtype = "bf16" if seed % 2 == 0 else "f32"
+        wl = _small_embed(600 + seed, dtype)
+        st = o.scale_table(wl.adapters)
+        y = o.run(wl, scale_table=st)
+        Ed = brute.widen(wl.W, dtype)
+        tok, ss = wl.meta["token_ids"], wl.meta["seq_slot"]
+        for i in range(wl.n_rows):
+            t, s = int(tok[i]), int(ss[i])
+            if not 0 <= t < wl.n_out:
+                assert np.all(np.isnan(y[i])), f"row {i} with token {t} written"
+                continue
+            want = Ed[t].copy()
+            if brute.resolved(s, len(st), set(), st):
+                want = want + float(st[s]) * (brute.widen(wl.meta["a_file"][s], dtype)
+                                              @ brute.widen(wl.meta["b_file"][s], dtype).T)[t]
+            _close(y[i], want, 1e-12, f"embed seed {seed} row {i}")
+
+
+@pin
+def row_delta_agrees_with_the_matvec(o):
+    """ferrox lora.rs test row_delta_agrees_with_the_matvec_on_a_unit_vector: row r
+    of the gathered delta at column c is entry r of the matvec delta on e_c."""
+    wl = _small_embed(610, "f32", n_vocab=6, n_embd=8, n=6)
+    wl.meta["token_ids"] = np.arange(6, dtype=np.int32)
+    wl.meta["seq_slot"] = np.full(6, 1, np.int32)
+    wl.W = np.zeros_like(wl.W)
+    st = o.scale_table(wl.adapters)
+    rows = o.run(wl, scale_table=st)
+    r = o.embed_route(wl, st)
+    eye = np.eye(8, dtype=np.float32)
+    cols = o.apply(np.zeros((6, 8), np.float32), r, eye, np.full(8, 1, np.int32), 0)  # [c][r]
+    assert np.array_equal(rows, cols.T)
+    assert np.any(rows != 0)
 
 
 @pin

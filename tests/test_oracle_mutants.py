@@ -10,6 +10,8 @@ Each mutant is a build of oracle/lora_oracle.c with ORC_MUTANT=k (CPU only):
 13 grouped expert range end treated as inclusive
 14 grouped row slot read relative to its expert's first row
 15 a stack applies its first adapter only
+16 the embedding gather reads B transposed
+17 the embedding pair copied without its transpose
 """
 import shutil
 
@@ -19,7 +21,7 @@ import oracle
 import oracle_pins
 from oracle import build as obuild
 
-MUTANTS = list(range(1, 16))
+MUTANTS = list(range(1, 18))
 
 
 @pytest.fixture(scope="module")
