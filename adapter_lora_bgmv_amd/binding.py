@@ -27,7 +27,8 @@ EXPORTS = ("lora_last_error", "lora_version", "lora_init", "lora_scale", "lora_s
            "lora_build_seq_slot", "lora_workspace_bytes", "lora_shrink", "lora_expand_fold",
            "lora_apply", "lora_apply_segmented", "lora_apply_moe_gather",
            "lora_set_profile_events", "lora_moe_grouped_shrink", "lora_moe_grouped_expand_fold",
-           "lora_apply_moe_grouped", "lora_apply_stack")
+           "lora_apply_moe_grouped", "lora_apply_stack", "lora_embedding_pair",
+           "lora_embed_rows")
 
 
 class LoraError(RuntimeError):
@@ -88,6 +89,9 @@ def lib() -> C.CDLL:
                                          vp, u32, vp, u32, vp, sz, vp]
     L.lora_apply_stack.argtypes = [i32, u32, u32, vp, u32, C.POINTER(lora_route), C.POINTER(vp),
                                    u32, vp, u32, u32, vp, u32, vp, sz, vp]
+    L.lora_embedding_pair.argtypes = [i32, u32, u32, u32, u32, vp, u32, u32, vp, vp]
+    L.lora_embed_rows.argtypes = [i32, u32, u32, vp, u32, C.POINTER(lora_route), vp, vp, u32, vp,
+                                  u32, vp]
     _lib = L
     return L
 
@@ -290,3 +294,22 @@ def lora_apply_stack(dtype: int, n_out: int, k_in: int, W, w_row_stride: int, ro
                                   rarr if L else None, sarr if L else None, L, _ptr(x),
                                   x_row_stride, n, _ptr(y), y_row_stride, _ptr(workspace),
                                   workspace_bytes, _stream(stream)))
+
+
+def lora_embedding_pair(a_file: np.ndarray, b_file: np.ndarray, n_vocab: int, n_embd: int) -> np.ndarray:
+    """A [rank][n_embd] in the one layout from one file-layout embedding pair
+    (A_file [n_vocab][rank], B_file [n_embd][rank]); B is A_file unchanged."""
+    a = np.ascontiguousarray(a_file)
+    b = np.ascontiguousarray(b_file)
+    dt = LORA_BF16 if a.dtype == np.uint16 else LORA_F32
+    out = np.empty((b.shape[1] if b.ndim == 2 else 0, n_embd), a.dtype)
+    _check(lib().lora_embedding_pair(dt, n_vocab, n_embd, a.shape[0], a.shape[1], a.ctypes.data,
+                                     b.shape[0], b.shape[1], b.ctypes.data, out.ctypes.data))
+    return out
+
+
+def lora_embed_rows(dtype: int, n_vocab: int, n_embd: int, E, e_row_stride: int, route,
+                    token_ids, seq_slot, n: int, y, y_row_stride: int, stream=None):
+    _check(lib().lora_embed_rows(dtype, n_vocab, n_embd, _ptr(E), e_row_stride, _route_ref(route),
+                                 _ptr(token_ids), _ptr(seq_slot), n, _ptr(y), y_row_stride,
+                                 _stream(stream)))

@@ -133,6 +133,19 @@ struct StackFold {
   int n_levels;
 };
 
+// The token-embedding row gather (k_embed.hip).
+struct EmbedArgs {
+  const void *E;        // [n_vocab][e_row_stride]
+  int e_row_stride;
+  int n_vocab, n_embd, n;
+  RouteDev rd;          // A [R][n_embd], B [n_vocab][R]
+  int has_lora;
+  const int32_t *token_ids;  // [n]
+  const int32_t *seq_slot;   // [n]
+  void *y;              // [n][y_row_stride]
+  int y_row_stride;
+};
+
 size_t prep_lds_bytes(const PrepArgs &a);
 
 hipError_t launch_shrink_f32(const RouteDev &rd, const Routing &rt, const float *x, int x_stride,
@@ -144,6 +157,7 @@ hipError_t launch_expand_fold(const RouteDev &rd, int dtype, const Routing &rt, 
                               void *y, int y_stride, int n_out, int n, hipStream_t st);
 hipError_t launch_expand_fold_stack(const StackFold &f, int dtype, void *y, int y_stride, int n_out, int n,
                                     hipStream_t st);
+hipError_t launch_embed_rows(const EmbedArgs &a, int dtype, hipStream_t st);
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &a, int to, int tr, hipStream_t st);
 hipError_t launch_decode_main(const DecodeArgs &a, hipStream_t st);

@@ -814,6 +814,78 @@ int lora_apply_moe_grouped(int32_t dtype, uint32_t n_experts, uint32_t n_out, ui
                    workspace_bytes, (int)n_experts, st);
 }
 
+int lora_embedding_pair(int32_t dtype, uint32_t n_vocab, uint32_t n_embd, uint32_t a_rows, uint32_t a_cols,
+                        const void *a_file, uint32_t b_rows, uint32_t b_cols, const void *b_file, void *a_out) {
+  clear_err();
+  const char *what = "lora_embedding_pair";
+  if (int e = check_dtype(dtype, what)) return e;
+  if (n_vocab != a_rows || n_embd != b_rows || a_cols != b_cols || a_cols == 0)
+    return fail(LORA_ERR_SHAPE,
+                "%s: embedding [n_vocab %u x n_embd %u]: A_file is [%u x %u] and B_file [%u x %u]; they must be "
+                "[n_vocab x rank] and [n_embd x rank] with one rank >= 1",
+                what, n_vocab, n_embd, a_rows, a_cols, b_rows, b_cols);
+  if (!a_file || !b_file || !a_out)
+    return fail(LORA_ERR_NULL_PTR, "%s: a_file %p, b_file %p, a_out %p must be non-NULL", what, a_file, b_file,
+                a_out);
+  const size_t esz = dtype == LORA_F32 ? 4 : 2;
+  const uint32_t rank = a_cols;
+  for (uint32_t k = 0; k < rank; ++k)
+    for (uint32_t e = 0; e < n_embd; ++e)
+      std::memcpy((char *)a_out + ((size_t)k * n_embd + e) * esz, (const char *)b_file + ((size_t)e * rank + k) * esz,
+                  esz);
+  return LORA_OK;
+}
+
+int lora_embed_rows(int32_t dtype, uint32_t n_vocab, uint32_t n_embd, const void *E, uint32_t e_row_stride,
+                    const lora_route *route, const int32_t *token_ids, const int32_t *seq_slot, uint32_t n, void *y,
+                    uint32_t y_row_stride, void *stream) {
+  clear_err();
+  const char *what = "lora_embed_rows";
+  // a row gather of a [n_vocab x n_embd] matrix: every output row is n_embd long
+  if (int e = check_dtype(dtype, what)) return e;
+  if (n_vocab == 0 || n_embd == 0)
+    return fail(LORA_ERR_SHAPE, "%s: embedding [n_vocab %u x n_embd %u]: both dimensions must be >= 1", what,
+                n_vocab, n_embd);
+  if (n > kMaxRows)
+    return fail(LORA_ERR_SHAPE, "%s: embedding [n_vocab %u x n_embd %u]: n %u rows exceeds the limit %u", what,
+                n_vocab, n_embd, n, kMaxRows);
+  if (e_row_stride < n_embd || y_row_stride < n_embd)
+    return fail(LORA_ERR_STRIDE, "%s: embedding [n_vocab %u x n_embd %u]: e_row_stride %u and y_row_stride %u "
+                "must be >= n_embd %u", what, n_vocab, n_embd, e_row_stride, y_row_stride, n_embd);
+  if (dtype == LORA_BF16 && (n_embd % 8 || e_row_stride % 8 || y_row_stride % 8))
+    return fail(LORA_ERR_UNSUPPORTED, "%s: embedding [n_vocab %u x n_embd %u]: bf16 needs n_embd, e_row_stride %u "
+                "and y_row_stride %u to be multiples of 8", what, n_vocab, n_embd, e_row_stride, y_row_stride);
+  if (route) {
+    if (int e = check_route(what, route, dtype, n_vocab, n_embd)) return e;
+  }
+  if (n == 0) return LORA_OK;
+  if (!E || !token_ids || !y || (route && !seq_slot))
+    return fail(LORA_ERR_NULL_PTR, "%s: embedding [n_vocab %u x n_embd %u]: E, token_ids, y%s must be non-NULL",
+                what, n_vocab, n_embd, route ? ", seq_slot" : "");
+  if (dtype == LORA_BF16 && (!aligned16(E) || !aligned16(y)))
+    return fail(LORA_ERR_UNSUPPORTED, "%s: bf16 needs 16-byte aligned E %p and y %p", what, E, y);
+  if (int e = check_device(what)) return e;
+  EmbedArgs a{};
+  a.E = E;
+  a.e_row_stride = (int)e_row_stride;
+  a.n_vocab = (int)n_vocab;
+  a.n_embd = (int)n_embd;
+  a.n = (int)n;
+  a.rd = route_dev(route);
+  a.has_lora = route != nullptr;
+  a.token_ids = token_ids;
+  a.seq_slot = seq_slot;
+  a.y = y;
+  a.y_row_stride = (int)y_row_stride;
+  hipStream_t st = (hipStream_t)stream;
+  prof_record(0, st);
+  prof_record(1, st);
+  const int e = launch_status(launch_embed_rows(a, dtype, st), what);
+  prof_record(2, st);
+  prof_record(3, st);
+  return e;
+}
+
 int lora_apply_stack(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W, uint32_t w_row_stride,
                      const lora_route *routes, const int32_t *const *seq_slots, uint32_t n_levels,
                      const void *x, uint32_t x_row_stride, uint32_t n, void *y, uint32_t y_row_stride,

@@ -44,8 +44,18 @@ class DeviceWorkload:
         self.device = device
         self.dtype = B.LORA_BF16 if wl.dtype == "bf16" else B.LORA_F32
         self.W = to_device(wl.W, device)
-        self.A = to_device(wl.A, device)
-        self.Bp = to_device(wl.B, device)
+        if wl.kind == "embed":
+            # the file-layout embedding pairs into the one layout, through the
+            # library's host helper: A = B_file transposed, B = A_file
+            self.A = to_device(np.stack([B.lora_embedding_pair(a, b, wl.n_out, wl.k_in)
+                                         for a, b in zip(wl.meta["a_file"], wl.meta["b_file"])]),
+                               device)
+            self.Bp = to_device(wl.meta["a_file"], device)
+        else:
+            self.A = to_device(wl.A, device)
+            self.Bp = to_device(wl.B, device)
+        # a gathered embedding row is n_embd (k_in) wide; a projection's is n_out
+        self.out_w = wl.k_in if wl.kind == "embed" else wl.n_out
         n, k = wl.x.shape
         xs = k + x_extra_cols
         xh = np.zeros((n, xs), wl.x.dtype)
@@ -54,7 +64,7 @@ class DeviceWorkload:
         self.x_row_stride = xs
         # y's rows may be wider than n_out, with the projection's columns at
         # y_col_offset inside them (an interleaved [Q|K|V] row, say)
-        self.y_row_stride = y_col_offset + wl.n_out + y_extra_cols
+        self.y_row_stride = y_col_offset + self.out_w + y_extra_cols
         self.y_col_offset = y_col_offset
         tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
         self.y_full = torch.empty((n, self.y_row_stride), dtype=tdt, device=device)
@@ -63,7 +73,13 @@ class DeviceWorkload:
                                  else np.asarray(scale_table, np.float32))
         ns = wl.null_slots if null_slots is None else null_slots
         self.route = None
-        if wl.kind == "moe":
+        if wl.kind == "embed":
+            self.route = B.DeviceRoute(self.A, self.Bp, self.scale_table_host, null_slots=ns)
+            self.token_ids = to_device(wl.meta["token_ids"].astype(np.int32), device)
+            self.seq_slot_host = np.asarray(wl.meta["seq_slot"], np.int32)
+            self.seq_slot = to_device(self.seq_slot_host, device)
+            op, groups = None, 1
+        elif wl.kind == "moe":
             self.route = B.DeviceRoute(self.A, self.Bp, self.scale_table_host, null_slots=ns,
                                        n_experts=wl.n_experts)
             self.indices = to_device(wl.indices.astype(np.int32), device)
@@ -103,8 +119,8 @@ class DeviceWorkload:
                 self.seq_slot = to_device(self.seq_slot_host, device)
                 op = B.LORA_OP_APPLY
         self.op = op
-        self.ws_bytes = B.lora_workspace_bytes(op, self.dtype, n, wl.n_out, wl.k_in, wl.max_rank,
-                                               groups)
+        self.ws_bytes = 0 if op is None else B.lora_workspace_bytes(
+            op, self.dtype, n, wl.n_out, wl.k_in, wl.max_rank, groups)
         self.workspace = torch.zeros(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
 
     @property
@@ -125,6 +141,10 @@ class DeviceWorkload:
                                    self.x_row_stride, self.seg_indptr, self.seg_slot,
                                    len(wl.seg_slot), self.n, y, self.y_row_stride,
                                    self.workspace, self.ws_bytes, stream)
+        elif wl.kind == "embed":
+            B.lora_embed_rows(self.dtype, wl.n_out, wl.k_in, self.W, wl.k_in, r, self.token_ids,
+                              self.seq_slot if route else None, self.n, y, self.y_row_stride,
+                              stream)
         elif wl.kind == "stack":
             lv = self.levels if route else []
             B.lora_apply_stack(self.dtype, wl.n_out, wl.k_in, self.W, wl.k_in,
@@ -146,13 +166,13 @@ class DeviceWorkload:
         return y
 
     def y_host(self, y=None) -> np.ndarray:
-        """y as f64 numpy, trimmed to n_out columns."""
+        """y as f64 numpy, trimmed to the output's columns."""
         y = self.y if y is None else y
-        h = bf16_bits(y)[:, :self.wl.n_out]
+        h = bf16_bits(y)[:, :self.out_w]
         if h.dtype == np.uint16:
             return (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         return h.astype(np.float64)
 
     def y_bits(self, y=None) -> np.ndarray:
         y = self.y if y is None else y
-        return bf16_bits(y)[:, :self.wl.n_out].copy()
+        return bf16_bits(y)[:, :self.out_w].copy()

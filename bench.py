@@ -45,17 +45,18 @@ WORKLOAD_TEXT = {
     "moe_down_gather": "MoE down_proj gather: 64 experts W_e 2048x1408 bf16, 512 tokens top-6, rank-16 pair per (adapter, expert), 4 adapters",
     "moe_down_grouped": "MoE down_proj grouped: 64 experts W_e 2048x1408 bf16, 2048 tokens top-6 = 12288 rows sorted by expert (expert_offsets), rank-16 pair per (adapter, expert), 4 adapters",
     "adapter_stack": "adapter stack: q_proj W 4096x4096 bf16, 3 levels x 8 slots r=16 alpha 32, 64 rows, each level's slot per row uniform in [-1, 8)",
+    "token_embedding": "token-embedding gather: E 32000x4096 bf16, 8 adapters r=16 alpha 32 stored flipped (A_file [n_vocab][r], B_file [n_embd][r]), 4096 tokens uniform over the vocabulary, slots uniform in [-1, 8)",
     "spec_verify_kv": "speculative verify, K projection: W_k 1024x4096 bf16, 16 slots r=16 alpha 32, 4 sequences x 9 draft tokens = 36 rows, output into the K columns of interleaved [Q|K|V] rows (6144 elements)",
 }
 ROTATE = {"single_projection_f32": 4, "decode_bgmv": 16, "fused_gate_up": 4,
           "prefill_segmented": 8, "moe_down_gather": 2, "moe_down_grouped": 2,
-          "spec_verify_kv": 64, "adapter_stack": 16}
+          "spec_verify_kv": 64, "adapter_stack": 16, "token_embedding": 2}
 BOUND = {"single_projection_f32": "latency", "decode_bgmv": "hbm", "fused_gate_up": "hbm",
          "prefill_segmented": "mfma", "moe_down_gather": "hbm", "moe_down_grouped": "hbm",
-         "spec_verify_kv": "latency", "adapter_stack": "hbm"}
+         "spec_verify_kv": "latency", "adapter_stack": "hbm", "token_embedding": "hbm"}
 # the five workloads of the path, then the variants built beyond them
 OTHERS = ("single_projection_f32", "fused_gate_up", "prefill_segmented", "moe_down_gather",
-          "moe_down_grouped", "spec_verify_kv", "adapter_stack")
+          "moe_down_grouped", "spec_verify_kv", "adapter_stack", "token_embedding")
 
 
 def device_kwargs(wl):
@@ -154,11 +155,30 @@ def stack_counts(wl, scale_tables):
             "main_kernel": "decode_main_kernel (base partial tiles + first level's shrink)"}
 
 
+def embed_counts(wl, scale_table):
+    """A token-embedding gather: the gathered rows of E, each touched slot's A once,
+    one row of B per adapted row, y once (plus the token ids and slots)."""
+    esz = 2 if wl.dtype == "bf16" else 4
+    R, ne, nv = wl.max_rank, wl.k_in, wl.n_out
+    tok, ss = wl.meta["token_ids"], wl.meta["seq_slot"]
+    live = (tok >= 0) & (tok < nv)
+    ok = live & np.array([0 <= s < len(scale_table) and scale_table[s] != 0 for s in ss])
+    touched = len(set(int(s) for s, g in zip(ss, ok) if g))
+    n = int(live.sum())
+    path = n * ne * esz * 2 + touched * R * ne * esz + int(ok.sum()) * R * esz + len(tok) * 8
+    flops = 2.0 * int(ok.sum()) * R * ne
+    return {"rows": n, "adapted_rows": int(ok.sum()), "touched_pairs": touched,
+            "path_bytes": path, "path_flops": flops, "main_bytes": path, "main_flops": flops,
+            "main_kernel": "embed_rows_kernel (row gather + delta)"}
+
+
 def algorithmic_counts(wl, scale_table):
     """Algorithmic bytes and flops: W once (each expert that has rows), each touched
     nonzero-scale pair's A and B once at max_rank, x once, y once."""
     if wl.kind == "stack":
         return stack_counts(wl, scale_table)
+    if wl.kind == "embed":
+        return embed_counts(wl, scale_table)
     esz = 2 if wl.dtype == "bf16" else 4
     pairs, groups = resolve_rows(wl, scale_table)
     live = pairs[pairs >= -1]

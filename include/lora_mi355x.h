@@ -182,8 +182,8 @@ size_t lora_workspace_bytes(int32_t op, int32_t dtype, uint32_t n_rows, uint32_t
  * Measurement aid (atlas lora_delta.rs lora_no_apply doc: apply cost is
  * measured apart from everything else).  With n >= 4 HIP events set, every
  * later fused call on the calling thread (lora_apply, lora_apply_segmented,
- * lora_apply_moe_gather, lora_apply_moe_grouped, lora_apply_stack) records
- * on its stream events[0] before its first kernel, events[1] right before
+ * lora_apply_moe_gather, lora_apply_moe_grouped, lora_apply_stack,
+ * lora_embed_rows) records on its stream events[0] before its first kernel, events[1] right before
  * its main kernel (after the route plan and shrink kernel where there is
  * one), events[2] right after the main kernel, and events[3] after its last
  * kernel (the decode epilogue, or a stack's further levels, where there are
@@ -309,6 +309,42 @@ int lora_apply_moe_grouped(int32_t dtype, uint32_t n_experts, uint32_t n_out, ui
                            const int32_t *expert_offsets, const int32_t *seq_slot, uint32_t n,
                            void *y, uint32_t y_row_stride, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/*
+ * Token-embedding pair into the one layout (ferrox lora.rs module doc
+ * "Layouts": an embedding adapter is stored flipped, because the graph
+ * gathers a row per token; frink lora_attach.rs checked_pair, embedding
+ * branch).  The file's A_file is [n_vocab][rank] and its B_file
+ * [n_embd][rank]; in the one layout B is A_file unchanged and
+ * a_out [rank][n_embd] = B_file transposed.  All arrays [host], row-major,
+ * dtype elements.  Errors: SHAPE (naming all six dimensions) unless
+ * a_rows == n_vocab, b_rows == n_embd and a_cols == b_cols >= 1; NULL_PTR.
+ * Pure host code: no HIP call.
+ */
+int lora_embedding_pair(int32_t dtype, uint32_t n_vocab, uint32_t n_embd, uint32_t a_rows,
+                        uint32_t a_cols, const void *a_file, uint32_t b_rows, uint32_t b_cols,
+                        const void *b_file, void *a_out);
+
+/*
+ * Token-embedding row gather with the routed delta (ferrox lora.rs
+ * LoraDelta::add_row_to: the delta of one row of the adapted matrix, which
+ * a row gather needs):
+ *   y[i, :] = E[t, :] + scale_table[s] * (B_s[t, :] A_s),
+ *   t = token_ids[i], s = seq_slot[i],
+ * with the route in the one layout: route->k_in = n_embd (A_s is
+ * [max_rank][n_embd]), route->n_out = n_vocab (B_s is [n_vocab][max_rank]).
+ * A row whose slot skips gets E[t, :] bit for bit; a row whose token lies
+ * outside [0, n_vocab) is not written (token values live in device memory
+ * and are not validated on the host).  The rank sum runs in f32 and a bf16
+ * y is rounded once.  E [dev] [n_vocab][e_row_stride]; token_ids, seq_slot
+ * [dev] int32 [n]; y [dev] [n][y_row_stride >= n_embd].  route may be NULL
+ * (a plain gather; seq_slot may then be NULL).  No workspace.  bf16 needs
+ * n_embd and both strides to be multiples of 8 and 16-byte aligned E and y.
+ */
+int lora_embed_rows(int32_t dtype, uint32_t n_vocab, uint32_t n_embd, const void *E,
+                    uint32_t e_row_stride, const lora_route *route, const int32_t *token_ids,
+                    const int32_t *seq_slot, uint32_t n, void *y, uint32_t y_row_stride,
+                    void *stream);
 
 /*
  * Adapter stack (ferrox lora.rs LoraStack and module doc: every adapter

@@ -268,3 +268,36 @@ def test_stack_workspace_grows_with_levels(L):
 
 def test_stack_empty_batch_launches_nothing(L):
     assert _stack_call(L, [_route(), _route()], 2, n=0) == 0
+
+
+def test_embedding_pair_is_the_transpose_of_b_file():
+    rng = np.random.default_rng(3)
+    for dt in (np.float32, np.uint16):
+        a_file = rng.integers(0, 60000, (50, 7)).astype(dt)
+        b_file = rng.integers(0, 60000, (24, 7)).astype(dt)
+        a = B.lora_embedding_pair(a_file, b_file, 50, 24)
+        assert a.shape == (7, 24) and np.array_equal(a, b_file.T)
+
+
+def test_embedding_pair_refuses_misfit_shapes(L):
+    a = np.zeros((50, 7), np.float32)
+    b = np.zeros((24, 6), np.float32)
+    out = np.zeros((7, 24), np.float32)
+    rc = L.lora_embedding_pair(B.LORA_F32, 50, 24, 50, 7, a.ctypes.data, 24, 6, b.ctypes.data,
+                               out.ctypes.data)
+    msg = L.lora_last_error().decode()
+    assert rc == -1 and "[50 x 7]" in msg and "[24 x 6]" in msg and "n_vocab 50" in msg
+
+
+def test_embed_rows_validation(L):
+    r = B.lora_route(FAKE, FAKE, FAKE, 4, 64, 1000, 16, B.LORA_BF16)  # k_in n_embd, n_out n_vocab
+    call = lambda **k: L.lora_embed_rows(k.get("dt", B.LORA_BF16), k.get("nv", 1000),
+                                         k.get("ne", 64), FAKE, k.get("es", 64),
+                                         C.byref(k.get("r", r)), FAKE, FAKE, 8, FAKE,
+                                         k.get("ys", 64), None)
+    assert call(ne=60, es=64, ys=64) == -5 and "multiples of 8" in L.lora_last_error().decode()
+    assert call(ys=32) == -3
+    assert call(nv=999) == -1  # the route's n_out is the vocabulary
+    assert "[n_out 1000 x k_in 64]" in L.lora_last_error().decode()
+    assert L.lora_embed_rows(B.LORA_BF16, 1000, 64, None, 64, C.byref(r), None, None, 0, None, 64,
+                             None) == 0

@@ -233,8 +233,17 @@ def _pad_case(case, k_to=8, o_to=8, r_to=16):
         return out
     if case["kind"] in ("moe", "moe_grouped"):
         c["W"] = pad(case["W"], (len(case["W"]), O, K)).tolist()
-    else:
+    elif case["kind"] != "embed":
         c["W"] = pad(case["W"], (O, K)).tolist()
+    if case["kind"] == "embed":  # the table's rows are n_embd = k_in wide; the vocabulary stays
+        c["E"] = pad(case["E"], (o, K)).tolist()
+        c["a_file"] = pad(case["a_file"], (len(case["a_file"]), o, R)).tolist()
+        c["b_file"] = pad(case["b_file"], (len(case["b_file"]), K, R)).tolist()
+        c["k_in"], c["max_rank"] = K, R
+        y = np.zeros((len(case["y"]), K))
+        y[:, :k] = golden_cases.expected_y(case)
+        y[np.isnan(y[:, 0])] = np.nan
+        return c, y
     if case["kind"] == "stack":
         c["levels"] = [dict(lv, A=pad(lv["A"], (len(lv["A"]), R, K)).tolist(),
                             B=pad(lv["B"], (len(lv["B"]), O, R)).tolist()) for lv in case["levels"]]
@@ -503,6 +512,58 @@ def test_stream_k_partition(orc, seed, k, n_out, n, R):
     torch.cuda.synchronize()
     assert np.array_equal(first, again)  # the arrival order does not change the sums
     rows = _sample_rows(n, extra=(0, n - 1), k=48, seed=seed)
+    ref = orc.run(wl, rows=rows, scale_table=dw.scale_table_host)
+    check(dw.y_host()[rows], ref, "bf16", wl.name)
+
+
+# ------------------------------------------------------------------ token-embedding gather
+def _embed_small(seed, dtype, n_vocab, n_embd, n, R):
+    rng = np.random.default_rng(seed)
+    ranks = [int(v) for v in rng.integers(1, R + 1, size=4)]
+    wl = WL.token_embedding(seed, n_vocab=n_vocab, n_embd=n_embd, n=n, n_slots=4, rank=R,
+                            alpha=8.0, dtype=dtype, max_rank=R, ranks=ranks)
+    tok = wl.meta["token_ids"].copy()
+    tok[[0, n // 2]] = [n_vocab, -5]  # outside the vocabulary: not written
+    wl.meta["token_ids"] = tok
+    return wl
+
+
+@pytest.mark.parametrize("seed,dtype,n_vocab,n_embd,n,R", [
+    (110, "bf16", 1000, 264, 70, 16),
+    (111, "bf16", 517, 4104, 9, 32),     # two column blocks, the second ragged
+    (112, "f32", 300, 37, 21, 5),
+])
+def test_embed_small(orc, seed, dtype, n_vocab, n_embd, n, R):
+    """ferrox LoraDelta::add_row_to: a gathered row is E[token] plus s times that
+    token's row of B A; the pair arrives flipped and is brought into the one
+    layout by lora_embedding_pair.  Rows whose token is outside the vocabulary
+    keep their sentinel; rows whose slot skips are the table row bit for bit."""
+    wl = _embed_small(seed, dtype, n_vocab, n_embd, n, R)
+    dw = DeviceWorkload(wl)
+    dw.y.fill_(float("nan"))
+    dw.run()
+    torch.cuda.synchronize()
+    got = dw.y_host()
+    ref = orc.run(wl, scale_table=dw.scale_table_host)
+    out = np.isnan(ref[:, 0])
+    assert out.sum() == 2 and np.all(np.isnan(got[out]))
+    check(got[~out], ref[~out], dtype, wl.name)
+    base = dw.y_host(dw.run(route=False).clone())
+    torch.cuda.synchronize()
+    st = dw.scale_table_host
+    skip = [i for i, s in enumerate(wl.meta["seq_slot"])
+            if not out[i] and not (0 <= s < len(st) and st[s] != 0)]
+    assert skip and np.array_equal(got[skip], base[skip])
+    check(base[~out], orc.run(wl, route=False)[~out], dtype, "plain gather")
+
+
+def test_embed_full_size(orc):
+    """E [32000 x 4096] bf16, 8 rank-16 adapters, 4096 tokens: sampled rows."""
+    wl = WL.token_embedding()
+    dw = DeviceWorkload(wl)
+    dw.run()
+    torch.cuda.synchronize()
+    rows = _sample_rows(dw.n, extra=(0, dw.n - 1), k=96)
     ref = orc.run(wl, rows=rows, scale_table=dw.scale_table_host)
     check(dw.y_host()[rows], ref, "bf16", wl.name)
 
