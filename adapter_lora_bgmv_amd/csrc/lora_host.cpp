@@ -71,7 +71,8 @@ struct Cfg {
   int partial_slots;  // partial tiles the GEMM's split-K may store
   bool decode;   // the one-launch decode kernel (k_decode.hip)
   int units;     // upper bound of shrink units
-  int t_splits;  // k chunks of the shrink; the consumer sums the partials
+  int t_splits;     // k chunks of the shrink; the consumer sums the partials
+  int t_splits_ws;  // the most k chunks any routing of this shape may take (workspace sizing)
 };
 
 int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
@@ -88,7 +89,13 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
   // Shrink k chunks: enough workgroups to cover the chip for small batches,
   // chunks of at least 256 columns.  A function of (n, k_in) only, so the
   // workspace size does not depend on the routing.
-  c.t_splits = R > 0 ? clampi(512 / ((n + kShrinkRows - 1) / kShrinkRows), 1, std::min(kMaxShrinkSplits, std::max(1, k_in / 256))) : 1;
+  // about 512 shrink workgroups: the units are row blocks of 64 for few
+  // pairs, and about one per pair when many pairs share the rows (MoE);
+  // the workspace holds partials for the most chunks the shape allows
+  const int ks_max = std::min(kMaxShrinkSplits, std::max(1, k_in / 256));
+  const int units_est = std::max((n + kShrinkRows - 1) / kShrinkRows, std::min(n, n_pairs));
+  c.t_splits = R > 0 ? clampi(512 / std::max(1, units_est), 1, ks_max) : 1;
+  c.t_splits_ws = R > 0 ? ks_max : 1;
   if (c.decode) {
     // k ranges of at most kDecodeMaxStages 64-column stages
     const int nst = (k_in + 63) / 64;
@@ -151,7 +158,7 @@ WsLayout ws_layout(const Cfg &c, int n, int R, int k_in) {
   }
   const size_t ntile = (size_t)c.max_mtiles * c.n_ntiles;
   w.counters = off; off = up256(off + (c.partial_slots > 0 ? ntile * 4 : 0));
-  w.shrink_counters = off; off = up256(off + (c.t_splits > 1 ? (size_t)c.units * 4 : 0));
+  w.shrink_counters = off; off = up256(off + (c.t_splits_ws > 1 ? (size_t)c.units * 4 : 0));
   w.pos_row = off; off = up256(off + (size_t)n * 4);
   w.pos_pair = off; off = up256(off + (size_t)n * 4);
   w.routes = off; off = up256(off + (size_t)n * 4);
@@ -159,7 +166,7 @@ WsLayout ws_layout(const Cfg &c, int n, int R, int k_in) {
   w.pair_cnt = off; off = up256(off + (R > 0 ? (size_t)(kMaxKeys + 1) * 4 : 0));  // any table size
   w.tiles = off; off = up256(off + (size_t)c.max_mtiles * 16);
   w.n_tiles = off; off = up256(off + 16);
-  w.t = off; off = up256(off + (c.t_splits > 1 ? (size_t)c.t_splits * n * R * 4 : 0));
+  w.t = off; off = up256(off + (c.t_splits_ws > 1 ? (size_t)c.t_splits_ws * n * R * 4 : 0));
   w.t_final = off; off = up256(off + (size_t)n * R * 4);
   w.tt = off; off = up256(off + (size_t)n * R * 4);  // [n][2R] bf16
   w.partials = off;
