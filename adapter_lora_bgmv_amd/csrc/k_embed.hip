@@ -4,72 +4,86 @@
 // of the adapted matrix (ferrox lora.rs LoraDelta::add_row_to), with the
 // embedding pair in the one layout (A [rank][n_embd], B [n_vocab][rank]).
 // Memory-bound: a gathered row of E, one row of B per row, and each touched
-// slot's A, which every row on that slot shares.  A workgroup takes 8 rows
-// and 2048 columns, 8 columns per thread; the rows' B entries go to LDS and
-// each distinct slot among the 8 rows reads its A rows once for all of its
-// rows.  The rank sum runs k ascending in f32; y is rounded once.
+// slot's A, which every row on that slot shares.  A workgroup takes 16 rows
+// and 1024 columns, 4 columns per thread, its rows ordered by pair; the
+// rows' B entries go to LDS and each pair's A rows are read once for all
+// of its rows.  The rank sum runs k ascending in f32; y is rounded once.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace lora {
 
-constexpr int kEmbedRows = 8;
-constexpr int kEmbedCols = 256 * 8;
+constexpr int kEmbedRows = 16;
+constexpr int kEmbedVec = 4;                  // columns per thread
+constexpr int kEmbedCols = 256 * kEmbedVec;   // columns per workgroup
 
-template <typename T> struct Vec8;
-template <> struct Vec8<u16> {
-  static __device__ __forceinline__ void load(const u16 *p, int valid, float *v) {
-    if (valid >= 8) {
-      const uint4 w = *(const uint4 *)p;
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[2 * j] = bf2f((u16)(u[j] & 0xffffu));
-        v[2 * j + 1] = bf2f((u16)(u[j] >> 16));
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = j < valid ? bf2f(p[j]) : 0.f;
-    }
+template <typename T> struct Vec4;
+// bf16 rows are multiples of 8 long, 16-byte aligned: whole 8-byte pieces
+template <> struct Vec4<u16> {
+  static __device__ __forceinline__ void load(const u16 *p, float *v, int) {
+    const uint2 w = *(const uint2 *)p;
+    v[0] = bf2f((u16)(w.x & 0xffffu));
+    v[1] = bf2f((u16)(w.x >> 16));
+    v[2] = bf2f((u16)(w.y & 0xffffu));
+    v[3] = bf2f((u16)(w.y >> 16));
   }
-  static __device__ __forceinline__ void copy(const u16 *src, u16 *dst, int valid) {
-    if (valid >= 8) {
-      *(uint4 *)dst = *(const uint4 *)src;
-    } else {
-      for (int j = 0; j < valid; ++j) dst[j] = src[j];
-    }
+  static __device__ __forceinline__ void copy(const u16 *src, u16 *dst, int) { *(uint2 *)dst = *(const uint2 *)src; }
+  static __device__ __forceinline__ void store(u16 *p, const float *v, int) {
+    uint2 w;
+    w.x = pack2(f2bf(v[0]), f2bf(v[1]));
+    w.y = pack2(f2bf(v[2]), f2bf(v[3]));
+    *(uint2 *)p = w;
   }
-  static __device__ __forceinline__ void store(u16 *p, int valid, const float *v) {
-    if (valid >= 8) {
-      uint4 w;
-      w.x = pack2(f2bf(v[0]), f2bf(v[1]));
-      w.y = pack2(f2bf(v[2]), f2bf(v[3]));
-      w.z = pack2(f2bf(v[4]), f2bf(v[5]));
-      w.w = pack2(f2bf(v[6]), f2bf(v[7]));
-      *(uint4 *)p = w;
-    } else {
-      for (int j = 0; j < valid; ++j) p[j] = f2bf(v[j]);
-    }
+  static __device__ __forceinline__ float one(const u16 *p) { return bf2f(*p); }
+  // the same 4 columns held packed (so that many k rows stay in flight)
+  typedef uint2 raw;
+  static __device__ __forceinline__ raw load_raw(const u16 *p, int) { return *(const uint2 *)p; }
+  static __device__ __forceinline__ void store_raw(u16 *p, raw w, int) { *(uint2 *)p = w; }
+  static __device__ __forceinline__ float at(raw w, int j) {
+    const uint32_t u = j < 2 ? w.x : w.y;
+    return bf2f((u16)((j & 1) ? (u >> 16) : (u & 0xffffu)));
   }
 };
-template <> struct Vec8<float> {
-  static __device__ __forceinline__ void load(const float *p, int valid, float *v) {
+// f32 rows take any length and stride: element by element, up to `valid`
+template <> struct Vec4<float> {
+  static __device__ __forceinline__ void load(const float *p, float *v, int valid) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = j < valid ? p[j] : 0.f;
+    for (int j = 0; j < 4; ++j) v[j] = j < valid ? p[j] : 0.f;
   }
   static __device__ __forceinline__ void copy(const float *src, float *dst, int valid) {
-    for (int j = 0; j < valid && j < 8; ++j) dst[j] = src[j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < valid) dst[j] = src[j];
   }
-  static __device__ __forceinline__ void store(float *p, int valid, const float *v) {
-    for (int j = 0; j < valid && j < 8; ++j) p[j] = v[j];
+  static __device__ __forceinline__ void store(float *p, const float *v, int valid) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < valid) p[j] = v[j];
+  }
+  static __device__ __forceinline__ float one(const float *p) { return *p; }
+  typedef float4 raw;
+  static __device__ __forceinline__ raw load_raw(const float *p, int valid) {
+    float v[4];
+    load(p, v, valid);
+    return make_float4(v[0], v[1], v[2], v[3]);
+  }
+  static __device__ __forceinline__ float at(raw w, int j) { return j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w; }
+  static __device__ __forceinline__ void store_raw(float *p, raw w, int valid) {
+    const float v[4] = {w.x, w.y, w.z, w.w};
+    store(p, v, valid);
   }
 };
 
+// A workgroup takes 16 rows and 1024 columns (4 per thread).  It orders its
+// rows by pair in LDS, so that walking them in that order each pair's A rows
+// are loaded once (when the pair changes) and shared by all of its rows; the
+// accumulators are indexed by that order, which keeps them in registers.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_rows_kernel(EmbedArgs a) {
-  __shared__ float bsh[kEmbedRows][256];  // B[t, 0:R] of each row, f32
-  __shared__ int s_tok[kEmbedRows], s_q[kEmbedRows];
-  __shared__ float s_sig[kEmbedRows];
+  __shared__ float bsh[kEmbedRows][256];  // B[t, 0:R] of the row at each sorted place, f32
+  __shared__ int r_tok[kEmbedRows], r_q[kEmbedRows];
+  __shared__ float r_sig[kEmbedRows];
+  __shared__ int p_row[kEmbedRows], p_q[kEmbedRows];  // by sorted place: row (in the block), pair
   const int tid = threadIdx.x;
   const int i0 = blockIdx.y * kEmbedRows;
   const RouteDev &rd = a.rd;
@@ -87,67 +101,84 @@ __global__ __launch_bounds__(256) void embed_rows_kernel(EmbedArgs a) {
         if (q >= 0) sig = rd.scale_table[s];
       }
     }
-    s_tok[tid] = tok;
-    s_q[tid] = q;
-    s_sig[tid] = sig;
+    r_tok[tid] = tok;
+    r_q[tid] = q;
+    r_sig[tid] = sig;
+  }
+  __syncthreads();
+  if (tid < kEmbedRows) {  // place of this row in (pair, row) order
+    const int q = r_q[tid];
+    int place = 0;
+    for (int r = 0; r < kEmbedRows; ++r) {
+      const int qr = r_q[r];
+      place += qr < q || (qr == q && r < tid);
+    }
+    p_row[place] = tid;
+    p_q[place] = q;
   }
   __syncthreads();
   for (int e = tid; e < kEmbedRows * rd.R; e += 256) {
-    const int r = e / rd.R, k = e % rd.R;
-    if (s_q[r] >= 0) {
-      const T *Bq = (const T *)rd.b_table[s_q[r]];
-      float v[8];
-      Vec8<T>::load(Bq + (size_t)s_tok[r] * rd.R + k, 1, v);
-      bsh[r][k] = v[0];
-    }
+    const int p = e / rd.R, k = e % rd.R;
+    const int q = p_q[p];
+    if (q >= 0) bsh[p][k] = Vec4<T>::one((const T *)rd.b_table[q] + (size_t)r_tok[p_row[p]] * rd.R + k);
   }
   __syncthreads();
-  const int c0 = blockIdx.x * kEmbedCols + tid * 8;
+  const int c0 = blockIdx.x * kEmbedCols + tid * kEmbedVec;
   if (c0 >= a.n_embd) return;
-  const int valid = min(8, a.n_embd - c0);
-  float acc[kEmbedRows][8];
+  const int valid = min(kEmbedVec, a.n_embd - c0);
+  // every row's piece of E goes out first and is in flight during the rank
+  // sums (the stores to y below could otherwise hold each load back)
+  typename Vec4<T>::raw e_raw[kEmbedRows];
 #pragma unroll
-  for (int r = 0; r < kEmbedRows; ++r)
+  for (int p = 0; p < kEmbedRows; ++p) {
+    const int tok = r_tok[p_row[p]];
+    if (tok >= 0) e_raw[p] = Vec4<T>::load_raw((const T *)a.E + (size_t)tok * a.e_row_stride + c0, valid);
+  }
+  float acc[kEmbedRows][kEmbedVec];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[r][j] = 0.f;
-  // every distinct slot of the workgroup's rows once: its A rows against
-  // the B entries of all of its rows
+  for (int p = 0; p < kEmbedRows; ++p)
 #pragma unroll
-  for (int lead = 0; lead < kEmbedRows; ++lead) {
-    const int q = s_q[lead];
-    if (q < 0) continue;
-    bool first = true;
+    for (int j = 0; j < kEmbedVec; ++j) acc[p][j] = 0.f;
+  // k in blocks of 8: at each change of pair along the sorted rows, the
+  // block's 8 rows of that pair's A go out together, then every row of the
+  // pair takes them
+  constexpr int KC = 8;
+  for (int kc = 0; kc < rd.R; kc += KC) {
+    typename Vec4<T>::raw ar[KC];
+    int cur = kSkip;
 #pragma unroll
-    for (int r = 0; r < lead; ++r) first = first && s_q[r] != q;
-    if (!first) continue;
-    const T *Aq = (const T *)rd.a_table[q] + c0;
-    for (int k = 0; k < rd.R; ++k) {
-      float av[8];
-      Vec8<T>::load(Aq + (size_t)k * a.n_embd, valid, av);
+    for (int p = 0; p < kEmbedRows; ++p) {
+      const int q = p_q[p];
+      if (q < 0) continue;
+      if (q != cur) {
+        cur = q;
+        const T *Aq = (const T *)rd.a_table[q] + (size_t)kc * a.n_embd + c0;
 #pragma unroll
-      for (int r = 0; r < kEmbedRows; ++r) {
-        if (s_q[r] != q) continue;
-        const float b = bsh[r][k];
+        for (int kk = 0; kk < KC; ++kk)
+          if (kc + kk < rd.R) ar[kk] = Vec4<T>::load_raw(Aq + (size_t)kk * a.n_embd, valid);
+      }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[r][j] += b * av[j];
+      for (int kk = 0; kk < KC; ++kk) {
+        if (kc + kk >= rd.R) break;
+        const float b = bsh[p][kc + kk];
+#pragma unroll
+        for (int j = 0; j < kEmbedVec; ++j) acc[p][j] += b * Vec4<T>::at(ar[kk], j);
       }
     }
   }
 #pragma unroll
-  for (int r = 0; r < kEmbedRows; ++r) {
-    const int tok = s_tok[r];
-    if (tok < 0) continue;
-    const T *er = (const T *)a.E + (size_t)tok * a.e_row_stride + c0;
+  for (int p = 0; p < kEmbedRows; ++p) {
+    const int r = p_row[p];
+    if (r_tok[r] < 0) continue;
     T *yr = (T *)a.y + (size_t)(i0 + r) * a.y_row_stride + c0;
-    if (s_q[r] < 0) {  // base only: the table row, bit for bit
-      Vec8<T>::copy(er, yr, valid);
+    if (p_q[p] < 0) {  // base only: the table row, bit for bit
+      Vec4<T>::store_raw(yr, e_raw[p], valid);
       continue;
     }
-    float ev[8];
-    Vec8<T>::load(er, valid, ev);
+    float ev[kEmbedVec];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ev[j] = ev[j] + s_sig[r] * acc[r][j];
-    Vec8<T>::store(yr, valid, ev);
+    for (int j = 0; j < kEmbedVec; ++j) ev[j] = Vec4<T>::at(e_raw[p], j) + r_sig[r] * acc[p][j];
+    Vec4<T>::store(yr, ev, valid);
   }
 }
 

@@ -43,7 +43,12 @@ __global__ __launch_bounds__(256) void shrink_f32_kernel(RouteDev rd, Routing rt
 }
 
 // ---------------------------------------------------------------- f32 apply
-// y_i = W x_i + s B_s (A_s x_i), one row per blockIdx.y, 64 outputs per block.
+// y_i = W x_i + s B_s (A_s x_i), one row per blockIdx.y, 16 outputs per
+// block: each wave takes 4 outputs at once, their loads in flight together
+// (a wave per output one after another would be a chain of memory round
+// trips).  Each dot runs lanes-strided over k, then a fixed butterfly.
+constexpr int kF32Out = 16;
+
 __global__ __launch_bounds__(256) void apply_f32_kernel(RouteDev rd, Routing rt, bool has_lora,
                                                         const float *W, long long w_group_stride,
                                                         int w_stride, const float *x,
@@ -67,19 +72,32 @@ __global__ __launch_bounds__(256) void apply_f32_kernel(RouteDev rd, Routing rt,
     }
   }
   __syncthreads();
-  const int o_end = min(n_out, (int)(blockIdx.x + 1) * 64);
-  for (int o = blockIdx.x * 64 + wave; o < o_end; o += 4) {
-    float acc = 0.f;
-    for (int c = lane; c < k_in; c += 64) acc += Wg[(size_t)o * w_stride + c] * xi[c];
-    acc = wave_sum(acc);
-    if (q >= 0) {
-      const float *B = (const float *)rd.b_table[q];
-      float d = 0.f;
-      for (int k = lane; k < rd.R; k += 64) d += B[(size_t)o * rd.R + k] * tsh[k];
-      d = wave_sum(d);
-      acc = acc + rd.scale_table[sidx] * d;
+  const int o0 = blockIdx.x * kF32Out + wave * 4;
+  int oo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) oo[j] = min(o0 + j, n_out - 1);  // a clamped duplicate is not written
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int c = lane; c < k_in; c += 64) {
+    const float xv = xi[c];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] += Wg[(size_t)oo[j] * w_stride + c] * xv;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = wave_sum(acc[j]);
+  if (q >= 0) {
+    const float *B = (const float *)rd.b_table[q];
+    float d[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int k = lane; k < rd.R; k += 64) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d[j] += B[(size_t)oo[j] * rd.R + k] * tsh[k];
     }
-    if (lane == 0) y[(size_t)i * y_stride + o] = acc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = acc[j] + rd.scale_table[sidx] * wave_sum(d[j]);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (o0 + j < n_out) y[(size_t)i * y_stride + o0 + j] = acc[j];
   }
 }
 
@@ -156,7 +174,7 @@ hipError_t launch_shrink_f32(const RouteDev &rd, const Routing &rt, const float 
 hipError_t launch_apply_f32(const RouteDev &rd, const Routing &rt, bool has_lora, const float *W,
                             long long w_group_stride, int w_stride, const float *x, int x_stride,
                             int k_in, int n_out, int n, float *y, int y_stride, hipStream_t st) {
-  dim3 grid((n_out + 63) / 64, n);
+  dim3 grid((n_out + kF32Out - 1) / kF32Out, n);
   hipLaunchKernelGGL(apply_f32_kernel, grid, dim3(256), 0, st, rd, rt, has_lora, W,
                      w_group_stride, w_stride, x, x_stride, k_in, n_out, y, y_stride);
   return hipGetLastError();
