@@ -102,7 +102,9 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
     c.to = kDecodeTileOut; c.tr = kDecodeMaxRows;
     c.splits = (nst + kDecodeMaxStages - 1) / kDecodeMaxStages;
   } else if (moe) {
-    c.to = 256; c.tr = 64; c.splits = 1;
+    // one row tile per expert where the batch allows: an expert's W slab is
+    // read once per row tile (128-row tiles from ~96 rows per expert on)
+    c.to = 256; c.tr = n / std::max(1, groups) >= 96 ? 128 : 64; c.splits = 1;
   } else if (n <= 64) {
     c.to = 64; c.tr = 64; c.splits = clampi(k_in / 1024, 1, 8);
   } else if (n <= 128) {

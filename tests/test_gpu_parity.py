@@ -103,13 +103,15 @@ def test_segmented_small(orc, seed, dtype, lens):
     check(dw.y_host(), ref, dtype, wl.name)
 
 
-@pytest.mark.parametrize("seed,dtype,E,top_k,n_tok", [
-    (20, "bf16", 5, 2, 37),
-    (21, "bf16", 9, 3, 70),
-    (22, "f32", 4, 2, 11),
+@pytest.mark.parametrize("seed,dtype,E,top_k,n_tok,R", [
+    (20, "bf16", 5, 2, 37, 16),
+    (21, "bf16", 9, 3, 70, 16),
+    (22, "f32", 4, 2, 11, 16),
+    (23, "bf16", 4, 2, 230, 16),   # ~115 rows per expert: 128-row tiles
+    (24, "bf16", 3, 2, 200, 48),   # the same with a rank that does not divide 64
 ])
-def test_moe_small(orc, seed, dtype, E, top_k, n_tok):
-    wl = WL.random_small(seed, dtype=dtype, k=72, n_out=48, n=n_tok, n_slots=3, max_rank=16,
+def test_moe_small(orc, seed, dtype, E, top_k, n_tok, R):
+    wl = WL.random_small(seed, dtype=dtype, k=72, n_out=48, n=n_tok, n_slots=3, max_rank=R,
                          kind="moe", n_experts=E, top_k=top_k)
     dw = DeviceWorkload(wl)
     dw.run()
@@ -140,6 +142,7 @@ def test_moe_invalid_expert_rows_not_written(orc):
     (25, "bf16", 9, 300, 136, 264),    # 300 rows over 9 experts: several row tiles per expert
     (26, "bf16", 64, 200, 64, 32),     # more experts than rows per expert, many empty
     (27, "f32", 4, 23, 37, 29),
+    (28, "bf16", 3, 700, 200, 264),    # ~233 rows per expert: 128-row tiles, a ragged last one
 ])
 def test_moe_grouped_small(orc, seed, dtype, E, n, k, n_out):
     """atlas moe_lora_grouped_down: rows sorted by expert, ranges from
