@@ -160,6 +160,21 @@ def test_moe_grouped_small(orc, seed, dtype, E, n, k, n_out):
     check(got[~outside], ref[~outside], dtype, wl.name)
 
 
+def test_moe_grouped_base_only(orc):
+    """route == NULL: every row inside an expert range is W_e x, rows outside keep their sentinel."""
+    wl = WL.random_small(29, dtype="bf16", k=136, n_out=96, n=150, n_slots=3, max_rank=16,
+                         kind="moe_grouped", n_experts=4)
+    dw = DeviceWorkload(wl)
+    dw.y.fill_(float("nan"))
+    dw.run(route=False)
+    torch.cuda.synchronize()
+    ref = orc.run(wl, route=False)
+    got = dw.y_host()
+    outside = np.isnan(ref[:, 0])
+    assert np.all(np.isnan(got[outside]))
+    check(got[~outside], ref[~outside], "bf16", "grouped base only")
+
+
 def test_moe_grouped_equals_gather_sorted():
     """The grouped call on the gather's routing slots sorted by expert gives the
     gather's rows, bit for bit: each output is reduced row-locally in the same order."""
@@ -615,6 +630,21 @@ def test_stack_of_one_and_skipping_levels_are_the_apply():
     torch.cuda.synchronize()
     assert np.array_equal(bf16_bits(one), bf16_bits(ap))
     assert np.array_equal(bf16_bits(three), bf16_bits(ap))
+
+
+def test_stack_of_no_levels_is_the_base(orc):
+    """n_levels == 0: the base-only output, equal to a base-only apply bit for bit."""
+    wl = WL.random_stack(106, dtype="bf16", k=256, n_out=64, n=20, n_levels=2, n_slots=3, max_rank=16)
+    dw = DeviceWorkload(wl)
+    y0 = bf16_bits(dw.run(route=False).clone())
+    ap = torch.empty_like(dw.y)
+    aws = torch.zeros(B.lora_workspace_bytes(0, B.LORA_BF16, dw.n, wl.n_out, wl.k_in, 16),
+                      dtype=torch.uint8, device="cuda")
+    B.lora_apply(B.LORA_BF16, wl.n_out, wl.k_in, dw.W, wl.k_in, None, dw.x, dw.x_row_stride, None,
+                 dw.n, ap, dw.y_row_stride, aws, aws.numel())
+    torch.cuda.synchronize()
+    assert np.array_equal(y0, bf16_bits(ap))
+    check(dw.y_host(), orc.run(wl, route=False), "bf16", "stack of no levels")
 
 
 def test_stack_full_size(orc):
