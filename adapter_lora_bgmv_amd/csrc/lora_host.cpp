@@ -73,6 +73,8 @@ struct Cfg {
   int units;     // upper bound of shrink units
   int t_splits;     // k chunks of the shrink; the consumer sums the partials
   int t_splits_ws;  // the most k chunks any routing of this shape may take (workspace sizing)
+  long long zero_tiles;  // tile counters any tiling of this shape may use (64 x 64 tiles are the smallest)
+  int zero_units;        // shrink arrival counters any routing of this shape may use
 };
 
 int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
@@ -127,6 +129,8 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
     c.k_per_split = ((kslabs + c.splits - 1) / c.splits) * 64;
   }
   c.max_mtiles = (n + c.tr - 1) / c.tr + (moe ? groups : 0);
+  c.zero_tiles = (long long)((n + 63) / 64 + (moe ? groups : 0)) * ((n_out + 63) / 64);
+  c.zero_units = (n + kShrinkRows - 1) / kShrinkRows + n;
   c.n_ntiles = (n_out + c.to - 1) / c.to;
   const long long tiles = (long long)c.max_mtiles * c.n_ntiles;
   c.partial_slots = c.splits > 1 ? (int)(tiles * c.splits) : 0;
@@ -158,14 +162,16 @@ WsLayout ws_layout(const Cfg &c, int n, int R, int k_in) {
     w.total = off;
     return w;
   }
-  const size_t ntile = (size_t)c.max_mtiles * c.n_ntiles;
-  w.counters = off; off = up256(off + (c.partial_slots > 0 ? ntile * 4 : 0));
-  w.shrink_counters = off; off = up256(off + (c.t_splits_ws > 1 ? (size_t)c.units * 4 : 0));
+  // The words that must be zero between calls come first, sized for any
+  // tiling and routing of the shape, so that every call of the shape --
+  // routed with any rank, or base only -- finds them at the same offsets.
+  w.counters = off; off = up256(off + (size_t)c.zero_tiles * 4);
+  w.shrink_counters = off; off = up256(off + (size_t)c.zero_units * 4);
+  w.pair_cnt = off; off = up256(off + (size_t)(kMaxKeys + 1) * 4);  // any table size, then the arrival count
   w.pos_row = off; off = up256(off + (size_t)n * 4);
   w.pos_pair = off; off = up256(off + (size_t)n * 4);
   w.routes = off; off = up256(off + (size_t)n * 4);
-  w.ranks = off; off = up256(off + (R > 0 ? (size_t)n * 4 : 0));
-  w.pair_cnt = off; off = up256(off + (R > 0 ? (size_t)(kMaxKeys + 1) * 4 : 0));  // any table size
+  w.ranks = off; off = up256(off + (size_t)n * 4);
   w.tiles = off; off = up256(off + (size_t)c.max_mtiles * 16);
   w.n_tiles = off; off = up256(off + 16);
   w.t = off; off = up256(off + (c.t_splits_ws > 1 ? (size_t)c.t_splits_ws * n * R * 4 : 0));
@@ -457,7 +463,7 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
   if (R > 0) {
     pa.ranks = (int *)(ws + L.ranks);
     pa.pair_cnt = (unsigned *)(ws + L.pair_cnt);
-    pa.prep_done = pa.pair_cnt + n_pairs;
+    pa.prep_done = pa.pair_cnt + kMaxKeys;  // past every pair count, at a fixed word
   }
   pa.counters = (unsigned *)(ws + L.shrink_counters);
   pa.k_splits = c.t_splits;
@@ -567,11 +573,14 @@ size_t lora_workspace_bytes(int32_t op, int32_t dtype, uint32_t n_rows, uint32_t
            (levels - 1) * stack_level_layout(dtype, (int)n_rows, (int)max_rank, (int)k_in).total;
   }
   if (dtype != LORA_BF16 || n_rows == 0) return 0;
-  // pairs are counted generously: any table size the call may use
+  // pairs are counted generously (any table size the call may use), and the
+  // base-only call of the same shape fits too
   const int groups = (int)(n_groups ? n_groups : 1);
   const Cfg c = choose_cfg(op, (int)n_rows, (int)n_out, (int)k_in, groups, (int)max_rank,
                            max_rank ? (int)n_rows : 0);
-  return ws_layout(c, (int)n_rows, (int)max_rank, (int)k_in).total;
+  const Cfg c0 = choose_cfg(op, (int)n_rows, (int)n_out, (int)k_in, groups, 0, 0);
+  return std::max(ws_layout(c, (int)n_rows, (int)max_rank, (int)k_in).total,
+                  ws_layout(c0, (int)n_rows, 0, (int)k_in).total);
 }
 
 int lora_shrink(const lora_route *route, const void *x, uint32_t x_row_stride, const int32_t *seq_slot,

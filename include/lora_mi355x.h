@@ -46,11 +46,14 @@
  *  - Workspace: the fused entry points take a caller-owned device
  *    workspace of at least lora_workspace_bytes(...) bytes.  It must be
  *    zero-filled before its first use with a given problem shape (op,
- *    n_rows, n_out, k_in, max_rank, n_groups); every call that returns
- *    LORA_OK leaves the words that must start at zero at zero again, so the
- *    same shape can be called again with no memset (none is recorded into a
- *    captured graph).  Reusing one workspace for another shape needs a new
- *    zero fill.  Concurrent calls sharing one workspace race.
+ *    n_rows, n_out, k_in, n_groups); every call that returns LORA_OK leaves
+ *    the words that must start at zero at zero again, so the same shape can
+ *    be called again with no memset (none is recorded into a captured
+ *    graph).  Those words sit at offsets that depend on the shape alone, so
+ *    routed calls of any rank up to the sized max_rank and base-only calls
+ *    of one shape may share a workspace (lora_workspace_bytes covers the
+ *    base-only call too).  Reusing one workspace for another shape needs a
+ *    new zero fill.  Concurrent calls sharing one workspace race.
  */
 #ifndef LORA_MI355X_H
 #define LORA_MI355X_H

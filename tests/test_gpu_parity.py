@@ -369,6 +369,34 @@ def test_skip_rows_are_base_bit_for_bit(orc):
     check(dw.y_host(y_routed), ref, "bf16", "routed with skips")
 
 
+@pytest.mark.parametrize("kind,seed,k,n_out,n,R", [
+    ("decode", 35, 520, 264, 150, 48),     # routed on 128 x 128 tiles, base only stream-K
+    ("decode", 36, 2048, 296, 100, 16),    # classic split-k both ways
+    ("segmented", 37, 512, 256, 0, 32),    # stream-K both ways
+    ("moe", 38, 200, 96, 60, 16),
+])
+def test_routed_and_base_only_share_a_workspace(kind, seed, k, n_out, n, R):
+    """Routed and base-only calls of one shape alternate on one workspace; each
+    gives the bits of the same call on a fresh workspace."""
+    if kind == "segmented":
+        wl = WL.random_small(seed, dtype="bf16", k=k, n_out=n_out, n_slots=3, max_rank=R,
+                             kind="segmented", seg_lens=[100, 70, 0, 130])
+    elif kind == "moe":
+        wl = WL.random_small(seed, dtype="bf16", k=k, n_out=n_out, n=n, n_slots=3, max_rank=R,
+                             kind="moe", n_experts=4, top_k=2)
+    else:
+        wl = WL.random_small(seed, dtype="bf16", k=k, n_out=n_out, n=n, n_slots=4, max_rank=R)
+    fresh = {}
+    for route in (True, False):
+        d = DeviceWorkload(wl)
+        fresh[route] = bf16_bits(d.run(route=route).clone())
+    dw = DeviceWorkload(wl)
+    for route in (True, False, True, False, True):
+        got = bf16_bits(dw.run(route=route).clone())
+        torch.cuda.synchronize()
+        assert np.array_equal(got, fresh[route]), route
+
+
 def test_all_rows_skipped_equals_base():
     wl = WL.random_small(31, dtype="bf16", k=256, n_out=128, n=17, n_slots=3, max_rank=16)
     dw = DeviceWorkload(wl)
