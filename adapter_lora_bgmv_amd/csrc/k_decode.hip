@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_main_kernel(DecodeArgs p) {
 // four features): t is then needed for 16 rows only.  Every load that does
 // not depend on another goes out first: the row's route, the S partials, t.
 constexpr int kEpiOut = 64;  // output features per epilogue workgroup
-__global__ __launch_bounds__(256) void decode_epilogue_kernel(DecodeArgs p) {
+__global__ __launch_bounds__(256) void decode_epilogue_kernel(DecodeArgs p, StackFold f) {
   __shared__ __attribute__((aligned(16))) float st[16 * 256];  // t of the 16 rows, 16 x R
   const int tid = threadIdx.x;
   const int R = p.R;
@@ -401,6 +401,51 @@ __global__ __launch_bounds__(256) void decode_epilogue_kernel(DecodeArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) v[j] = v[j] + sig * d[j];
   }
+  // an adapter stack's further levels, in level order, from their final t:
+  // every level's slot, then its table entries, go out together, so the
+  // levels cost one chain of round trips, not one each
+  if (f.n_levels > 0) {
+    int sl[kMaxStackLevels];
+#pragma unroll
+    for (int l = 0; l < kMaxStackLevels; ++l) sl[l] = l < f.n_levels ? f.lv[l].seq_slot[i] : -1;
+    const u16 *bl[kMaxStackLevels];
+    float sc[kMaxStackLevels];
+#pragma unroll
+    for (int l = 0; l < kMaxStackLevels; ++l) {
+      const StackLevel &L = f.lv[l];
+      const bool in = l < f.n_levels && sl[l] >= 0 && sl[l] < L.max_loras;
+      const void *ta = in ? L.a_table[sl[l]] : nullptr;
+      const void *tb = in ? L.b_table[sl[l]] : nullptr;
+      const float s = in ? L.scale_table[sl[l]] : 0.f;
+      const bool ok = ta != nullptr && tb != nullptr && s != 0.0f;
+      bl[l] = ok ? (const u16 *)tb + (size_t)o * L.R : nullptr;
+      sc[l] = s;
+    }
+#pragma unroll
+    for (int l = 0; l < kMaxStackLevels; ++l) {
+      if (bl[l] == nullptr) continue;
+      const StackLevel &L = f.lv[l];
+      const float *tl = L.t + (size_t)i * L.R;
+      float d[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int r0 = 0; r0 < L.R; r0 += 8) {  // ranks in order, 8 at a time
+        float tr[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) tr[c] = tl[r0 + c];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4 bb = ldg16(bl[l] + (size_t)j * L.R + r0);
+          const uint32_t w[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            d[j] += bf2f((u16)(w[c] & 0xffffu)) * tr[2 * c];
+            d[j] += bf2f((u16)(w[c] >> 16)) * tr[2 * c + 1];
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = v[j] + sc[l] * d[j];
+    }
+  }
   *(uint2 *)(p.y + (size_t)i * p.y_row_stride + o) =
       make_uint2(pack2(f2bf(v[0]), f2bf(v[1])), pack2(f2bf(v[2]), f2bf(v[3])));
 }
@@ -420,9 +465,12 @@ hipError_t launch_decode_main(const DecodeArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode_epilogue(const DecodeArgs &a, hipStream_t st) {
-  if (a.S == 1 && !a.has_lora) return hipSuccess;  // the main launch stored y
-  hipLaunchKernelGGL(decode_epilogue_kernel, dim3(a.n_tiles * (kTO / kEpiOut) * 4), dim3(256), 0, st, a);
+hipError_t launch_decode_epilogue(const DecodeArgs &a, const StackFold *stack, hipStream_t st) {
+  StackFold f{};
+  if (stack) f = *stack;
+  if (a.S == 1 && !a.has_lora)  // the main launch stored y; a stack always has a routed first level
+    return f.n_levels ? hipErrorInvalidValue : hipSuccess;
+  hipLaunchKernelGGL(decode_epilogue_kernel, dim3(a.n_tiles * (kTO / kEpiOut) * 4), dim3(256), 0, st, a, f);
   return hipGetLastError();
 }
 

@@ -586,6 +586,13 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   if (threadIdx.x == 0) *a.prep_done = 0u;
 }
 
+// A stack's further levels: every level's shrink units in one grid.
+__global__ __launch_bounds__(256) void shrink_levels_kernel(ShrinkLevels s) {
+  extern __shared__ int lds[];
+  const int l = (int)blockIdx.x / s.blocks_per_level;
+  shrink_unit(s.lv[l], (int)blockIdx.x - l * s.blocks_per_level, lds);
+}
+
 size_t prep_lds_bytes(const PrepArgs &a) {
   const int ml = a.has_lora ? a.rd.max_loras : 0;
   const int NG = a.rt.n_experts;
@@ -595,6 +602,17 @@ size_t prep_lds_bytes(const PrepArgs &a) {
                                (a.ranks ? 0 : (size_t)a.n * 4)
                          : 0;
   return plan > shr ? plan : shr;
+}
+
+hipError_t launch_shrink_levels(const ShrinkLevels &s, hipStream_t st) {
+  if (s.n_levels <= 0 || s.blocks_per_level <= 0) return hipSuccess;
+  size_t lds = 0;
+  for (int l = 0; l < s.n_levels; ++l) {
+    const size_t b = prep_lds_bytes(s.lv[l]);
+    lds = b > lds ? b : lds;
+  }
+  hipLaunchKernelGGL(shrink_levels_kernel, dim3(s.n_levels * s.blocks_per_level), dim3(256), lds, st, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st) {

@@ -146,7 +146,17 @@ struct EmbedArgs {
   int y_row_stride;
 };
 
+// The shrinks of a stack's further levels in one launch: level l takes
+// blocks [l * blocks_per_level, (l + 1) * blocks_per_level), each level's
+// arguments those of a standalone shrink (no plan, no routes).
+struct ShrinkLevels {
+  PrepArgs lv[kMaxStackLevels];
+  int n_levels;
+  int blocks_per_level;
+};
+
 size_t prep_lds_bytes(const PrepArgs &a);
+hipError_t launch_shrink_levels(const ShrinkLevels &s, hipStream_t st);
 
 hipError_t launch_shrink_f32(const RouteDev &rd, const Routing &rt, const float *x, int x_stride,
                              int k_in, int n, float *t, hipStream_t st);
@@ -161,6 +171,7 @@ hipError_t launch_embed_rows(const EmbedArgs &a, int dtype, hipStream_t st);
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &a, int to, int tr, hipStream_t st);
 hipError_t launch_decode_main(const DecodeArgs &a, hipStream_t st);
-hipError_t launch_decode_epilogue(const DecodeArgs &a, hipStream_t st);
+// `stack` (or null): an adapter stack's further levels, folded into the same rounding.
+hipError_t launch_decode_epilogue(const DecodeArgs &a, const StackFold *stack, hipStream_t st);
 
 }  // namespace lora

@@ -397,11 +397,13 @@ int run_f32_timed(const char *what, F launch, hipStream_t st) {
 }
 
 // The bf16 fused path shared by the three apply entry points.
+// `stack` (or null): an adapter stack's further levels, whose t are ready;
+// on the decode path the epilogue folds them in and *stack_folded is set.
 int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, bool has_lora,
               uint32_t n_out, uint32_t k_in, const void *W, long long w_group_stride,
               uint32_t w_row_stride, const void *x, uint32_t x_row_stride, uint32_t n, void *y,
               uint32_t y_row_stride, void *workspace, size_t workspace_bytes, int groups,
-              hipStream_t st) {
+              hipStream_t st, const StackFold *stack = nullptr, bool *stack_folded = nullptr) {
   const int R = has_lora ? rd.R : 0;
   const int n_pairs = has_lora ? rd.max_loras * rd.n_experts : 0;
   const Cfg c = choose_cfg(op, (int)n, (int)n_out, (int)k_in, groups, R, n_pairs);
@@ -441,7 +443,9 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
     prof_record(1, st);
     if (int e = launch_status(launch_decode_main(da, st), what)) return e;
     prof_record(2, st);
-    const int e = launch_status(launch_decode_epilogue(da, st), what);
+    const bool fold = stack && stack->n_levels > 0 && has_lora;
+    const int e = launch_status(launch_decode_epilogue(da, fold ? stack : nullptr, st), what);
+    if (stack_folded) *stack_folded = fold && e == LORA_OK;
     prof_record(3, st);
     return e;
   }
@@ -946,19 +950,15 @@ int lora_apply_stack(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W
   const lora_route *r0 = n_levels ? &routes[0] : nullptr;
   const RouteDev rd0 = route_dev(r0);
   const Routing rt0 = routing_decode(r0 ? seq_slots[0] : nullptr);
-  int e;
-  if (dtype == LORA_F32)
-    e = run_f32_timed(what, [&] { return launch_apply_f32(rd0, rt0, r0 != nullptr, (const float *)W, 0,
-                                                          (int)w_row_stride, (const float *)x, (int)x_row_stride,
-                                                          (int)k_in, (int)n_out, (int)n, (float *)y,
-                                                          (int)y_row_stride, st); }, st);
-  else
-    e = run_fused(what, LORA_OP_APPLY, rt0, rd0, r0 != nullptr, n_out, k_in, W, 0, w_row_stride, x, x_row_stride,
-                  n, y, y_row_stride, workspace, apply_bytes, 1, st);
-  if (e || n_levels <= 1) return e;
-  // every further level: its shrink into its own t, then one fold of all of them
+  int e = LORA_OK;
+  // every further level's shrink into its own t first (the bf16 shrinks of
+  // all levels in one launch); then the first level's apply, whose decode
+  // epilogue folds the further levels in the same rounding, or else one
+  // fold of all of them after it
   StackFold f{};
-  f.n_levels = (int)n_levels - 1;
+  f.n_levels = n_levels > 1 ? (int)n_levels - 1 : 0;
+  ShrinkLevels sl{};
+  sl.n_levels = dtype == LORA_BF16 ? f.n_levels : 0;
   char *tp = (char *)workspace + apply_bytes;
   for (uint32_t l = 1; l < n_levels; ++l) {
     const RouteDev rd = route_dev(&routes[l]);
@@ -968,8 +968,9 @@ int lora_apply_stack(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W
     if (dtype == LORA_F32) {
       e = launch_status(launch_shrink_f32(rd, rt, (const float *)x, (int)x_row_stride, (int)k_in, (int)n, t, st),
                         what);
+      if (e) return e;
     } else {
-      PrepArgs pa{};
+      PrepArgs &pa = sl.lv[l - 1];
       pa.rd = rd;
       pa.rt = rt;
       pa.has_lora = true;
@@ -984,12 +985,25 @@ int lora_apply_stack(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W
       pa.n_pairs = (int)routes[l].max_loras;
       pa.do_plan = 0;
       pa.n_units = (int)((n + kShrinkRows - 1) / kShrinkRows) + (int)std::min<uint32_t>(n, routes[l].max_loras);
-      e = launch_status(launch_prep(pa, st), what);
+      sl.blocks_per_level = std::max(sl.blocks_per_level, pa.n_units * pa.k_splits);
     }
     tp += lay.total;
-    if (e) return e;
     f.lv[l - 1] = StackLevel{rd.a_table, rd.b_table, rd.scale_table, seq_slots[l], t, rd.max_loras, rd.R};
   }
+  if (sl.n_levels) {
+    e = launch_status(launch_shrink_levels(sl, st), what);
+    if (e) return e;
+  }
+  bool folded = false;
+  if (dtype == LORA_F32)
+    e = run_f32_timed(what, [&] { return launch_apply_f32(rd0, rt0, r0 != nullptr, (const float *)W, 0,
+                                                          (int)w_row_stride, (const float *)x, (int)x_row_stride,
+                                                          (int)k_in, (int)n_out, (int)n, (float *)y,
+                                                          (int)y_row_stride, st); }, st);
+  else
+    e = run_fused(what, LORA_OP_APPLY, rt0, rd0, r0 != nullptr, n_out, k_in, W, 0, w_row_stride, x, x_row_stride,
+                  n, y, y_row_stride, workspace, apply_bytes, 1, st, &f, &folded);
+  if (e || f.n_levels == 0 || folded) return e;
   e = launch_status(launch_expand_fold_stack(f, dtype, y, (int)y_row_stride, (int)n_out, (int)n, st), what);
   prof_record(3, st);
   return e;
