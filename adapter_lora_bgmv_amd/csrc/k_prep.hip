@@ -54,6 +54,23 @@ __device__ int block_exscan(int *a, int L, int *wsum) {
 __device__ __forceinline__ int pk_key(int w) { return (w >> 13) - 1; }
 __device__ __forceinline__ int pk_pair(int w) { return (w & 0x1fff) - 2; }
 
+// A wave's 64 rows split into runs of equal keys (a new run where the key
+// changes from the lane before).  `bnds` has a bit per run start; a run
+// start's run ends at the next start (or lane 64); a lane's run starts at
+// the highest start at or below it.  Sorted rows (a prefill segment, an
+// expert's range) make a few long runs, unsorted rows runs of one.
+__device__ __forceinline__ uint64_t run_starts(int k, int lane) {
+  const int kp = __shfl_up(k, 1, 64);
+  return __ballot(lane == 0 || kp != k);
+}
+__device__ __forceinline__ int run_end(uint64_t bnds, int lane) {
+  const uint64_t later = bnds & ~((2ull << lane) - 1ull);
+  return later ? __ffsll((unsigned long long)later) - 1 : 64;
+}
+__device__ __forceinline__ int run_start(uint64_t bnds, int lane) {
+  return 63 - __clzll((unsigned long long)(bnds & ((2ull << lane) - 1ull)));
+}
+
 // Row ranges of a call: the segments of a segmented call, the experts of a
 // grouped MoE call ([n+1] non-decreasing starts); tables up to kSegLds
 // entries are copied to LDS for the routing.
@@ -140,53 +157,34 @@ __device__ __forceinline__ void route_all(const PrepArgs &a, int *pk, const int 
       if (r < a.n) pk[r] = ((key + 1) << 13) | (q + 2);
       qv[j] = r < a.n ? q : kSkip;
     }
-    if (ranked) {  // each row's rank within its pair: the pairs many of a wave's rows share take one atomic each
+    if (ranked) {  // each row's rank within its pair: every run of equal pairs in a wave's rows takes its ranks with one atomic
       const int lane = threadIdx.x & 63;
-      const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        int q = qv[j], rank = -1;
-        uint64_t todo = __ballot(q >= 0);
-        for (int round = 0; round < 2 && todo; ++round) {
-          const int leader = __ffsll((unsigned long long)todo) - 1;
-          const int v = __builtin_amdgcn_readlane(q, leader);
-          const uint64_t m = __ballot(q == v);
-          int base = 0;
-          if (lane == leader) base = (int)atomicAdd(&a.pair_cnt[v], (unsigned)__popcll(m));
-          base = __builtin_amdgcn_readlane(base, leader);
-          if (q == v) {
-            rank = base + (int)__popcll(m & below);
-            q = kSkip;
-          }
-          todo &= ~m;
-        }
-        if (q >= 0) rank = (int)atomicAdd(&a.pair_cnt[q], 1u);
+        const int q = qv[j];
+        const uint64_t bnds = run_starts(q, lane);
+        int base = 0;
+        if (q >= 0 && ((bnds >> lane) & 1ull))
+          base = (int)atomicAdd(&a.pair_cnt[q], (unsigned)(run_end(bnds, lane) - lane));
+        const int rs = run_start(bnds, lane);
+        base = __shfl(base, rs, 64);
         const int r = r0 + 256 * j;
-        if (r < a.n) a.ranks[r] = rank;
+        if (r < a.n) a.ranks[r] = q >= 0 ? base + (lane - rs) : -1;
       }
     }
   }
 }
 
-// Adds to cnt[k] the number of rows with k = f(pk[r]) >= 0.  Each wave takes
-// 64 rows at a time: the values held by many of its lanes are counted with
-// one atomic each (a prefill segment, an expert), the rest lane by lane.
+// Adds to cnt[k] the number of rows with k = f(pk[r]) >= 0: each wave takes
+// 64 rows at a time and adds every run of equal keys with one atomic.
 template <typename F>
 __device__ __forceinline__ void count_rows(const int *pk, int n, int *cnt, F f) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int r0 = wave * 64; r0 < n; r0 += 256) {
     const int r = r0 + lane;
-    int k = r < n ? f(pk[r]) : -1;
-    uint64_t todo = __ballot(k >= 0);
-    for (int round = 0; round < 2 && todo; ++round) {
-      const int leader = __ffsll((unsigned long long)todo) - 1;
-      const int v = __builtin_amdgcn_readlane(k, leader);
-      const uint64_t m = __ballot(k == v);
-      if (lane == leader) atomicAdd(&cnt[v], (int)__popcll(m));
-      if (k == v) k = -1;
-      todo &= ~m;
-    }
-    if (k >= 0) atomicAdd(&cnt[k], 1);
+    const int k = r < n ? f(pk[r]) : -1;
+    const uint64_t bnds = run_starts(k, lane);
+    if (k >= 0 && ((bnds >> lane) & 1ull)) atomicAdd(&cnt[k], run_end(bnds, lane) - lane);
   }
 }
 
@@ -279,30 +277,19 @@ __device__ __forceinline__ void plan_block(const PrepArgs &a, int *lds) {
   const int total = block_exscan(cnt, NK, wsum);
   if (tid == 0) cnt[NK] = total;
   __syncthreads();
-  // scatter: the keys many of a wave's 64 rows share take one atomic each
-  // (those rows keep their order), the rest one atomic per row
+  // scatter: each run of equal keys in a wave's 64 rows takes its places
+  // with one atomic (its rows keep their order)
   for (int r0 = wave * 64; r0 < a.n; r0 += 256) {
     const int r = r0 + lane;
     const int w = r < a.n ? pk[r] : 0;
-    int k = r < a.n ? pk_key(w) : -1;
-    uint64_t todo = __ballot(k >= 0);
-    for (int round = 0; round < 2 && todo; ++round) {
-      const int leader = __ffsll((unsigned long long)todo) - 1;
-      const int v = __builtin_amdgcn_readlane(k, leader);
-      const uint64_t m = __ballot(k == v);
-      int base = 0;
-      if (lane == leader) base = atomicAdd(&fill[v], (int)__popcll(m));
-      base = __builtin_amdgcn_readlane(base, leader);
-      if (k == v) {
-        const int pos = cnt[v] + base + (int)__popcll(m & below);
-        a.plan.pos_row[pos] = r;
-        a.plan.pos_pair[pos] = pk_pair(w);
-        k = -1;
-      }
-      todo &= ~m;
-    }
+    const int k = r < a.n ? pk_key(w) : -1;
+    const uint64_t bnds = run_starts(k, lane);
+    int base = 0;
+    if (k >= 0 && ((bnds >> lane) & 1ull)) base = atomicAdd(&fill[k], run_end(bnds, lane) - lane);
+    const int rs = run_start(bnds, lane);
+    base = __shfl(base, rs, 64);
     if (k >= 0) {
-      const int pos = cnt[k] + atomicAdd(&fill[k], 1);
+      const int pos = cnt[k] + base + (lane - rs);
       a.plan.pos_row[pos] = r;
       a.plan.pos_pair[pos] = pk_pair(w);
     }
@@ -384,19 +371,44 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
   const int first = info[1] * kShrinkRows;
 
   if (ranked) {  // the rows of pstar whose rank falls in [first, first + kShrinkRows)
-    for (int r0 = tid; r0 < a.n; r0 += 256 * 8) {
-      int rk[8], w[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool in = r0 + 256 * j < a.n;
-        rk[j] = in ? a.ranks[r0 + 256 * j] : -1;
-        w[j] = in ? a.routes[r0 + 256 * j] : 0;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (rk[j] >= first && rk[j] < first + kShrinkRows && pk_pair(w[j]) == pstar) rows[rk[j] - first] = r0 + 256 * j;
+    const int total = (int)a.pair_cnt[pstar];
+    const int want = min(kShrinkRows, total - first);
+    // a grouped call's pair lives in its expert's row range: scan only that,
+    // and the whole batch if the range does not hold every wanted row
+    // (offsets that are not non-decreasing)
+    int r_lo = 0, r_hi = a.n;
+    if (a.rt.mode == kModeMoeGrouped) {
+      const int e = pstar % a.rd.n_experts;
+      r_lo = min(max(a.rt.expert_offsets[e], 0), a.n);
+      r_hi = min(max(a.rt.expert_offsets[e + 1], r_lo), a.n);
     }
-    if (tid == 0) info[3] = (int)a.pair_cnt[pstar];
+    for (int pass = 0; pass < 2; ++pass) {
+      __syncthreads();  // every thread has read the last pass's count
+      if (tid == 0) info[2] = 0;
+      __syncthreads();
+      int found = 0;
+      for (int r0 = r_lo + tid; r0 < r_hi; r0 += 256 * 8) {
+        int rk[8], w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const bool in = r0 + 256 * j < r_hi;
+          rk[j] = in ? a.ranks[r0 + 256 * j] : -1;
+          w[j] = in ? a.routes[r0 + 256 * j] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (rk[j] >= first && rk[j] < first + kShrinkRows && pk_pair(w[j]) == pstar) {
+            rows[rk[j] - first] = r0 + 256 * j;
+            ++found;
+          }
+      }
+      if (found) atomicAdd(&info[2], found);
+      __syncthreads();
+      if (info[2] == want || (r_lo == 0 && r_hi == a.n)) break;  // uniform
+      r_lo = 0;
+      r_hi = a.n;
+    }
+    if (tid == 0) info[3] = total;
   } else {
     // rows of pstar in row order, ranks [first, first + kShrinkRows): thread t
     // counts them in its 16-row span, an exclusive scan gives its first rank

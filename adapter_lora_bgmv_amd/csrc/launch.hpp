@@ -109,7 +109,7 @@ constexpr int kDecodeMaxSplit = 16;
 
 // Rows per shrink unit; its 64-column stages in LDS at a time (16 KB each).
 constexpr int kShrinkRows = 64;
-constexpr int kShrinkStages = 4;
+constexpr int kShrinkStages = 3;
 // Largest k split of the shrink units.
 constexpr int kMaxShrinkSplits = 8;
 // Largest key space the one-workgroup plan handles (LDS histogram).
