@@ -29,6 +29,8 @@
 // no delta arithmetic, so they equal the base-only launch bit for bit.
 // Every output element is reduced in an order that does not depend on the
 // batch's other rows or on n_out.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -51,22 +53,21 @@ struct Rows {  // the batch's routes, resolved once per workgroup
   int list[64];       // rows grouped by slot (row order within one)
   int start[65];      // list offsets per touched slot
   int slot[64];       // touched slots in order of first appearance
+  const u16 *aq[64];  // the touched slot's A (its table entry, read once)
   int T;              // touched slots
+  uint32_t ea[2][64], eb[2][64];  // the row's A and B table entries (low, high words; LDS-DMA)
+  float esc[64];                  // the row's scale table entry (LDS-DMA)
 };
 
 // Routes, in three steps that keep their latency off the stream of W:
 // at the start wave 0 sends seq_slot to LDS by LDS-DMA (issued before the
-// first stage, so it has landed once that stage has); after the first stage
-// it loads the three table entries each slot needs into registers; after
-// the last stage, when they have long arrived, it resolves the rows by the
-// rule of resolve_slot and groups them by slot, slots numbered in order of
-// first appearance: one round of ballots per touched slot.
-constexpr int kEnt = 3;  // loads of fetch_entries
-struct RowEntries {
-  const void *a, *b;
-  float sc;
-  bool in;
-};
+// first stage, so it has landed once that stage has); once it has, the
+// table entries each row needs go to LDS the same way (five 4-byte DMAs:
+// the halves of A's and B's pointers, the scale), counted by the explicit
+// waits like the stages; later, when they have landed, wave 0 resolves the
+// rows by the rule of resolve_slot and groups them by slot, slots numbered
+// in order of first appearance: one round of ballots per touched slot.
+constexpr int kEnt = 5;  // DMAs of fetch_entries
 
 __device__ __forceinline__ void fetch_slots(const DecodeArgs &p, Rows &s) {
   const int lane = threadIdx.x & 63;
@@ -74,28 +75,38 @@ __device__ __forceinline__ void fetch_slots(const DecodeArgs &p, Rows &s) {
     dma4(p.seq_slot + min(lane, p.n - 1), lds_addr(&s.raw[0]));
 }
 
-__device__ __forceinline__ RowEntries fetch_entries(const DecodeArgs &p, const Rows &s) {
-  const int lane = threadIdx.x & 63;
-  RowEntries e{nullptr, nullptr, 0.f, false};
-  const int slot = lane < p.n ? s.raw[lane] : -1;
-  e.in = slot >= 0 && slot < p.rd.max_loras;
-  if (e.in) {
-    e.a = p.rd.a_table[slot];
-    e.b = p.rd.b_table[slot];
-    e.sc = p.rd.scale_table[slot];
-  }
-  return e;
+__device__ __forceinline__ bool row_in_pool(const DecodeArgs &p, const Rows &s, int lane, int *slot) {
+  *slot = lane < p.n ? s.raw[lane] : -1;
+  return *slot >= 0 && *slot < p.rd.max_loras;
 }
 
-__device__ void resolve_rows(Rows &s, const RowEntries &e) {
+// Wave 0, once seq_slot has landed.  Every lane issues all five DMAs (a row
+// that does not index the pool reads its seq_slot word again), so the count
+// in flight is the same for every wave 0.
+__device__ __forceinline__ void fetch_entries(const DecodeArgs &p, Rows &s) {
+  const int lane = threadIdx.x & 63;
+  int slot;
+  const bool in = row_in_pool(p, s, lane, &slot);
+  const uint32_t *dummy = (const uint32_t *)(p.seq_slot + min(lane, p.n - 1));
+  const uint32_t *pa = in ? (const uint32_t *)(p.rd.a_table + slot) : dummy;
+  const uint32_t *pb = in ? (const uint32_t *)(p.rd.b_table + slot) : dummy;
+  dma4(pa, lds_addr(&s.ea[0][0]));
+  dma4(in ? pa + 1 : dummy, lds_addr(&s.ea[1][0]));
+  dma4(pb, lds_addr(&s.eb[0][0]));
+  dma4(in ? pb + 1 : dummy, lds_addr(&s.eb[1][0]));
+  dma4(in ? (const uint32_t *)(p.rd.scale_table + slot) : dummy, lds_addr(&s.esc[0]));
+}
+
+// Wave 0, once the entries have landed.
+__device__ void resolve_rows(const DecodeArgs &p, Rows &s) {
   const int lane = threadIdx.x & 63;
   if (threadIdx.x >= 64) return;
-  // The entries pass through an empty asm here, so that the compiler tests
-  // them here, after the stream of W, and not right after their loads.
-  uint64_t a = (uint64_t)e.a, b = (uint64_t)e.b;
-  float sc = e.sc;
-  asm volatile("" : "+v"(a), "+v"(b), "+v"(sc));
-  const int q = e.in && a != 0 && b != 0 && sc != 0.f ? s.raw[lane] : kSkip;
+  int slot;
+  const bool in = row_in_pool(p, s, lane, &slot);
+  const uint64_t a = in ? ((uint64_t)s.ea[1][lane] << 32) | s.ea[0][lane] : 0;
+  const uint64_t b = in ? ((uint64_t)s.eb[1][lane] << 32) | s.eb[0][lane] : 0;
+  const float sc = in ? s.esc[lane] : 0.f;
+  const int q = in && a != 0 && b != 0 && sc != 0.f ? slot : kSkip;
   s.q[lane] = q;
   s.bq[lane] = q >= 0 ? (const u16 *)b : nullptr;
   s.sig[lane] = q >= 0 ? sc : 0.f;
@@ -103,11 +114,15 @@ __device__ void resolve_rows(Rows &s, const RowEntries &e) {
   uint64_t todo = __ballot(q >= 0);
   int T = 0, pos = 0;
   while (todo) {  // uniform: the lowest row not yet grouped names the next slot
-    const int v = __builtin_amdgcn_readlane(q, __ffsll((unsigned long long)todo) - 1);
+    const int first = __ffsll((unsigned long long)todo) - 1;
+    const int v = __builtin_amdgcn_readlane(q, first);
+    const uint64_t av = ((uint64_t)__builtin_amdgcn_readlane((int)(a >> 32), first) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a, first);
     const uint64_t m = __ballot(q == v);
     if (q == v) s.list[pos + __popcll(m & below)] = lane;
     if (lane == 0) {
       s.slot[T] = v;
+      s.aq[T] = (const u16 *)av;
       s.start[T] = pos;
     }
     pos += __popcll(m);
@@ -131,14 +146,22 @@ __device__ __forceinline__ void zero_past(uint4 *slot, int k0, int ke, int chunk
 // The range's stages of A_u's 16 rows and of the slot's x rows (gathered, up
 // to 64, in groups of 16) go to LDS in one go; wave g then takes row group g
 // through every stage.
-__device__ void shrink_unit(const DecodeArgs &p, const Rows &s, int uidx, int k0, int k1, uint4 *lds) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ int unit_groups(const Rows &s, int R, int uidx) {
+  const int u = uidx / (R / 16);
+  return (s.start[u + 1] - s.start[u] + 15) / 16;  // groups of 16 gathered rows (<= 4)
+}
+
+// LDS bytes a unit of G row groups stages over ns 64-column stages.
+__device__ __forceinline__ int unit_bytes(int G, int ns) { return ns * (16 + 16 * G) * 128; }
+
+// Issues the unit's DMAs: wave w takes instructions w, w + 8, ...
+__device__ void unit_issue(const DecodeArgs &p, const Rows &s, int uidx, int k0, int k1, uint4 *lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int R = p.R, RB = R / 16;
   const int rb = uidx % RB, u = uidx / RB;
-  const int c = blockIdx.x % p.S;  // the k range: the partial's index
-  const u16 *A = (const u16 *)p.rd.a_table[s.slot[u]];
+  const u16 *A = s.aq[u];
   const int m = s.start[u + 1] - s.start[u];
-  const int G = (m + 15) / 16;  // groups of 16 gathered rows (<= 4)
+  const int G = (m + 15) / 16;
   const int ns = (k1 - k0 + 63) / 64;
   const int RU = 16 + 16 * G;   // rows of a unit stage: A's 16, then the x rows
   const int per = RU / 8;       // DMA instructions per unit stage
@@ -155,7 +178,21 @@ __device__ void shrink_unit(const DecodeArgs &p, const Rows &s, int uidx, int k0
     const int kk = k0 + st * 64 + ((lane & 7) ^ ((rr >> 1) & 7)) * 8;
     dma16(rowp + (kk < k1 ? kk : k0), lds_addr(lds + (st * RU + k8 * 8) * 8));
   }
-  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// Zeroes what the unit fetched past the k range; then the unit's MFMAs (wave
+// g takes row group g) and its partial of t.  The unit's stages have landed
+// for every wave before this is called.
+__device__ void unit_compute(const DecodeArgs &p, const Rows &s, int uidx, int k0, int k1, uint4 *lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int R = p.R, RB = R / 16;
+  const int rb = uidx % RB, u = uidx / RB;
+  const int c = blockIdx.x % p.S;  // the k range: the partial's index
+  const int m = s.start[u + 1] - s.start[u];
+  const int G = (m + 15) / 16;
+  const int ns = (k1 - k0 + 63) / 64;
+  const int RU = 16 + 16 * G;
+  const int per = RU / 8;
   if (k0 + ns * 64 > k1) {  // the last stage runs past the chunk
     for (int ii = wave; ii < ns * per; ii += kNW) {
       const int st = ii / per, k8 = ii % per;
@@ -163,8 +200,8 @@ __device__ void shrink_unit(const DecodeArgs &p, const Rows &s, int uidx, int k0
       zero_past(lds + (st * RU + k8 * 8) * 8 + lane, k0 + st * 64, k1, ((lane & 7) ^ ((rr >> 1) & 7)) * 8);
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __syncthreads();
   }
-  __syncthreads();
   if (wave < G) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     const int ra = lane & 15, rx = 16 + wave * 16 + (lane & 15);
@@ -183,6 +220,13 @@ __device__ void shrink_unit(const DecodeArgs &p, const Rows &s, int uidx, int k0
       *(f32x4 *)(p.t_part + ((size_t)c * p.n + row) * R + rb * 16 + (lane >> 4) * 4) = acc;
     }
   }
+}
+
+__device__ void shrink_unit(const DecodeArgs &p, const Rows &s, int uidx, int k0, int k1, uint4 *lds) {
+  unit_issue(p, s, uidx, k0, k1, lds);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  unit_compute(p, s, uidx, k0, k1, lds);
   __syncthreads();  // the ring is reused by the next unit
 }
 
@@ -237,11 +281,10 @@ __global__ __launch_bounds__(kNW * 64) void decode_main_kernel(DecodeArgs p) {
   // wave 0: once seq_slot has landed (older than every stage), the table
   // entries go out; they are younger than the first npro stages, so wave 0
   // allows for them (kEnt more operations in flight) when it waits for those
-  RowEntries ent{nullptr, nullptr, 0.f, false};
   const bool ents = p.has_lora && wave == 0;
   if (ents) {
     wait_stages<kLPW, kNS - 1>(npro);
-    ent = fetch_entries(p, s);
+    fetch_entries(p, s);
   }
 
   const int ob0 = (wave % OWAVES) * OBW, rb0 = (wave / OWAVES) * RBW;
@@ -250,22 +293,38 @@ __global__ __launch_bounds__(kNW * 64) void decode_main_kernel(DecodeArgs p) {
   for (int a = 0; a < OBW; ++a)
 #pragma unroll
     for (int b = 0; b < RBW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int st = 0; st < nstage; ++st) {
-    // stage st has landed for every wave (at most kNS - 2 younger stages in
-    // flight); chunks past the k range are zeroed first
+  // On a full k range the routes are resolved at stage kEarly, once the table
+  // entries are sure to have landed (they went out before stage kEarly), and
+  // this workgroup's first shrink unit sends its stages into the ring slots
+  // of stages 2 .. 4, which no later stage takes; its MFMAs then run right
+  // after the loop instead of behind a round trip of their own.  Each wave
+  // issues exactly xw of those DMAs, which the later stage waits allow for.
+  constexpr int kEarly = kNS - 1;
+  static_assert(kEarly + 1 < kDecodeMaxStages && kDecodeMaxStages - kNS == 2, "free slots 2 .. kEarly - 1");
+  const bool early_ok = p.has_lora && nstage == kDecodeMaxStages && ke - kb == 64 * kDecodeMaxStages;
+  bool early = false;
+  // one stage: wait until it has landed (at most kNS - 2 younger stages, and
+  // X more operations issued after them, in flight), zero what lies past the
+  // k range, `mid` before the barrier, the barrier, refill the ring, `post`,
+  // then the stage's fragments and MFMAs
+  auto stage = [&](int st, auto xc, auto mid, auto post) {
+    constexpr int X = decltype(xc)::value;
+    const int younger = min(kNS - 2, nstage - 1 - st);
     if (ents && st < npro)
-      wait_stages<kLPW, kNS - 2, kEnt>(min(kNS - 2, nstage - 1 - st));
+      wait_stages<kLPW, kNS - 2, kEnt>(younger);
     else
-      wait_stages<kLPW, kNS - 2>(min(kNS - 2, nstage - 1 - st));
+      wait_stages<kLPW, kNS - 2, X>(younger);
     if (kb + st * 64 + 64 > ke) {
 #pragma unroll
       for (int j = 0; j < kLPW; ++j)
         zero_past(&ring[st % kNS][(wave + kNW * j) * 64 + lane], kb + st * 64, ke, sch[j]);
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     }
+    mid();
     block_barrier();
     // every wave is done with stage st - 1: its slot takes stage st + kNS - 1
     if (st + kNS - 1 < nstage) issue(st + kNS - 1);
+    post();
     const uint4 *sl = ring[st % kNS];
     uint4 af[2][OBW], bf[2][RBW];
 #pragma unroll
@@ -288,11 +347,49 @@ __global__ __launch_bounds__(kNW * 64) void decode_main_kernel(DecodeArgs p) {
       for (int a = 0; a < OBW; ++a)
 #pragma unroll
         for (int b = 0; b < RBW; ++b) acc[a][b] = mfma16(af[h][a], bf[h][b], acc[a][b]);
+  };
+  using X0 = std::integral_constant<int, 0>;
+  auto none = [] {};
+  const int st1 = early_ok ? kEarly : nstage;
+  for (int st = 0; st < st1; ++st) stage(st, X0{}, none, none);
+  int xw = 0;
+  if (early_ok) {
+    stage(kEarly, X0{},
+          [&] {
+            if (wave == 0) {  // its LDS writes land before the barrier
+              resolve_rows(p, s);
+              __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+            }
+          },
+          [&] {
+            if (tl < s.T * (p.R / 16)) {
+              const int G = unit_groups(s, p.R, tl);
+              if (unit_bytes(G, kDecodeMaxStages) <= 3 * (int)sizeof(ring[0])) {
+                unit_issue(p, s, tl, kb, ke, &ring[2][0]);
+                xw = 2 + 2 * G;  // (16 + 16 G) / 8 instructions per unit stage, 8 stages over 8 waves
+                early = true;
+              }
+            }
+          });
+    for (int st = kEarly + 1; st < nstage; ++st) {
+      if (xw == 0) stage(st, X0{}, none, none);
+      else if (xw == 4) stage(st, std::integral_constant<int, 4>{}, none, none);
+      else if (xw == 6) stage(st, std::integral_constant<int, 6>{}, none, none);
+      else stage(st, std::integral_constant<int, 8>{}, none, none);
+    }
   }
 
   // the routes first (the table entries arrived long ago; no store is
   // outstanding yet that the wait for them would include)
-  if (p.has_lora) resolve_rows(s, ent);
+  if (p.has_lora && !early_ok) {
+    if (wave == 0) __builtin_amdgcn_s_waitcnt(0);  // the entries (the last stage's wait may allow them)
+    resolve_rows(p, s);
+  }
+  if (early) {  // the early unit: only its DMAs are in flight
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    unit_compute(p, s, tl, kb, ke, &ring[2][0]);
+  }
   // D layout: column (row) l%16 of the row block, outputs 4 (l/16) .. +3 of
   // the output block
   const bool direct = p.S == 1 && !p.has_lora;  // nothing left for an epilogue: store y now
@@ -320,7 +417,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_main_kernel(DecodeArgs p) {
     p.row_b[tid] = s.bq[tid];
   }
   const int units = s.T * (p.R / 16);  // of this k range
-  for (int uidx = tl; uidx < units; uidx += p.n_tiles) shrink_unit(p, s, uidx, kb, ke, &ring[0][0]);
+  for (int uidx = tl + (early ? p.n_tiles : 0); uidx < units; uidx += p.n_tiles)
+    shrink_unit(p, s, uidx, kb, ke, &ring[0][0]);
 }
 
 // y for 16 rows x 64 output features per workgroup, one thread per (row,
