@@ -75,6 +75,9 @@ __device__ __forceinline__ int run_start(uint64_t bnds, int lane) {
 // grouped MoE call ([n+1] non-decreasing starts); tables up to kSegLds
 // entries are copied to LDS for the routing.
 constexpr int kSegLds = 4096;
+// Segments a shrink unit looks through for its adapter's first one.
+constexpr int kSegScan = 64;
+
 __device__ __forceinline__ bool has_ranges(const Routing &rt) {
   return rt.mode == kModeSegmented || rt.mode == kModeMoeGrouped;
 }
@@ -373,14 +376,23 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
   if (ranked) {  // the rows of pstar whose rank falls in [first, first + kShrinkRows)
     const int total = (int)a.pair_cnt[pstar];
     const int want = min(kShrinkRows, total - first);
-    // a grouped call's pair lives in its expert's row range: scan only that,
-    // and the whole batch if the range does not hold every wanted row
-    // (offsets that are not non-decreasing)
+    // a grouped call's pair lives in its expert's row range, a segmented
+    // call's usually in the first segment bound to its adapter: scan only
+    // that, and the whole batch if the range does not hold every wanted row
+    // (offsets that are not non-decreasing, an adapter on several segments)
     int r_lo = 0, r_hi = a.n;
     if (a.rt.mode == kModeMoeGrouped) {
       const int e = pstar % a.rd.n_experts;
       r_lo = min(max(a.rt.expert_offsets[e], 0), a.n);
       r_hi = min(max(a.rt.expert_offsets[e + 1], r_lo), a.n);
+    } else if (a.rt.mode == kModeSegmented && a.rt.n_seg <= kSegScan) {
+      // pairs of a segmented call are pool slots (one W group)
+      for (int g = 0; g < a.rt.n_seg; ++g)
+        if (a.rt.seg_slot[g] == pstar) {
+          r_lo = min(max(a.rt.seg_indptr[g], 0), a.n);
+          r_hi = min(max(a.rt.seg_indptr[g + 1], r_lo), a.n);
+          break;
+        }
     }
     for (int pass = 0; pass < 2; ++pass) {
       __syncthreads();  // every thread has read the last pass's count
