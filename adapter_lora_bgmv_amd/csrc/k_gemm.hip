@@ -561,6 +561,7 @@ hipError_t launch_gemm(const GemmArgs &a, int to, int tr, hipStream_t st) {
   else if (to == 256 && tr == 64 && mode == kOneTile) LORA_GEMM(256, 64, 4, 1, 3, kOneTile);
   else if (to == 256 && tr == 128 && mode == kOneTile) LORA_GEMM(256, 128, 4, 2, 3, kOneTile);
   else if (to == 256 && tr == 256 && mode == kStreamK) LORA_GEMM(256, 256, 2, 4, 2, kStreamK);
+  else if (to == 256 && tr == 128 && mode == kStreamK) LORA_GEMM(256, 128, 4, 2, 3, kStreamK);
   else
     return hipErrorInvalidValue;
 #undef LORA_GEMM

@@ -77,6 +77,8 @@ struct Cfg {
   int zero_units;        // shrink arrival counters any routing of this shape may use
 };
 
+constexpr int kStreamKNarrowRows = 256;
+
 int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 // Tile shape and split factor.  Up to 128 rows the split factor depends on
@@ -112,7 +114,11 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
   } else if (n <= 128) {
     c.to = 128; c.tr = 128; c.splits = clampi(k_in / 1024, 1, 4);
   } else {
-    c.to = 256; c.tr = 256; c.splits = 1;
+    // up to kStreamKNarrowRows rows W is the stream to keep moving: 256 x 128
+    // tiles leave LDS for three 48 KB stages (two in flight) where 256 x 256
+    // tiles fit two 64 KB ones; the row tiles of one W tile sweep k together,
+    // so W still comes from HBM about once
+    c.to = 256; c.tr = n <= kStreamKNarrowRows ? 128 : 256; c.splits = 1;
   }
   // stream-K stages the LoRA term through LDS, which takes ranks dividing 64;
   // other ranks go to 128 x 128 tiles

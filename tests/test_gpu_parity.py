@@ -74,6 +74,7 @@ SMALL = [
     (19, "bf16", 3648, 136, 9, 3, 32),    # 57 stages: the last k range is one stage, its second shrink chunk empty
     (20, "bf16", 8192, 72, 5, 2, 16),     # the largest k_in of the decode kernels: 16 k ranges
     (21, "bf16", 8200, 40, 6, 2, 16),     # one column block past it: the tiled path
+    (22, "bf16", 520, 296, 200, 6, 32),   # stream-K on 256 x 128 tiles: ragged rows, outputs and k
     (6, "f32", 96, 80, 13, 5, 16),
     (7, "f32", 37, 29, 9, 3, 5),          # f32 takes any shape
 ]
@@ -90,6 +91,7 @@ def test_decode_small(orc, case):
 @pytest.mark.parametrize("seed,dtype,lens", [
     (10, "bf16", [5, 0, 17, 64, 3, 100]),
     (11, "bf16", [512, 300, 1, 0]),
+    (13, "bf16", [60, 0, 90, 50]),       # 200 rows: stream-K on 256 x 128 tiles
     (12, "f32", [4, 0, 9, 2]),
 ])
 def test_segmented_small(orc, seed, dtype, lens):
