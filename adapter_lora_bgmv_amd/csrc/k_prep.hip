@@ -160,19 +160,32 @@ __device__ __forceinline__ void route_all(const PrepArgs &a, int *pk, const int 
       if (r < a.n) pk[r] = ((key + 1) << 13) | (q + 2);
       qv[j] = r < a.n ? q : kSkip;
     }
-    if (ranked) {  // each row's rank within its pair: every run of equal pairs in a wave's rows takes its ranks with one atomic
+    if (ranked) {  // each row's rank within its pair: the rows of one pair in a wave take their ranks with one atomic
       const int lane = threadIdx.x & 63;
+      const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int q = qv[j];
-        const uint64_t bnds = run_starts(q, lane);
-        int base = 0;
-        if (q >= 0 && ((bnds >> lane) & 1ull))
-          base = (int)atomicAdd(&a.pair_cnt[q], (unsigned)(run_end(bnds, lane) - lane));
-        const int rs = run_start(bnds, lane);
-        base = __shfl(base, rs, 64);
+        // group the wave's rows by pair (one round of ballots per pair, the
+        // lowest lane of a pair leading it), then every leader's atomic goes
+        // out in one instruction
+        uint64_t todo = __ballot(q >= 0), mine = 0;
+        int lead = lane;
+        while (todo) {  // uniform
+          const int l0 = __ffsll((unsigned long long)todo) - 1;
+          const int v = __builtin_amdgcn_readlane(q, l0);
+          const uint64_t m = __ballot(q == v);
+          if (q == v) {
+            lead = l0;
+            mine = m;
+          }
+          todo &= ~m;
+        }
+        unsigned got = 0;
+        if (q >= 0 && lane == lead) got = atomicAdd(&a.pair_cnt[q], (unsigned)__popcll(mine));
+        const int base = __shfl((int)got, lead, 64);
         const int r = r0 + 256 * j;
-        if (r < a.n) a.ranks[r] = q >= 0 ? base + (lane - rs) : -1;
+        if (r < a.n) a.ranks[r] = q >= 0 ? base + (int)__popcll(mine & below) : -1;
       }
     }
   }
