@@ -4,18 +4,21 @@
 // of the adapted matrix (ferrox lora.rs LoraDelta::add_row_to), with the
 // embedding pair in the one layout (A [rank][n_embd], B [n_vocab][rank]).
 // Memory-bound: a gathered row of E, one row of B per row, and each touched
-// slot's A, which every row on that slot shares.  A workgroup takes 16 rows
-// and 1024 columns, 4 columns per thread, its rows ordered by pair; the
-// rows' B entries go to LDS and each pair's A rows are read once for all
-// of its rows.  The rank sum runs k ascending in f32; y is rounded once.
+// slot's A, which every row on that slot shares.  A workgroup takes 64 rows
+// and 256 columns (wave w its rows 16 w .. +15, 4 columns per lane); for
+// every 8 ranks the A rows of the workgroup's pairs go to LDS once and all
+// four waves read them there, so each pair's A is read once per workgroup.
+// The rank sum runs k ascending in f32; y is rounded once.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace lora {
 
-constexpr int kEmbedRows = 16;
-constexpr int kEmbedVec = 4;                  // columns per thread
-constexpr int kEmbedCols = 256 * kEmbedVec;   // columns per workgroup
+constexpr int kEmbedRows = 64;               // rows per workgroup, 16 per wave
+constexpr int kEmbedVec = 4;                 // columns per lane
+constexpr int kEmbedCols = 64 * kEmbedVec;   // columns per workgroup (every wave takes all of them)
+constexpr int kEmbedKC = 8;                  // ranks per pass
+constexpr int kEmbedLds = 32 * 1024;         // bytes of staged A per pass
 
 template <typename T> struct Vec4;
 // bf16 rows are multiples of 8 long, 16-byte aligned: whole 8-byte pieces
@@ -74,23 +77,26 @@ template <> struct Vec4<float> {
   }
 };
 
-// A workgroup takes 16 rows and 1024 columns (4 per thread).  It orders its
-// rows by pair in LDS, so that walking them in that order each pair's A rows
-// are loaded once (when the pair changes) and shared by all of its rows; the
-// accumulators are indexed by that order, which keeps them in registers.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_rows_kernel(EmbedArgs a) {
-  __shared__ float bsh[kEmbedRows][256];  // B[t, 0:R] of the row at each sorted place, f32
-  __shared__ int r_tok[kEmbedRows], r_q[kEmbedRows];
+  constexpr int PG = kEmbedLds / (kEmbedKC * kEmbedCols * (int)sizeof(T));  // pairs staged per pass
+  __shared__ __attribute__((aligned(16))) T ash[PG][kEmbedKC][kEmbedCols];   // A rows of PG pairs
+  __shared__ float bsh[kEmbedRows][kEmbedKC];  // B[t, kc .. kc + KC) of each row, f32
+  __shared__ int r_tok[kEmbedRows], r_q[kEmbedRows], r_d[kEmbedRows];  // token, pair, place in d_pair
   __shared__ float r_sig[kEmbedRows];
-  __shared__ int p_row[kEmbedRows], p_q[kEmbedRows];  // by sorted place: row (in the block), pair
-  const int tid = threadIdx.x;
+  __shared__ const T *r_b[kEmbedRows];  // the row's B row
+  __shared__ int d_pair[kEmbedRows];    // the workgroup's pairs, in order of first appearance
+  __shared__ const T *d_a[kEmbedRows];  // their A
+  __shared__ int n_d;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i0 = blockIdx.y * kEmbedRows;
   const RouteDev &rd = a.rd;
-  if (tid < kEmbedRows) {
+  const int R = rd.R;
+  if (tid < kEmbedRows) {  // one row per lane of wave 0
     const int i = i0 + tid;
     int tok = -1, q = kSkip;
     float sig = 0.f;
+    const T *brow = nullptr;
     if (i < a.n) {
       tok = a.token_ids[i];
       if (tok < 0 || tok >= a.n_vocab) {
@@ -98,86 +104,105 @@ __global__ __launch_bounds__(256) void embed_rows_kernel(EmbedArgs a) {
       } else if (a.has_lora) {
         const int s = a.seq_slot[i];
         q = resolve_slot(s, 0, rd.max_loras, 1, rd.a_table, rd.b_table, rd.scale_table);
-        if (q >= 0) sig = rd.scale_table[s];
+        if (q >= 0) {
+          sig = rd.scale_table[s];
+          brow = (const T *)rd.b_table[q] + (size_t)tok * R;
+        }
       }
     }
     r_tok[tid] = tok;
     r_q[tid] = q;
     r_sig[tid] = sig;
-  }
-  __syncthreads();
-  if (tid < kEmbedRows) {  // place of this row in (pair, row) order
-    const int q = r_q[tid];
-    int place = 0;
-    for (int r = 0; r < kEmbedRows; ++r) {
-      const int qr = r_q[r];
-      place += qr < q || (qr == q && r < tid);
+    r_b[tid] = brow;
+    // the distinct pairs, in order of first appearance: one round of
+    // ballots per pair, then their A entries in one round trip
+    uint64_t todo = __ballot(q >= 0);
+    int nd = 0, mine = -1;
+    while (todo) {  // uniform
+      const int l0 = __ffsll((unsigned long long)todo) - 1;
+      const int v = __builtin_amdgcn_readlane(q, l0);
+      const uint64_t m = __ballot(q == v);
+      if (q == v) mine = nd;
+      if (lane == l0) d_pair[nd] = v;
+      ++nd;
+      todo &= ~m;
     }
-    p_row[place] = tid;
-    p_q[place] = q;
+    r_d[tid] = mine;
+    if (lane < nd) d_a[lane] = (const T *)rd.a_table[d_pair[lane]];
+    if (lane == 0) n_d = nd;
   }
   __syncthreads();
-  for (int e = tid; e < kEmbedRows * rd.R; e += 256) {
-    const int p = e / rd.R, k = e % rd.R;
-    const int q = p_q[p];
-    if (q >= 0) bsh[p][k] = Vec4<T>::one((const T *)rd.b_table[q] + (size_t)r_tok[p_row[p]] * rd.R + k);
-  }
-  __syncthreads();
-  const int c0 = blockIdx.x * kEmbedCols + tid * kEmbedVec;
-  if (c0 >= a.n_embd) return;
-  const int valid = min(kEmbedVec, a.n_embd - c0);
+  const int nd = n_d;
+  const int c0 = blockIdx.x * kEmbedCols + lane * kEmbedVec;
+  const int valid = c0 < a.n_embd ? min(kEmbedVec, a.n_embd - c0) : 0;
   // every row's piece of E goes out first and is in flight during the rank
   // sums (the stores to y below could otherwise hold each load back)
-  typename Vec4<T>::raw e_raw[kEmbedRows];
+  typename Vec4<T>::raw e_raw[16];
 #pragma unroll
-  for (int p = 0; p < kEmbedRows; ++p) {
-    const int tok = r_tok[p_row[p]];
-    if (tok >= 0) e_raw[p] = Vec4<T>::load_raw((const T *)a.E + (size_t)tok * a.e_row_stride + c0, valid);
+  for (int j = 0; j < 16; ++j) {
+    const int tok = r_tok[wave * 16 + j];
+    if (tok >= 0 && valid > 0) e_raw[j] = Vec4<T>::load_raw((const T *)a.E + (size_t)tok * a.e_row_stride + c0, valid);
   }
-  float acc[kEmbedRows][kEmbedVec];
+  float acc[16][kEmbedVec];
 #pragma unroll
-  for (int p = 0; p < kEmbedRows; ++p)
+  for (int j = 0; j < 16; ++j)
 #pragma unroll
-    for (int j = 0; j < kEmbedVec; ++j) acc[p][j] = 0.f;
-  // k in blocks of 8: at each change of pair along the sorted rows, the
-  // block's 8 rows of that pair's A go out together, then every row of the
-  // pair takes them
-  constexpr int KC = 8;
-  for (int kc = 0; kc < rd.R; kc += KC) {
-    typename Vec4<T>::raw ar[KC];
-    int cur = kSkip;
-#pragma unroll
-    for (int p = 0; p < kEmbedRows; ++p) {
-      const int q = p_q[p];
-      if (q < 0) continue;
-      if (q != cur) {
-        cur = q;
-        const T *Aq = (const T *)rd.a_table[q] + (size_t)kc * a.n_embd + c0;
-#pragma unroll
-        for (int kk = 0; kk < KC; ++kk)
-          if (kc + kk < rd.R) ar[kk] = Vec4<T>::load_raw(Aq + (size_t)kk * a.n_embd, valid);
+    for (int v = 0; v < kEmbedVec; ++v) acc[j][v] = 0.f;
+  for (int kc = 0; kc < R && nd > 0; kc += kEmbedKC) {
+    __syncthreads();  // every wave is done with the last pass's B
+    for (int e = tid; e < kEmbedRows * kEmbedKC; e += 256) {
+      const int r = e / kEmbedKC, kk = e % kEmbedKC;
+      const T *brow = r_b[r];
+      bsh[r][kk] = brow != nullptr && kc + kk < R ? Vec4<T>::one(brow + kc + kk) : 0.f;
+    }
+    for (int g0 = 0; g0 < nd; g0 += PG) {
+      __syncthreads();  // every wave is done with the last pass's A (and this pass's B has landed)
+      const int np = min(PG, nd - g0);
+      // the pass's A: pair g0 + ps, rank kc + kk, the workgroup's columns, in
+      // pieces of kEmbedVec columns (consecutive threads, consecutive pieces)
+      for (int e = tid; e < np * kEmbedKC * 64; e += 256) {
+        const int ps = e / (kEmbedKC * 64), kk = (e / 64) % kEmbedKC, cl = e % 64;
+        const int cc = blockIdx.x * kEmbedCols + cl * kEmbedVec;
+        const int vv = cc < a.n_embd ? min(kEmbedVec, a.n_embd - cc) : 0;
+        T *dst = &ash[ps][kk][cl * kEmbedVec];
+        if (kc + kk < R && vv > 0)
+          Vec4<T>::store_raw(dst, Vec4<T>::load_raw(d_a[g0 + ps] + (size_t)(kc + kk) * a.n_embd + cc, vv), kEmbedVec);
       }
+      __syncthreads();
+      if (valid > 0) {
 #pragma unroll
-      for (int kk = 0; kk < KC; ++kk) {
-        if (kc + kk >= rd.R) break;
-        const float b = bsh[p][kc + kk];
+        for (int j = 0; j < 16; ++j) {
+          const int r = wave * 16 + j;
+          const int d = r_d[r] - g0;  // uniform over the wave
+          if (d < 0 || d >= np) continue;
 #pragma unroll
-        for (int j = 0; j < kEmbedVec; ++j) acc[p][j] += b * Vec4<T>::at(ar[kk], j);
+          for (int kk = 0; kk < kEmbedKC; ++kk) {
+            if (kc + kk >= R) break;
+            const float b = bsh[r][kk];
+            const typename Vec4<T>::raw av = *(const typename Vec4<T>::raw *)&ash[d][kk][lane * kEmbedVec];
+#pragma unroll
+            for (int v = 0; v < kEmbedVec; ++v) acc[j][v] += b * Vec4<T>::at(av, v);
+          }
+        }
       }
     }
   }
+  if (valid == 0) return;
+  // every load has landed: the stores below then need no waits of their
+  // own (a wait for a load would also wait for every store before it)
+  wait_vmcnt<0>();
 #pragma unroll
-  for (int p = 0; p < kEmbedRows; ++p) {
-    const int r = p_row[p];
+  for (int j = 0; j < 16; ++j) {
+    const int r = wave * 16 + j;
     if (r_tok[r] < 0) continue;
     T *yr = (T *)a.y + (size_t)(i0 + r) * a.y_row_stride + c0;
-    if (p_q[p] < 0) {  // base only: the table row, bit for bit
-      Vec4<T>::store_raw(yr, e_raw[p], valid);
+    if (r_q[r] < 0) {  // base only: the table row, bit for bit
+      Vec4<T>::store_raw(yr, e_raw[j], valid);
       continue;
     }
     float ev[kEmbedVec];
 #pragma unroll
-    for (int j = 0; j < kEmbedVec; ++j) ev[j] = Vec4<T>::at(e_raw[p], j) + r_sig[r] * acc[p][j];
+    for (int v = 0; v < kEmbedVec; ++v) ev[v] = Vec4<T>::at(e_raw[j], v) + r_sig[r] * acc[j][v];
     Vec4<T>::store(yr, ev, valid);
   }
 }

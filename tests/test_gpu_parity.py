@@ -565,10 +565,10 @@ def test_stream_k_partition(orc, seed, k, n_out, n, R):
 
 
 # ------------------------------------------------------------------ token-embedding gather
-def _embed_small(seed, dtype, n_vocab, n_embd, n, R):
+def _embed_small(seed, dtype, n_vocab, n_embd, n, R, n_slots=4):
     rng = np.random.default_rng(seed)
-    ranks = [int(v) for v in rng.integers(1, R + 1, size=4)]
-    wl = WL.token_embedding(seed, n_vocab=n_vocab, n_embd=n_embd, n=n, n_slots=4, rank=R,
+    ranks = [int(v) for v in rng.integers(1, R + 1, size=n_slots)]
+    wl = WL.token_embedding(seed, n_vocab=n_vocab, n_embd=n_embd, n=n, n_slots=n_slots, rank=R,
                             alpha=8.0, dtype=dtype, max_rank=R, ranks=ranks)
     tok = wl.meta["token_ids"].copy()
     tok[[0, n // 2]] = [n_vocab, -5]  # outside the vocabulary: not written
@@ -576,17 +576,19 @@ def _embed_small(seed, dtype, n_vocab, n_embd, n, R):
     return wl
 
 
-@pytest.mark.parametrize("seed,dtype,n_vocab,n_embd,n,R", [
-    (110, "bf16", 1000, 264, 70, 16),
-    (111, "bf16", 517, 4104, 9, 32),     # two column blocks, the second ragged
-    (112, "f32", 300, 37, 21, 5),
+@pytest.mark.parametrize("seed,dtype,n_vocab,n_embd,n,R,n_slots", [
+    (110, "bf16", 1000, 264, 70, 16, 4),
+    (111, "bf16", 517, 4104, 9, 32, 4),     # two column blocks, the second ragged
+    (112, "f32", 300, 37, 21, 5, 4),
+    (113, "bf16", 800, 520, 130, 16, 12),   # more pairs in a workgroup than one pass stages
+    (114, "f32", 200, 70, 75, 8, 10),
 ])
-def test_embed_small(orc, seed, dtype, n_vocab, n_embd, n, R):
+def test_embed_small(orc, seed, dtype, n_vocab, n_embd, n, R, n_slots):
     """ferrox LoraDelta::add_row_to: a gathered row is E[token] plus s times that
     token's row of B A; the pair arrives flipped and is brought into the one
     layout by lora_embedding_pair.  Rows whose token is outside the vocabulary
     keep their sentinel; rows whose slot skips are the table row bit for bit."""
-    wl = _embed_small(seed, dtype, n_vocab, n_embd, n, R)
+    wl = _embed_small(seed, dtype, n_vocab, n_embd, n, R, n_slots)
     dw = DeviceWorkload(wl)
     dw.y.fill_(float("nan"))
     dw.run()
