@@ -39,11 +39,7 @@ namespace lora {
 namespace {
 
 constexpr int kNW = 8;                               // waves per workgroup
-constexpr int kTO = kDecodeTileOut;                  // output features per tile
-constexpr int kRS = kTO + kDecodeMaxRows;            // rows of a stage: W rows, then x rows
-constexpr int kLPW = kRS / 8 / kNW;                  // DMA instructions per wave per stage
-constexpr int kNS = 6;                               // ring depth: 6 x 24 KB
-static_assert(kLPW * 8 * kNW == kRS, "stage rows must split evenly over the waves");
+constexpr int kNS = 6;                               // ring depth: 6 stages of TO + 64 rows
 
 struct Rows {  // the batch's routes, resolved once per workgroup
   int raw[64];        // seq_slot, as the caller gave it (LDS-DMA)
@@ -232,10 +228,15 @@ __device__ void shrink_unit(const DecodeArgs &p, const Rows &s, int uidx, int k0
 
 }  // namespace
 
-// NB: 16-row blocks of the batch that hold rows (n <= 16 NB).  Wave w owns
+// NB: 16-row blocks of the batch that hold rows (n <= 16 NB); TO: output
+// features per tile.  Wave w owns
 // output blocks OBW (w % OWAVES) .. +OBW-1 and row blocks RBW (w / OWAVES) ..
-template <int NB>
+template <int NB, int TO>
 __global__ __launch_bounds__(kNW * 64) void decode_main_kernel(DecodeArgs p) {
+  constexpr int kTO = TO;
+  constexpr int kRS = kTO + kDecodeMaxRows;  // rows of a stage: W rows, then x rows
+  constexpr int kLPW = kRS / 8 / kNW;        // DMA instructions per wave per stage
+  static_assert(kLPW * 8 * kNW == kRS, "stage rows must split evenly over the waves");
   constexpr int RWAVES = NB >= 2 ? 2 : 1;  // waves across the row blocks
   constexpr int OWAVES = kNW / RWAVES;     // waves across the output blocks
   constexpr int OBW = kTO / 16 / OWAVES;   // output blocks per wave
@@ -429,7 +430,8 @@ __global__ __launch_bounds__(256) void decode_epilogue_kernel(DecodeArgs p, Stac
   __shared__ __attribute__((aligned(16))) float st[16 * 256];  // t of the 16 rows, 16 x R
   const int tid = threadIdx.x;
   const int R = p.R;
-  constexpr int OPT = kTO / kEpiOut;  // output groups per tile
+  const int kTO = p.tile_out;
+  const int OPT = kTO / kEpiOut;  // output groups per tile
   const int rg = blockIdx.x % 4, og = blockIdx.x / 4;  // row group, output group
   const int tl = og / OPT;
   const int i = rg * 16 + (tid >> 4), oo = (og % OPT) * kEpiOut + (tid & 15) * 4, o = tl * kTO + oo;
@@ -552,14 +554,20 @@ hipError_t launch_decode_main(const DecodeArgs &a, hipStream_t st) {
   const int grid = a.n_tiles * a.S;
   if (grid == 0) return hipSuccess;
   const int nb = (a.n + 15) / 16;
-  if (nb <= 1)
-    hipLaunchKernelGGL(decode_main_kernel<1>, dim3(grid), dim3(kNW * 64), 0, st, a);
-  else if (nb == 2)
-    hipLaunchKernelGGL(decode_main_kernel<2>, dim3(grid), dim3(kNW * 64), 0, st, a);
-  else if (nb <= 4)
-    hipLaunchKernelGGL(decode_main_kernel<4>, dim3(grid), dim3(kNW * 64), 0, st, a);
-  else
+#define LORA_DECODE(NB, TO) hipLaunchKernelGGL((decode_main_kernel<NB, TO>), dim3(grid), dim3(kNW * 64), 0, st, a)
+  const bool small = a.tile_out == kDecodeTileOutSmall;
+  if (!small && a.tile_out != kDecodeTileOut) return hipErrorInvalidValue;
+  if (nb <= 1) {  // one row block: the small tile leaves waves without output blocks
+    if (small) return hipErrorInvalidValue;
+    LORA_DECODE(1, kDecodeTileOut);
+  } else if (nb == 2) {
+    if (small) LORA_DECODE(2, kDecodeTileOutSmall); else LORA_DECODE(2, kDecodeTileOut);
+  } else if (nb <= 4) {
+    if (small) LORA_DECODE(4, kDecodeTileOutSmall); else LORA_DECODE(4, kDecodeTileOut);
+  } else {
     return hipErrorInvalidValue;
+  }
+#undef LORA_DECODE
   return hipGetLastError();
 }
 
@@ -568,7 +576,7 @@ hipError_t launch_decode_epilogue(const DecodeArgs &a, const StackFold *stack, h
   if (stack) f = *stack;
   if (a.S == 1 && !a.has_lora)  // the main launch stored y; a stack always has a routed first level
     return f.n_levels ? hipErrorInvalidValue : hipSuccess;
-  hipLaunchKernelGGL(decode_epilogue_kernel, dim3(a.n_tiles * (kTO / kEpiOut) * 4), dim3(256), 0, st, a, f);
+  hipLaunchKernelGGL(decode_epilogue_kernel, dim3(a.n_tiles * (a.tile_out / kEpiOut) * 4), dim3(256), 0, st, a, f);
   return hipGetLastError();
 }
 

@@ -90,9 +90,10 @@ struct DecodeArgs {
   int has_lora;
   int R;
   int S, k_per_split;   // k split of the base contraction (k_per_split: a multiple of 64)
-  int n_tiles;          // ceil(n_out / kDecodeTileOut)
+  int n_tiles;          // ceil(n_out / tile_out)
+  int tile_out;         // output features per tile: kDecodeTileOut, or kDecodeTileOutSmall
   int n_chunks;         // k chunks of the shrink partials: the S k ranges
-  float *partials;      // [n_tiles][S][64 rows][kDecodeTileOut] partial tiles
+  float *partials;      // [n_tiles][S][64 rows][tile_out] partial tiles
   float *t_part;        // [n_chunks][n][R] shrink partials, one per k chunk
   int *row_q;           // [64] each row's slot or kSkip, for the epilogue
   float *row_sig;       // [64] each row's scale
@@ -104,6 +105,11 @@ struct DecodeArgs {
 // 64 x 8 x 16 = 8192 on this path).
 constexpr int kDecodeMaxRows = 64;
 constexpr int kDecodeTileOut = 128;
+// Projections up to this many outputs (and batches past one 16-row block)
+// take tiles of kDecodeTileOutSmall outputs, so that their launch still
+// spreads over the chip.
+constexpr int kDecodeTileOutSmall = 64;
+constexpr int kDecodeSmallTileMaxOut = 2048;
 constexpr int kDecodeMaxStages = 8;
 constexpr int kDecodeMaxSplit = 16;
 

@@ -103,7 +103,11 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
   if (c.decode) {
     // k ranges of at most kDecodeMaxStages 64-column stages
     const int nst = (k_in + 63) / 64;
-    c.to = kDecodeTileOut; c.tr = kDecodeMaxRows;
+    // a small projection takes 64-output tiles (more workgroups; every
+    // output is reduced in the same order either way), unless one 16-row
+    // block holds the batch
+    c.to = n_out <= kDecodeSmallTileMaxOut && n > 16 ? kDecodeTileOutSmall : kDecodeTileOut;
+    c.tr = kDecodeMaxRows;
     c.splits = (nst + kDecodeMaxStages - 1) / kDecodeMaxStages;
   } else if (moe) {
     // one row tile per expert where the batch allows: an expert's W slab is
@@ -162,7 +166,7 @@ WsLayout ws_layout(const Cfg &c, int n, int R, int k_in) {
   if (c.decode) {  // partial tiles; shrink partials; per-row routes
     const size_t nchunks = R > 0 ? (size_t)c.splits : 0;  // the shrink's k chunks are the k ranges
     w.partials = off;
-    off = up256(off + (c.splits > 1 || R > 0 ? (size_t)c.n_ntiles * c.splits * 64 * kDecodeTileOut * 4 : 0));
+    off = up256(off + (c.splits > 1 || R > 0 ? (size_t)c.n_ntiles * c.splits * 64 * c.to * 4 : 0));
     w.t = off; off = up256(off + nchunks * n * R * 4);
     w.rows = off; off = up256(off + (R > 0 ? 64 * (4 + 4 + 8) : 0));
     w.total = off;
@@ -439,6 +443,7 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
     da.S = c.splits;
     da.k_per_split = c.k_per_split;
     da.n_tiles = c.n_ntiles;
+    da.tile_out = c.to;
     da.n_chunks = R > 0 ? c.splits : 0;
     da.partials = (float *)(ws + L.partials);
     da.t_part = (float *)(ws + L.t);
