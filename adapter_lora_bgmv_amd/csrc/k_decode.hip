@@ -9,18 +9,20 @@
 // 128-byte lines move far faster than the 64-byte half lines of MFMA
 // fragments loaded straight into registers.  So:
 //
-//  * decode_main_kernel: a workgroup owns a tile of 128 output features x
-//    all rows x one k range of at most 512 columns (k is split S ways; S
-//    depends on k_in only).  Each 64-column stage of the tile's W rows and
-//    of the batch's x rows goes to LDS by LDS-DMA, whole lines, stored
-//    XOR-swizzled so the MFMA fragment reads hit distinct banks; a ring of
-//    stages keeps 120 KB in flight per CU.  The waves own disjoint (output
-//    block, row block) pairs over the whole range, so they need no
-//    reduction; the f32 partial tile goes to the workspace.  The shrink
-//    t = A_q x rides along: once its tile is stored, a workgroup runs shrink
-//    units (touched slot, 16-rank block) of its k range, each staging
-//    A_q's rows and the slot's x rows the same way, so each A_q is read once
-//    per call.  Nothing in this launch waits for another workgroup;
+//  * decode_main_kernel: a workgroup owns a tile of 128 output features
+//    (64 for small projections) x all rows x one k range of at most 512
+//    columns (k is split S ways; S depends on k_in only).  Each 64-column
+//    stage of the tile's W rows and of the batch's x rows goes to LDS by
+//    LDS-DMA, whole lines, stored XOR-swizzled so the MFMA fragment reads
+//    hit distinct banks; a ring of stages keeps 120 KB in flight per CU.
+//    The waves own disjoint (output block, row block) pairs over the whole
+//    range, so they need no reduction; the f32 partial tile goes to the
+//    workspace.  The shrink t = A_q x rides along: a workgroup runs shrink
+//    units (touched slot, 16-rank block) of its k range, each staging A_q's
+//    rows and the slot's x rows the same way, so each A_q is read once per
+//    call; on a full k range the first unit's stages go out mid-stream into
+//    ring slots the W stream has finished with.  Nothing in this launch
+//    waits for another workgroup;
 //  * decode_epilogue_kernel: y = bf16(sum_z partial_z + s_q sum_r B_q[o, r]
 //    t_i[r]), the S partials in split order, t summed over the k ranges in
 //    range order, the rank sum in f32 in rank order, one rounding.
