@@ -75,7 +75,8 @@ SMALL = [
     (20, "bf16", 8192, 72, 5, 2, 16),     # the largest k_in of the decode kernels: 16 k ranges
     (21, "bf16", 8200, 40, 6, 2, 16),     # one column block past it: the tiled path
     (22, "bf16", 520, 296, 200, 6, 32),   # stream-K on 256 x 128 tiles: ragged rows, outputs and k
-    (23, "bf16", 1024, 200, 64, 1, 16),   # most rows on one slot: 3-4 row groups in its shrink unit
+    (23, "bf16", 1024, 200, 64, 1, 16),   # most rows on one slot: 3 row groups in its shrink unit
+    (50, "bf16", 1024, 200, 64, 1, 16),   # 50 rows on one slot: 4 row groups, the unit after the W loop
     (24, "bf16", 2048, 136, 60, 2, 32),   # two slots, two rank blocks each, full 512-column k ranges
     (6, "f32", 96, 80, 13, 5, 16),
     (7, "f32", 37, 29, 9, 3, 5),          # f32 takes any shape
