@@ -75,6 +75,8 @@ __device__ __forceinline__ int run_start(uint64_t bnds, int lane) {
 // grouped MoE call ([n+1] non-decreasing starts); tables up to kSegLds
 // entries are copied to LDS for the routing.
 constexpr int kSegLds = 4096;
+// Pairs a wave's rows are grouped by before the rest go by runs of equal pairs.
+constexpr int kRankGroups = 8;
 // Segments a shrink unit looks through for its adapter's first one.
 constexpr int kSegScan = 64;
 
@@ -167,25 +169,36 @@ __device__ __forceinline__ void route_all(const PrepArgs &a, int *pk, const int 
       for (int j = 0; j < J; ++j) {
         const int q = qv[j];
         // group the wave's rows by pair (one round of ballots per pair, the
-        // lowest lane of a pair leading it), then every leader's atomic goes
-        // out in one instruction
-        uint64_t todo = __ballot(q >= 0), mine = 0;
-        int lead = lane;
-        while (todo) {  // uniform
+        // lowest lane of a pair leading it) for up to kRankGroups pairs; the
+        // rows of a wave with more pairs go by runs of equal pairs; then
+        // every leader's atomic goes out in one instruction
+        uint64_t todo = __ballot(q >= 0);
+        int lead = lane, off = 0, cnt = 0;
+        for (int it = 0; todo && it < kRankGroups; ++it) {  // uniform
           const int l0 = __ffsll((unsigned long long)todo) - 1;
           const int v = __builtin_amdgcn_readlane(q, l0);
           const uint64_t m = __ballot(q == v);
           if (q == v) {
             lead = l0;
-            mine = m;
+            off = (int)__popcll(m & below);
           }
+          if (lane == l0) cnt = (int)__popcll(m);
           todo &= ~m;
         }
+        if (todo) {  // uniform
+          const bool left = (todo >> lane) & 1ull;
+          const uint64_t bnds = run_starts(left ? q : -2 - lane, lane);  // other lanes end every run
+          if (left) {
+            lead = run_start(bnds, lane);
+            off = lane - lead;
+            if (lane == lead) cnt = run_end(bnds, lane) - lane;
+          }
+        }
         unsigned got = 0;
-        if (q >= 0 && lane == lead) got = atomicAdd(&a.pair_cnt[q], (unsigned)__popcll(mine));
+        if (q >= 0 && lane == lead) got = atomicAdd(&a.pair_cnt[q], (unsigned)cnt);
         const int base = __shfl((int)got, lead, 64);
         const int r = r0 + 256 * j;
-        if (r < a.n) a.ranks[r] = q >= 0 ? base + (int)__popcll(mine & below) : -1;
+        if (r < a.n) a.ranks[r] = q >= 0 ? base + off : -1;
       }
     }
   }
