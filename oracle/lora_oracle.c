@@ -301,8 +301,18 @@ void orc_apply_rows(const void *W, int w_stride, const orc_route *r, int dtype, 
 #pragma omp parallel for schedule(dynamic, 1)
   for (int j = 0; j < n_rows; ++j) {
     size_t i = (size_t)rows[j];
-    apply_row(W, 0, w_stride, r, dtype, k_in, n_out, x, xrow(i, x_stride, k_in),
-              seq_slot ? seq_slot[i] : -1, 0, y + (size_t)j * n_out);
+#if ORC_MUTANT == 18
+    size_t xi = (size_t)j;
+#else
+    size_t xi = i;
+#endif
+#if ORC_MUTANT == 19
+    size_t si = (size_t)j;
+#else
+    size_t si = i;
+#endif
+    apply_row(W, 0, w_stride, r, dtype, k_in, n_out, x, xrow(xi, x_stride, k_in),
+              seq_slot ? seq_slot[si] : -1, 0, y + (size_t)j * n_out);
   }
 }
 
@@ -332,7 +342,12 @@ void orc_apply_segmented(const void *W, int w_stride, const orc_route *r, int dt
       }
     }
     if (!found) continue;
-    apply_row(W, 0, w_stride, r, dtype, k_in, n_out, x, xrow((size_t)i, x_stride, k_in), slot,
+#if ORC_MUTANT == 20
+    size_t xi = (size_t)j;
+#else
+    size_t xi = (size_t)i;
+#endif
+    apply_row(W, 0, w_stride, r, dtype, k_in, n_out, x, xrow(xi, x_stride, k_in), slot,
               0, y + (size_t)j * n_out);
   }
 }
@@ -354,7 +369,11 @@ void orc_apply_moe_gather(const void *W, long long expert_stride, int w_stride,
     int j = rows[jj];
     int e = indices[j];
     if (e < 0 || e >= n_experts) continue;
+#if ORC_MUTANT == 21
+    int a = token_slot[jj / top_k];
+#else
     int a = token_slot[j / top_k];
+#endif
     apply_row(W, (size_t)e * (size_t)expert_stride, w_stride, r, dtype, k_in, n_out, x,
               xrow((size_t)j, x_stride, k_in), a, e, y + (size_t)jj * n_out);
   }
@@ -407,7 +426,11 @@ void orc_apply_moe_grouped(const void *W, long long expert_stride, int w_stride,
 #pragma omp parallel for schedule(dynamic, 1)
   for (int jj = 0; jj < n_rows; ++jj) {
     int j = rows[jj];
+#if ORC_MUTANT == 22
+    int e = expert_of(expert_offsets, n_experts, jj);
+#else
     int e = expert_of(expert_offsets, n_experts, j);
+#endif
     if (e < 0) continue;
     int a = seq_slot ? grouped_slot(seq_slot, expert_offsets, e, j) : -1;
     apply_row(W, (size_t)e * (size_t)expert_stride, w_stride, r, dtype, k_in, n_out, x,
@@ -477,7 +500,11 @@ void orc_apply_stack(const void *W, int w_stride, const orc_route *const *routes
     for (int l = 0; l < n_levels; ++l) {
 #endif
       const orc_route *r = routes[l];
+#if ORC_MUTANT == 23
+      int slot = seq_slots[l][jj];
+#else
       int slot = seq_slots[l][i];
+#endif
       int idx = resolve(r, slot, 0);
       if (idx < 0) continue; /* this level adds nothing to the row */
       double *t = (double *)malloc(sizeof(double) * (size_t)r->max_rank);
@@ -510,7 +537,11 @@ void orc_embed_rows(const void *E, int e_stride, const orc_route *r, int dtype, 
     if (tok < 0 || tok >= n_vocab) continue;
     double *yo = y + (size_t)jj * n_embd;
     for (int c = 0; c < n_embd; ++c) yo[c] = widen(E, dtype, (size_t)tok * e_stride + c);
+#if ORC_MUTANT == 24
+    int slot = seq_slot ? seq_slot[jj] : -1;
+#else
     int slot = seq_slot ? seq_slot[i] : -1;
+#endif
     int idx = resolve(r, slot, 0);
     if (idx < 0) continue;
     double s = (double)r->scale[slot];

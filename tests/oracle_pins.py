@@ -492,3 +492,48 @@ def integer_routing_exact(o):
             want = want * 2 + int(st[s] * 2) * (Bi[s] @ (Ai[s] @ xi[i]))
             want = want / 2.0
         assert np.array_equal(y[i], want.astype(np.float64)), (i, s)
+
+
+@pin
+def row_subsets_equal_the_full_call(o):
+    """Every entry point that takes a list of rows (the sampled checks at full
+    size use them) gives, for a list in any order and with a repeat, exactly the
+    full call's outputs of the listed rows, position by position: a subset that
+    read another row's input or slot, or wrote another position, would show."""
+    rows = np.array([5, 0, 3, 5, 7, 2], np.int32)
+
+    def same(full, sub, what):
+        assert np.array_equal(sub, full[rows], equal_nan=True), what
+        assert not np.all(np.isnan(sub)), what
+
+    wl = WL.random_small(700, dtype="bf16", k=14, n_out=9, n=8, n_slots=4, max_rank=4)
+    st = o.scale_table(wl.adapters)
+    ss = np.array([1, -1, 0, 2, 3, 0, 9, 1], np.int32)
+    r = o.route_for(wl, st)
+    same(o.apply(wl.W, r, wl.x, ss, 1), o.apply(wl.W, r, wl.x, ss, 1, rows=rows), "apply")
+    wl = WL.random_small(701, dtype="f32", k=10, n_out=6, n_slots=3, max_rank=4,
+                         kind="segmented", seg_lens=[2, 3, 0, 3])
+    r = o.route_for(wl, o.scale_table(wl.adapters))
+    same(o.apply_segmented(wl.W, r, wl.x, wl.seg_indptr, wl.seg_slot, 0),
+         o.apply_segmented(wl.W, r, wl.x, wl.seg_indptr, wl.seg_slot, 0, rows=rows), "segmented")
+    wl = WL.random_small(702, dtype="bf16", k=9, n_out=6, n=4, n_slots=3, max_rank=4,
+                         kind="moe", n_experts=4, top_k=2)
+    r = o.route_for(wl, o.scale_table(wl.adapters))
+    same(o.apply_moe(wl.W, r, wl.x, wl.indices, wl.top_k, wl.token_slot, 1),
+         o.apply_moe(wl.W, r, wl.x, wl.indices, wl.top_k, wl.token_slot, 1, rows=rows), "moe")
+    wl = WL.random_small(703, dtype="bf16", k=10, n_out=7, n=9, n_slots=3, max_rank=4,
+                         kind="moe_grouped", n_experts=4)
+    r = o.route_for(wl, o.scale_table(wl.adapters))
+    same(o.apply_moe_grouped(wl.W, r, wl.x, wl.expert_offsets, wl.row_slot, 1),
+         o.apply_moe_grouped(wl.W, r, wl.x, wl.expert_offsets, wl.row_slot, 1, rows=rows),
+         "moe grouped")
+    wl = WL.random_stack(704, dtype="bf16", k=9, n_out=6, n=8, n_levels=2, n_slots=3, max_rank=4)
+    routes, _ = _stack_routes(o, wl)
+    sl = [lv["seq_slot"] for lv in wl.meta["levels"]]
+    same(o.apply_stack(wl.W, routes, wl.x, sl, 1), o.apply_stack(wl.W, routes, wl.x, sl, 1, rows=rows),
+         "stack")
+    wl = _small_embed(705, "bf16")
+    wl.meta["token_ids"][[0, 3]] = [4, 4]  # two rows on one token, different slots
+    wl.meta["seq_slot"][[0, 3]] = [0, 1]
+    st = o.scale_table(wl.adapters)
+    same(o.run(wl, scale_table=st), o.run(wl, rows=rows, scale_table=st), "embed")

@@ -12,6 +12,10 @@ Each mutant is a build of oracle/lora_oracle.c with ORC_MUTANT=k (CPU only):
 15 a stack applies its first adapter only
 16 the embedding gather reads B transposed
 17 the embedding pair copied without its transpose
+18 a listed row's x read at its list position    19 a listed row's slot read at its list position
+20 a listed segmented row's x at its position    21 a listed gather row's token at its position
+22 a listed grouped row's expert at its position 23 a listed stack row's level slot at its position
+24 a listed embedding row's slot at its position
 """
 import shutil
 
@@ -21,7 +25,7 @@ import oracle
 import oracle_pins
 from oracle import build as obuild
 
-MUTANTS = list(range(1, 18))
+MUTANTS = list(range(1, 25))
 
 
 @pytest.fixture(scope="module")
