@@ -1,38 +1,49 @@
-// k_decode.hip -- the decode-shaped apply (n <= 64 rows): a main launch and an
-// epilogue launch.
+// k_decode.hip -- the decode-shaped apply (n <= 64 rows): base contraction,
+// split-K reduction, expand and fold in one launch, after the shrink.
 //
 //     y_i = W x_i + s_q B_q (A_q x_i),   q = the slot row i resolves to
 //
-// (ferrox lora.rs module doc; atlas lora_delta.rs apply_lora_bgmv: shrink,
-// then expand-and-fold).  At decode sizes the cost is streaming W once, and
-// what limits that on this chip is how fast the bytes reach the CUs: whole
-// 128-byte lines move far faster than the 64-byte half lines of MFMA
-// fragments loaded straight into registers.  So:
+// (ferrox-core "weight_matrix/lora.rs", module doc; atlas "lora_delta.rs",
+// apply_lora_bgmv doc: the shrink t = A x, then the expand-and-fold).  At
+// decode sizes the cost is reading W once; on this chip a stream of W runs
+// fastest as loads of whole 128-byte lines into registers, all of a
+// workgroup's share requested early.  The layout:
 //
-//  * decode_main_kernel: a workgroup owns a tile of 128 output features
-//    (64 for small projections) x all rows x one k range of at most 512
-//    columns (k is split S ways; S depends on k_in only).  Each 64-column
-//    stage of the tile's W rows and of the batch's x rows goes to LDS by
-//    LDS-DMA, whole lines, stored XOR-swizzled so the MFMA fragment reads
-//    hit distinct banks; a ring of stages keeps 120 KB in flight per CU.
-//    The waves own disjoint (output block, row block) pairs over the whole
-//    range, so they need no reduction; the f32 partial tile goes to the
-//    workspace.  The shrink t = A_q x rides along: a workgroup runs shrink
-//    units (touched slot, 16-rank block) of its k range, each staging A_q's
-//    rows and the slot's x rows the same way, so each A_q is read once per
-//    call; on a full k range the first unit's stages go out mid-stream into
-//    ring slots the W stream has finished with.  Nothing in this launch
-//    waits for another workgroup;
-//  * decode_epilogue_kernel: y = bf16(sum_z partial_z + s_q sum_r B_q[o, r]
-//    t_i[r]), the S partials in split order, t summed over the k ranges in
-//    range order, the rank sum in f32 in rank order, one rounding.
-// With no adapters and no k split the main launch stores y itself.
+//  * workgroup (g, z) owns output tile g (TO = 16 NSW outputs) over k range z
+//    (kKR = 512 columns; S = ceil(k_in / 512) ranges).  Its x rows over the
+//    range go to LDS once (LDS-DMA, whole lines, XOR-swizzled).  Each of its
+//    NSW waves owns a slice of 16 outputs: it requests its 16 W rows x 512
+//    columns (sixteen 16-byte loads per lane, whole lines, through a buffer
+//    resource), then, one 64-column stage at a time as the loads land, lays
+//    the stage out in a wave-private LDS buffer and runs the MFMAs of its 16
+//    outputs against every row block of x.  No block-wide barrier sits in
+//    the stream.
+//  * split-K: every slice's f32 partial [16 outputs x rows] goes to the
+//    workspace through device-coherent stores; contributor z finalizes the
+//    slices z, z + S, ... of its tile once all S contributors of the tile have
+//    stored theirs (a bounded wait on the tile's arrival count; the
+//    contributors of a tile are consecutive workgroups, so in-order dispatch
+//    always runs them together).  Finalizing sums the S partials in range
+//    order, adds s_q B_q t_i in f32 (ranks in order), an adapter stack's
+//    further levels, and rounds y once.
+//  * the shrink: when the pool's units (slot x 16-rank block) fit, the last
+//    waves of the first few tiles' workgroups ("carriers") each take one
+//    unit over their k range besides their W slice: the slot's A rows are
+//    requested between the two halves of the W stream and contracted with
+//    the same x rows in LDS, giving a piece of t for every row (pieces by
+//    pool slot, not by row, so no route is needed to place them).  Carriers
+//    never wait before they count themselves in, and every tile waits for
+//    the carriers' pieces before it finalizes; the carrier workgroups are
+//    the first of the launch and at most 32, so they all run whatever else
+//    is resident.  A larger pool takes a prep launch (k_prep.hip) that
+//    leaves t in the workspace first.
+//
 // Skipped rows (slot < 0 or past the pool, NULL table entry, zero scale) get
-// no delta arithmetic, so they equal the base-only launch bit for bit.
-// Every output element is reduced in an order that does not depend on the
-// batch's other rows or on n_out.
-#include <type_traits>
-
+// no delta arithmetic: their y is the sum of the same partials in the same
+// order as a base-only call's.  Every output element's reduction order is a
+// function of k_in alone (ranges of 512 columns, stages of 64, two 32-column
+// MFMA steps per stage), so it does not depend on n_out, on the batch's other
+// rows or on the routing.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -40,545 +51,510 @@ namespace lora {
 
 namespace {
 
-constexpr int kNW = 8;                               // waves per workgroup
-constexpr int kNS = 6;                               // ring depth: 6 stages of TO + 64 rows
+constexpr int kKR = kDecodeKR;       // columns per k range
+constexpr int kNSt = kKR / 64;       // 64-column stages per range
+// s_waitcnt with only the vector-memory counter constrained: at most n
+// operations still in flight (0 <= n <= 32).
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+#define LORA_W(N) case N: wait_vmcnt<N>(); break;
+    LORA_W(1) LORA_W(2) LORA_W(3) LORA_W(4) LORA_W(5) LORA_W(6) LORA_W(7) LORA_W(8)
+    LORA_W(9) LORA_W(10) LORA_W(11) LORA_W(12) LORA_W(13) LORA_W(14) LORA_W(15) LORA_W(16)
+    LORA_W(17) LORA_W(18) LORA_W(19) LORA_W(20) LORA_W(21) LORA_W(22) LORA_W(23) LORA_W(24)
+    LORA_W(25) LORA_W(26) LORA_W(27) LORA_W(28) LORA_W(29) LORA_W(30) LORA_W(31) LORA_W(32)
+#undef LORA_W
+    default: wait_vmcnt<0>(); break;
+  }
+}
 
-struct Rows {  // the batch's routes, resolved once per workgroup
-  int raw[64];        // seq_slot, as the caller gave it (LDS-DMA)
-  int q[64];          // slot or kSkip
-  const u16 *bq[64];  // the row's B (rows that resolve)
-  float sig[64];      // the row's scale
-  int list[64];       // rows grouped by slot (row order within one)
-  int start[65];      // list offsets per touched slot
-  int slot[64];       // touched slots in order of first appearance
-  const u16 *aq[64];  // the touched slot's A (its table entry, read once)
-  int T;              // touched slots
-  uint32_t ea[2][64], eb[2][64];  // the row's A and B table entries (low, high words; LDS-DMA)
-  float esc[64];                  // the row's scale table entry (LDS-DMA)
+// The wait for a tile's contributors gives up after this many ticks of the
+// 100 MHz real-time counter (0.5 s: only a fault elsewhere gets there), so
+// every wave reaches the end of the kernel.
+constexpr uint64_t kTileWaitTicks = 50000000ull;
+
+// Polls a counter until it reaches `target` or `ticks` pass.  Each poll is
+// a device-scope atomic load, which reads past this XCD's L2.
+__device__ __forceinline__ unsigned poll(unsigned *ctr) {
+  return __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned spin_until(unsigned *ctr, unsigned target, uint64_t ticks) {
+  unsigned v = poll(ctr);
+  if (v < target) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (v < target && __builtin_amdgcn_s_memrealtime() - t0 < ticks) {
+      __builtin_amdgcn_s_sleep(4);
+      v = poll(ctr);
+    }
+  }
+  asm volatile("" ::: "memory");
+  return v;
+}
+
+// The compiler barriers keep every memory access on its side of the atomic:
+// the stores before it have completed (the caller waited for them) and the
+// loads after it depend on what it returned.
+__device__ __forceinline__ unsigned wave_atomic_add(unsigned *p, unsigned v) {
+  unsigned old = 0;
+  asm volatile("" ::: "memory");
+  if ((threadIdx.x & 63) == 0) old = __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = (unsigned)__builtin_amdgcn_readfirstlane((int)old);
+  asm volatile("" ::: "memory");
+  return old;
+}
+__device__ __forceinline__ void wave_store0(unsigned *p) {
+  if ((threadIdx.x & 63) == 0) __hip_atomic_store(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A slice: 16 rows of a row-major matrix (W's outputs, or A's ranks) over
+// the k range [kb, ke), as sixteen whole-line loads per lane: load 2 st + h
+// carries rows 8 h .. 8 h + 7 (lane l: row 8 h + l / 8, 16-byte chunk l % 8)
+// of stage st.  The loads go through a buffer resource over the slice's
+// rows (scalar) with one 32-bit offset per lane and row group; rows past the
+// matrix read its last row instead.
+struct Slice {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t off[2];  // byte offset of this lane's chunk at column kb, rows 8 h + l / 8
 };
-
-// Routes, in three steps that keep their latency off the stream of W:
-// at the start wave 0 sends seq_slot to LDS by LDS-DMA (issued before the
-// first stage, so it has landed once that stage has); once it has, the
-// table entries each row needs go to LDS the same way (five 4-byte DMAs:
-// the halves of A's and B's pointers, the scale), counted by the explicit
-// waits like the stages; later, when they have landed, wave 0 resolves the
-// rows by the rule of resolve_slot and groups them by slot, slots numbered
-// in order of first appearance: one round of ballots per touched slot.
-constexpr int kEnt = 5;  // DMAs of fetch_entries
-
-__device__ __forceinline__ void fetch_slots(const DecodeArgs &p, Rows &s) {
+__device__ __forceinline__ Slice make_slice(const u16 *base, int row_stride, int row0, int rows, int kb) {
   const int lane = threadIdx.x & 63;
-  if (threadIdx.x < 64 && p.has_lora)
-    dma4(p.seq_slot + min(lane, p.n - 1), lds_addr(&s.raw[0]));
-}
-
-__device__ __forceinline__ bool row_in_pool(const DecodeArgs &p, const Rows &s, int lane, int *slot) {
-  *slot = lane < p.n ? s.raw[lane] : -1;
-  return *slot >= 0 && *slot < p.rd.max_loras;
-}
-
-// Wave 0, once seq_slot has landed.  Every lane issues all five DMAs (a row
-// that does not index the pool reads its seq_slot word again), so the count
-// in flight is the same for every wave 0.
-__device__ __forceinline__ void fetch_entries(const DecodeArgs &p, Rows &s) {
-  const int lane = threadIdx.x & 63;
-  int slot;
-  const bool in = row_in_pool(p, s, lane, &slot);
-  const uint32_t *dummy = (const uint32_t *)(p.seq_slot + min(lane, p.n - 1));
-  const uint32_t *pa = in ? (const uint32_t *)(p.rd.a_table + slot) : dummy;
-  const uint32_t *pb = in ? (const uint32_t *)(p.rd.b_table + slot) : dummy;
-  dma4(pa, lds_addr(&s.ea[0][0]));
-  dma4(in ? pa + 1 : dummy, lds_addr(&s.ea[1][0]));
-  dma4(pb, lds_addr(&s.eb[0][0]));
-  dma4(in ? pb + 1 : dummy, lds_addr(&s.eb[1][0]));
-  dma4(in ? (const uint32_t *)(p.rd.scale_table + slot) : dummy, lds_addr(&s.esc[0]));
-}
-
-// Wave 0, once the entries have landed.
-__device__ void resolve_rows(const DecodeArgs &p, Rows &s) {
-  const int lane = threadIdx.x & 63;
-  if (threadIdx.x >= 64) return;
-  int slot;
-  const bool in = row_in_pool(p, s, lane, &slot);
-  const uint64_t a = in ? ((uint64_t)s.ea[1][lane] << 32) | s.ea[0][lane] : 0;
-  const uint64_t b = in ? ((uint64_t)s.eb[1][lane] << 32) | s.eb[0][lane] : 0;
-  const float sc = in ? s.esc[lane] : 0.f;
-  const int q = in && a != 0 && b != 0 && sc != 0.f ? slot : kSkip;
-  s.q[lane] = q;
-  s.bq[lane] = q >= 0 ? (const u16 *)b : nullptr;
-  s.sig[lane] = q >= 0 ? sc : 0.f;
-  const uint64_t below = (1ull << lane) - 1ull;
-  uint64_t todo = __ballot(q >= 0);
-  int T = 0, pos = 0;
-  while (todo) {  // uniform: the lowest row not yet grouped names the next slot
-    const int first = __ffsll((unsigned long long)todo) - 1;
-    const int v = __builtin_amdgcn_readlane(q, first);
-    const uint64_t av = ((uint64_t)__builtin_amdgcn_readlane((int)(a >> 32), first) << 32) |
-                        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a, first);
-    const uint64_t m = __ballot(q == v);
-    if (q == v) s.list[pos + __popcll(m & below)] = lane;
-    if (lane == 0) {
-      s.slot[T] = v;
-      s.aq[T] = (const u16 *)av;
-      s.start[T] = pos;
-    }
-    pos += __popcll(m);
-    ++T;
-    todo &= ~m;
-  }
-  if (lane == 0) {
-    s.T = T;
-    s.start[T] = pos;
-  }
-}
-
-// Zeroes, after its stage has landed, each 16-byte chunk this lane fetched
-// from past the k range (it fetched column 0 of its row instead).
-__device__ __forceinline__ void zero_past(uint4 *slot, int k0, int ke, int chunk) {
-  if (k0 + chunk >= ke) *slot = z4();
-}
-
-// One shrink unit (touched slot u, rank block rb) of this workgroup's k
-// range: the range's partial of t for the rows of slot u, ranks 16 rb .. +15.
-// The range's stages of A_u's 16 rows and of the slot's x rows (gathered, up
-// to 64, in groups of 16) go to LDS in one go; wave g then takes row group g
-// through every stage.
-__device__ __forceinline__ int unit_groups(const Rows &s, int R, int uidx) {
-  const int u = uidx / (R / 16);
-  return (s.start[u + 1] - s.start[u] + 15) / 16;  // groups of 16 gathered rows (<= 4)
-}
-
-// LDS bytes a unit of G row groups stages over ns 64-column stages.
-__device__ __forceinline__ int unit_bytes(int G, int ns) { return ns * (16 + 16 * G) * 128; }
-
-// Issues the unit's DMAs: wave w takes instructions w, w + 8, ...
-__device__ void unit_issue(const DecodeArgs &p, const Rows &s, int uidx, int k0, int k1, uint4 *lds) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int R = p.R, RB = R / 16;
-  const int rb = uidx % RB, u = uidx / RB;
-  const u16 *A = s.aq[u];
-  const int m = s.start[u + 1] - s.start[u];
-  const int G = (m + 15) / 16;
-  const int ns = (k1 - k0 + 63) / 64;
-  const int RU = 16 + 16 * G;   // rows of a unit stage: A's 16, then the x rows
-  const int per = RU / 8;       // DMA instructions per unit stage
-  for (int ii = wave; ii < ns * per; ii += kNW) {
-    const int st = ii / per, k8 = ii % per;
-    const int rr = k8 * 8 + (lane >> 3);  // row of the unit stage
-    const u16 *rowp;
-    if (rr < 16) {
-      rowp = A + (size_t)(rb * 16 + rr) * p.k_in;
-    } else {
-      const int j = min(rr - 16, m - 1);
-      rowp = p.x + (size_t)s.list[s.start[u] + j] * p.x_row_stride;
-    }
-    const int kk = k0 + st * 64 + ((lane & 7) ^ ((rr >> 1) & 7)) * 8;
-    dma16(rowp + (kk < k1 ? kk : k0), lds_addr(lds + (st * RU + k8 * 8) * 8));
-  }
-}
-
-// Zeroes what the unit fetched past the k range; then the unit's MFMAs (wave
-// g takes row group g) and its partial of t.  The unit's stages have landed
-// for every wave before this is called.
-__device__ void unit_compute(const DecodeArgs &p, const Rows &s, int uidx, int k0, int k1, uint4 *lds) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int R = p.R, RB = R / 16;
-  const int rb = uidx % RB, u = uidx / RB;
-  const int c = blockIdx.x % p.S;  // the k range: the partial's index
-  const int m = s.start[u + 1] - s.start[u];
-  const int G = (m + 15) / 16;
-  const int ns = (k1 - k0 + 63) / 64;
-  const int RU = 16 + 16 * G;
-  const int per = RU / 8;
-  if (k0 + ns * 64 > k1) {  // the last stage runs past the chunk
-    for (int ii = wave; ii < ns * per; ii += kNW) {
-      const int st = ii / per, k8 = ii % per;
-      const int rr = k8 * 8 + (lane >> 3);
-      zero_past(lds + (st * RU + k8 * 8) * 8 + lane, k0 + st * 64, k1, ((lane & 7) ^ ((rr >> 1) & 7)) * 8);
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    __syncthreads();
-  }
-  if (wave < G) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int ra = lane & 15, rx = 16 + wave * 16 + (lane & 15);
-    for (int st = 0; st < ns; ++st) {
-      const uint4 *sl = lds + st * RU * 8;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int ch = 4 * h + (lane >> 4);
-        acc = mfma16(sl[ra * 8 + (ch ^ ((ra >> 1) & 7))], sl[rx * 8 + (ch ^ ((rx >> 1) & 7))], acc);
-      }
-    }
-    // D: ranks 4 (l/16) .. +3 of gathered row 16 g + l%16
-    const int j = wave * 16 + (lane & 15);
-    if (j < m) {
-      const int row = s.list[s.start[u] + j];
-      *(f32x4 *)(p.t_part + ((size_t)c * p.n + row) * R + rb * 16 + (lane >> 4) * 4) = acc;
-    }
-  }
-}
-
-__device__ void shrink_unit(const DecodeArgs &p, const Rows &s, int uidx, int k0, int k1, uint4 *lds) {
-  unit_issue(p, s, uidx, k0, k1, lds);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  unit_compute(p, s, uidx, k0, k1, lds);
-  __syncthreads();  // the ring is reused by the next unit
-}
-
-}  // namespace
-
-// NB: 16-row blocks of the batch that hold rows (n <= 16 NB); TO: output
-// features per tile.  Wave w owns
-// output blocks OBW (w % OWAVES) .. +OBW-1 and row blocks RBW (w / OWAVES) ..
-template <int NB, int TO>
-__global__ __launch_bounds__(kNW * 64) void decode_main_kernel(DecodeArgs p) {
-  constexpr int kTO = TO;
-  constexpr int kRS = kTO + kDecodeMaxRows;  // rows of a stage: W rows, then x rows
-  constexpr int kLPW = kRS / 8 / kNW;        // DMA instructions per wave per stage
-  static_assert(kLPW * 8 * kNW == kRS, "stage rows must split evenly over the waves");
-  constexpr int RWAVES = NB >= 2 ? 2 : 1;  // waves across the row blocks
-  constexpr int OWAVES = kNW / RWAVES;     // waves across the output blocks
-  constexpr int OBW = kTO / 16 / OWAVES;   // output blocks per wave
-  constexpr int RBW = NB / RWAVES;         // row blocks per wave
-  static_assert(OWAVES * OBW * 16 == kTO && RWAVES * RBW == NB, "wave tiling");
-  __shared__ __attribute__((aligned(16))) uint4 ring[kNS][kRS * 8];
-  __shared__ Rows s;
-
-  // every argument the first DMAs need comes in with the first batch of
-  // scalar loads (the route pointer too, which the compiler would otherwise
-  // load behind a branch, one more round trip before the first stage)
-  asm volatile("" ::"s"(p.seq_slot), "s"(p.has_lora));
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = p.k_in;
-  const int tl = blockIdx.x / p.S, z = blockIdx.x % p.S;
-  const int o0 = tl * kTO;
-  const int kb = min(z * p.k_per_split, K), ke = min(kb + p.k_per_split, K);
-  const int nstage = (ke - kb + 63) / 64;
-  // Each DMA instruction moves 8 whole 128-byte row segments: lane l takes
-  // row 8i + l/8 of the stage and the chunk that belongs at slot l%8 of it.
-  // Rows past n_out or past the batch read a valid row instead; their
-  // outputs are never stored.
-  const u16 *src[kLPW];
-  int sch[kLPW];
-#pragma unroll
-  for (int j = 0; j < kLPW; ++j) {
-    const int rr = (wave + kNW * j) * 8 + (lane >> 3);
-    src[j] = rr < kTO ? p.W + (size_t)min(o0 + rr, p.n_out - 1) * p.w_row_stride
-                      : p.x + (size_t)min(rr - kTO, p.n - 1) * p.x_row_stride;
-    sch[j] = ((lane & 7) ^ ((rr >> 1) & 7)) * 8;
-  }
-  auto issue = [&](int st) {
-    const int k0 = kb + st * 64;
-#pragma unroll
-    for (int j = 0; j < kLPW; ++j) {
-      const int kk = k0 + sch[j] < ke ? k0 + sch[j] : kb;
-      dma16(src[j] + kk, lds_addr(&ring[st % kNS][(wave + kNW * j) * 64]));
-    }
-  };
-  fetch_slots(p, s);
-  const int npro = min(kNS - 1, nstage);  // stages issued before the loop
-  for (int st = 0; st < npro; ++st) issue(st);
-  // wave 0: once seq_slot has landed (older than every stage), the table
-  // entries go out; they are younger than the first npro stages, so wave 0
-  // allows for them (kEnt more operations in flight) when it waits for those
-  const bool ents = p.has_lora && wave == 0;
-  if (ents) {
-    wait_stages<kLPW, kNS - 1>(npro);
-    fetch_entries(p, s);
-  }
-
-  const int ob0 = (wave % OWAVES) * OBW, rb0 = (wave / OWAVES) * RBW;
-  f32x4 acc[OBW][RBW];
-#pragma unroll
-  for (int a = 0; a < OBW; ++a)
-#pragma unroll
-    for (int b = 0; b < RBW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // On a full k range the routes are resolved at stage kEarly, once the table
-  // entries are sure to have landed (they went out before stage kEarly), and
-  // this workgroup's first shrink unit sends its stages into the ring slots
-  // of stages 2 .. 4, which no later stage takes; its MFMAs then run right
-  // after the loop instead of behind a round trip of their own.  Each wave
-  // issues exactly xw of those DMAs, which the later stage waits allow for.
-  constexpr int kEarly = kNS - 1;
-  static_assert(kEarly + 1 < kDecodeMaxStages && kDecodeMaxStages - kNS == 2, "free slots 2 .. kEarly - 1");
-  const bool early_ok = p.has_lora && nstage == kDecodeMaxStages && ke - kb == 64 * kDecodeMaxStages;
-  bool early = false;
-  // one stage: wait until it has landed (at most kNS - 2 younger stages, and
-  // X more operations issued after them, in flight), zero what lies past the
-  // k range, `mid` before the barrier, the barrier, refill the ring, `post`,
-  // then the stage's fragments and MFMAs
-  auto stage = [&](int st, auto xc, auto mid, auto post) {
-    constexpr int X = decltype(xc)::value;
-    const int younger = min(kNS - 2, nstage - 1 - st);
-    if (ents && st < npro)
-      wait_stages<kLPW, kNS - 2, kEnt>(younger);
-    else
-      wait_stages<kLPW, kNS - 2, X>(younger);
-    if (kb + st * 64 + 64 > ke) {
-#pragma unroll
-      for (int j = 0; j < kLPW; ++j)
-        zero_past(&ring[st % kNS][(wave + kNW * j) * 64 + lane], kb + st * 64, ke, sch[j]);
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    }
-    mid();
-    block_barrier();
-    // every wave is done with stage st - 1: its slot takes stage st + kNS - 1
-    if (st + kNS - 1 < nstage) issue(st + kNS - 1);
-    post();
-    const uint4 *sl = ring[st % kNS];
-    uint4 af[2][OBW], bf[2][RBW];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = 4 * h + (lane >> 4);
-#pragma unroll
-      for (int a = 0; a < OBW; ++a) {
-        const int r = (ob0 + a) * 16 + (lane & 15);
-        af[h][a] = sl[r * 8 + (c ^ ((r >> 1) & 7))];
-      }
-#pragma unroll
-      for (int b = 0; b < RBW; ++b) {
-        const int r = kTO + (rb0 + b) * 16 + (lane & 15);
-        bf[h][b] = sl[r * 8 + (c ^ ((r >> 1) & 7))];
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int a = 0; a < OBW; ++a)
-#pragma unroll
-        for (int b = 0; b < RBW; ++b) acc[a][b] = mfma16(af[h][a], bf[h][b], acc[a][b]);
-  };
-  using X0 = std::integral_constant<int, 0>;
-  auto none = [] {};
-  const int st1 = early_ok ? kEarly : nstage;
-  for (int st = 0; st < st1; ++st) stage(st, X0{}, none, none);
-  int xw = 0;
-  if (early_ok) {
-    stage(kEarly, X0{},
-          [&] {
-            if (wave == 0) {  // its LDS writes land before the barrier
-              resolve_rows(p, s);
-              __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-            }
-          },
-          [&] {
-            if (tl < s.T * (p.R / 16)) {
-              const int G = unit_groups(s, p.R, tl);
-              if (unit_bytes(G, kDecodeMaxStages) <= 3 * (int)sizeof(ring[0])) {
-                unit_issue(p, s, tl, kb, ke, &ring[2][0]);
-                xw = 2 + 2 * G;  // (16 + 16 G) / 8 instructions per unit stage, 8 stages over 8 waves
-                early = true;
-              }
-            }
-          });
-    for (int st = kEarly + 1; st < nstage; ++st) {
-      if (xw == 0) stage(st, X0{}, none, none);
-      else if (xw == 4) stage(st, std::integral_constant<int, 4>{}, none, none);
-      else if (xw == 6) stage(st, std::integral_constant<int, 6>{}, none, none);
-      else stage(st, std::integral_constant<int, 8>{}, none, none);
-    }
-  }
-
-  // the routes first (the table entries arrived long ago; no store is
-  // outstanding yet that the wait for them would include)
-  if (p.has_lora && !early_ok) {
-    if (wave == 0) __builtin_amdgcn_s_waitcnt(0);  // the entries (the last stage's wait may allow them)
-    resolve_rows(p, s);
-  }
-  if (early) {  // the early unit: only its DMAs are in flight
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    unit_compute(p, s, tl, kb, ke, &ring[2][0]);
-  }
-  // D layout: column (row) l%16 of the row block, outputs 4 (l/16) .. +3 of
-  // the output block
-  const bool direct = p.S == 1 && !p.has_lora;  // nothing left for an epilogue: store y now
-  float *part = p.partials + ((size_t)tl * p.S + z) * (kDecodeMaxRows * kTO);
-#pragma unroll
-  for (int a = 0; a < OBW; ++a)
-#pragma unroll
-    for (int b = 0; b < RBW; ++b) {
-      const int i = (rb0 + b) * 16 + (lane & 15), oo = (ob0 + a) * 16 + (lane >> 4) * 4;
-      if (i >= p.n) continue;
-      const f32x4 v = acc[a][b];
-      if (direct) {
-        if (o0 + oo < p.n_out)
-          *(uint2 *)(p.y + (size_t)i * p.y_row_stride + o0 + oo) =
-              make_uint2(pack2(f2bf(v[0]), f2bf(v[1])), pack2(f2bf(v[2]), f2bf(v[3])));
-      } else {
-        *(f32x4 *)(part + i * kTO + oo) = v;
-      }
-    }
-  if (!p.has_lora) return;
-  __syncthreads();  // the routes are resolved and the ring is free
-  if (blockIdx.x == 0 && tid < 64) {  // the epilogue's per-row routes
-    p.row_q[tid] = s.q[tid];
-    p.row_sig[tid] = s.sig[tid];
-    p.row_b[tid] = s.bq[tid];
-  }
-  const int units = s.T * (p.R / 16);  // of this k range
-  for (int uidx = tl + (early ? p.n_tiles : 0); uidx < units; uidx += p.n_tiles)
-    shrink_unit(p, s, uidx, kb, ke, &ring[0][0]);
-}
-
-// y for 16 rows x 64 output features per workgroup, one thread per (row,
-// four features): t is then needed for 16 rows only.  Every load that does
-// not depend on another goes out first: the row's route, the S partials, t.
-constexpr int kEpiOut = 64;  // output features per epilogue workgroup
-__global__ __launch_bounds__(256) void decode_epilogue_kernel(DecodeArgs p, StackFold f) {
-  __shared__ __attribute__((aligned(16))) float st[16 * 256];  // t of the 16 rows, 16 x R
-  const int tid = threadIdx.x;
-  const int R = p.R;
-  const int kTO = p.tile_out;
-  const int OPT = kTO / kEpiOut;  // output groups per tile
-  const int rg = blockIdx.x % 4, og = blockIdx.x / 4;  // row group, output group
-  const int tl = og / OPT;
-  const int i = rg * 16 + (tid >> 4), oo = (og % OPT) * kEpiOut + (tid & 15) * 4, o = tl * kTO + oo;
-  if (rg * 16 >= p.n) return;  // no rows in this group
-  const bool live = i < p.n && o < p.n_out;
-  const bool lora = p.has_lora;
-  // the row's route: slot, B and scale load together
-  const int q = live && lora ? p.row_q[i] : kSkip;
-  const u16 *rb_ = live && lora ? p.row_b[i] : nullptr;
-  const float sig = live && lora ? p.row_sig[i] : 0.f;
-  f32x4 a[kDecodeMaxSplit];
-  const float *pp = p.partials + (size_t)tl * p.S * (kDecodeMaxRows * kTO) + i * kTO + oo;
-#pragma unroll
-  for (int z = 0; z < kDecodeMaxSplit; ++z)
-    a[z] = live && z < p.S ? *(const f32x4 *)(pp + (size_t)z * (kDecodeMaxRows * kTO)) : f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nr = min(16, p.n - rg * 16);  // rows of this group
-  if (lora)  // stage t of the group's rows in LDS: the k ranges' partials summed in range order
-    for (int e = tid * 4; e < nr * R; e += 256 * 4) {
-      const float *tp = p.t_part + (size_t)rg * 16 * R + e;
-      f32x4 w[kDecodeMaxSplit];
-#pragma unroll
-      for (int c = 0; c < kDecodeMaxSplit; ++c)
-        w[c] = c < p.n_chunks ? *(const f32x4 *)(tp + (size_t)c * p.n * R) : f32x4{0.f, 0.f, 0.f, 0.f};
-      f32x4 v = w[0];
-#pragma unroll
-      for (int c = 1; c < kDecodeMaxSplit; ++c)
-        if (c < p.n_chunks) v += w[c];
-      *(f32x4 *)(st + e) = v;
-    }
-  const u16 *Bq = q >= 0 ? rb_ + (size_t)o * R : nullptr;
-  uint4 b[2][4];  // ranks 0..15 of the thread's four B rows
+  Slice sl;
+  // every argument is uniform over the wave; readfirstlane lets the compiler
+  // see that, so the resource lives in scalar registers (a per-lane resource
+  // would turn every load into a loop over the distinct values)
+  const uint64_t b64 = (uint64_t)(uintptr_t)(base + (size_t)__builtin_amdgcn_readfirstlane(row0) * row_stride);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b64), hi = __builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32));
+  sl.rs = __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)(((uint64_t)hi << 32) | lo), 0, 0x7ffffff0, 0x00020000);
+  const int last = rows - 1 - row0;
 #pragma unroll
   for (int h = 0; h < 2; ++h)
+    sl.off[h] = (uint32_t)((min(8 * h + (lane >> 3), last) * row_stride + kb + (lane & 7) * 8) * 2);
+  return sl;
+}
+__device__ __forceinline__ uint4 buf_ld16(const __amdgpu_buffer_rsrc_t &rs, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+}
+// A whole range (512 columns): stages [ST0, ST1), the stage step in the
+// instruction's immediate offset.
+template <int ST0, int ST1>
+__device__ __forceinline__ void issue_full(const Slice &sl, uint4 (&v)[2 * kNSt]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[h][j] = Bq && h * 8 < R ? ldg16(Bq + (size_t)j * R + h * 8) : z4();
-  __syncthreads();
-  if (!live) return;
-  f32x4 v = a[0];
+  for (int st = ST0; st < ST1; ++st)
 #pragma unroll
-  for (int z = 1; z < kDecodeMaxSplit; ++z)  // split order
-    if (z < p.S) v += a[z];
-  if (q >= 0) {
-    const float *ti = st + (i - rg * 16) * R;
-    float d[4] = {0.f, 0.f, 0.f, 0.f};
-    auto fma8 = [&](const uint4 *bb, int r0) {
-      float tr[8];
+    for (int h = 0; h < 2; ++h) v[2 * st + h] = buf_ld16(sl.rs, sl.off[h] + st * 128);
+}
+// The last, shorter range: its nst stages; a chunk past ke reads column kb
+// and is zeroed once it lands.
+__device__ __forceinline__ void issue_part(const Slice &sl, int kb, int ke, int nst, uint4 (&v)[2 * kNSt]) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) tr[c] = ti[r0 + c];
+  for (int st = 0; st < kNSt; ++st) {
+    if (st < nst) {
+      const bool past = kb + st * 64 + (lane & 7) * 8 >= ke;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w[4] = {bb[j].x, bb[j].y, bb[j].z, bb[j].w};
+      for (int h = 0; h < 2; ++h)
+        v[2 * st + h] = buf_ld16(sl.rs, past ? sl.off[h] - (lane & 7) * 16 : sl.off[h] + st * 128);
+    }
+  }
+}
+
+// The MFMAs of a slice against the x rows in LDS, stage by stage as its
+// loads land (`extra` more vector-memory operations issued after all of
+// them, `mid` more between the first and the second half of a whole range).
+// acc[b] = D[16 slice rows][16 x rows of row block b]: lane l holds slice
+// rows 4 (l / 16) .. +3 of x row 16 b + l % 16.
+template <int NB, bool FULL>
+__device__ __forceinline__ void slice_mma(uint4 (&v)[2 * kNSt], const uint4 *xs, uint4 *wb, int kb, int ke, int nst,
+                                          f32x4 (&acc)[NB], int extra = 0, int mid = 0) {
+  const int lane = threadIdx.x & 63;
+  constexpr int XR = 16 * NB;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          d[j] += bf2f((u16)(w[c] & 0xffffu)) * tr[2 * c];
-          d[j] += bf2f((u16)(w[c] >> 16)) * tr[2 * c + 1];
+  for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < kNSt; ++st) {
+    if (FULL || st < nst) {
+      if (FULL) {  // a constant once the loop is unrolled, plus the operations issued after
+        wait_vm(2 * (kNSt - 1 - st) + extra + (st < kNSt / 2 ? mid : 0));
+      } else {
+        wait_vm(2 * (nst - 1 - st) + extra);
+        if (kb + st * 64 + (lane & 7) * 8 >= ke) v[2 * st] = v[2 * st + 1] = z4();
+      }
+      uint4 *buf = wb + (st & 1) * 128;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 8 * h + (lane >> 3);
+        buf[r * 8 + ((lane & 7) ^ ((r >> 1) & 7))] = v[2 * st + h];
+      }
+      const uint4 *xst = xs + st * XR * 8;
+      uint4 af[2], xf[2][NB];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = 4 * h + (lane >> 4);
+        const int r = lane & 15;
+        af[h] = buf[r * 8 + (c ^ ((r >> 1) & 7))];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int rx = 16 * b + (lane & 15);
+          xf[h][b] = xst[rx * 8 + (c ^ ((rx >> 1) & 7))];
         }
       }
-    };
-    fma8(b[0], 0);
-    if (R > 8) fma8(b[1], 8);
-    for (int r0 = 16; r0 < R; r0 += 8) {  // ranks past 16, in order
-      uint4 bb[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bb[j] = ldg16(Bq + (size_t)j * R + r0);
-      fma8(bb, r0);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b] = mfma16(af[h], xf[h][b], acc[b]);
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = v[j] + sig * d[j];
   }
-  // an adapter stack's further levels, in level order, from their final t:
-  // every level's slot, then its table entries, go out together, so the
-  // levels cost one chain of round trips, not one each
-  if (f.n_levels > 0) {
-    int sl[kMaxStackLevels];
+}
+
+__device__ __forceinline__ float *slice_partial(const DecodeArgs &p, int g, int z, int j) {
+  return p.partials + ((size_t)(g * p.S + z) * kDecodeSlices + j) * kDecodeSliceFloats;
+}
+
+// A row's route by the rule of every entry point: slot in the pool, both
+// table entries non-NULL, scale non-zero; otherwise *bq = NULL.
+struct RowRoute {
+  const u16 *bq;
+  float sig;
+  int slot;
+};
+__device__ __forceinline__ RowRoute row_route_decode(const DecodeArgs &p, int i) {
+  RowRoute r{nullptr, 0.f, kSkip};
+  const int slot = p.has_lora && i < p.n ? p.seq_slot[i] : -1;
+  const bool in = slot >= 0 && slot < p.rd.max_loras;
+  const void *a = in ? p.rd.a_table[slot] : nullptr;
+  const void *b = in ? p.rd.b_table[slot] : nullptr;
+  const float sc = in ? p.rd.scale_table[slot] : 0.f;
+  if (a != nullptr && b != nullptr && sc != 0.0f) {
+    r.bq = (const u16 *)b;
+    r.sig = sc;
+    r.slot = slot;
+  }
+  return r;
+}
+
+// A table entry read through the scalar cache: the vector memory path of a
+// CU is queued behind its share of W, the scalar one is not.  `idx` is
+// uniform over the wave; the read goes through the constant address space,
+// so the compiler issues it as a scalar load and waits for it where the
+// value is first used.
+__device__ __forceinline__ uint64_t scalar_entry(const void *const *tab, int idx) {
+  const __attribute__((address_space(4))) uint64_t *t =
+      (const __attribute__((address_space(4))) uint64_t *)(uintptr_t)tab;
+  return t[__builtin_amdgcn_readfirstlane(idx)];
+}
+
+// One finalization item, by one wave: slice j of tile g, row block b.  Every
+// contributor's partial (and, with the shrink in this launch, every piece
+// of t) has been stored; rr is the route of this lane's row.  Every load the
+// item needs goes out before any arithmetic: the S partials, then t (from
+// the pieces of the row's slot, or as a prep launch left it), then B.
+__device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFold &f, const RowRoute &rr, int g, int j,
+                                              int b, float *tb) {
+  const int lane = threadIdx.x & 63;
+  const int i = 16 * b + (lane & 15);
+  const int ic = min(i, p.n - 1);
+  const int o = g * p.tile_out + 16 * j + 4 * (lane >> 4);
+  const bool routed = rr.bq != nullptr;
+  const int R = p.R;
+  // the S partials in range order, eight in flight at a time
+  constexpr int kG = 8;
+  f32x4 part[kG];
+  auto load_parts = [&](int z0) {
 #pragma unroll
-    for (int l = 0; l < kMaxStackLevels; ++l) sl[l] = l < f.n_levels ? f.lv[l].seq_slot[i] : -1;
-    const u16 *bl[kMaxStackLevels];
-    float sc[kMaxStackLevels];
+    for (int zz = 0; zz < kG; ++zz)
+      part[zz] = z0 + zz < p.S ? ld16_coherent(coherent_rsrc(slice_partial(p, g, z0 + zz, j), kDecodeSliceFloats * 4),
+                                               (uint32_t)(b * 64 + lane) * 16, 0)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  load_parts(0);
+  const bool any = __ballot(routed && i < p.n) != 0;
+  // t of row i, ranks 4 (l / 16) .. +3 of every 16-rank block, from the
+  // pieces of its slot's units: the S ranges summed in range order; the
+  // row's four lanes meet in tb
+  if (p.unit_tiles > 0 && any) {
+    const int P = p.rd.max_loras;
+    const auto tall = coherent_rsrc(p.t_part, (uint32_t)((size_t)p.S * P * p.n * R * 4));
+    const int q = routed ? rr.slot : 0;
+    for (int rb = 0; rb < R / 16; ++rb) {
+      const uint32_t off = (uint32_t)((q * p.n + ic) * R + rb * 16 + 4 * (lane >> 4)) * 4;
+      f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int z0 = 0; z0 < p.S; z0 += 8) {
+        f32x4 pz[8];
 #pragma unroll
-    for (int l = 0; l < kMaxStackLevels; ++l) {
-      const StackLevel &L = f.lv[l];
-      const bool in = l < f.n_levels && sl[l] >= 0 && sl[l] < L.max_loras;
-      const void *ta = in ? L.a_table[sl[l]] : nullptr;
-      const void *tb = in ? L.b_table[sl[l]] : nullptr;
-      const float s = in ? L.scale_table[sl[l]] : 0.f;
-      const bool ok = ta != nullptr && tb != nullptr && s != 0.0f;
-      bl[l] = ok ? (const u16 *)tb + (size_t)o * L.R : nullptr;
-      sc[l] = s;
+        for (int zz = 0; zz < 8; ++zz)
+          pz[zz] = z0 + zz < p.S ? ld16_coherent(tall, off, (uint32_t)((z0 + zz) * P * p.n * R) * 4)
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int zz = 0; zz < 8; ++zz)
+          if (z0 + zz < p.S) sum = z0 + zz == 0 ? pz[zz] : sum + pz[zz];
+      }
+      *(f32x4 *)(tb + (lane & 15) * R + rb * 16 + 4 * (lane >> 4)) = sum;
     }
+  }
+  if (i >= p.n || o >= p.n_out) return;
+  float d[4] = {0.f, 0.f, 0.f, 0.f};
+  if (routed) {  // B_q[o .. o+3] t_i, ranks in order, 8 at a time
+    const u16 *bq = rr.bq + (size_t)o * R;
+    const float *ti = p.unit_tiles > 0 ? tb + (lane & 15) * R : p.t + (size_t)i * R;
+    for (int r0 = 0; r0 < R; r0 += 16) {  // 16 ranks: every B load of the step in flight together
+      uint4 bb[4][2];
 #pragma unroll
-    for (int l = 0; l < kMaxStackLevels; ++l) {
-      if (bl[l] == nullptr) continue;
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) bb[c][h] = ldg16(bq + (size_t)c * R + r0 + 8 * h);
+      float tr[16];
+#pragma unroll
+      for (int e = 0; e < 16; e += 4) {
+        const f32x4 t4 = *(const f32x4 *)(ti + r0 + e);
+        tr[e] = t4[0];
+        tr[e + 1] = t4[1];
+        tr[e + 2] = t4[2];
+        tr[e + 3] = t4[3];
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t w[4] = {bb[c][h].x, bb[c][h].y, bb[c][h].z, bb[c][h].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            d[c] += bf2f((u16)(w[e] & 0xffffu)) * tr[8 * h + 2 * e];
+            d[c] += bf2f((u16)(w[e] >> 16)) * tr[8 * h + 2 * e + 1];
+          }
+        }
+    }
+  }
+  f32x4 v = part[0];
+#pragma unroll
+  for (int zz = 1; zz < kG; ++zz)
+    if (zz < p.S) v += part[zz];
+  for (int z0 = kG; z0 < p.S; z0 += kG) {  // k_in past 4096: more ranges, in order
+    load_parts(z0);
+#pragma unroll
+    for (int zz = 0; zz < kG; ++zz)
+      if (z0 + zz < p.S) v += part[zz];
+  }
+  if (routed) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = v[c] + rr.sig * d[c];
+  }
+  // an adapter stack's further levels, in level order, from their final t
+  if (f.n_levels > 0 && p.has_lora) {
+    for (int l = 0; l < f.n_levels; ++l) {
       const StackLevel &L = f.lv[l];
+      const int sl = L.seq_slot[i];
+      const bool in = sl >= 0 && sl < L.max_loras;
+      const void *ta = in ? L.a_table[sl] : nullptr;
+      const void *tb2 = in ? L.b_table[sl] : nullptr;
+      const float sc = in ? L.scale_table[sl] : 0.f;
+      if (ta == nullptr || tb2 == nullptr || sc == 0.0f) continue;
+      const u16 *bl = (const u16 *)tb2 + (size_t)o * L.R;
       const float *tl = L.t + (size_t)i * L.R;
-      float d[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int r0 = 0; r0 < L.R; r0 += 8) {  // ranks in order, 8 at a time
+      float e4[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int r0 = 0; r0 < L.R; r0 += 8) {
         float tr[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) tr[c] = tl[r0 + c];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint4 bb = ldg16(bl[l] + (size_t)j * L.R + r0);
+        for (int c = 0; c < 4; ++c) {
+          const uint4 bb = ldg16(bl + (size_t)c * L.R + r0);
           const uint32_t w[4] = {bb.x, bb.y, bb.z, bb.w};
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            d[j] += bf2f((u16)(w[c] & 0xffffu)) * tr[2 * c];
-            d[j] += bf2f((u16)(w[c] >> 16)) * tr[2 * c + 1];
+          for (int e = 0; e < 4; ++e) {
+            e4[c] += bf2f((u16)(w[e] & 0xffffu)) * tr[2 * e];
+            e4[c] += bf2f((u16)(w[e] >> 16)) * tr[2 * e + 1];
           }
         }
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = v[j] + sc[l] * d[j];
+      for (int c = 0; c < 4; ++c) v[c] = v[c] + sc * e4[c];
     }
   }
   *(uint2 *)(p.y + (size_t)i * p.y_row_stride + o) =
       make_uint2(pack2(f2bf(v[0]), f2bf(v[1])), pack2(f2bf(v[2]), f2bf(v[3])));
 }
 
-hipError_t launch_decode_main(const DecodeArgs &a, hipStream_t st) {
+}  // namespace
+
+// NB: 16-row blocks of the batch (n <= 16 NB); NSW: waves, one slice of 16
+// outputs each (TO = 16 NSW outputs per tile).
+template <int NB, int NSW>
+__global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFold f) {
+  constexpr int XR = 16 * NB;
+  constexpr int NSL = NSW;      // slices per tile
+  constexpr int NC = decode_carriers(NSW);  // shrink carriers per workgroup: its last NC waves
+  __shared__ __attribute__((aligned(16))) uint4 xs[kNSt * XR * 8];
+  __shared__ __attribute__((aligned(16))) uint4 wb[NSW][2 * 128];
+  __shared__ int s_done, s_cdone, s_ready;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = blockIdx.x / p.S, z = blockIdx.x % p.S;
+  const int kb = z * kKR, ke = min(kb + kKR, p.k_in);
+  const int nst = (ke - kb + 63) / 64;
+  const int o0 = g * p.tile_out;
+  const bool full = ke - kb == kKR;  // eight whole stages
+  const int RB = p.R / 16;
+  uint4 v[2 * kNSt];
+  const Slice wsl = make_slice(p.W, p.w_row_stride, o0 + 16 * wave, p.n_out, kb);
+
+  // x rows over the range: stages st = wave, wave + NSW, ... (2 NB DMAs each)
+  for (int st = wave; st < nst; st += NSW) {
+#pragma unroll
+    for (int i = 0; i < 2 * NB; ++i) {
+      const int r = 8 * i + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      const int k = kb + st * 64 + c * 8;
+      dma16(p.x + (size_t)min(r, p.n - 1) * p.x_row_stride + (k < ke ? k : kb), lds_addr(&xs[(st * XR + 8 * i) * 8]));
+    }
+  }
+  if (tid == 0) {
+    s_done = 0;
+    s_cdone = 0;
+    s_ready = 0;
+  }
+  // The shrink rides this launch on the last NC waves of the first
+  // unit_tiles tiles: carrier c of tile g takes unit k = g NC + c, rank
+  // block k % RB of pool slot k / RB, for every row (the rows of other slots
+  // are simply not read back).  Its A rows, found through a scalar read of
+  // the table, are requested between the two halves of its W rows.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const bool carrier = p.unit_tiles > 0 && g < p.unit_tiles && wv >= NSW - NC;
+  const int uk = carrier ? g * NC + (wv - (NSW - NC)) : 0;
+  const bool unit = carrier && uk < p.rd.max_loras * RB;
+  // the carrier's A: a scalar read in flight while the first half of W goes
+  // out; its rows go out between the halves, so that they land mid-stream
+  const uint64_t aentry = p.unit_tiles > 0 ? scalar_entry(p.rd.a_table, unit ? uk / RB : 0) : 0;
+  if (full) issue_full<0, kNSt / 2>(wsl, v);
+  else issue_part(wsl, kb, ke, nst, v);
+  int uslot = -1, urb = 0;
+  uint4 va[2 * kNSt];
+  const u16 *A = (const u16 *)aentry;
+  if (unit && A != nullptr) {
+    uslot = uk / RB;
+    urb = uk % RB;
+    const Slice asl = make_slice(A + (size_t)urb * 16 * p.k_in, p.k_in, 0, 16, kb);
+    if (full) issue_full<0, kNSt>(asl, va);
+    else issue_part(asl, kb, ke, nst, va);
+  }
+  if (full) issue_full<kNSt / 2, kNSt>(wsl, v);
+  const int na = uslot >= 0 ? 2 * nst : 0;  // the unit's A loads
+  wait_vm(2 * nst + na);  // this wave's x stages have landed
+  if (!full)
+    for (int st = wave; st < nst; st += NSW) {
+      if (kb + st * 64 + 64 <= ke) continue;
+#pragma unroll
+      for (int i = 0; i < 2 * NB; ++i) {
+        const int r = 8 * i + (lane >> 3);
+        if (kb + st * 64 + ((lane & 7) ^ ((r >> 1) & 7)) * 8 >= ke) xs[(st * XR + 8 * i) * 8 + lane] = z4();
+      }
+    }
+  __syncthreads();  // x is in LDS
+
+  f32x4 acc[NB], acct[NB];
+  // A went out between W's halves (a whole range) or after all of W
+  if (full) slice_mma<NB, true>(v, xs, wb[wave], kb, ke, nst, acc, 0, na);
+  else slice_mma<NB, false>(v, xs, wb[wave], kb, ke, nst, acc, na);
+  if (uslot >= 0) {
+    if (full) slice_mma<NB, true>(va, xs, wb[wave], kb, ke, nst, acct);
+    else slice_mma<NB, false>(va, xs, wb[wave], kb, ke, nst, acct);
+  }
+  if (p.S == 1 && !p.has_lora && f.n_levels == 0) {  // nothing to sum: y directly
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int i = 16 * b + (lane & 15), o = o0 + 16 * wave + 4 * (lane >> 4);
+      if (i < p.n && o < p.n_out)
+        *(uint2 *)(p.y + (size_t)i * p.y_row_stride + o) =
+            make_uint2(pack2(f2bf(acc[b][0]), f2bf(acc[b][1])), pack2(f2bf(acc[b][2]), f2bf(acc[b][3])));
+    }
+    return;
+  }
+  {
+    const auto rs = coherent_rsrc(slice_partial(p, g, z, wave), kDecodeSliceFloats * 4);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) st16_coherent(rs, (uint32_t)(b * 64 + lane) * 16, 0, acc[b]);
+  }
+  if (uslot >= 0) {  // this range's piece of the slot's t: ranks urb 16 + 4 (l / 16) .. +3 of every row
+    const int P = p.rd.max_loras;
+    const auto ts = coherent_rsrc(p.t_part, (uint32_t)((size_t)p.S * P * p.n * p.R * 4));
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int i = 16 * b + (lane & 15);
+      if (i < p.n)
+        st16_coherent(ts, (uint32_t)(((z * P + uslot) * p.n + i) * p.R + urb * 16 + 4 * (lane >> 4)) * 4, 0,
+                      acct[b]);
+    }
+  }
+  wait_vmcnt<0>();
+  // the last wave of the workgroup to have stored counts the workgroup in
+  // (and the last carrier its shrink pieces); each tile's words sit on a
+  // cache line of their own
+  unsigned *tcnt = p.tile_cnt + (size_t)g * kDecodeCtrStride;
+  unsigned *tpass = tcnt + 1;
+  int last = 0, clast = 0;
+  if (lane == 0) {
+    last = atomicAdd(&s_done, 1) == NSW - 1;
+    if (carrier) clast = atomicAdd(&s_cdone, 1) == NC - 1;
+  }
+  // a carrier workgroup whose pieces are all stored counts itself into every
+  // tile (one atomic per lane), so that each tile's finalizers watch their
+  // own line: a tile is ready at S + unit_tiles S arrivals
+  if (__builtin_amdgcn_readfirstlane(clast)) {
+    asm volatile("" ::: "memory");
+    for (int t = lane; t < p.n_tiles; t += 64)
+      __hip_atomic_fetch_add(p.tile_cnt + (size_t)t * kDecodeCtrStride, 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (__builtin_amdgcn_readfirstlane(last)) (void)wave_atomic_add(tcnt, 1u);
+  // finalization items of this contributor: slices j = z, z + S, ... < NSL,
+  // every row block; item m NB + b goes to wave (m NB + b) % NSW
+  const int nsl_mine = z < NSL ? (NSL - 1 - z) / p.S + 1 : 0;
+  const int n_items = nsl_mine * NB;
+  if (wave >= n_items) return;
+  // wave 0 alone polls the tile's arrival count (few pollers keep the line
+  // free for the arrivals); the workgroup's other item waves wait on LDS
+  const RowRoute rr0 = row_route_decode(p, 16 * (wave % NB) + (lane & 15));  // in flight during the wait
+  if (wave == 0) {
+    spin_until(tcnt, (unsigned)((1 + p.unit_tiles) * p.S), kTileWaitTicks);
+    if (lane == 0) __hip_atomic_store(&s_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  } else {
+    while (__hip_atomic_load(&s_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+      __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+  const unsigned items_per_tile = (unsigned)(NSL * NB);
+  for (int it = wave; it < n_items; it += NSW) {
+    const int j = z + p.S * (it / NB), b = it % NB;
+    const RowRoute rr = it == wave ? rr0 : row_route_decode(p, 16 * b + (lane & 15));
+    finalize_item(p, f, rr, g, j, b, (float *)&wb[wave][0]);
+    if (wave_atomic_add(tpass, 1u) == items_per_tile - 1) {  // every item is past the wait
+      wave_store0(tcnt);
+      wave_store0(tpass);
+    }
+  }
+}
+
+hipError_t launch_decode(const DecodeArgs &a, const StackFold *stack, hipStream_t st) {
   const int grid = a.n_tiles * a.S;
   if (grid == 0) return hipSuccess;
+  StackFold f{};
+  if (stack) f = *stack;
   const int nb = (a.n + 15) / 16;
-#define LORA_DECODE(NB, TO) hipLaunchKernelGGL((decode_main_kernel<NB, TO>), dim3(grid), dim3(kNW * 64), 0, st, a)
-  const bool small = a.tile_out == kDecodeTileOutSmall;
-  if (!small && a.tile_out != kDecodeTileOut) return hipErrorInvalidValue;
-  if (nb <= 1) {  // one row block: the small tile leaves waves without output blocks
-    if (small) return hipErrorInvalidValue;
-    LORA_DECODE(1, kDecodeTileOut);
-  } else if (nb == 2) {
-    if (small) LORA_DECODE(2, kDecodeTileOutSmall); else LORA_DECODE(2, kDecodeTileOut);
-  } else if (nb <= 4) {
-    if (small) LORA_DECODE(4, kDecodeTileOutSmall); else LORA_DECODE(4, kDecodeTileOut);
+  const int nsw = a.tile_out / 16;
+#define LORA_DECODE(NB, NSW) \
+  hipLaunchKernelGGL((decode_kernel<NB, NSW>), dim3(grid), dim3(NSW * 64), 0, st, a, f)
+  if (nsw == 8) {
+    if (nb <= 1) LORA_DECODE(1, 8);
+    else if (nb == 2) LORA_DECODE(2, 8);
+    else if (nb <= 4) LORA_DECODE(4, 8);
+    else return hipErrorInvalidValue;
+  } else if (nsw == 4) {
+    if (nb <= 1) LORA_DECODE(1, 4);
+    else if (nb == 2) LORA_DECODE(2, 4);
+    else if (nb <= 4) LORA_DECODE(4, 4);
+    else return hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;
   }
 #undef LORA_DECODE
-  return hipGetLastError();
-}
-
-hipError_t launch_decode_epilogue(const DecodeArgs &a, const StackFold *stack, hipStream_t st) {
-  StackFold f{};
-  if (stack) f = *stack;
-  if (a.S == 1 && !a.has_lora)  // the main launch stored y; a stack always has a routed first level
-    return f.n_levels ? hipErrorInvalidValue : hipSuccess;
-  hipLaunchKernelGGL(decode_epilogue_kernel, dim3(a.n_tiles * (a.tile_out / kEpiOut) * 4), dim3(256), 0, st, a, f);
   return hipGetLastError();
 }
 

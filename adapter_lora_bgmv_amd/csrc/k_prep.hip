@@ -395,6 +395,12 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
     info[0] = lo;
     info[1] = u - cnt[lo];
   }
+  // every slot of rows[] holds a row index or -1 before anyone looks for rows:
+  // a count that disagrees with the rows found (a workspace that was not
+  // zeroed, a call cut short between the route and prep launches) then
+  // leaves -1 entries, which read row 0 and store nothing, never an address
+  // outside the operands
+  if (tid < kShrinkRows) rows[tid] = -1;
   __syncthreads();
   const int pstar = info[0];
   const int first = info[1] * kShrinkRows;
@@ -482,9 +488,12 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
     if (tid == 0) info[3] = c;
   }
   __syncthreads();
-  const int nrows = min(kShrinkRows, info[3] - first);
+  const int nrows = max(0, min(kShrinkRows, info[3] - first));
 
   const u16 *A = (const u16 *)a.rd.a_table[pstar];
+  // a stale count may name a pair that has no table entry: nothing to shrink
+  // (uniform over the workgroup)
+  if (A == nullptr || nrows == 0) return;
   const int R = a.rd.R, K = a.k_in;
   const float sig = a.rd.scale_table[pstar / a.rd.n_experts];
   const int G = (nrows + 15) / 16;  // row groups of 16 (<= kShrinkRows / 16)
@@ -517,7 +526,7 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
         const int st = ii / per, k8 = ii % per;
         const int rr = k8 * 8 + (lane >> 3);  // row of the stage
         const u16 *rowp = rr < RA ? A + (size_t)(rg * 64 + rr) * K
-                                  : a.x + (size_t)rows[min(rr - RA, nrows - 1)] * a.x_stride;
+                                  : a.x + (size_t)max(rows[min(rr - RA, nrows - 1)], 0) * a.x_stride;
         const int kk = kb0 + st * 64 + ((lane & 7) ^ ((rr >> 1) & 7)) * 8;
         dma16(rowp + (kk < kc1 ? kk : kc0), lds_addr(stg + (st * RU + k8 * 8) * 8));
       }
@@ -553,7 +562,7 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
 #pragma unroll
       for (int g = 0; g < kShrinkRows / 16; ++g) {
         const int i = g * 16 + (lane & 15);
-        if (g >= G || i >= nrows) continue;
+        if (g >= G || i >= nrows || rows[i] < 0) continue;
         // D column = lane%16 (the row), D rows = ranks 4*(lane/16) .. +3 of the wave's block
         const int rk = rg * 64 + wave * 16 + (lane >> 4) * 4;
         float *dst = tout + (size_t)rows[i] * R + rk;
@@ -582,6 +591,7 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
   // chunk order, every chunk's 16-byte load in flight together
   for (int e = tid * 4; e < nrows * R; e += 256 * 4) {
     const int i = e / R, r = e - i * R;
+    if (rows[i] < 0) continue;
     const size_t off = (size_t)rows[i] * R + r;
     f32x4 v[kMaxShrinkSplits];
 #pragma unroll

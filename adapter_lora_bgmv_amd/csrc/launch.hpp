@@ -75,8 +75,11 @@ struct GemmArgs {
 // Workgroups of a stream-K launch: one per CU of the chip.
 constexpr int kStreamKGrid = 256;
 
-// The decode-shaped apply (k_decode.hip): main launch (base partial tiles and
-// the shrink) + epilogue launch, n <= 64 rows.
+// The decode-shaped apply (k_decode.hip), n <= 64 rows: after the shrink
+// (prep kernel), one launch.  Workgroup (g, z) = tile g of tile_out outputs x
+// k range z of kDecodeKR columns; its f32 partial of each 16-output slice
+// goes to `partials`, and contributor z finalizes slices z, z + S, ... of its
+// tile.
 struct DecodeArgs {
   const u16 *W;
   int w_row_stride;
@@ -88,30 +91,46 @@ struct DecodeArgs {
   RouteDev rd;
   const int32_t *seq_slot;
   int has_lora;
-  int R;
-  int S, k_per_split;   // k split of the base contraction (k_per_split: a multiple of 64)
+  int R;                // max_rank (0: base only)
+  int S;                // k ranges
   int n_tiles;          // ceil(n_out / tile_out)
-  int tile_out;         // output features per tile: kDecodeTileOut, or kDecodeTileOutSmall
-  int n_chunks;         // k chunks of the shrink partials: the S k ranges
-  float *partials;      // [n_tiles][S][64 rows][tile_out] partial tiles
-  float *t_part;        // [n_chunks][n][R] shrink partials, one per k chunk
-  int *row_q;           // [64] each row's slot or kSkip, for the epilogue
-  float *row_sig;       // [64] each row's scale
-  const u16 **row_b;    // [64] each row's B
+  int tile_out;         // outputs per tile: 16 x the waves (128 or 64)
+  float *partials;      // [n_tiles][S][kDecodeSlices][kDecodeSliceFloats]
+  // The shrink: with unit_tiles > 0 it rides this launch (the upper half of
+  // the waves of the first unit_tiles tiles, see k_decode.hip) and leaves
+  // range pieces [S][max_loras][n][R] in t_part (max_loras x R <=
+  // kDecodeUnitRanks); otherwise a prep launch wrote t [n][R].
+  int unit_tiles;
+  float *t_part;
+  const float *t;
+  // words that are zero between calls: tile g's at tile_cnt + g
+  // kDecodeCtrStride, a cache line each: [0] contributors that stored their
+  // partials plus shrink-carrier workgroups done, [1] finalization items
+  // past the wait for them
+  unsigned *tile_cnt;
 };
 
-// Largest batch the decode kernels take, their tile width, the most
-// 64-column stages one k range takes, the largest k split (so k_in <=
-// 64 x 8 x 16 = 8192 on this path).
+// Largest batch the decode kernel takes; columns per k range; the largest
+// k split (so k_in <= 512 x 16 = 8192 on this path); slices (16 outputs)
+// per tile at most; floats of one slice partial (64 rows x 16 outputs).
 constexpr int kDecodeMaxRows = 64;
+constexpr int kDecodeKR = 512;
+constexpr int kDecodeMaxSplit = 16;
+constexpr int kDecodeSlices = 8;
+constexpr int kDecodeSliceFloats = 64 * 16;
+constexpr int kDecodeCtrStride = 32;  // words: 128 bytes
+// The most pool ranks (slots x max_rank) the shrink takes inside the decode
+// launch: 16 units of 16 ranks.
+constexpr int kDecodeUnitRanks = 256;
 constexpr int kDecodeTileOut = 128;
-// Projections up to this many outputs (and batches past one 16-row block)
-// take tiles of kDecodeTileOutSmall outputs, so that their launch still
-// spreads over the chip.
+// Projections up to this many outputs take tiles of kDecodeTileOutSmall
+// outputs, so that their launch still spreads over the chip.
 constexpr int kDecodeTileOutSmall = 64;
 constexpr int kDecodeSmallTileMaxOut = 2048;
-constexpr int kDecodeMaxStages = 8;
-constexpr int kDecodeMaxSplit = 16;
+// Waves of a decode workgroup of nsw waves that carry a shrink unit: the
+// upper half of a 128-output tile's, every wave of a 64-output tile's (the
+// small tiles' launches have fewer workgroups to spread the units over).
+constexpr int decode_carriers(int nsw) { return nsw >= 8 ? nsw / 2 : nsw; }
 
 // Rows per shrink unit; its 64-column stages in LDS at a time (16 KB each).
 constexpr int kShrinkRows = 64;
@@ -176,8 +195,7 @@ hipError_t launch_expand_fold_stack(const StackFold &f, int dtype, void *y, int 
 hipError_t launch_embed_rows(const EmbedArgs &a, int dtype, hipStream_t st);
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs &a, int to, int tr, hipStream_t st);
-hipError_t launch_decode_main(const DecodeArgs &a, hipStream_t st);
 // `stack` (or null): an adapter stack's further levels, folded into the same rounding.
-hipError_t launch_decode_epilogue(const DecodeArgs &a, const StackFold *stack, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs &a, const StackFold *stack, hipStream_t st);
 
 }  // namespace lora

@@ -88,7 +88,7 @@ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pairs) {
   Cfg c{};
   const bool moe = op == LORA_OP_MOE_GATHER || op == LORA_OP_MOE_GROUPED;
-  c.decode = op == LORA_OP_APPLY && n <= kDecodeMaxRows && k_in <= 64 * kDecodeMaxStages * kDecodeMaxSplit;
+  c.decode = op == LORA_OP_APPLY && n <= kDecodeMaxRows && k_in <= kDecodeKR * kDecodeMaxSplit;
   c.units = R > 0 ? (n + kShrinkRows - 1) / kShrinkRows + std::min(n, n_pairs) : 0;
   // Shrink k chunks: enough workgroups to cover the chip for small batches,
   // chunks of at least 256 columns.  A function of (n, k_in) only, so the
@@ -101,14 +101,11 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
   c.t_splits = R > 0 ? clampi(512 / std::max(1, units_est), 1, ks_max) : 1;
   c.t_splits_ws = R > 0 ? ks_max : 1;
   if (c.decode) {
-    // k ranges of at most kDecodeMaxStages 64-column stages
-    const int nst = (k_in + 63) / 64;
-    // a small projection takes 64-output tiles (more workgroups; every
-    // output is reduced in the same order either way), unless one 16-row
-    // block holds the batch
-    c.to = n_out <= kDecodeSmallTileMaxOut && n > 16 ? kDecodeTileOutSmall : kDecodeTileOut;
+    // k ranges of kDecodeKR columns; a small projection takes 64-output tiles
+    // (more workgroups; every output is reduced in the same order either way)
+    c.to = n_out <= kDecodeSmallTileMaxOut ? kDecodeTileOutSmall : kDecodeTileOut;
     c.tr = kDecodeMaxRows;
-    c.splits = (nst + kDecodeMaxStages - 1) / kDecodeMaxStages;
+    c.splits = (k_in + kDecodeKR - 1) / kDecodeKR;
   } else if (moe) {
     // one row tile per expert where the batch allows: an expert's W slab is
     // read once per row tile (128-row tiles from ~96 rows per expert on)
@@ -132,8 +129,7 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
     c.to = 128; c.tr = 128; c.splits = clampi(k_in / 1024, 1, 4);
   }
   if (c.decode) {
-    const int nst = (k_in + 63) / 64;
-    c.k_per_split = ((nst + c.splits - 1) / c.splits) * 64;
+    c.k_per_split = kDecodeKR;
   } else {
     const int kslabs = (k_in + 63) / 64;
     c.k_per_split = ((kslabs + c.splits - 1) / c.splits) * 64;
@@ -155,7 +151,9 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
 }
 
 struct WsLayout {
-  size_t counters, shrink_counters, pos_row, pos_pair, routes, ranks, pair_cnt, tiles, n_tiles, t, t_final, tt, partials, rows, total;
+  size_t counters, shrink_counters, pos_row, pos_pair, routes, ranks, pair_cnt, tiles, n_tiles, t, t_final, tt, partials, total;
+  // the decode kernel's zero-between-calls words
+  size_t tile_cnt;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -163,12 +161,21 @@ size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 WsLayout ws_layout(const Cfg &c, int n, int R, int k_in) {
   WsLayout w{};
   size_t off = 0;
-  if (c.decode) {  // partial tiles; shrink partials; per-row routes
-    const size_t nchunks = R > 0 ? (size_t)c.splits : 0;  // the shrink's k chunks are the k ranges
+  if (c.decode) {
+    // the tiles' arrival counters (zero between calls; their offsets depend
+    // on n_out alone), the prep shrink's arrival counters, the slice
+    // partials, the shrink's partials, then t
+    const size_t tiles = (size_t)c.n_ntiles;
+    w.tile_cnt = off; off = up256(off + tiles * kDecodeCtrStride * 4);
+    w.shrink_counters = off; off = up256(off + (size_t)c.zero_units * 4);
     w.partials = off;
-    off = up256(off + (c.splits > 1 || R > 0 ? (size_t)c.n_ntiles * c.splits * 64 * c.to * 4 : 0));
-    w.t = off; off = up256(off + nchunks * n * R * 4);
-    w.rows = off; off = up256(off + (R > 0 ? 64 * (4 + 4 + 8) : 0));
+    off = up256(off + tiles * c.splits * kDecodeSlices * kDecodeSliceFloats * 4);
+    // the shrink's partials: the prep launch's k chunks, or this launch's
+    // range pieces, whichever is larger
+    const size_t prep_parts = (size_t)(c.t_splits_ws > 1 ? c.t_splits_ws : 0) * n * R;
+    const size_t pieces = (size_t)c.splits * kDecodeUnitRanks * n;
+    w.t = off; off = up256(off + (R > 0 ? std::max(prep_parts, pieces) * 4 : 0));
+    w.t_final = off; off = up256(off + (size_t)n * R * 4);
     w.total = off;
     return w;
   }
@@ -441,22 +448,49 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
     da.has_lora = has_lora;
     da.R = R;
     da.S = c.splits;
-    da.k_per_split = c.k_per_split;
     da.n_tiles = c.n_ntiles;
     da.tile_out = c.to;
-    da.n_chunks = R > 0 ? c.splits : 0;
     da.partials = (float *)(ws + L.partials);
+    da.t = (const float *)(ws + L.t_final);
     da.t_part = (float *)(ws + L.t);
-    da.row_q = (int *)(ws + L.rows);
-    da.row_sig = (float *)(ws + L.rows + 64 * 4);
-    da.row_b = (const u16 **)(ws + L.rows + 64 * 8);
-    prof_record(0, st);
-    prof_record(1, st);
-    if (int e = launch_status(launch_decode_main(da, st), what)) return e;
-    prof_record(2, st);
+    da.tile_cnt = (unsigned *)(ws + L.tile_cnt);
+    // The shrink rides the decode launch when its units (pool slots x
+    // 16-rank blocks) fit on the carriers of a few tiles: those workgroups,
+    // the first ones of the launch, never wait before they count themselves
+    // in, and every other workgroup waits for them, so at most 32 of them
+    // keeps the launch safe wherever 32 workgroups fit at once.  Otherwise a
+    // prep launch computes t first.
+    const int carriers = decode_carriers(c.to / 16);
+    const int units = R > 0 ? rd.max_loras * (R / 16) : 0;
+    const int ut = (units + carriers - 1) / carriers;
+    da.unit_tiles = R > 0 && R <= 64 && rd.max_loras * R <= kDecodeUnitRanks && ut <= c.n_ntiles &&
+                            ut * c.splits <= 32
+                        ? ut
+                        : 0;
     const bool fold = stack && stack->n_levels > 0 && has_lora;
-    const int e = launch_status(launch_decode_epilogue(da, fold ? stack : nullptr, st), what);
+    prof_record(0, st);
+    if (has_lora && da.unit_tiles == 0) {  // the shrink: t [n][R] for the rows that resolve
+      PrepArgs pa{};
+      pa.rd = rd;
+      pa.rt = rt;
+      pa.has_lora = true;
+      pa.x = (const u16 *)x;
+      pa.x_stride = (int)x_row_stride;
+      pa.k_in = (int)k_in;
+      pa.n = (int)n;
+      pa.k_splits = c.t_splits;
+      pa.t = (float *)(ws + L.t);
+      pa.t_final = (float *)(ws + L.t_final);
+      pa.counters = (unsigned *)(ws + L.shrink_counters);
+      pa.n_pairs = n_pairs;
+      pa.do_plan = 0;
+      pa.n_units = c.units;
+      if (int e = launch_status(launch_prep(pa, st), what)) return e;
+    }
+    prof_record(1, st);
+    const int e = launch_status(launch_decode(da, fold ? stack : nullptr, st), what);
     if (stack_folded) *stack_folded = fold && e == LORA_OK;
+    prof_record(2, st);
     prof_record(3, st);
     return e;
   }

@@ -11,14 +11,16 @@ Method:
   * inputs are synthetic (seed 0) and resident in HBM before timing starts;
   * every step uses the next of R device copies of the inputs, so a step
     never finds its data in the 256 MiB last-level cache or the L2;
-  * the timed region replays a HIP graph of R consecutive steps (what a
-    serving loop does; the library allocates and synchronises nothing), K
-    steps bracketed by synchronize() on both sides;
+  * W untimed warmup steps run eagerly; the timed region is one replay of a
+    HIP graph of exactly K consecutive steps (what a serving loop does; the
+    library allocates and synchronises nothing), bracketed by synchronize()
+    on both sides; the graph's result is then checked against an eager step;
   * the dominant kernel's time comes from HIP events the library records
     around its kernels (lora_set_profile_events) over K further steps
     launched eagerly -- the same kernels on the same rotation;
   * the oracle (plain fp64 C, OpenMP over rows) is timed on the host cores
-    over whole batches of the same workload, as a baseline only.
+    over whole batches of the same workload, as a baseline only: the median
+    of three samples on all cores, and one sample on one core.
 
 Prints one JSON line.  `--gpus N` with N > 1 is refused: this build measures
 one GPU.
@@ -80,7 +82,7 @@ def parse():
     p.add_argument("--no-others", action="store_true", help="skip the other workloads")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     p.add_argument("--no-base", action="store_true", help="skip the base-only (no adapter) timing")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--cpu-seconds", type=float, default=5.0)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run one 256 MiB device copy, a known-size reference for "
                         "hardware byte counters")
@@ -133,7 +135,7 @@ def stack_counts(wl, scale_tables):
     R, k, o, n = wl.max_rank, wl.k_in, wl.n_out, wl.n_rows
     live = np.zeros(n, bool)
     a_bytes = b_bytes = 0
-    lora_flops = 0.0
+    lora_flops = expand_flops = 0.0
     first = None
     for lv, st in zip(wl.meta["levels"], scale_tables):
         ss = lv["seq_slot"]
@@ -142,17 +144,20 @@ def stack_counts(wl, scale_tables):
         a_bytes += touched * R * k * esz
         b_bytes += touched * o * R * esz
         lora_flops += 2.0 * ok.sum() * R * (k + o)
+        expand_flops += 2.0 * ok.sum() * R * o
         live |= ok
         if first is None:
-            first = (touched * R * k * esz, int(ok.sum()))
+            first = (touched * R * k * esz, 2.0 * ok.sum() * R * k)
     w_bytes, x_bytes, y_bytes = o * k * esz, n * k * esz, n * o * esz
     return {"rows": n, "adapted_rows": int(live.sum()), "touched_pairs": None,
             "path_bytes": w_bytes + a_bytes + b_bytes + x_bytes + y_bytes,
             "path_flops": 2.0 * n * o * k + lora_flops,
-            # the first level's decode main launch: W and x once, its touched A, its t
-            "main_bytes": w_bytes + x_bytes + first[0] + first[1] * R * 4,
-            "main_flops": 2.0 * n * o * k + 2.0 * first[1] * R * k,
-            "main_kernel": "decode_main_kernel (base partial tiles + first level's shrink)"}
+            # the decode launch: W, x and y once, the first level's touched A
+            # (its shrink rides the launch) and every level's touched B; the
+            # further levels' A are read by the launch before it
+            "main_bytes": w_bytes + x_bytes + y_bytes + first[0] + b_bytes,
+            "main_flops": 2.0 * n * o * k + first[1] + expand_flops,
+            "main_kernel": "decode_kernel (base + split-K reduction + first level's shrink + every level's expand and fold)"}
 
 
 def embed_counts(wl, scale_table):
@@ -201,10 +206,9 @@ def algorithmic_counts(wl, scale_table):
         "path_flops": base_flops + shrink_flops + expand_flops,
     }
     if decode_path(wl):
-        # main launch: W and x once, the touched A once, t out; the epilogue
-        # launch reads the touched B and t and writes y
-        out.update(main_bytes=w_bytes + x_bytes + a_bytes + t_bytes, main_flops=base_flops + shrink_flops,
-                   main_kernel="decode_main_kernel (base partial tiles + shrink)")
+        # one launch moves everything: W, x, the touched A and B, y
+        out.update(main_bytes=out["path_bytes"], main_flops=out["path_flops"],
+                   main_kernel="decode_kernel (base + split-K reduction + shrink + expand + fold, one launch)")
     else:
         # the fused GEMM: W, touched B, x, y, and the f32 t it reads
         out.update(main_bytes=w_bytes + b_bytes + x_bytes + y_bytes + t_bytes, main_flops=base_flops + expand_flops,
@@ -259,35 +263,33 @@ def time_workload(name, steps, warmup, apply=True):
     R = ROTATE[name]
     dws = [DeviceWorkload(wl, **device_kwargs(wl)) for _ in range(R)]
     counts = algorithmic_counts(wl, dws[0].scale_table_host)
-    steps = max(R, (steps + R - 1) // R * R)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        for i in range(max(warmup, R)):
+        for i in range(warmup):
             dws[i % R].run(route=apply)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
 
-    # one graph of R consecutive steps, one per input copy
+    # one graph of exactly `steps` consecutive steps, cycling over the copies
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for i in range(R):
-            dws[i].run(route=apply)
-    ref = dws[0].y_bits()
-    for _ in range(2):
-        g.replay()
-    torch.cuda.synchronize()
-    if not np.array_equal(dws[0].y_bits(), ref):
-        raise RuntimeError(f"{name}: graph replay differs from the eager result")
-
+        for i in range(steps):
+            dws[i % R].run(route=apply)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps // R):
-        g.replay()
+    g.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / steps
+    # the graph's last write to copy 0 against an eager step on the same inputs
+    got = dws[0].y_bits()
+    dws[0].run(route=apply)
+    torch.cuda.synchronize()
+    if not np.array_equal(dws[0].y_bits(), got):
+        raise RuntimeError(f"{name}: graph replay differs from the eager result")
+    del g
 
     # per-kernel durations: HIP events the library records around its
     # kernels, created without the system-scope fence (timing-only events)
@@ -358,24 +360,40 @@ def measured_traffic(kernel, workload):
 
 # ------------------------------------------------------------------ CPU baseline
 def cpu_baseline(name, seconds):
+    """The oracle over whole batches of the workload: the median of three
+    samples of about `seconds` each on all host threads, and one on one thread."""
     import oracle
-    from adapter_lora_bgmv_amd import workloads as WL
     wl = workload(name)
     orc = oracle.get()
     st = orc.scale_table(wl.adapters)
     counts = algorithmic_counts(wl, st)
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        orc.run(wl, scale_table=st)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or reps >= 1000:
-            break
-    return {"value": counts["adapted_rows"] * reps / el, "unit": "rows/s", "cores": orc.threads,
-            "kind": "oracle",
-            "sample": f"{reps} whole {name} batches ({counts['rows']} rows, "
-                      f"{counts['adapted_rows']} adapted) through the fp64 oracle, {el:.1f} s"}
+    rows = counts["adapted_rows"] or counts["rows"]
+
+    def sample():
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            orc.run(wl, scale_table=st)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or reps >= 1000:
+                return reps, el
+
+    cores = orc.threads
+    samples = [sample() for _ in range(3)]
+    rates = sorted(rows * r / e for r, e in samples)
+    orc.set_threads(1)
+    try:
+        r1, e1 = sample()
+    finally:
+        orc.set_threads(cores)
+    return {"value": rates[1], "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": f"median of 3 samples of whole {name} batches ({counts['rows']} rows, "
+                      f"{counts['adapted_rows']} adapted) through the fp64 oracle, "
+                      f"{', '.join(f'{r} in {e:.1f} s' for r, e in samples)}",
+            "samples": rates,
+            "single_core": {"value": rows * r1 / e1, "unit": "rows/s", "cores": 1,
+                            "sample": f"{r1} batches in {e1:.1f} s"}}
 
 
 def main():
@@ -419,6 +437,8 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": head["main_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    # the same bytes (or flops) over the whole step, launch gaps included
+    roof["step_frac"] = (head["path_TFLOPs"] if bound == "mfma" else head["path_GBps"]) / roof["peak"]
     kname = counts["main_kernel"].split(" ")[0]
     roof["traffic"] = measured_traffic(kname, name)
     roof["kernel"] = counts["main_kernel"]

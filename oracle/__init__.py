@@ -111,12 +111,17 @@ class Oracle:
         L.orc_embedding_pair.argtypes = [C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p]
         L.orc_mutant.restype = C.c_int
         L.orc_threads.restype = C.c_int
+        L.orc_set_threads.argtypes = [C.c_int]
         self.L = L
 
     # -------------------------------------------------------------- helpers
     @property
     def threads(self) -> int:
         return int(self.L.orc_threads())
+
+    def set_threads(self, n: int) -> None:
+        """Threads the row loops use from now on (timing only)."""
+        self.L.orc_set_threads(int(n))
 
     @property
     def mutant(self) -> int:

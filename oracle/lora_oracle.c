@@ -590,3 +590,13 @@ int orc_threads(void) {
   return 1;
 #endif
 }
+
+/* Threads for the loops over rows from now on (timing only; the results do
+   not depend on it: every row is computed by one thread in a fixed order). */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
