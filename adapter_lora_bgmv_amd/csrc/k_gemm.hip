@@ -20,22 +20,26 @@
 // A k tail that does not fill a stage is zeroed in LDS once it has landed.
 //
 // The low-rank term rides the same accumulators as a k-extension that runs
-// FIRST, before the base contraction (ferrox lora.rs "expand + fold"; atlas
+// after the base contraction (ferrox lora.rs "expand + fold"; atlas
 // lora_delta.rs dense_gemm_tc_scaled_acc folds the scaled expand into the
 // output the same way):
 //     acc[o, i] += sum_kappa B_q[o, kappa] * T[i, kappa]
 // where T holds s_q * t_i split into a bf16 high and low part (so the f32
 // intermediate t is carried at ~16 significant bits; the shrink writes it),
-// and rows of another pair, or skipped rows, contribute exact zeros.  Starting from +0, a skipped
-// row's accumulator is still +0 when the base contraction begins, so its
-// output is bit-identical to the base-only launch of the same shape.
+// and rows of another pair, or skipped rows, contribute exact zeros.  A
+// base-only accumulator that starts at +0 is never -0 afterwards, so adding
+// those zeros leaves a skipped row bit-identical to the base-only launch.
 //
-// Split-K: the workgroups that share a tile each take their own k range;
-// the last to arrive (a device-scope counter) sums the partial tiles in k
-// order and writes y, so results do not depend on arrival order.  The
-// extension runs in the tile's last contributor (in k order), first thing in
-// its range.  A base-only accumulator that starts at +0 never ends at -0, so
-// the +0 the extension leaves in a skipped row's partial changes no sum.
+// Split-K: the `splits` workgroups of a tile each take one of the same k
+// ranges, whatever the tile (the range bounds are a function of k_in and
+// the split count, which the host picks from the batch size and k_in
+// alone); the last to arrive (a device-scope counter) sums the partial tiles
+// in k order and writes y, so results do not depend on arrival order.  A
+// row's LoRA term goes into the partial of contributor q mod splits (q its
+// pair), whichever tile holds the row.  So an output element's sum is the
+// same whatever tile its row lands in, whatever the other rows' routing, and
+// whatever the output count: a skipped row equals the base-only call's, and
+// a projection cut into blocks of output features equals the whole one.
 #include <algorithm>
 #include <type_traits>
 
@@ -44,8 +48,9 @@
 
 namespace lora {
 
-// MODE: kOneTile (a workgroup per tile), kSplitK (classic split-K), kStreamK.
-enum { kOneTile = 0, kSplitK = 1, kStreamK = 2 };
+// MODE: kOneTile (a workgroup per tile), kSplitK (the tile's k ranges on
+// `splits` workgroups).
+enum { kOneTile = 0, kSplitK = 1 };
 
 template <int BO, int BR, int WGO, int WGR, int NS, int MODE>
 __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
@@ -69,23 +74,10 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wo = wave % WGO, wr = wave / WGO;
-  // Work partition.  A unit is one 64-wide k stage of one output tile; the
-  // tiles' units are numbered tile by tile, and workgroup w takes units
-  // [w U / G, (w+1) U / G).  With G = tiles x splits that is the classic
-  // split-K (each tile cut into the same `splits` k ranges, whatever the tile
-  // count); in stream-K mode G is one workgroup per CU and a workgroup's range
-  // may end inside a tile and go on into the next, so every CU gets the same
-  // number of stages and no second wave of workgroups trails the first.
-  // Row tiles: the plan's count (<= max_mtiles).  Stream-K partitions the
-  // largest count the call can make, so that the partition, and with it the
-  // partial tiles the workspace must hold, is fixed by the shapes alone; the
-  // units of tiles the plan did not make are skipped.
-  const int mreal = *p.plan.n_tiles;
-  const int mtiles = MODE == kStreamK ? p.max_mtiles : mreal;
-  const int ntiles = mtiles * p.n_ntiles;
+  // Work partition: workgroup w takes tile w / splits, k range w mod splits.
+  const int mtiles = *p.plan.n_tiles;
+  const int G = mtiles * p.n_ntiles * p.splits;
   const int nst = (p.k_in + 63) / 64;
-  const long long U = (long long)ntiles * nst;
-  const int G = MODE == kStreamK ? (int)min((long long)p.grid, U) : ntiles * p.splits;
   const int b = blockIdx.x;
   if (b >= G) return;
   // The chip hands workgroups to its 8 XCDs in turn, each XCD with its own
@@ -93,14 +85,9 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
   // on neighbouring tiles, which its L2 then serves.
   const int xq = G / 8, xr = G % 8, xcd = b % 8;
   const int w = xcd * xq + min(xcd, xr) + b / 8;
-  const long long u_beg = MODE == kStreamK ? (long long)w * U / G : 0;
-  const long long u_end = MODE == kStreamK ? (long long)(w + 1) * U / G : 0;
-  // the workgroup whose range holds unit u
-  auto owner = [&](long long u) { return (int)(((u + 1) * G - 1) / U); };
 
-  // One segment of the workgroup's range: tile t, its stages [sb, se);
-  // wf..wl are the tile's contributors.
-  auto segment = [&](int seg, int t, int sb, int se, int wf, int wl) {
+  // Tile t, its stages [sb, se); wf..wl are the tile's contributors.
+  auto segment = [&](int t, int sb, int se, int wf, int wl) {
   // Tile order: groups of up to 8 row tiles, rows fastest, so consecutive
   // tiles share W tiles and x tiles.
   const int gm0 = t / (8 * p.n_ntiles) * 8;  // first row tile of the group
@@ -108,10 +95,8 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
   const int tg = t - gm0 * p.n_ntiles;  // place within the group
   const int mt = gm0 + tg % gsz;
   const int nt = tg / gsz;
-  if (mt >= mreal) return;  // every contributor skips it alike
   const int4 tile = p.plan.tiles[mt];
   const int o0 = nt * BO;
-  if (seg > 0) __syncthreads();  // the previous tile is done with s_row and the ring
   for (int i = tid; i < BR; i += NW * 64) {
     const bool in = i < tile.z;
     const int q = in ? p.plan.pos_pair[tile.y + i] : kSkip;
@@ -229,8 +214,9 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
   // R dividing 64, T's rows go to LDS once (one or two 64-column chunks) and
   // each run's B slice (BO rows x R, repeated to 64 columns) streams through
   // an LDS-DMA ring, so every byte is fetched once per workgroup; only the
-  // waves whose rows meet the run do its MFMAs.  The tile's contributors
-  // share the runs out: contributor j takes runs j, j + C, j + 2C, ...
+  // waves whose rows meet the run do its MFMAs.  The tile's C contributors
+  // share the runs out by pair: contributor j takes the pairs q with
+  // q mod C = j.
   if (p.has_lora && p.R <= 64 && 64 % p.R == 0) {
     constexpr int LPB = BO / 8 / NW;  // DMA instructions per wave per B stage
     constexpr int LPT = BR / 8 / NW;  // per 64-column chunk of T
@@ -241,14 +227,16 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
     const int R = p.R, nck = (2 * R + 63) / 64;
     uint4 *const tlds = &ring[0][0];
     uint4 *const blds = tlds + 2 * BR * 8;
+    const int C = wl - wf + 1, jc = w - wf;
     block_barrier();  // every wave is done with the ring
     if (wave == 0) {
       const uint64_t below = (1ull << lane) - 1ull;
       int ns = 0, ne = 0;
       for (int i = lane; i < BR; i += 64) {
         const int q = s_pair[i];
-        const bool st = q >= 0 && (i == 0 || s_pair[i - 1] != q);
-        const bool en = q >= 0 && (i + 1 == BR || s_pair[i + 1] != q);
+        const bool mine = q >= 0 && q % C == jc;
+        const bool st = mine && (i == 0 || s_pair[i - 1] != q);
+        const bool en = mine && (i + 1 == BR || s_pair[i + 1] != q);
         const uint64_t ms = __ballot(st), me = __ballot(en);
         if (st) s_run[ns + (int)__popcll(ms & below)] = i;
         if (en) s_rend[ne + (int)__popcll(me & below)] = i + 1;
@@ -258,8 +246,7 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
       if (lane == 0) s_nrun = ns;
     }
     block_barrier();
-    const int C = wl - wf + 1, jc = w - wf;
-    const int nmine = s_nrun > jc ? (s_nrun - jc + C - 1) / C : 0;
+    const int nmine = s_nrun;
     if (nmine > 0) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -275,7 +262,7 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
         }
       }
       auto issue_b = [&](int s) {
-        const u16 *Bq = s_bq[s_run[jc + s * C]];
+        const u16 *Bq = s_bq[s_run[s]];
 #pragma unroll
         for (int j = 0; j < LPB; ++j) {
           const int rr = (wave + NW * j) * 8 + (lane >> 3);
@@ -297,7 +284,7 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
         }
         block_barrier();
         if (s + EB - 1 < nmine) issue_b(s + EB - 1);
-        const int i0 = s_run[jc + s * C], i1 = s_rend[jc + s * C];
+        const int i0 = s_run[s], i1 = s_rend[s];
         if (i0 >= (wr + 1) * WR || i1 <= wr * WR) continue;  // none of this wave's rows
         const uint4 *bs = blds + (s % EB) * BO * 8;
         // one 32-column half of the B slice, and at most four of its output
@@ -333,7 +320,7 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
         }
       }
     }
-  } else if constexpr (MODE != kStreamK) {  // (stream-K launches take R dividing 64 only)
+  } else if constexpr (BO * BR < 256 * 256) {  // (256 x 256 launches take R dividing 64 only)
   if (p.has_lora && w == wl) {
   // Other ranks: the tile's last contributor loads the operands into
   // registers.  Items are (run of equal pairs within a 16-row block, 32-wide
@@ -462,9 +449,8 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
     // fragment (bo, br) of wave v sits at byte ((v NBO + bo) NBR + br) KB, lane l at +16 l
     const int wbase = __builtin_amdgcn_readfirstlane(wave) * NBO * NBR * 1024;
     const auto slot_rsrc = [&](int cw) {
-      const int first = MODE == kStreamK ? (int)((long long)cw * U / G / nst) : t;
       // the same for every lane: keeps the resource in scalar registers
-      const int slot = __builtin_amdgcn_readfirstlane(cw + (t == first ? 0 : G));
+      const int slot = __builtin_amdgcn_readfirstlane(cw);
       return coherent_rsrc(p.partials + (size_t)slot * TT, TT * 4);
     };
     {
@@ -529,39 +515,27 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
   }
   };  // segment
 
-  if constexpr (MODE == kStreamK) {
-    int seg = 0;
-    for (long long u = u_beg; u < u_end; ++seg) {
-      const int t = (int)(u / nst);
-      const long long tu = (long long)t * nst;
-      const int sb = (int)(u - tu);
-      const int se = (int)(min(u_end, tu + nst) - tu);
-      u = tu + se;
-      segment(seg, t, sb, se, owner(tu), owner(tu + nst - 1));
-    }
-  } else {  // one segment; 32-bit arithmetic
-    const int t = w / p.splits;
-    const int j = w - t * p.splits;
-    segment(0, t, j * nst / p.splits, (j + 1) * nst / p.splits, t * p.splits, t * p.splits + p.splits - 1);
-  }
+  const int t = w / p.splits;
+  const int j = w - t * p.splits;
+  segment(t, j * nst / p.splits, (j + 1) * nst / p.splits, t * p.splits, t * p.splits + p.splits - 1);
 }
 
 hipError_t launch_gemm(const GemmArgs &a, int to, int tr, hipStream_t st) {
-  const long long units = (long long)a.max_mtiles * a.n_ntiles * ((a.k_in + 63) / 64);
-  const int grid = a.stream_k ? (int)std::min<long long>(a.grid, units) : a.max_mtiles * a.n_ntiles * a.splits;
+  const int grid = a.max_mtiles * a.n_ntiles * a.splits;
   if (grid == 0) return hipSuccess;
   // ring depth: as many 64-column stages as fit in about 128 KB of LDS
 #define LORA_GEMM(BO, BR, WGO, WGR, NS, MODE) \
   hipLaunchKernelGGL((gemm_bf16_kernel<BO, BR, WGO, WGR, NS, MODE>), dim3(grid), dim3(WGO * WGR * 64), 0, st, a)
-  const int mode = a.stream_k ? kStreamK : (a.splits > 1 ? kSplitK : kOneTile);
+  const int mode = a.splits > 1 ? kSplitK : kOneTile;
+  // the 256 x 256 tiles stage the LoRA term through LDS only
+  if (to == 256 && tr == 256 && a.has_lora && (a.R > 64 || 64 % a.R != 0)) return hipErrorInvalidValue;
   if (to == 64 && tr == 64 && mode == kOneTile) LORA_GEMM(64, 64, 2, 2, 8, kOneTile);
   else if (to == 64 && tr == 64 && mode == kSplitK) LORA_GEMM(64, 64, 2, 2, 8, kSplitK);
   else if (to == 128 && tr == 128 && mode == kOneTile) LORA_GEMM(128, 128, 2, 2, 4, kOneTile);
   else if (to == 128 && tr == 128 && mode == kSplitK) LORA_GEMM(128, 128, 2, 2, 4, kSplitK);
   else if (to == 256 && tr == 64 && mode == kOneTile) LORA_GEMM(256, 64, 4, 1, 3, kOneTile);
   else if (to == 256 && tr == 128 && mode == kOneTile) LORA_GEMM(256, 128, 4, 2, 3, kOneTile);
-  else if (to == 256 && tr == 256 && mode == kStreamK) LORA_GEMM(256, 256, 2, 4, 2, kStreamK);
-  else if (to == 256 && tr == 128 && mode == kStreamK) LORA_GEMM(256, 128, 4, 2, 3, kStreamK);
+  else if (to == 256 && tr == 256 && mode == kOneTile) LORA_GEMM(256, 256, 2, 4, 2, kOneTile);
   else
     return hipErrorInvalidValue;
 #undef LORA_GEMM

@@ -241,65 +241,6 @@ __device__ __forceinline__ void plan_block(const PrepArgs &a, int *lds) {
   } else {  // no route buffer (the standalone shrink): route here
     for (int r0 = 0; r0 < a.n; r0 += 256 * 8) route_all(a, pk, nullptr, r0);
   }
-  const uint64_t below = (1ull << lane) - 1ull;
-  if (a.stable) {
-    // Rows of one key keep their index order, so every call with the same
-    // routing makes the same tiles.  Wave v takes the rows [v C, (v+1) C):
-    // it counts its rows per key, the per-wave counts become per-wave starts,
-    // and it places its rows in order, 64 at a time, one ballot per key.
-    int *wc[4] = {fill, pk + a.n, pk + a.n + NK, pk + a.n + 2 * NK};  // [NK] each
-    for (int k = tid; k < NK; k += 256) wc[1][k] = wc[2][k] = wc[3][k] = 0;
-    __syncthreads();
-    const int C = (a.n + 255) / 256 * 64;
-    const int rb = min(wave * C, a.n), re = min(rb + C, a.n);
-    int *mine = wave == 0 ? fill : pk + a.n + (wave - 1) * NK;
-    for (int r0 = rb; r0 < re; r0 += 64) {
-      const int r = r0 + lane;
-      int k = r < re ? pk_key(pk[r]) : -1;
-      for (uint64_t todo = __ballot(k >= 0); todo;) {
-        const int leader = __ffsll((unsigned long long)todo) - 1;
-        const int v = __builtin_amdgcn_readlane(k, leader);
-        const uint64_t m = __ballot(k == v);
-        if (lane == leader) mine[v] += (int)__popcll(m);
-        if (k == v) k = -1;
-        todo &= ~m;
-      }
-    }
-    __syncthreads();
-    for (int k = tid; k < NK; k += 256) cnt[k] = wc[0][k] + wc[1][k] + wc[2][k] + wc[3][k];
-    __syncthreads();
-    const int total = block_exscan(cnt, NK, wsum);
-    if (tid == 0) cnt[NK] = total;
-    for (int k = tid; k < NK; k += 256) {
-      int run = cnt[k];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int c = wc[v][k];
-        wc[v][k] = run;
-        run += c;
-      }
-    }
-    __syncthreads();
-    for (int r0 = rb; r0 < re; r0 += 64) {
-      const int r = r0 + lane;
-      const int w = r < re ? pk[r] : 0;
-      int k = r < re ? pk_key(w) : -1;
-      for (uint64_t todo = __ballot(k >= 0); todo;) {
-        const int leader = __ffsll((unsigned long long)todo) - 1;
-        const int v = __builtin_amdgcn_readlane(k, leader);
-        const uint64_t m = __ballot(k == v);
-        const int base = mine[v];
-        if (k == v) {
-          const int pos = base + (int)__popcll(m & below);
-          a.plan.pos_row[pos] = r;
-          a.plan.pos_pair[pos] = pk_pair(w);
-          k = -1;
-        }
-        if (lane == leader) mine[v] = base + (int)__popcll(m);
-        todo &= ~m;
-      }
-    }
-  } else {
   __syncthreads();
   count_rows(pk, a.n, cnt, [](int w) { return pk_key(w); });
   __syncthreads();
@@ -322,7 +263,6 @@ __device__ __forceinline__ void plan_block(const PrepArgs &a, int *lds) {
       a.plan.pos_row[pos] = r;
       a.plan.pos_pair[pos] = pk_pair(w);
     }
-  }
   }
   __syncthreads();
   // row tiles: group g owns sorted positions [cnt[g*(ml+1)], cnt[(g+1)*(ml+1)])
@@ -657,7 +597,7 @@ size_t prep_lds_bytes(const PrepArgs &a) {
   const int ml = a.has_lora ? a.rd.max_loras : 0;
   const int NG = a.rt.n_experts;
   const int NK = NG * (ml + 1);
-  size_t plan = a.do_plan ? (size_t)(2 * NK + NG + 8 + a.n + (a.stable ? 3 * NK : 0)) * 4 : 0;
+  size_t plan = a.do_plan ? (size_t)(2 * NK + NG + 8 + a.n) * 4 : 0;
   size_t shr = a.n_units ? (size_t)((a.n_pairs + 8 + kShrinkRows + 3) & ~3) * 4 + (size_t)kShrinkStages * 128 * 128 +
                                (a.ranks ? 0 : (size_t)a.n * 4)
                          : 0;

@@ -37,7 +37,6 @@ struct PrepArgs {
   int tile_rows;  // main kernel rows per tile
   int n_units;    // shrink units (grid = do_plan + n_units * k_splits)
   int *routes;    // [n] every row's packed route (the route kernel writes it)
-  int stable;     // rows of one key keep their index order in the plan
   // With routes: the route kernel also counts the rows of every pair and
   // gives each row its rank among them (in no particular order), so that a
   // shrink unit finds its rows without sorting; the last prep workgroup to
@@ -65,18 +64,14 @@ struct GemmArgs {
   const u16 *tt;   // [n][2R] the shrink's output scaled by the pair's scale, bf16 high parts
                    // (columns 0..R-1) and what they leave over (R..2R-1)
   int R;
-  int splits;      // classic split-K: k ranges per tile
-  int stream_k;    // 1: `grid` workgroups share out all tiles' k stages evenly
-  int grid;
-  float *partials; // [slots][BO*BR] partial tiles
+  int splits;      // split-K: k ranges per tile, the same ranges for every tile
+  float *partials; // [tiles * splits][BO*BR] partial tiles
   unsigned *counters;  // [tiles] arrival counters, zero between calls
 };
 
-// Workgroups of a stream-K launch: one per CU of the chip.
-constexpr int kStreamKGrid = 256;
-
-// The decode-shaped apply (k_decode.hip), n <= 64 rows: after the shrink
-// (prep kernel), one launch.  Workgroup (g, z) = tile g of tile_out outputs x
+// The decode-shaped apply (k_decode.hip), n <= 64 rows, in one launch (after
+// a prep launch for the shrink when the pool is too large for the launch's
+// carrier waves).  Workgroup (g, z) = tile g of tile_out outputs x
 // k range z of kDecodeKR columns; its f32 partial of each 16-output slice
 // goes to `partials`, and contributor z finalizes slices z, z + S, ... of its
 // tile.

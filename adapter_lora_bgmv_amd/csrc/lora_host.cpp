@@ -67,7 +67,6 @@ int check_device(const char *what) {
 // ------------------------------------------------------------ tiling
 struct Cfg {
   int to, tr, splits, k_per_split, max_mtiles, n_ntiles;
-  bool stream_k;      // the GEMM shares all tiles' k stages out over kStreamKGrid workgroups
   int partial_slots;  // partial tiles the GEMM's split-K may store
   bool decode;   // the one-launch decode kernel (k_decode.hip)
   int units;     // upper bound of shrink units
@@ -77,14 +76,16 @@ struct Cfg {
   int zero_units;        // shrink arrival counters any routing of this shape may use
 };
 
-constexpr int kStreamKNarrowRows = 256;
+constexpr int kNarrowTileMaxRows = 256;  // 256 x 128 GEMM tiles up to this many rows
 
 int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-// Tile shape and split factor.  Up to 128 rows the split factor depends on
-// (op, n, k_in) only, never on n_out, so every output element's reduction
-// order is the same whether a fused projection is applied whole or part by
-// part; larger batches pick it from the tile count to fill the chip.
+// Tile shape and split factor.  The split factor is a function of the
+// operation, the batch size and k_in, never of n_out, the rank or the
+// routing; every output element's reduction order follows from the split
+// factor and k_in alone (not from the tile shape), so it is the same whether
+// a fused projection is applied whole or part by part, and a skipped row's
+// is the base-only call's.
 Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pairs) {
   Cfg c{};
   const bool moe = op == LORA_OP_MOE_GATHER || op == LORA_OP_MOE_GROUPED;
@@ -115,18 +116,18 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
   } else if (n <= 128) {
     c.to = 128; c.tr = 128; c.splits = clampi(k_in / 1024, 1, 4);
   } else {
-    // up to kStreamKNarrowRows rows W is the stream to keep moving: 256 x 128
+    // up to kNarrowTileMaxRows rows W is the stream to keep moving: 256 x 128
     // tiles leave LDS for three 48 KB stages (two in flight) where 256 x 256
-    // tiles fit two 64 KB ones; the row tiles of one W tile sweep k together,
-    // so W still comes from HBM about once
-    c.to = 256; c.tr = n <= kStreamKNarrowRows ? 128 : 256; c.splits = 1;
-  }
-  // stream-K stages the LoRA term through LDS, which takes ranks dividing 64;
-  // other ranks go to 128 x 128 tiles
-  c.stream_k = !c.decode && !moe && n > 128;
-  if (c.stream_k && R > 0 && (R > 64 || 64 % R != 0)) {
-    c.stream_k = false;
-    c.to = 128; c.tr = 128; c.splits = clampi(k_in / 1024, 1, 4);
+    // tiles fit two 64 KB ones; the row tiles of one W tile run on
+    // neighbouring workgroups, so W still comes from HBM about once.  One k
+    // range per tile: on the fused gate/up shape (256 rows, 22016 x 4096) two
+    // or four ranges were slower (their partial tiles cost more than the
+    // extra workgroups gain).  The 256 x 256 tiles stage the LoRA term
+    // through LDS, which takes ranks dividing 64; other ranks keep 256 x 128
+    // tiles (the tile shape does not change any element's reduction order).
+    const bool lds_rank = R == 0 || (R <= 64 && 64 % R == 0);
+    c.to = 256; c.tr = n <= kNarrowTileMaxRows || !lds_rank ? 128 : 256;
+    c.splits = 1;
   }
   if (c.decode) {
     c.k_per_split = kDecodeKR;
@@ -140,13 +141,6 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
   c.n_ntiles = (n_out + c.to - 1) / c.to;
   const long long tiles = (long long)c.max_mtiles * c.n_ntiles;
   c.partial_slots = c.splits > 1 ? (int)(tiles * c.splits) : 0;
-  if (c.stream_k) {
-    // Partial tiles arise unless every workgroup's range is whole tiles; then
-    // a workgroup stores at most two (its first and its last tile).
-    const long long nst = (k_in + 63) / 64, U = tiles * nst;
-    const long long G = std::min<long long>(kStreamKGrid, U);
-    c.partial_slots = nst == 1 || (U % G == 0 && (U / G) % nst == 0) ? 0 : (int)(2 * G);
-  }
   return c;
 }
 
@@ -521,9 +515,6 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
   pa.plan = plan;
   pa.tile_rows = c.tr;
   pa.n_units = c.units;
-  // a stream-K tile's k ranges differ from tile to tile: a row's result
-  // depends on its tile, so the tiles must not depend on timing
-  pa.stable = c.stream_k;
   prof_record(0, st);
   if (int e = launch_status(launch_prep(pa, st), what)) return e;
   prof_record(1, st);
@@ -548,8 +539,6 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
   ga.tt = pa.tt;
   ga.R = R;
   ga.splits = c.splits;
-  ga.stream_k = c.stream_k;
-  ga.grid = kStreamKGrid;
   ga.partials = (float *)(ws + L.partials);
   ga.counters = (unsigned *)(ws + L.counters);
   const int e = launch_status(launch_gemm(ga, c.to, c.tr, st), what);

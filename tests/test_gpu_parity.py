@@ -74,7 +74,7 @@ SMALL = [
     (19, "bf16", 3648, 136, 9, 3, 32),    # 57 stages: the last k range is one stage, its second shrink chunk empty
     (20, "bf16", 8192, 72, 5, 2, 16),     # the largest k_in of the decode kernels: 16 k ranges
     (21, "bf16", 8200, 40, 6, 2, 16),     # one column block past it: the tiled path
-    (22, "bf16", 520, 296, 200, 6, 32),   # stream-K on 256 x 128 tiles: ragged rows, outputs and k
+    (22, "bf16", 520, 296, 200, 6, 32),   # 256 x 128 tiles: ragged rows, outputs and k
     (23, "bf16", 1024, 200, 64, 1, 16),   # most rows on one slot: 3 row groups in its shrink unit
     (50, "bf16", 1024, 200, 64, 1, 16),   # 50 rows on one slot: 4 row groups, the unit after the W loop
     (24, "bf16", 2048, 136, 60, 2, 32),   # two slots, two rank blocks each, full 512-column k ranges
@@ -94,7 +94,7 @@ def test_decode_small(orc, case):
 @pytest.mark.parametrize("seed,dtype,lens", [
     (10, "bf16", [5, 0, 17, 64, 3, 100]),
     (11, "bf16", [512, 300, 1, 0]),
-    (13, "bf16", [60, 0, 90, 50]),       # 200 rows: stream-K on 256 x 128 tiles
+    (13, "bf16", [60, 0, 90, 50]),       # 200 rows: 256 x 128 tiles
     (12, "f32", [4, 0, 9, 2]),
 ])
 def test_segmented_small(orc, seed, dtype, lens):
@@ -375,9 +375,9 @@ def test_skip_rows_are_base_bit_for_bit(orc):
 
 
 @pytest.mark.parametrize("kind,seed,k,n_out,n,R", [
-    ("decode", 35, 520, 264, 150, 48),     # routed on 128 x 128 tiles, base only stream-K
+    ("decode", 35, 520, 264, 150, 48),     # rank 48: the register-staged LoRA term
     ("decode", 36, 2048, 296, 100, 16),    # classic split-k both ways
-    ("segmented", 37, 512, 256, 0, 32),    # stream-K both ways
+    ("segmented", 37, 512, 256, 0, 32),    # 256 x 256 tiles both ways
     ("moe", 38, 200, 96, 60, 16),
 ])
 def test_routed_and_base_only_share_a_workspace(kind, seed, k, n_out, n, R):
@@ -546,16 +546,16 @@ def test_full_config_parity(orc, name):
 
 
 @pytest.mark.parametrize("seed,k,n_out,n,R", [
-    (15, 2112, 1000, 300, 32),   # 264 k stages over 256 workgroups: ranges cross tile edges
-    (16, 128, 8000, 2100, 32),   # 288 tiles of 2 stages: ranges hold whole tiles and pieces
+    (15, 2112, 1000, 300, 32),   # 33 k stages in one range, a ragged last stage
+    (16, 128, 8000, 2100, 32),   # 9 x 32 tiles of 256 x 256, 2 stages each, no split
     (17, 1024, 2048, 520, 16),   # rank 16: T's columns past 2R are zero in LDS
-    (18, 640, 1000, 300, 128),   # rank 128: 128 x 128 tiles, the register-staged LoRA term
+    (18, 640, 1000, 300, 128),   # rank 128: 256 x 128 tiles, the register-staged LoRA term
+    (19, 4096, 264, 400, 64),    # 256 x 256 tiles over the whole k, a ragged output tile
 ])
-def test_stream_k_partition(orc, seed, k, n_out, n, R):
-    """Batches over 128 rows share every tile's k stages out evenly over one
-    workgroup per CU; a range that starts or ends inside a tile leaves a
-    partial tile, which the tile's last arrival sums in k order.  The tile's
-    contributors share its runs of equal pairs out for the LoRA term."""
+def test_large_batch_tiles(orc, seed, k, n_out, n, R):
+    """Batches over 128 rows take 256-output tiles, each over the whole k
+    range on one workgroup, the LoRA term after the base contraction; runs
+    give the same bits twice."""
     wl = WL.random_small(seed, dtype="bf16", k=k, n_out=n_out, n=n, n_slots=6, max_rank=R)
     dw = DeviceWorkload(wl)
     first = bf16_bits(dw.run().clone())
