@@ -18,6 +18,7 @@ LIB_PATH = Path(__file__).resolve().parent / "_lib" / "liblora_mi355x.so"
 
 LORA_F32, LORA_BF16 = 0, 1
 LORA_OP_APPLY, LORA_OP_SEGMENTED, LORA_OP_MOE_GATHER, LORA_OP_MOE_GROUPED, LORA_OP_STACK = 0, 1, 2, 3, 4
+LORA_NOALLOC_SCRATCH_BYTES = 32 << 20  # lora_apply_noalloc's device array, per GPU
 STATUS = {0: "LORA_OK", -1: "LORA_ERR_SHAPE", -2: "LORA_ERR_NULL_PTR", -3: "LORA_ERR_STRIDE",
           -4: "LORA_ERR_DTYPE", -5: "LORA_ERR_UNSUPPORTED", -6: "LORA_ERR_LAUNCH",
           -7: "LORA_ERR_WORKSPACE"}
@@ -25,7 +26,7 @@ STATUS = {0: "LORA_OK", -1: "LORA_ERR_SHAPE", -2: "LORA_ERR_NULL_PTR", -3: "LORA
 # every symbol include/lora_mi355x.h declares
 EXPORTS = ("lora_last_error", "lora_version", "lora_init", "lora_scale", "lora_scale_table",
            "lora_build_seq_slot", "lora_workspace_bytes", "lora_shrink", "lora_expand_fold",
-           "lora_apply", "lora_apply_segmented", "lora_apply_moe_gather",
+           "lora_apply", "lora_apply_noalloc", "lora_apply_segmented", "lora_apply_moe_gather",
            "lora_set_profile_events", "lora_moe_grouped_shrink", "lora_moe_grouped_expand_fold",
            "lora_apply_moe_grouped", "lora_apply_stack", "lora_embedding_pair",
            "lora_embed_rows")
@@ -77,6 +78,7 @@ def lib() -> C.CDLL:
     L.lora_shrink.argtypes = [RP, vp, u32, vp, u32, vp, vp]
     L.lora_expand_fold.argtypes = [RP, vp, vp, u32, vp, u32, vp]
     L.lora_apply.argtypes = [i32, u32, u32, vp, u32, RP, vp, u32, vp, u32, vp, u32, vp, sz, vp]
+    L.lora_apply_noalloc.argtypes = [i32, u32, u32, vp, u32, RP, vp, u32, vp, u32, vp, u32, vp]
     L.lora_apply_segmented.argtypes = [i32, u32, u32, vp, u32, RP, vp, u32, vp, vp, u32, u32, vp,
                                        u32, vp, sz, vp]
     L.lora_apply_moe_gather.argtypes = [i32, u32, u32, u32, vp, C.c_uint64, u32,
@@ -235,6 +237,13 @@ def lora_apply(dtype: int, n_out: int, k_in: int, W, w_row_stride: int, route, x
     _check(lib().lora_apply(dtype, n_out, k_in, _ptr(W), w_row_stride, _route_ref(route), _ptr(x),
                             x_row_stride, _ptr(seq_slot), n, _ptr(y), y_row_stride,
                             _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def lora_apply_noalloc(dtype: int, n_out: int, k_in: int, W, w_row_stride: int, route, x,
+                       x_row_stride: int, seq_slot, n: int, y, y_row_stride: int, stream=None):
+    _check(lib().lora_apply_noalloc(dtype, n_out, k_in, _ptr(W), w_row_stride, _route_ref(route),
+                                    _ptr(x), x_row_stride, _ptr(seq_slot), n, _ptr(y), y_row_stride,
+                                    _stream(stream)))
 
 
 def lora_apply_segmented(dtype: int, n_out: int, k_in: int, W, w_row_stride: int, route, x,

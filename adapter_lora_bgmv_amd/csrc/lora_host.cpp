@@ -10,11 +10,15 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/lora_mi355x.h"
 #include "launch.hpp"
 
 using namespace lora;
+
+// The array itself (see ScratchDev below).
+static __device__ __align__(256) unsigned char scratch[LORA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -62,6 +66,28 @@ int check_device(const char *what) {
   }
   if (g_dev_ok[dev] < 0) return fail(LORA_ERR_LAUNCH, "%s: device %d is not a gfx950", what, dev);
   return LORA_OK;
+}
+
+// ------------------------------------------------------------ scratch for callers that cannot allocate
+// lora_apply_noalloc's workspace: one array per device, held until the
+// process ends.  The words that must be zero between calls of any shape lie
+// in its first kScratchZeroBytes; everything else lies above them.  Host
+// code uses the address hipGetSymbolAddress gives on each device, never the
+// array's name.
+constexpr size_t kScratchBytes = LORA_NOALLOC_SCRATCH_BYTES;
+constexpr size_t kScratchZeroBytes = 1u << 20;
+static_assert(kScratchZeroBytes % 16 == 0 && kScratchZeroBytes < kScratchBytes, "zero region");
+
+struct ScratchDev {
+  void *ptr;    // the array's address on this device
+  bool zeroed;  // its zero region has been cleared by a call made outside stream capture
+};
+std::mutex g_scratch_mu;
+ScratchDev g_scratch[64];
+
+__global__ void zero_kernel(uint4 *p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // ------------------------------------------------------------ tiling
@@ -148,11 +174,15 @@ struct WsLayout {
   size_t counters, shrink_counters, pos_row, pos_pair, routes, ranks, pair_cnt, tiles, n_tiles, t, t_final, tt, partials, total;
   // the decode kernel's zero-between-calls words
   size_t tile_cnt;
+  size_t zero_end;  // the words that must be zero between calls lie below this offset
 };
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-WsLayout ws_layout(const Cfg &c, int n, int R, int k_in) {
+// `data_base`: the first byte past the words that must be zero between
+// calls may not lie below it (0: packed); a shared scratch buffer keeps
+// every shape's zero words below one fixed offset that way.
+WsLayout ws_layout(const Cfg &c, int n, int R, int k_in, size_t data_base = 0) {
   WsLayout w{};
   size_t off = 0;
   if (c.decode) {
@@ -162,6 +192,7 @@ WsLayout ws_layout(const Cfg &c, int n, int R, int k_in) {
     const size_t tiles = (size_t)c.n_ntiles;
     w.tile_cnt = off; off = up256(off + tiles * kDecodeCtrStride * 4);
     w.shrink_counters = off; off = up256(off + (size_t)c.zero_units * 4);
+    w.zero_end = off; off = std::max(off, data_base);
     w.partials = off;
     off = up256(off + tiles * c.splits * kDecodeSlices * kDecodeSliceFloats * 4);
     // the shrink's partials: the prep launch's k chunks, or this launch's
@@ -179,6 +210,7 @@ WsLayout ws_layout(const Cfg &c, int n, int R, int k_in) {
   w.counters = off; off = up256(off + (size_t)c.zero_tiles * 4);
   w.shrink_counters = off; off = up256(off + (size_t)c.zero_units * 4);
   w.pair_cnt = off; off = up256(off + (size_t)(kMaxKeys + 1) * 4);  // any table size, then the arrival count
+  w.zero_end = off; off = std::max(off, data_base);
   w.pos_row = off; off = up256(off + (size_t)n * 4);
   w.pos_pair = off; off = up256(off + (size_t)n * 4);
   w.routes = off; off = up256(off + (size_t)n * 4);
@@ -414,15 +446,18 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
               uint32_t n_out, uint32_t k_in, const void *W, long long w_group_stride,
               uint32_t w_row_stride, const void *x, uint32_t x_row_stride, uint32_t n, void *y,
               uint32_t y_row_stride, void *workspace, size_t workspace_bytes, int groups,
-              hipStream_t st, const StackFold *stack = nullptr, bool *stack_folded = nullptr) {
+              hipStream_t st, const StackFold *stack = nullptr, bool *stack_folded = nullptr,
+              size_t data_base = 0) {
   const int R = has_lora ? rd.R : 0;
   const int n_pairs = has_lora ? rd.max_loras * rd.n_experts : 0;
   const Cfg c = choose_cfg(op, (int)n, (int)n_out, (int)k_in, groups, R, n_pairs);
-  const WsLayout L = ws_layout(c, (int)n, R, (int)k_in);
-  if (!workspace || workspace_bytes < L.total)
+  const WsLayout L = ws_layout(c, (int)n, R, (int)k_in, data_base);
+  if (!workspace || workspace_bytes < L.total || (data_base && L.zero_end > data_base))
     return fail(LORA_ERR_WORKSPACE,
-                "%s: [n_out %u x k_in %u] at max_rank %d, n %u: workspace %p of %zu bytes, %zu needed", what,
-                n_out, k_in, R, n, workspace, workspace_bytes, L.total);
+                "%s: [n_out %u x k_in %u] at max_rank %d, n %u: workspace %p of %zu bytes, %zu needed%s", what,
+                n_out, k_in, R, n, workspace, workspace_bytes, L.total,
+                data_base && L.zero_end > data_base ? " (its counter words exceed the shared scratch's zero region)"
+                                                    : "");
   if (!aligned16(workspace))
     return fail(LORA_ERR_UNSUPPORTED, "%s: workspace %p is not 16-byte aligned", what, workspace);
   char *ws = (char *)workspace;
@@ -547,6 +582,26 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
   return e;
 }
 
+// The current device's scratch entry: the array's address is looked up once
+// per device, with that device current.
+int scratch_dev(const char *what, ScratchDev **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(LORA_ERR_LAUNCH, "%s: no HIP device is current", what);
+  if (dev < 0 || dev >= 64) return fail(LORA_ERR_LAUNCH, "%s: device index %d out of range", what, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchDev &d = g_scratch[dev];
+  if (!d.ptr) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(LORA_ERR_LAUNCH, "%s: hipGetSymbolAddress of the scratch array on device %d failed: %s", what,
+                  dev, hipGetErrorString(e));
+    d.ptr = p;
+  }
+  *out = &d;
+  return LORA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -570,7 +625,9 @@ const char *lora_version(void) { return "lora_mi355x 0.1 (gfx950)"; }
 
 int lora_init(void) {
   clear_err();
-  return check_device("lora_init");
+  if (int e = check_device("lora_init")) return e;
+  ScratchDev *d = nullptr;
+  return scratch_dev("lora_init", &d);
 }
 
 double lora_scale(double adapter_scale, double alpha, uint32_t rank, int32_t rslora) {
@@ -706,6 +763,64 @@ int lora_apply(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W, uint
                                           (float *)y, (int)y_row_stride, st); }, st);
   return run_fused(what, LORA_OP_APPLY, rt, rd, route != nullptr, n_out, k_in, W, 0, w_row_stride, x,
                    x_row_stride, n, y, y_row_stride, workspace, workspace_bytes, 1, st);
+}
+
+int lora_apply_noalloc(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W, uint32_t w_row_stride,
+                       const lora_route *route, const void *x, uint32_t x_row_stride, const int32_t *seq_slot,
+                       uint32_t n, void *y, uint32_t y_row_stride, void *stream) {
+  clear_err();
+  const char *what = "lora_apply_noalloc";
+  if (int e = check_proj(what, dtype, n_out, k_in, n, x_row_stride, y_row_stride, w_row_stride)) return e;
+  if (route) {
+    if (int e = check_route(what, route, dtype, n_out, k_in)) return e;
+  }
+  if (n == 0) return LORA_OK;
+  if (!W || !x || !y || (route && !seq_slot))
+    return fail(LORA_ERR_NULL_PTR, "%s: [n_out %u x k_in %u]: W %p, x %p, y %p%s must be non-NULL", what, n_out,
+                k_in, W, x, y, route ? " and seq_slot" : "");
+  if (dtype == LORA_BF16 && (!aligned16(W) || !aligned16(x) || !aligned16(y)))
+    return fail(LORA_ERR_UNSUPPORTED, "%s: bf16 needs 16-byte aligned W %p, x %p, y %p", what, W, x, y);
+  const RouteDev rd = route_dev(route);
+  if (dtype == LORA_BF16) {  // the size check, before any HIP call
+    const int R = route ? rd.R : 0;
+    const Cfg c = choose_cfg(LORA_OP_APPLY, (int)n, (int)n_out, (int)k_in, 1, R,
+                             route ? rd.max_loras * rd.n_experts : 0);
+    const WsLayout L = ws_layout(c, (int)n, R, (int)k_in, kScratchZeroBytes);
+    if (L.total > kScratchBytes || L.zero_end > kScratchZeroBytes)
+      return fail(LORA_ERR_WORKSPACE,
+                  "%s: [n_out %u x k_in %u] at max_rank %d, n %u needs %zu bytes of scratch; the limit is %zu", what,
+                  n_out, k_in, R, n, L.total, kScratchBytes);
+  }
+  if (int e = check_device(what)) return e;
+  const Routing rt = routing_decode(route ? seq_slot : nullptr);
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == LORA_F32)  // (this path uses no workspace)
+    return run_f32_timed(what, [&] { return launch_apply_f32(rd, rt, route != nullptr, (const float *)W, 0, (int)w_row_stride,
+                                          (const float *)x, (int)x_row_stride, (int)k_in, (int)n_out, (int)n,
+                                          (float *)y, (int)y_row_stride, st); }, st);
+  ScratchDev *d = nullptr;
+  if (int e = scratch_dev(what, &d)) return e;
+  // The zero region is cleared by the first call on the device, and by every
+  // call made under stream capture (a graph then carries its own clear).
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cap) != hipSuccess)
+    return fail(LORA_ERR_LAUNCH, "%s: cannot query the stream's capture status", what);
+  const bool capturing = cap != hipStreamCaptureStatusNone;
+  bool clear = capturing;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!d->zeroed) {
+      clear = true;
+      if (!capturing) d->zeroed = true;
+    }
+  }
+  if (clear) {
+    hipLaunchKernelGGL(zero_kernel, dim3(256), dim3(256), 0, st, (uint4 *)d->ptr, kScratchZeroBytes / 16);
+    if (int e = launch_status(hipGetLastError(), what)) return e;
+  }
+  return run_fused(what, LORA_OP_APPLY, rt, rd, route != nullptr, n_out, k_in, W, 0, w_row_stride, x,
+                   x_row_stride, n, y, y_row_stride, d->ptr, kScratchBytes, 1, st, nullptr, nullptr,
+                   kScratchZeroBytes);
 }
 
 int lora_apply_segmented(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W, uint32_t w_row_stride,

@@ -234,6 +234,28 @@ int lora_apply(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W,
                uint32_t y_row_stride, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): lora_apply with no
+ * workspace argument and the same results bit for bit.  Its intermediate
+ * results live in a device array that the library owns, of
+ * LORA_NOALLOC_SCRATCH_BYTES per GPU, held on each GPU it runs on until the
+ * process ends; the call itself allocates nothing.  A problem that needs
+ * more scratch than that (lora_workspace_bytes(LORA_OP_APPLY, ...) plus
+ * 1 MiB gives the need) returns LORA_ERR_WORKSPACE and launches nothing.
+ * Every call on one GPU uses that GPU's array and leaves what it wrote
+ * there: calls that overlap in time on one GPU (other streams, other
+ * threads) race; calls ordered on one stream do not.  The first call on a
+ * GPU, and every call made while `stream` is being captured, first clears
+ * the array's counter words with a small kernel on `stream`.  lora_init
+ * looks the array up on the current device ahead of the first call.
+ */
+#define LORA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int lora_apply_noalloc(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W,
+                       uint32_t w_row_stride, const lora_route *route, const void *x,
+                       uint32_t x_row_stride, const int32_t *seq_slot, uint32_t n, void *y,
+                       uint32_t y_row_stride, void *stream);
+
+/*
  * Segmented prefill apply (ferrox add_batch_to; atlas apply_lora_delta for
  * m contiguous rows on one pair): rows seg_indptr[g] .. seg_indptr[g+1]-1
  * use slot seg_slot[g]; otherwise the same definition as lora_apply.

@@ -95,6 +95,20 @@ def _apply(L, **kw):
     return rc, L.lora_last_error().decode()
 
 
+def test_noalloc_refuses_a_problem_beyond_its_scratch(L):
+    """lora_apply_noalloc checks its scratch need before any HIP call: a
+    16384-row batch at rank 64 over k_in 4096 needs more than the 32 MiB
+    array and is refused, the message naming the need and the limit."""
+    need = B.lora_workspace_bytes(0, B.LORA_BF16, 16384, 64, 4096, 64) + (1 << 20)
+    assert need > B.LORA_NOALLOC_SCRATCH_BYTES
+    r = _route(n_out=64, k_in=4096, R=64)
+    rc = L.lora_apply_noalloc(B.LORA_BF16, 64, 4096, FAKE, 4096, C.byref(r), FAKE, 4096, FAKE, 16384,
+                              FAKE, 64, None)
+    msg = L.lora_last_error().decode()
+    assert rc == -7, msg
+    assert f"the limit is {B.LORA_NOALLOC_SCRATCH_BYTES}" in msg and "n 16384" in msg
+
+
 def test_refuses_x_stride_below_k_in(L):
     rc, msg = _apply(L, x_stride=32)
     assert rc == -3
