@@ -26,17 +26,19 @@
 //    always runs them together).  Finalizing sums the S partials in range
 //    order, adds s_q B_q t_i in f32 (ranks in order), an adapter stack's
 //    further levels, and rounds y once.
-//  * the shrink: when the pool's units (slot x 16-rank block) fit, the last
-//    waves of the first few tiles' workgroups ("carriers") each take one
-//    unit over their k range besides their W slice: the slot's A rows are
-//    requested between the two halves of the W stream and contracted with
-//    the same x rows in LDS, giving a piece of t for every row (pieces by
-//    pool slot, not by row, so no route is needed to place them).  Carriers
-//    never wait before they count themselves in, and every tile waits for
-//    the carriers' pieces before it finalizes; the carrier workgroups are
-//    the first of the launch and at most 32, so they all run whatever else
-//    is resident.  A larger pool takes a prep launch (k_prep.hip) that
-//    leaves t in the workspace first.
+//  * the shrink: when the pool's units (slot x 16-rank block) fit, the
+//    workgroups of the first few tiles ("carriers") take two units each
+//    over their k range besides their W slices: each unit on half of the
+//    waves, which split the range's stages; a wave's part of the slot's A
+//    rows is requested between the two halves of its W stream and
+//    contracted with the same x rows in LDS; the parts are summed in LDS in
+//    stage order, giving a piece of t for every row (pieces by pool slot,
+//    not by row, so no route is needed to place them).  Carriers never wait
+//    before they count themselves in, and every tile waits for the
+//    carriers' pieces before it finalizes; the carrier workgroups are the
+//    first of the launch and at most 64, so they all run whatever else is
+//    resident.  A larger pool takes a prep launch (k_prep.hip) that leaves
+//    t in the workspace first.
 //
 // Skipped rows (slot < 0 or past the pool, NULL table entry, zero scale) get
 // no delta arithmetic: their y is the sum of the same partials in the same
@@ -205,6 +207,47 @@ __device__ __forceinline__ void slice_mma(uint4 (&v)[2 * kNSt], const uint4 *xs,
   }
 }
 
+// A carrier wave's part of a shrink unit: stages st0 .. st0 + SP - 1 of the
+// range (those below nst), whose loads v[0 .. 2 SP) have all landed, against
+// the same x rows; acc as in slice_mma.
+template <int NB, int SP>
+__device__ __forceinline__ void part_mma(uint4 (&v)[2 * SP], const uint4 *xs, uint4 *wb, int kb, int ke, int nst,
+                                         int st0, f32x4 (&acc)[NB]) {
+  const int lane = threadIdx.x & 63;
+  constexpr int XR = 16 * NB;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < SP; ++s) {
+    const int st = st0 + s;
+    if (st >= nst) break;
+    if (kb + st * 64 + (lane & 7) * 8 >= ke) v[2 * s] = v[2 * s + 1] = z4();
+    uint4 *buf = wb + (s & 1) * 128;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * h + (lane >> 3);
+      buf[r * 8 + ((lane & 7) ^ ((r >> 1) & 7))] = v[2 * s + h];
+    }
+    const uint4 *xst = xs + st * XR * 8;
+    uint4 af[2], xf[2][NB];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = 4 * h + (lane >> 4);
+      const int r = lane & 15;
+      af[h] = buf[r * 8 + (c ^ ((r >> 1) & 7))];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int rx = 16 * b + (lane & 15);
+        xf[h][b] = xst[rx * 8 + (c ^ ((rx >> 1) & 7))];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[b] = mfma16(af[h], xf[h][b], acc[b]);
+  }
+}
+
 __device__ __forceinline__ float *slice_partial(const DecodeArgs &p, int g, int z, int j) {
   return p.partials + ((size_t)(g * p.S + z) * kDecodeSlices + j) * kDecodeSliceFloats;
 }
@@ -267,6 +310,15 @@ __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFo
   };
   load_parts(0);
   const bool any = __ballot(routed && i < p.n) != 0;
+  // B_q[o .. o+3] over the first 16 ranks: it depends on nothing stored in
+  // this launch, so it goes out with the partials and the pieces
+  const bool expand = routed && i < p.n && o < p.n_out;
+  const u16 *bq = expand ? rr.bq + (size_t)o * R : nullptr;
+  uint4 b0[4][2];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) b0[c][h] = expand ? ldg16(bq + (size_t)c * R + 8 * h) : z4();
   // t of row i, ranks 4 (l / 16) .. +3 of every 16-rank block, from the
   // pieces of its slot's units: the S ranges summed in range order; the
   // row's four lanes meet in tb
@@ -292,15 +344,14 @@ __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFo
   }
   if (i >= p.n || o >= p.n_out) return;
   float d[4] = {0.f, 0.f, 0.f, 0.f};
-  if (routed) {  // B_q[o .. o+3] t_i, ranks in order, 8 at a time
-    const u16 *bq = rr.bq + (size_t)o * R;
+  if (routed) {  // B_q[o .. o+3] t_i, ranks in order, 16 at a time
     const float *ti = p.unit_tiles > 0 ? tb + (lane & 15) * R : p.t + (size_t)i * R;
     for (int r0 = 0; r0 < R; r0 += 16) {  // 16 ranks: every B load of the step in flight together
       uint4 bb[4][2];
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) bb[c][h] = ldg16(bq + (size_t)c * R + r0 + 8 * h);
+        for (int h = 0; h < 2; ++h) bb[c][h] = r0 == 0 ? b0[c][h] : ldg16(bq + (size_t)c * R + r0 + 8 * h);
       float tr[16];
 #pragma unroll
       for (int e = 0; e < 16; e += 4) {
@@ -381,10 +432,9 @@ template <int NB, int NSW>
 __global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFold f) {
   constexpr int XR = 16 * NB;
   constexpr int NSL = NSW;      // slices per tile
-  constexpr int NC = decode_carriers(NSW);  // shrink carriers per workgroup: its last NC waves
   __shared__ __attribute__((aligned(16))) uint4 xs[kNSt * XR * 8];
   __shared__ __attribute__((aligned(16))) uint4 wb[NSW][2 * 128];
-  __shared__ int s_done, s_cdone, s_ready;
+  __shared__ int s_done, s_ready;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = blockIdx.x / p.S, z = blockIdx.x % p.S;
@@ -408,35 +458,48 @@ __global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFol
   }
   if (tid == 0) {
     s_done = 0;
-    s_cdone = 0;
     s_ready = 0;
   }
-  // The shrink rides this launch on the last NC waves of the first
-  // unit_tiles tiles: carrier c of tile g takes unit k = g NC + c, rank
-  // block k % RB of pool slot k / RB, for every row (the rows of other slots
-  // are simply not read back).  Its A rows, found through a scalar read of
-  // the table, are requested between the two halves of its W rows.
+  // The shrink rides this launch on the first unit_tiles tiles: their
+  // workgroups take units (pool slot x 16-rank block) 2 g and 2 g + 1, each
+  // on half of the waves, which split the range's stages between them (SP
+  // stages each: the part's A rows, requested between the two halves of the
+  // wave's W rows, against the same x rows).  The parts are summed in LDS
+  // in stage order and stored as the unit's piece of t for every row (the
+  // rows of other slots are simply not read back).
+  constexpr int HW = NSW / 2;           // waves per unit
+  constexpr int SP = kNSt / HW;         // stages per wave's part
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const bool carrier = p.unit_tiles > 0 && g < p.unit_tiles && wv >= NSW - NC;
-  const int uk = carrier ? g * NC + (wv - (NSW - NC)) : 0;
-  const bool unit = carrier && uk < p.rd.max_loras * RB;
-  // the carrier's A: a scalar read in flight while the first half of W goes
-  // out; its rows go out between the halves, so that they land mid-stream
-  const uint64_t aentry = p.unit_tiles > 0 ? scalar_entry(p.rd.a_table, unit ? uk / RB : 0) : 0;
+  const bool cwg = p.unit_tiles > 0 && g < p.unit_tiles;  // a carrier workgroup
+  const int uk = 2 * g + wv / HW, pi = wv % HW;
+  const bool unit = cwg && uk < p.rd.max_loras * RB;
+  // the unit's A entry: a scalar read in flight while the first half of W
+  // goes out
+  const uint64_t aentry = cwg ? scalar_entry(p.rd.a_table, unit ? uk / RB : 0) : 0;
   if (full) issue_full<0, kNSt / 2>(wsl, v);
   else issue_part(wsl, kb, ke, nst, v);
   int uslot = -1, urb = 0;
-  uint4 va[2 * kNSt];
+  uint4 va[2 * SP];
   const u16 *A = (const u16 *)aentry;
+  const int st0 = pi * SP;
+  int na = 0;  // the part's A loads
   if (unit && A != nullptr) {
     uslot = uk / RB;
     urb = uk % RB;
     const Slice asl = make_slice(A + (size_t)urb * 16 * p.k_in, p.k_in, 0, 16, kb);
-    if (full) issue_full<0, kNSt>(asl, va);
-    else issue_part(asl, kb, ke, nst, va);
+#pragma unroll
+    for (int q = 0; q < SP; ++q) {
+      const int st = st0 + q;
+      if (st < nst) {
+        const bool past = kb + st * 64 + (lane & 7) * 8 >= ke;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          va[2 * q + h] = buf_ld16(asl.rs, past ? asl.off[h] - (lane & 7) * 16 : asl.off[h] + st * 128);
+        na += 2;
+      }
+    }
   }
   if (full) issue_full<kNSt / 2, kNSt>(wsl, v);
-  const int na = uslot >= 0 ? 2 * nst : 0;  // the unit's A loads
   wait_vm(2 * nst + na);  // this wave's x stages have landed
   if (!full)
     for (int st = wave; st < nst; st += NSW) {
@@ -453,10 +516,8 @@ __global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFol
   // A went out between W's halves (a whole range) or after all of W
   if (full) slice_mma<NB, true>(v, xs, wb[wave], kb, ke, nst, acc, 0, na);
   else slice_mma<NB, false>(v, xs, wb[wave], kb, ke, nst, acc, na);
-  if (uslot >= 0) {
-    if (full) slice_mma<NB, true>(va, xs, wb[wave], kb, ke, nst, acct);
-    else slice_mma<NB, false>(va, xs, wb[wave], kb, ke, nst, acct);
-  }
+  wait_vmcnt<0>();
+  if (uslot >= 0) part_mma<NB, SP>(va, xs, wb[wave], kb, ke, nst, st0, acct);
   if (p.S == 1 && !p.has_lora && f.n_levels == 0) {  // nothing to sum: y directly
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -472,36 +533,55 @@ __global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFol
 #pragma unroll
     for (int b = 0; b < NB; ++b) st16_coherent(rs, (uint32_t)(b * 64 + lane) * 16, 0, acc[b]);
   }
-  if (uslot >= 0) {  // this range's piece of the slot's t: ranks urb 16 + 4 (l / 16) .. +3 of every row
-    const int P = p.rd.max_loras;
-    const auto ts = coherent_rsrc(p.t_part, (uint32_t)((size_t)p.S * P * p.n * p.R * 4));
+  if (cwg) {
+    // the unit's parts meet in LDS (each wave's transpose buffer is free
+    // now); its first wave sums them in stage order and stores the piece:
+    // ranks urb 16 + 4 (l / 16) .. +3 of every row
+    f32x4 *mine = (f32x4 *)&wb[wave][0];
+    if (uslot >= 0) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int i = 16 * b + (lane & 15);
-      if (i < p.n)
-        st16_coherent(ts, (uint32_t)(((z * P + uslot) * p.n + i) * p.R + urb * 16 + 4 * (lane >> 4)) * 4, 0,
-                      acct[b]);
+      for (int b = 0; b < NB; ++b) mine[b * 64 + lane] = acct[b];
+    }
+    __syncthreads();
+    if (uslot >= 0 && pi == 0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        f32x4 sum = acct[b];
+        for (int q = 1; q < HW; ++q) sum += ((const f32x4 *)&wb[wave + q][0])[b * 64 + lane];
+        acct[b] = sum;
+      }
+      const int P = p.rd.max_loras;
+      const auto ts = coherent_rsrc(p.t_part, (uint32_t)((size_t)p.S * P * p.n * p.R * 4));
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int i = 16 * b + (lane & 15);
+        if (i < p.n)
+          st16_coherent(ts, (uint32_t)(((z * P + uslot) * p.n + i) * p.R + urb * 16 + 4 * (lane >> 4)) * 4, 0,
+                        acct[b]);
+      }
     }
   }
   wait_vmcnt<0>();
   // the last wave of the workgroup to have stored counts the workgroup in
-  // (and the last carrier its shrink pieces); each tile's words sit on a
-  // cache line of their own
+  // (a carrier workgroup into every tile: its pieces are stored too); each
+  // tile's words sit on a cache line of their own
   unsigned *tcnt = p.tile_cnt + (size_t)g * kDecodeCtrStride;
   unsigned *tpass = tcnt + 1;
-  int last = 0, clast = 0;
-  if (lane == 0) {
-    last = atomicAdd(&s_done, 1) == NSW - 1;
-    if (carrier) clast = atomicAdd(&s_cdone, 1) == NC - 1;
-  }
-  // a carrier workgroup whose pieces are all stored counts itself into every
-  // tile (one atomic per lane), so that each tile's finalizers watch their
-  // own line: a tile is ready at S + unit_tiles S arrivals
-  if (__builtin_amdgcn_readfirstlane(clast)) {
-    asm volatile("" ::: "memory");
-    for (int t = lane; t < p.n_tiles; t += 64)
-      __hip_atomic_fetch_add(p.tile_cnt + (size_t)t * kDecodeCtrStride, 1u, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+  int last = 0;
+  if (lane == 0) last = atomicAdd(&s_done, 1) == NSW - 1;
+  // a carrier workgroup whose pieces are all stored counts itself into its
+  // range's carrier count; the range's last carrier counts the range into
+  // every tile (one atomic per lane) and clears the range count, so that
+  // each tile's finalizers watch their own line and no line takes more
+  // than 2 S increments: a tile is ready at 2 S arrivals
+  if (cwg && __builtin_amdgcn_readfirstlane(last)) {
+    unsigned *ccnt = p.tile_cnt + (size_t)(p.n_tiles + z) * kDecodeCtrStride;
+    if (wave_atomic_add(ccnt, 1u) == (unsigned)p.unit_tiles - 1) {
+      wave_store0(ccnt);
+      for (int t = lane; t < p.n_tiles; t += 64)
+        __hip_atomic_fetch_add(p.tile_cnt + (size_t)t * kDecodeCtrStride, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   if (__builtin_amdgcn_readfirstlane(last)) (void)wave_atomic_add(tcnt, 1u);
   // finalization items of this contributor: slices j = z, z + S, ... < NSL,
@@ -513,7 +593,7 @@ __global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFol
   // free for the arrivals); the workgroup's other item waves wait on LDS
   const RowRoute rr0 = row_route_decode(p, 16 * (wave % NB) + (lane & 15));  // in flight during the wait
   if (wave == 0) {
-    spin_until(tcnt, (unsigned)((1 + p.unit_tiles) * p.S), kTileWaitTicks);
+    spin_until(tcnt, (unsigned)((p.unit_tiles > 0 ? 2 : 1) * p.S), kTileWaitTicks);
     if (lane == 0) __hip_atomic_store(&s_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   } else {
     while (__hip_atomic_load(&s_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)

@@ -98,10 +98,11 @@ struct DecodeArgs {
   int unit_tiles;
   float *t_part;
   const float *t;
-  // words that are zero between calls: tile g's at tile_cnt + g
-  // kDecodeCtrStride, a cache line each: [0] contributors that stored their
-  // partials plus shrink-carrier workgroups done, [1] finalization items
-  // past the wait for them
+  // words that are zero between calls, a cache line each (kDecodeCtrStride
+  // words apart): tile g's at tile_cnt + g kDecodeCtrStride, [0]
+  // contributors that stored their partials plus k ranges whose carriers
+  // are all done, [1] finalization items past the wait for them; then range
+  // z's carrier count at tile_cnt + (n_tiles + z) kDecodeCtrStride
   unsigned *tile_cnt;
 };
 
@@ -122,10 +123,8 @@ constexpr int kDecodeTileOut = 128;
 // outputs, so that their launch still spreads over the chip.
 constexpr int kDecodeTileOutSmall = 64;
 constexpr int kDecodeSmallTileMaxOut = 2048;
-// Waves of a decode workgroup of nsw waves that carry a shrink unit: the
-// upper half of a 128-output tile's, every wave of a 64-output tile's (the
-// small tiles' launches have fewer workgroups to spread the units over).
-constexpr int decode_carriers(int nsw) { return nsw >= 8 ? nsw / 2 : nsw; }
+// Workgroups of a decode launch that may carry the shrink's units.
+constexpr int kDecodeMaxCarrierWgs = 64;
 
 // Rows per shrink unit; its 64-column stages in LDS at a time (16 KB each).
 constexpr int kShrinkRows = 64;

@@ -190,7 +190,7 @@ WsLayout ws_layout(const Cfg &c, int n, int R, int k_in, size_t data_base = 0) {
     // on n_out alone), the prep shrink's arrival counters, the slice
     // partials, the shrink's partials, then t
     const size_t tiles = (size_t)c.n_ntiles;
-    w.tile_cnt = off; off = up256(off + tiles * kDecodeCtrStride * 4);
+    w.tile_cnt = off; off = up256(off + (tiles + c.splits) * kDecodeCtrStride * 4);
     w.shrink_counters = off; off = up256(off + (size_t)c.zero_units * 4);
     w.zero_end = off; off = std::max(off, data_base);
     w.partials = off;
@@ -484,16 +484,16 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
     da.t_part = (float *)(ws + L.t);
     da.tile_cnt = (unsigned *)(ws + L.tile_cnt);
     // The shrink rides the decode launch when its units (pool slots x
-    // 16-rank blocks) fit on the carriers of a few tiles: those workgroups,
-    // the first ones of the launch, never wait before they count themselves
-    // in, and every other workgroup waits for them, so at most 32 of them
-    // keeps the launch safe wherever 32 workgroups fit at once.  Otherwise a
-    // prep launch computes t first.
-    const int carriers = decode_carriers(c.to / 16);
+    // 16-rank blocks, two per carrier workgroup) fit on a few tiles: those
+    // workgroups, the first ones of the launch, never wait before they
+    // count themselves in, and every other workgroup waits for them, so at
+    // most kDecodeMaxCarrierWgs of them keeps the launch safe wherever that
+    // many workgroups fit at once (a quarter of the chip's CUs).  Otherwise
+    // a prep launch computes t first.
     const int units = R > 0 ? rd.max_loras * (R / 16) : 0;
-    const int ut = (units + carriers - 1) / carriers;
+    const int ut = (units + 1) / 2;
     da.unit_tiles = R > 0 && R <= 64 && rd.max_loras * R <= kDecodeUnitRanks && ut <= c.n_ntiles &&
-                            ut * c.splits <= 32
+                            ut * c.splits <= kDecodeMaxCarrierWgs
                         ? ut
                         : 0;
     const bool fold = stack && stack->n_levels > 0 && has_lora;
