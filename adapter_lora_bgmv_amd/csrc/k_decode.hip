@@ -160,13 +160,17 @@ __device__ __forceinline__ void issue_part(const Slice &sl, int kb, int ke, int 
 }
 
 // The MFMAs of a slice against the x rows in LDS, stage by stage as its
-// loads land (`extra` more vector-memory operations issued after all of
-// them, `mid` more between the first and the second half of a whole range).
+// loads land (on a shorter range `extra` more vector-memory operations were
+// issued after all of them; on a whole range MID more between its halves).
 // acc[b] = D[16 slice rows][16 x rows of row block b]: lane l holds slice
 // rows 4 (l / 16) .. +3 of x row 16 b + l % 16.
-template <int NB, bool FULL>
+// On a whole range every wait is a constant (MID, the loads issued between
+// the halves, is a template argument): a wait whose count is known only at
+// run time leaves the compiler unsure which loads have landed, and it then
+// waits for all of them before the first stage.
+template <int NB, bool FULL, int MID = 0>
 __device__ __forceinline__ void slice_mma(uint4 (&v)[2 * kNSt], const uint4 *xs, uint4 *wb, int kb, int ke, int nst,
-                                          f32x4 (&acc)[NB], int extra = 0, int mid = 0) {
+                                          f32x4 (&acc)[NB], int extra = 0) {
   const int lane = threadIdx.x & 63;
   constexpr int XR = 16 * NB;
 #pragma unroll
@@ -174,8 +178,8 @@ __device__ __forceinline__ void slice_mma(uint4 (&v)[2 * kNSt], const uint4 *xs,
 #pragma unroll
   for (int st = 0; st < kNSt; ++st) {
     if (FULL || st < nst) {
-      if (FULL) {  // a constant once the loop is unrolled, plus the operations issued after
-        wait_vm(2 * (kNSt - 1 - st) + extra + (st < kNSt / 2 ? mid : 0));
+      if (FULL) {  // a constant once the loop is unrolled
+        wait_vm(2 * (kNSt - 1 - st) + (st < kNSt / 2 ? MID : 0));
       } else {
         wait_vm(2 * (nst - 1 - st) + extra);
         if (kb + st * 64 + (lane & 7) * 8 >= ke) v[2 * st] = v[2 * st + 1] = z4();
@@ -326,15 +330,26 @@ __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFo
     const int P = p.rd.max_loras;
     const auto tall = coherent_rsrc(p.t_part, (uint32_t)((size_t)p.S * P * p.n * R * 4));
     const int q = routed ? rr.slot : 0;
+    auto piece_off = [&](int rb) { return (uint32_t)((q * p.n + ic) * R + rb * 16 + 4 * (lane >> 4)) * 4; };
+    const uint32_t zstep = (uint32_t)(P * p.n * R) * 4;
+    // the first rank block's first eight ranges go out with the partials and
+    // B, in straight-line code (a loop would start with a wait for them)
+    f32x4 pz[8];
+    {
+      const uint32_t off = piece_off(0);
+#pragma unroll
+      for (int zz = 0; zz < 8; ++zz)
+        pz[zz] = zz < p.S ? ld16_coherent(tall, off, zz * zstep) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     for (int rb = 0; rb < R / 16; ++rb) {
-      const uint32_t off = (uint32_t)((q * p.n + ic) * R + rb * 16 + 4 * (lane >> 4)) * 4;
+      const uint32_t off = piece_off(rb);
       f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int z0 = 0; z0 < p.S; z0 += 8) {
-        f32x4 pz[8];
+        if (rb > 0 || z0 > 0) {
 #pragma unroll
-        for (int zz = 0; zz < 8; ++zz)
-          pz[zz] = z0 + zz < p.S ? ld16_coherent(tall, off, (uint32_t)((z0 + zz) * P * p.n * R) * 4)
-                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int zz = 0; zz < 8; ++zz)
+            pz[zz] = z0 + zz < p.S ? ld16_coherent(tall, off, (z0 + zz) * zstep) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
         for (int zz = 0; zz < 8; ++zz)
           if (z0 + zz < p.S) sum = z0 + zz == 0 ? pz[zz] : sum + pz[zz];
@@ -476,17 +491,15 @@ __global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFol
   // the unit's A entry: a scalar read in flight while the first half of W
   // goes out
   const uint64_t aentry = cwg ? scalar_entry(p.rd.a_table, unit ? uk / RB : 0) : 0;
-  if (full) issue_full<0, kNSt / 2>(wsl, v);
-  else issue_part(wsl, kb, ke, nst, v);
   int uslot = -1, urb = 0;
   uint4 va[2 * SP];
-  const u16 *A = (const u16 *)aentry;
   const int st0 = pi * SP;
-  int na = 0;  // the part's A loads
-  if (unit && A != nullptr) {
-    uslot = uk / RB;
-    urb = uk % RB;
+  f32x4 acc[NB], acct[NB];
+  // The part's A loads: stages st0 .. st0 + SP - 1 below nst; returns how
+  // many went out.
+  auto issue_a = [&](const u16 *A) {
     const Slice asl = make_slice(A + (size_t)urb * 16 * p.k_in, p.k_in, 0, 16, kb);
+    int na = 0;
 #pragma unroll
     for (int q = 0; q < SP; ++q) {
       const int st = st0 + q;
@@ -498,10 +511,41 @@ __global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFol
         na += 2;
       }
     }
-  }
-  if (full) issue_full<kNSt / 2, kNSt>(wsl, v);
-  wait_vm(2 * nst + na);  // this wave's x stages have landed
-  if (!full)
+    return na;
+  };
+  if (full) {
+    // A whole range: each branch below runs from the W issue to the last
+    // MFMA with no join in between, so every wait is a constant the
+    // compiler can place (a join of paths with different loads in flight
+    // would make it wait for all of them before the first stage).
+    issue_full<0, kNSt / 2>(wsl, v);
+    const u16 *A = (const u16 *)aentry;
+    if (unit && A != nullptr) {  // the part's A rows go out between W's halves
+      uslot = uk / RB;
+      urb = uk % RB;
+      (void)issue_a(A);
+      issue_full<kNSt / 2, kNSt>(wsl, v);
+      wait_vm(2 * kNSt + 2 * SP);  // this wave's x stages have landed
+      __syncthreads();             // x is in LDS
+      slice_mma<NB, true, 2 * SP>(v, xs, wb[wave], kb, ke, nst, acc);
+    } else {
+      issue_full<kNSt / 2, kNSt>(wsl, v);
+      wait_vm(2 * kNSt);
+      __syncthreads();
+      slice_mma<NB, true, 0>(v, xs, wb[wave], kb, ke, nst, acc);
+    }
+  } else {
+    // the last, shorter range: A after all of W; the chunks of x past ke
+    // are zeroed once they land
+    issue_part(wsl, kb, ke, nst, v);
+    const u16 *A = (const u16 *)aentry;
+    int na = 0;
+    if (unit && A != nullptr) {
+      uslot = uk / RB;
+      urb = uk % RB;
+      na = issue_a(A);
+    }
+    wait_vm(2 * nst + na);
     for (int st = wave; st < nst; st += NSW) {
       if (kb + st * 64 + 64 <= ke) continue;
 #pragma unroll
@@ -510,12 +554,9 @@ __global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFol
         if (kb + st * 64 + ((lane & 7) ^ ((r >> 1) & 7)) * 8 >= ke) xs[(st * XR + 8 * i) * 8 + lane] = z4();
       }
     }
-  __syncthreads();  // x is in LDS
-
-  f32x4 acc[NB], acct[NB];
-  // A went out between W's halves (a whole range) or after all of W
-  if (full) slice_mma<NB, true>(v, xs, wb[wave], kb, ke, nst, acc, 0, na);
-  else slice_mma<NB, false>(v, xs, wb[wave], kb, ke, nst, acc, na);
+    __syncthreads();
+    slice_mma<NB, false>(v, xs, wb[wave], kb, ke, nst, acc, na);
+  }
   wait_vmcnt<0>();
   if (uslot >= 0) part_mma<NB, SP>(va, xs, wb[wave], kb, ke, nst, st0, acct);
   if (p.S == 1 && !p.has_lora && f.n_levels == 0) {  // nothing to sum: y directly
