@@ -168,7 +168,7 @@ __device__ __forceinline__ void issue_part(const Slice &sl, int kb, int ke, int 
 // the halves, is a template argument): a wait whose count is known only at
 // run time leaves the compiler unsure which loads have landed, and it then
 // waits for all of them before the first stage.
-template <int NB, bool FULL, int MID = 0>
+template <int NB, bool FULL, int MID = 0, int AFTER = 0>
 __device__ __forceinline__ void slice_mma(uint4 (&v)[2 * kNSt], const uint4 *xs, uint4 *wb, int kb, int ke, int nst,
                                           f32x4 (&acc)[NB], int extra = 0) {
   const int lane = threadIdx.x & 63;
@@ -179,7 +179,7 @@ __device__ __forceinline__ void slice_mma(uint4 (&v)[2 * kNSt], const uint4 *xs,
   for (int st = 0; st < kNSt; ++st) {
     if (FULL || st < nst) {
       if (FULL) {  // a constant once the loop is unrolled
-        wait_vm(2 * (kNSt - 1 - st) + (st < kNSt / 2 ? MID : 0));
+        wait_vm(2 * (kNSt - 1 - st) + AFTER + (st < kNSt / 2 ? MID : 0));
       } else {
         wait_vm(2 * (nst - 1 - st) + extra);
         if (kb + st * 64 + (lane & 7) * 8 >= ke) v[2 * st] = v[2 * st + 1] = z4();

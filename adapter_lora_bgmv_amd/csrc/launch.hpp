@@ -177,6 +177,14 @@ struct ShrinkLevels {
 size_t prep_lds_bytes(const PrepArgs &a);
 hipError_t launch_shrink_levels(const ShrinkLevels &s, hipStream_t st);
 
+// The standalone shrink and expand-fold by pool slot (k_bgmv.hip), bf16,
+// for batches of at most kBgmvMaxRows rows; x, t and y 16-byte aligned.
+constexpr int kBgmvMaxRows = 1024;
+hipError_t launch_bgmv_shrink(const RouteDev &rd, const int32_t *seq_slot, int n, const u16 *x, int x_stride,
+                              int k_in, float *t, hipStream_t st);
+hipError_t launch_bgmv_expand(const RouteDev &rd, const int32_t *seq_slot, int n, const float *t, u16 *y,
+                              int y_stride, int n_out, hipStream_t st);
+
 hipError_t launch_shrink_f32(const RouteDev &rd, const Routing &rt, const float *x, int x_stride,
                              int k_in, int n, float *t, hipStream_t st);
 hipError_t launch_apply_f32(const RouteDev &rd, const Routing &rt, bool has_lora, const float *W,

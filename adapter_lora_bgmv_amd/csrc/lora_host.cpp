@@ -701,6 +701,10 @@ int lora_shrink(const lora_route *route, const void *x, uint32_t x_row_stride, c
     return launch_status(launch_shrink_f32(rd, rt, (const float *)x, (int)x_row_stride, (int)route->k_in, (int)n,
                                            t, st),
                          what);
+  if (n <= (uint32_t)kBgmvMaxRows)  // decode-sized: by pool slot, each A read once
+    return launch_status(launch_bgmv_shrink(rd, seq_slot, (int)n, (const u16 *)x, (int)x_row_stride,
+                                            (int)route->k_in, t, st),
+                         what);
   PrepArgs pa{};
   pa.rd = rd;
   pa.rt = rt;
@@ -732,6 +736,12 @@ int lora_expand_fold(const lora_route *route, const float *t, const int32_t *seq
     return fail(LORA_ERR_NULL_PTR, "%s: [n_out %u x k_in %u]: t %p, seq_slot %p, y %p must be non-NULL", what,
                 route->n_out, route->k_in, (const void *)t, (const void *)seq_slot, y);
   if (int e = check_device(what)) return e;
+  // decode-sized bf16 batches: by pool slot, each B read once, 16-byte y
+  // pieces (which need 16-byte aligned rows)
+  if (route->dtype == LORA_BF16 && n <= (uint32_t)kBgmvMaxRows && aligned16(y) && aligned16(t))
+    return launch_status(launch_bgmv_expand(route_dev(route), seq_slot, (int)n, t, (u16 *)y, (int)y_row_stride,
+                                            (int)route->n_out, (hipStream_t)stream),
+                         what);
   return launch_status(launch_expand_fold(route_dev(route), route->dtype, routing_decode(seq_slot), t, y,
                                           (int)y_row_stride, (int)route->n_out, (int)n, (hipStream_t)stream),
                        what);

@@ -82,6 +82,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=32)
     p.add_argument("--config", default="decode_bgmv")
     p.add_argument("--no-others", action="store_true", help="skip the other workloads")
+    p.add_argument("--others", default=None,
+                   help="comma-separated subset of the other workloads (decode_bgmv_pair is one)")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     p.add_argument("--no-base", action="store_true", help="skip the base-only (no adapter) timing")
     p.add_argument("--cpu-seconds", type=float, default=5.0)
@@ -316,6 +318,55 @@ def time_workload(name, steps, warmup, apply=True):
                         "post_us_mean": float(post_ms.mean() * 1e3)}
 
 
+def time_pair(steps, warmup):
+    """The standalone two-step delta on the decode workload: lora_shrink then
+    lora_expand_fold (y += s B t in place), one graph of `steps` steps over
+    rotated input copies.  Its bytes: the touched A and B once, the adapted
+    rows' x, y read and written, t written and read."""
+    import torch
+    from adapter_lora_bgmv_amd import binding as B
+    from adapter_lora_bgmv_amd.harness import DeviceWorkload
+
+    wl = workload("decode_bgmv")
+    R = ROTATE["decode_bgmv"]
+    dws = [DeviceWorkload(wl) for _ in range(R)]
+    ts = [torch.empty(d.n, wl.max_rank, dtype=torch.float32, device="cuda") for d in dws]
+
+    def step(i, stream=None):
+        d = dws[i % R]
+        B.lora_shrink(d.route, d.x, d.x_row_stride, d.seq_slot, d.n, ts[i % R], stream)
+        B.lora_expand_fold(d.route, ts[i % R], d.seq_slot, d.n, d.y, d.y_row_stride, stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(steps):
+            step(i, side)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    del g
+    pairs, _ = resolve_rows(wl, dws[0].scale_table_host)
+    active = int((pairs >= 0).sum())
+    touched = len(set(int(q) for q in pairs if q >= 0))
+    Rk, k, o = wl.max_rank, wl.k_in, wl.n_out
+    path = touched * Rk * (k + o) * 2 + active * k * 2 + 2 * active * o * 2 + 2 * active * Rk * 4
+    flops = 2.0 * active * Rk * (k + o)
+    step_s = ms_per_step * 1e-3
+    return {"workload": "decode bgmv pair: lora_shrink + lora_expand_fold on the decode batch "
+                        "(16 slots r=16 over 4096 x 4096, 57 adapted rows), y += s B (A x) in place",
+            "ms_per_step": round(ms_per_step, 5), "rows_per_s": active / step_s,
+            "path_GBps": path / step_s / 1e9, "path_TFLOPs": flops / step_s / 1e12, "bound": "hbm",
+            "algorithmic_bytes": path, "algorithmic_flops": flops,
+            "frac_of_peak": path / step_s / 1e9 / HBM_PEAK_GBPS,
+            "kernels": "bgmv_shrink_kernel + bgmv_expand_kernel (two launches)"}
+
+
 def summarize(name, counts, t, base_t=None):
     main_s = t["main_us_mean"] * 1e-6
     step_s = t["ms_per_step"] * 1e-3
@@ -427,9 +478,13 @@ def main():
     print(f"# {name}: {json.dumps(head)}", file=sys.stderr, flush=True)
 
     others = {}
+    pick = set(a.others.split(",")) if a.others else None
+    if not a.no_others and name == "decode_bgmv" and (pick is None or "decode_bgmv_pair" in pick):
+        others["decode_bgmv_pair"] = time_pair(min(a.steps, 64), 8)
+        print(f"# decode_bgmv_pair: {json.dumps(others['decode_bgmv_pair'])}", file=sys.stderr, flush=True)
     if not a.no_others:
         for other in OTHERS:
-            if other == name:
+            if other == name or (pick is not None and other not in pick):
                 continue
             _, c2, t2 = time_workload(other, min(a.steps, 64), 8)
             others[other] = summarize(other, c2, t2)
