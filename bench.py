@@ -389,6 +389,9 @@ def summarize(name, counts, t, base_t=None):
         out["frac_of_peak"] = out["main_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
     elif BOUND[name] == "hbm":
         out["frac_of_peak"] = out["main_GBps"] / HBM_PEAK_GBPS
+    traffic = measured_traffic(counts["main_kernel"].split(" ")[0], name)
+    if traffic is not None:
+        out["traffic"] = traffic
     if base_t is not None:
         out["base_only_ms_per_step"] = round(base_t["ms_per_step"], 5)
         out["base_only_main_us"] = round(base_t["main_us_mean"], 2)
@@ -398,17 +401,21 @@ def summarize(name, counts, t, base_t=None):
 # ------------------------------------------------------------------ counters
 def measured_traffic(kernel, workload):
     """HBM bytes per dispatch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    runs, or None when those counters were taken on a different kernel source."""
+    runs, or None when there are none for this kernel and workload or they were
+    taken on different kernel or host sources."""
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     try:
         with open(os.path.join(root, "profiles", "hbm_traffic.json")) as f:
-            rec = json.load(f).get(kernel)
-        if not rec or rec.get("workload") != workload:
+            rec = json.load(f).get(f"{kernel}:{workload}")
+        if not rec:
             return None
-        with open(os.path.join(root, rec["source"]), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
-                return None
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(root, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["sources_sha256"]:
+            return None
         return rec["fetch_bytes_per_dispatch"] + rec["write_bytes_per_dispatch"]
     except (OSError, ValueError, KeyError):
         return None
