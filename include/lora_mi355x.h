@@ -225,8 +225,8 @@ int lora_expand_fold(const lora_route *route, const float *t, const int32_t *seq
  * identical to the skipped rows of a routed call with the same shape.
  * W [dev] [n_out][w_row_stride]; x, seq_slot, y as above (seq_slot may be
  * NULL when route is NULL).  workspace [dev], see the conventions above.
- * Decode-shaped batches (n up to a few hundred rows) are the target; n is
- * limited to 8192.
+ * Batches up to 64 rows take the one-launch decode kernel, larger ones the
+ * tiled GEMM; n is limited to 16384 (LORA_ERR_SHAPE above).
  */
 int lora_apply(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W,
                uint32_t w_row_stride, const lora_route *route, const void *x,
@@ -387,7 +387,7 @@ int lora_embed_rows(int32_t dtype, uint32_t n_vocab, uint32_t n_embd, const void
  * y is rounded at most twice whatever the depth.  workspace [dev] of at
  * least lora_workspace_bytes(LORA_OP_STACK, dtype, n, n_out, k_in, largest
  * max_rank, n_levels) bytes, zero-filled before its first use with a shape.
- * Decode-shaped batches (n up to 8192).
+ * Decode-shaped batches are the target; n is limited to 16384.
  */
 int lora_apply_stack(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W,
                      uint32_t w_row_stride, const lora_route *routes,
