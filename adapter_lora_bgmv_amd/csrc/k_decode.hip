@@ -71,7 +71,7 @@ __device__ __forceinline__ void wait_vm(int n) {
 
 // The wait for a tile's contributors gives up after this many ticks of the
 // 100 MHz real-time counter (0.5 s: only a fault elsewhere gets there), so
-// every wave reaches the end of the kernel.
+// every wave reaches the end of the kernel; the tile's outputs are then NaN.
 constexpr uint64_t kTileWaitTicks = 50000000ull;
 
 // Polls a counter until it reaches `target` or `ticks` pass.  Each poll is
@@ -633,19 +633,28 @@ __global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFol
   // wave 0 alone polls the tile's arrival count (few pollers keep the line
   // free for the arrivals); the workgroup's other item waves wait on LDS
   const RowRoute rr0 = row_route_decode(p, 16 * (wave % NB) + (lane & 15));  // in flight during the wait
+  // s_ready: 1 once every arrival is in, 2 if the wait gave up (then the
+  // tile's outputs are written as NaN: a loud failure, never partial sums)
   if (wave == 0) {
-    spin_until(tcnt, (unsigned)((p.unit_tiles > 0 ? 2 : 1) * p.S), kTileWaitTicks);
-    if (lane == 0) __hip_atomic_store(&s_ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const unsigned need = (unsigned)((p.unit_tiles > 0 ? 2 : 1) * p.S);
+    const unsigned got = spin_until(tcnt, need, kTileWaitTicks);
+    if (lane == 0) __hip_atomic_store(&s_ready, got >= need ? 1 : 2, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   } else {
     while (__hip_atomic_load(&s_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
       __builtin_amdgcn_s_sleep(1);
   }
   asm volatile("" ::: "memory");
+  const bool gave_up = __hip_atomic_load(&s_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 2;
   const unsigned items_per_tile = (unsigned)(NSL * NB);
   for (int it = wave; it < n_items; it += NSW) {
     const int j = z + p.S * (it / NB), b = it % NB;
     const RowRoute rr = it == wave ? rr0 : row_route_decode(p, 16 * b + (lane & 15));
-    finalize_item(p, f, rr, g, j, b, (float *)&wb[wave][0]);
+    if (gave_up) {
+      const int i = 16 * b + (lane & 15), o = g * p.tile_out + 16 * j + 4 * (lane >> 4);
+      if (i < p.n && o < p.n_out) *(uint2 *)(p.y + (size_t)i * p.y_row_stride + o) = make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
+    } else {
+      finalize_item(p, f, rr, g, j, b, (float *)&wb[wave][0]);
+    }
     if (wave_atomic_add(tpass, 1u) == items_per_tile - 1) {  // every item is past the wait
       wave_store0(tcnt);
       wave_store0(tpass);

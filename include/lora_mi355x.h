@@ -226,7 +226,11 @@ int lora_expand_fold(const lora_route *route, const float *t, const int32_t *seq
  * W [dev] [n_out][w_row_stride]; x, seq_slot, y as above (seq_slot may be
  * NULL when route is NULL).  workspace [dev], see the conventions above.
  * Batches up to 64 rows take the one-launch decode kernel, larger ones the
- * tiled GEMM; n is limited to 16384 (LORA_ERR_SHAPE above).
+ * tiled GEMM; n is limited to 16384 (LORA_ERR_SHAPE above).  The decode
+ * kernel's workgroups wait for each other within the launch; should such a
+ * wait ever give up (0.5 s, which only a device that cannot hold the
+ * launch's first workgroups at once would reach), the tile's outputs are
+ * written as NaN and the workspace must be zero-filled again.
  */
 int lora_apply(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W,
                uint32_t w_row_stride, const lora_route *route, const void *x,
