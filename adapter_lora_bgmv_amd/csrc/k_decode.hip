@@ -294,8 +294,9 @@ __device__ __forceinline__ uint64_t scalar_entry(const void *const *tab, int idx
 // of t) has been stored; rr is the route of this lane's row.  Every load the
 // item needs goes out before any arithmetic: the S partials, then t (from
 // the pieces of the row's slot, or as a prep launch left it), then B.
+template <typename WaitPieces>
 __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFold &f, const RowRoute &rr, int g, int j,
-                                              int b, float *tb) {
+                                              int b, float *tb, WaitPieces wait_pieces) {
   const int lane = threadIdx.x & 63;
   const int i = 16 * b + (lane & 15);
   const int ic = min(i, p.n - 1);
@@ -323,10 +324,13 @@ __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFo
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int h = 0; h < 2; ++h) b0[c][h] = expand ? ldg16(bq + (size_t)c * R + 8 * h) : z4();
+  // the shrink's pieces may still be on their way: the partials and B are in
+  // flight meanwhile (false: the wait gave up)
+  const bool pieces_ok = wait_pieces(p.unit_tiles > 0 && any);
   // t of row i, ranks 4 (l / 16) .. +3 of every 16-rank block, from the
   // pieces of its slot's units: the S ranges summed in range order; the
   // row's four lanes meet in tb
-  if (p.unit_tiles > 0 && any) {
+  if (p.unit_tiles > 0 && any && pieces_ok) {
     const int P = p.rd.max_loras;
     const auto tall = coherent_rsrc(p.t_part, (uint32_t)((size_t)p.S * P * p.n * R * 4));
     const int q = routed ? rr.slot : 0;
@@ -436,7 +440,8 @@ __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFo
     }
   }
   *(uint2 *)(p.y + (size_t)i * p.y_row_stride + o) =
-      make_uint2(pack2(f2bf(v[0]), f2bf(v[1])), pack2(f2bf(v[2]), f2bf(v[3])));
+      pieces_ok ? make_uint2(pack2(f2bf(v[0]), f2bf(v[1])), pack2(f2bf(v[2]), f2bf(v[3])))
+                : make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
 }
 
 }  // namespace
@@ -449,7 +454,7 @@ __global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFol
   constexpr int NSL = NSW;      // slices per tile
   __shared__ __attribute__((aligned(16))) uint4 xs[kNSt * XR * 8];
   __shared__ __attribute__((aligned(16))) uint4 wb[NSW][2 * 128];
-  __shared__ int s_done, s_ready;
+  __shared__ int s_done, s_ready, s_pready;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = blockIdx.x / p.S, z = blockIdx.x % p.S;
@@ -474,6 +479,7 @@ __global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFol
   if (tid == 0) {
     s_done = 0;
     s_ready = 0;
+    s_pready = 0;
   }
   // The shrink rides this launch on the first unit_tiles tiles: their
   // workgroups take units (pool slot x 16-rank block) 2 g and 2 g + 1, each
@@ -607,20 +613,21 @@ __global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFol
   // (a carrier workgroup into every tile: its pieces are stored too); each
   // tile's words sit on a cache line of their own
   unsigned *tcnt = p.tile_cnt + (size_t)g * kDecodeCtrStride;
-  unsigned *tpass = tcnt + 1;
+  unsigned *tpass = tcnt + 1, *tpieces = tcnt + 2;
   int last = 0;
   if (lane == 0) last = atomicAdd(&s_done, 1) == NSW - 1;
   // a carrier workgroup whose pieces are all stored counts itself into its
   // range's carrier count; the range's last carrier counts the range into
-  // every tile (one atomic per lane) and clears the range count, so that
-  // each tile's finalizers watch their own line and no line takes more
-  // than 2 S increments: a tile is ready at 2 S arrivals
+  // every tile's pieces word (one atomic per lane) and clears the range
+  // count, so that each tile's finalizers watch their own line and no line
+  // takes more than 2 S increments: a tile's partials are ready at S
+  // arrivals, the pieces at S ranges
   if (cwg && __builtin_amdgcn_readfirstlane(last)) {
     unsigned *ccnt = p.tile_cnt + (size_t)(p.n_tiles + z) * kDecodeCtrStride;
     if (wave_atomic_add(ccnt, 1u) == (unsigned)p.unit_tiles - 1) {
       wave_store0(ccnt);
       for (int t = lane; t < p.n_tiles; t += 64)
-        __hip_atomic_fetch_add(p.tile_cnt + (size_t)t * kDecodeCtrStride, 1u, __ATOMIC_RELAXED,
+        __hip_atomic_fetch_add(p.tile_cnt + (size_t)t * kDecodeCtrStride + 2, 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -636,7 +643,7 @@ __global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFol
   // s_ready: 1 once every arrival is in, 2 if the wait gave up (then the
   // tile's outputs are written as NaN: a loud failure, never partial sums)
   if (wave == 0) {
-    const unsigned need = (unsigned)((p.unit_tiles > 0 ? 2 : 1) * p.S);
+    const unsigned need = (unsigned)p.S;
     const unsigned got = spin_until(tcnt, need, kTileWaitTicks);
     if (lane == 0) __hip_atomic_store(&s_ready, got >= need ? 1 : 2, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   } else {
@@ -645,6 +652,25 @@ __global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFol
   }
   asm volatile("" ::: "memory");
   const bool gave_up = __hip_atomic_load(&s_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 2;
+  // the shrink's pieces: wave 0 waits for every range's carriers whether or
+  // not its rows need them (so that no carrier counts in after the words are
+  // cleared below), the other waves when theirs do
+  auto wait_pieces = [&](bool need) {
+    if (p.unit_tiles == 0) return true;
+    if (wave == 0) {
+      if (__hip_atomic_load(&s_pready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
+        const unsigned got = spin_until(tpieces, (unsigned)p.S, kTileWaitTicks);
+        if (lane == 0)
+          __hip_atomic_store(&s_pready, got >= (unsigned)p.S ? 1 : 2, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    } else {
+      if (!need) return true;
+      while (__hip_atomic_load(&s_pready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+    return __hip_atomic_load(&s_pready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 1;
+  };
   const unsigned items_per_tile = (unsigned)(NSL * NB);
   for (int it = wave; it < n_items; it += NSW) {
     const int j = z + p.S * (it / NB), b = it % NB;
@@ -653,11 +679,12 @@ __global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFol
       const int i = 16 * b + (lane & 15), o = g * p.tile_out + 16 * j + 4 * (lane >> 4);
       if (i < p.n && o < p.n_out) *(uint2 *)(p.y + (size_t)i * p.y_row_stride + o) = make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
     } else {
-      finalize_item(p, f, rr, g, j, b, (float *)&wb[wave][0]);
+      finalize_item(p, f, rr, g, j, b, (float *)&wb[wave][0], wait_pieces);
     }
-    if (wave_atomic_add(tpass, 1u) == items_per_tile - 1) {  // every item is past the wait
+    if (wave_atomic_add(tpass, 1u) == items_per_tile - 1) {  // every item is past the waits
       wave_store0(tcnt);
       wave_store0(tpass);
+      wave_store0(tpieces);
     }
   }
 }
