@@ -422,21 +422,35 @@ def measured_traffic(kernel, workload):
 
 
 # ------------------------------------------------------------------ CPU baseline
+# rows of each workload the oracle baseline times per batch (None: all of
+# them); a seeded sample keeps every config's CPU time bounded
+CPU_SAMPLE_ROWS = {"single_projection_f32": None, "decode_bgmv": None, "fused_gate_up": 32,
+                   "prefill_segmented": 32, "moe_down_gather": 96}
+
+
 def cpu_baseline(name, seconds):
-    """The oracle over whole batches of the workload: the median of three
-    samples of about `seconds` each on all host threads, and one on one thread."""
+    """The oracle over batches of the workload (or a seeded sample of its rows):
+    the median of three samples of about `seconds` each on all host threads,
+    and one on one thread, in rows of the workload per second."""
     import oracle
     wl = workload(name)
     orc = oracle.get()
     st = orc.scale_table(wl.adapters)
     counts = algorithmic_counts(wl, st)
-    rows = counts["adapted_rows"] or counts["rows"]
+    n_rows = counts["rows"]
+    k = CPU_SAMPLE_ROWS.get(name)
+    rows = None
+    if k is not None and k < n_rows:
+        rows = np.sort(np.random.default_rng(0).choice(len(wl.x), size=k, replace=False)).astype(np.int32)
+    # rows/s: adapted rows per batch for the decode batch (the headline's unit),
+    # otherwise every row
+    per_batch = (counts["adapted_rows"] if name == "decode_bgmv" else n_rows) if rows is None else len(rows)
 
     def sample():
         reps = 0
         t0 = time.perf_counter()
         while True:
-            orc.run(wl, scale_table=st)
+            orc.run(wl, rows=rows, scale_table=st)
             reps += 1
             el = time.perf_counter() - t0
             if el >= seconds or reps >= 1000:
@@ -444,18 +458,19 @@ def cpu_baseline(name, seconds):
 
     cores = orc.threads
     samples = [sample() for _ in range(3)]
-    rates = sorted(rows * r / e for r, e in samples)
+    rates = sorted(per_batch * r / e for r, e in samples)
     orc.set_threads(1)
     try:
         r1, e1 = sample()
     finally:
         orc.set_threads(cores)
+    what = (f"whole {name} batches ({counts['rows']} rows, {counts['adapted_rows']} adapted)" if rows is None
+            else f"a seeded sample of {len(rows)} of the {n_rows} rows of {name}")
     return {"value": rates[1], "unit": "rows/s", "cores": cores, "kind": "oracle",
-            "sample": f"median of 3 samples of whole {name} batches ({counts['rows']} rows, "
-                      f"{counts['adapted_rows']} adapted) through the fp64 oracle, "
+            "sample": f"median of 3 samples of {what} through the fp64 oracle, "
                       f"{', '.join(f'{r} in {e:.1f} s' for r, e in samples)}",
             "samples": rates,
-            "single_core": {"value": rows * r1 / e1, "unit": "rows/s", "cores": 1,
+            "single_core": {"value": per_batch * r1 / e1, "unit": "rows/s", "cores": 1,
                             "sample": f"{r1} batches in {e1:.1f} s"}}
 
 
@@ -495,6 +510,8 @@ def main():
                 continue
             _, c2, t2 = time_workload(other, min(a.steps, 64), 8)
             others[other] = summarize(other, c2, t2)
+            if not a.no_cpu and other in CPU_SAMPLE_ROWS:
+                others[other]["cpu_baseline"] = cpu_baseline(other, a.cpu_seconds / 2)
             print(f"# {other}: {json.dumps(others[other])}", file=sys.stderr, flush=True)
 
     bound = BOUND[name]
