@@ -82,13 +82,11 @@ constexpr int kShrinkWaves = 4;
 // Workgroup (s, r): rank r of slot s.  Wave w takes the 512-column k steps
 // w, w + 4, ...; lane l the 8 columns 8 l of each step.  A lane's sum over
 // its columns (k order), the wave's butterfly, then the four waves in order.
-__global__ __launch_bounds__(64 * kShrinkWaves) void bgmv_shrink_kernel(RouteDev rd, const int32_t *seq_slot, int n,
-                                                                         const u16 *x, int x_stride, int k_in,
-                                                                         float *t) {
+__device__ __forceinline__ void shrink_slot_rank(const RouteDev &rd, const int32_t *seq_slot, int n, const u16 *x,
+                                                 int x_stride, int k_in, float *t, int s, int r) {
   __shared__ int rows[kBgmvMaxRows];
   __shared__ int s_cnt;
   __shared__ float part[kShrinkWaves][4];
-  const int s = blockIdx.x / rd.R, r = blockIdx.x % rd.R;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int v0 = wave == 0 && lane < n ? seq_slot[lane] : -1;  // in flight with the table reads
   if (!slot_live(rd, s)) return;  // the same for the whole workgroup
@@ -145,6 +143,22 @@ __global__ __launch_bounds__(64 * kShrinkWaves) void bgmv_shrink_kernel(RouteDev
     }
     __syncthreads();
   }
+}
+
+__global__ __launch_bounds__(64 * kShrinkWaves) void bgmv_shrink_kernel(RouteDev rd, const int32_t *seq_slot, int n,
+                                                                         const u16 *x, int x_stride, int k_in,
+                                                                         float *t) {
+  shrink_slot_rank(rd, seq_slot, n, x, x_stride, k_in, t, blockIdx.x / rd.R, blockIdx.x % rd.R);
+}
+
+// An adapter stack's further levels: level l takes workgroups
+// [l blocks_per_level, (l + 1) blocks_per_level), (slot, rank) as above.
+__global__ __launch_bounds__(64 * kShrinkWaves) void bgmv_shrink_levels_kernel(BgmvLevels L, const u16 *x,
+                                                                                int x_stride, int k_in, int n) {
+  const int l = blockIdx.x / L.blocks_per_level, b = blockIdx.x % L.blocks_per_level;
+  const RouteDev &rd = L.rd[l];
+  if (b >= rd.max_loras * rd.R) return;  // the same for the whole workgroup
+  shrink_slot_rank(rd, L.seq_slot[l], n, x, x_stride, k_in, L.t[l], b / rd.R, b % rd.R);
 }
 
 constexpr int kExpandWaves = 4;
@@ -250,6 +264,14 @@ hipError_t launch_bgmv_shrink(const RouteDev &rd, const int32_t *seq_slot, int n
   if (grid == 0 || n == 0) return hipSuccess;
   hipLaunchKernelGGL(bgmv_shrink_kernel, dim3(grid), dim3(64 * kShrinkWaves), 0, st, rd, seq_slot, n, x, x_stride,
                      k_in, t);
+  return hipGetLastError();
+}
+
+hipError_t launch_bgmv_shrink_levels(const BgmvLevels &L, const u16 *x, int x_stride, int k_in, int n,
+                                     hipStream_t st) {
+  const int grid = L.n_levels * L.blocks_per_level;
+  if (grid == 0 || n == 0) return hipSuccess;
+  hipLaunchKernelGGL(bgmv_shrink_levels_kernel, dim3(grid), dim3(64 * kShrinkWaves), 0, st, L, x, x_stride, k_in, n);
   return hipGetLastError();
 }
 

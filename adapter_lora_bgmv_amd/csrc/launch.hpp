@@ -184,6 +184,17 @@ hipError_t launch_bgmv_shrink(const RouteDev &rd, const int32_t *seq_slot, int n
                               int k_in, float *t, hipStream_t st);
 hipError_t launch_bgmv_expand(const RouteDev &rd, const int32_t *seq_slot, int n, const float *t, u16 *y,
                               int y_stride, int n_out, hipStream_t st);
+// The same shrink for an adapter stack's further levels, in one launch:
+// level l writes t[l] [n][R_l] for its rows that resolve.
+struct BgmvLevels {
+  RouteDev rd[kMaxStackLevels];
+  const int32_t *seq_slot[kMaxStackLevels];
+  float *t[kMaxStackLevels];
+  int n_levels;
+  int blocks_per_level;  // the largest max_loras x R over the levels
+};
+hipError_t launch_bgmv_shrink_levels(const BgmvLevels &L, const u16 *x, int x_stride, int k_in, int n,
+                                     hipStream_t st);
 
 hipError_t launch_shrink_f32(const RouteDev &rd, const Routing &rt, const float *x, int x_stride,
                              int k_in, int n, float *t, hipStream_t st);

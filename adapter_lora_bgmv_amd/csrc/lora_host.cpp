@@ -1117,7 +1117,13 @@ int lora_apply_stack(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W
   StackFold f{};
   f.n_levels = n_levels > 1 ? (int)n_levels - 1 : 0;
   ShrinkLevels sl{};
-  sl.n_levels = dtype == LORA_BF16 ? f.n_levels : 0;
+  // decode-sized bf16 stacks: the further levels' shrinks by pool slot, each
+  // level's t written whole (no k-split partials); larger batches take the
+  // k-split shrink units
+  const bool by_slot = dtype == LORA_BF16 && n <= (uint32_t)kBgmvMaxRows;
+  BgmvLevels bl{};
+  bl.n_levels = by_slot ? f.n_levels : 0;
+  sl.n_levels = dtype == LORA_BF16 && !by_slot ? f.n_levels : 0;
   char *tp = (char *)workspace + apply_bytes;
   for (uint32_t l = 1; l < n_levels; ++l) {
     const RouteDev rd = route_dev(&routes[l]);
@@ -1128,6 +1134,11 @@ int lora_apply_stack(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W
       e = launch_status(launch_shrink_f32(rd, rt, (const float *)x, (int)x_row_stride, (int)k_in, (int)n, t, st),
                         what);
       if (e) return e;
+    } else if (by_slot) {
+      bl.rd[l - 1] = rd;
+      bl.seq_slot[l - 1] = seq_slots[l];
+      bl.t[l - 1] = t;
+      bl.blocks_per_level = std::max(bl.blocks_per_level, rd.max_loras * rd.R);
     } else {
       PrepArgs &pa = sl.lv[l - 1];
       pa.rd = rd;
@@ -1151,6 +1162,10 @@ int lora_apply_stack(int32_t dtype, uint32_t n_out, uint32_t k_in, const void *W
   }
   if (sl.n_levels) {
     e = launch_status(launch_shrink_levels(sl, st), what);
+    if (e) return e;
+  }
+  if (bl.n_levels) {
+    e = launch_status(launch_bgmv_shrink_levels(bl, (const u16 *)x, (int)x_row_stride, (int)k_in, (int)n, st), what);
     if (e) return e;
   }
   bool folded = false;
