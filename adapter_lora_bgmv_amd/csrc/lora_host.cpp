@@ -135,8 +135,11 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
     c.splits = (k_in + kDecodeKR - 1) / kDecodeKR;
   } else if (moe) {
     // one row tile per expert where the batch allows: an expert's W slab is
-    // read once per row tile (128-row tiles from ~96 rows per expert on)
-    c.to = 256; c.tr = n / std::max(1, groups) >= 96 ? 128 : 64; c.splits = 1;
+    // read once per row tile (128-row tiles from ~96 rows per expert on,
+    // 256-row tiles from ~160 when the rank fits the LDS LoRA path)
+    const int per = n / std::max(1, groups);
+    const bool lds_rank = R == 0 || (R <= 64 && 64 % R == 0);
+    c.to = 256; c.tr = per >= 160 && lds_rank ? 256 : (per >= 96 ? 128 : 64); c.splits = 1;
   } else if (n <= 64) {
     c.to = 64; c.tr = 64; c.splits = clampi(k_in / 1024, 1, 8);
   } else if (n <= 128) {

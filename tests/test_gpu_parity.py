@@ -142,17 +142,19 @@ def test_moe_invalid_expert_rows_not_written(orc):
     check(got[keep], ref[keep], "bf16", "moe valid rows")
 
 
-@pytest.mark.parametrize("seed,dtype,E,n,k,n_out", [
-    (24, "bf16", 5, 90, 72, 48),
-    (25, "bf16", 9, 300, 136, 264),    # 300 rows over 9 experts: several row tiles per expert
-    (26, "bf16", 64, 200, 64, 32),     # more experts than rows per expert, many empty
-    (27, "f32", 4, 23, 37, 29),
-    (28, "bf16", 3, 700, 200, 264),    # ~233 rows per expert: 128-row tiles, a ragged last one
+@pytest.mark.parametrize("seed,dtype,E,n,k,n_out,R", [
+    (24, "bf16", 5, 90, 72, 48, 16),
+    (25, "bf16", 9, 300, 136, 264, 16),   # 300 rows over 9 experts: several row tiles per expert
+    (26, "bf16", 64, 200, 64, 32, 16),    # more experts than rows per expert, many empty
+    (27, "f32", 4, 23, 37, 29, 16),
+    (28, "bf16", 3, 700, 200, 264, 16),   # ~233 rows per expert: one ragged 256-row tile each
+    (35, "bf16", 4, 1300, 200, 520, 16),  # ~325 rows per expert: a whole 256-row tile and a ragged one
+    (36, "bf16", 3, 700, 200, 264, 48),   # rank 48 (not a divisor of 64): 128-row tiles
 ])
-def test_moe_grouped_small(orc, seed, dtype, E, n, k, n_out):
+def test_moe_grouped_small(orc, seed, dtype, E, n, k, n_out, R):
     """atlas moe_lora_grouped_down: rows sorted by expert, ranges from
     expert_offsets; rows outside every range keep their sentinel."""
-    wl = WL.random_small(seed, dtype=dtype, k=k, n_out=n_out, n=n, n_slots=3, max_rank=16,
+    wl = WL.random_small(seed, dtype=dtype, k=k, n_out=n_out, n=n, n_slots=3, max_rank=R,
                          kind="moe_grouped", n_experts=E)
     dw = DeviceWorkload(wl)
     dw.y.fill_(float("nan"))
