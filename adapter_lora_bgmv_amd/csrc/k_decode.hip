@@ -11,13 +11,14 @@
 //
 //  * workgroup (g, z) owns output tile g (TO = 16 NSW outputs) over k range z
 //    (kKR = 512 columns; S = ceil(k_in / 512) ranges).  Its x rows over the
-//    range go to LDS once (LDS-DMA, whole lines, XOR-swizzled).  Each of its
-//    NSW waves owns a slice of 16 outputs: it requests its 16 W rows x 512
-//    columns (sixteen 16-byte loads per lane, whole lines, through a buffer
-//    resource), then, one 64-column stage at a time as the loads land, lays
-//    the stage out in a wave-private LDS buffer and runs the MFMAs of its 16
-//    outputs against every row block of x.  No block-wide barrier sits in
-//    the stream.
+//    range go to LDS once (LDS-DMA, whole lines, XOR-swizzled), requested by
+//    its first four waves, which count themselves in on an LDS word once
+//    theirs have landed.  Each of its NSW W waves owns a slice of 16
+//    outputs: it requests its 16 W rows x 512 columns (sixteen 16-byte loads
+//    per lane, whole lines, through a buffer resource), then, one 64-column
+//    stage at a time as the loads land, lays the stage out in a wave-private
+//    LDS buffer and runs the MFMAs of its 16 outputs against every row block
+//    of x.  No block-wide barrier sits in the stream.
 //  * split-K: every slice's f32 partial [16 outputs x rows] goes to the
 //    workspace through device-coherent stores; contributor z finalizes the
 //    slices z, z + S, ... of its tile once all S contributors of the tile have
@@ -26,17 +27,19 @@
 //    always runs them together).  Finalizing sums the S partials in range
 //    order, adds s_q B_q t_i in f32 (ranks in order), an adapter stack's
 //    further levels, and rounds y once.
-//  * the shrink: when the pool's units (slot x 16-rank block) fit, the
-//    workgroups of the first few tiles ("carriers") take two units each
-//    over their k range besides their W slices: each unit on half of the
-//    waves, which split the range's stages; a wave's part of the slot's A
-//    rows is requested between the two halves of its W stream and
-//    contracted with the same x rows in LDS; the parts are summed in LDS in
-//    stage order, giving a piece of t for every row (pieces by pool slot,
-//    not by row, so no route is needed to place them).  Carriers never wait
-//    before they count themselves in, and every tile waits for the
-//    carriers' pieces before it finalizes; the carrier workgroups are the
-//    first of the launch and at most 64, so they all run whatever else is
+//  * the shrink: when the pool's units (slot x 16-rank block) fit, the two
+//    unit waves of the workgroups of the first few tiles ("carriers") take
+//    one unit each over their k range.  The unit's 16 A rows are requested
+//    into MFMA operand layout before the workgroup's W (the W waves wait at
+//    a block barrier until then: on this chip a request made behind a CU's
+//    W stream waits for most of it), then contracted with the x rows of the
+//    slot's rows only, gathered from LDS 16 at a time: a piece of t for
+//    those rows (pieces by pool slot, so no route is needed to place them),
+//    stored while W still streams.  A range's last unit counts the range
+//    into every tile's arrival word, and every tile waits for its S
+//    contributors and the S ranges before it finalizes.  Carriers never wait
+//    before they count themselves in; the carrier workgroups are the first
+//    of the launch and at most 64, so they all run whatever else is
 //    resident.  A larger pool takes a prep launch (k_prep.hip) that leaves
 //    t in the workspace first.
 //
@@ -211,45 +214,19 @@ __device__ __forceinline__ void slice_mma(uint4 (&v)[2 * kNSt], const uint4 *xs,
   }
 }
 
-// A carrier wave's part of a shrink unit: stages st0 .. st0 + SP - 1 of the
-// range (those below nst), whose loads v[0 .. 2 SP) have all landed, against
-// the same x rows; acc as in slice_mma.
-template <int NB, int SP>
-__device__ __forceinline__ void part_mma(uint4 (&v)[2 * SP], const uint4 *xs, uint4 *wb, int kb, int ke, int nst,
-                                         int st0, f32x4 (&acc)[NB]) {
-  const int lane = threadIdx.x & 63;
-  constexpr int XR = 16 * NB;
-#pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < SP; ++s) {
-    const int st = st0 + s;
-    if (st >= nst) break;
-    if (kb + st * 64 + (lane & 7) * 8 >= ke) v[2 * s] = v[2 * s + 1] = z4();
-    uint4 *buf = wb + (s & 1) * 128;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = 8 * h + (lane >> 3);
-      buf[r * 8 + ((lane & 7) ^ ((r >> 1) & 7))] = v[2 * s + h];
-    }
-    const uint4 *xst = xs + st * XR * 8;
-    uint4 af[2], xf[2][NB];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = 4 * h + (lane >> 4);
-      const int r = lane & 15;
-      af[h] = buf[r * 8 + (c ^ ((r >> 1) & 7))];
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int rx = 16 * b + (lane & 15);
-        xf[h][b] = xst[rx * 8 + (c ^ ((rx >> 1) & 7))];
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int b = 0; b < NB; ++b) acc[b] = mfma16(af[h], xf[h][b], acc[b]);
+// A W wave that requested x rows counts itself in on an LDS word once they
+// have landed (NAFTER vector memory operations were issued after them); every
+// W wave waits there for the NXW waves that request x before its first
+// stage reads x.
+template <int NAFTER, int NXW>
+__device__ __forceinline__ void x_ready(int wv, int *ctr) {
+  if (wv < NXW) {
+    wait_vmcnt<NAFTER>();
+    asm volatile("" ::: "memory");
+    if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
+  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < NXW) __builtin_amdgcn_s_sleep(1);
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ float *slice_partial(const DecodeArgs &p, int g, int z, int j) {
@@ -292,11 +269,11 @@ __device__ __forceinline__ uint64_t scalar_entry(const void *const *tab, int idx
 // One finalization item, by one wave: slice j of tile g, row block b.  Every
 // contributor's partial (and, with the shrink in this launch, every piece
 // of t) has been stored; rr is the route of this lane's row.  Every load the
-// item needs goes out before any arithmetic: the S partials, then t (from
-// the pieces of the row's slot, or as a prep launch left it), then B.
-template <typename WaitPieces>
+// item needs goes out before any arithmetic: the S partials, B over the
+// first 16 ranks, then t (from the pieces of the row's slot, or as a prep
+// launch left it).
 __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFold &f, const RowRoute &rr, int g, int j,
-                                              int b, float *tb, WaitPieces wait_pieces) {
+                                              int b, float *tb) {
   const int lane = threadIdx.x & 63;
   const int i = 16 * b + (lane & 15);
   const int ic = min(i, p.n - 1);
@@ -315,8 +292,7 @@ __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFo
   };
   load_parts(0);
   const bool any = __ballot(routed && i < p.n) != 0;
-  // B_q[o .. o+3] over the first 16 ranks: it depends on nothing stored in
-  // this launch, so it goes out with the partials and the pieces
+  // B_q[o .. o+3] over the first 16 ranks: it goes out with the partials
   const bool expand = routed && i < p.n && o < p.n_out;
   const u16 *bq = expand ? rr.bq + (size_t)o * R : nullptr;
   uint4 b0[4][2];
@@ -324,20 +300,18 @@ __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFo
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int h = 0; h < 2; ++h) b0[c][h] = expand ? ldg16(bq + (size_t)c * R + 8 * h) : z4();
-  // the shrink's pieces may still be on their way: the partials and B are in
-  // flight meanwhile (false: the wait gave up)
-  const bool pieces_ok = wait_pieces(p.unit_tiles > 0 && any);
   // t of row i, ranks 4 (l / 16) .. +3 of every 16-rank block, from the
   // pieces of its slot's units: the S ranges summed in range order; the
   // row's four lanes meet in tb
-  if (p.unit_tiles > 0 && any && pieces_ok) {
+  if (p.unit_tiles > 0 && any) {
     const int P = p.rd.max_loras;
     const auto tall = coherent_rsrc(p.t_part, (uint32_t)((size_t)p.S * P * p.n * R * 4));
     const int q = routed ? rr.slot : 0;
     auto piece_off = [&](int rb) { return (uint32_t)((q * p.n + ic) * R + rb * 16 + 4 * (lane >> 4)) * 4; };
     const uint32_t zstep = (uint32_t)(P * p.n * R) * 4;
-    // the first rank block's first eight ranges go out with the partials and
-    // B, in straight-line code (a loop would start with a wait for them)
+    // the first rank block's first eight ranges go out right after the
+    // partials and B, in straight-line code (a loop would start with a wait
+    // for them)
     f32x4 pz[8];
     {
       const uint32_t off = piece_off(0);
@@ -440,34 +414,48 @@ __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFo
     }
   }
   *(uint2 *)(p.y + (size_t)i * p.y_row_stride + o) =
-      pieces_ok ? make_uint2(pack2(f2bf(v[0]), f2bf(v[1])), pack2(f2bf(v[2]), f2bf(v[3])))
-                : make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
+      make_uint2(pack2(f2bf(v[0]), f2bf(v[1])), pack2(f2bf(v[2]), f2bf(v[3])));
 }
 
 }  // namespace
 
-// NB: 16-row blocks of the batch (n <= 16 NB); NSW: waves, one slice of 16
-// outputs each (TO = 16 NSW outputs per tile).
+// NB: 16-row blocks of the batch (n <= 16 NB); NSW: W waves, one slice of
+// 16 outputs each (TO = 16 NSW outputs per tile).  A workgroup's waves by
+// role (a SIMD issues the requests of its older waves first):
+//  * waves 0 and 1, the unit waves, carry the shrink on the first
+//    unit_tiles tiles;
+//  * waves 2 .. NSW + 1, the W waves, stream W;
+//  * waves 0 .. 3 also request the range's x rows into LDS; each of them,
+//    once its own have landed, counts itself in on an LDS word that the W
+//    waves watch before their first stage reads x (no block barrier between
+//    the W loads and the first MFMAs).
 template <int NB, int NSW>
-__global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFold f) {
+__global__ __launch_bounds__((NSW + 2) * 64) void decode_kernel(DecodeArgs p, StackFold f) {
   constexpr int XR = 16 * NB;
-  constexpr int NSL = NSW;      // slices per tile
+  constexpr int NSL = NSW;  // slices per tile
+  constexpr int NXW = 4;    // waves that request x
   __shared__ __attribute__((aligned(16))) uint4 xs[kNSt * XR * 8];
   __shared__ __attribute__((aligned(16))) uint4 wb[NSW][2 * 128];
-  __shared__ int s_done, s_ready, s_pready;
+  __shared__ int s_rows[2][64];
+  __shared__ int s_done, s_ready, s_xready;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int g = blockIdx.x / p.S, z = blockIdx.x % p.S;
   const int kb = z * kKR, ke = min(kb + kKR, p.k_in);
   const int nst = (ke - kb + 63) / 64;
   const int o0 = g * p.tile_out;
   const bool full = ke - kb == kKR;  // eight whole stages
   const int RB = p.R / 16;
-  uint4 v[2 * kNSt];
-  const Slice wsl = make_slice(p.W, p.w_row_stride, o0 + 16 * wave, p.n_out, kb);
+  if (tid == 0) {
+    s_done = 0;
+    s_ready = 0;
+    s_xready = 0;
+  }
+  __syncthreads();
 
-  // x rows over the range: stages st = wave, wave + NSW, ... (2 NB DMAs each)
-  for (int st = wave; st < nst; st += NSW) {
+  // x rows over the range: stages st = wave, wave + NXW, ... (2 NB DMAs each)
+  for (int st = wave; wave < NXW && st < nst; st += NXW) {
 #pragma unroll
     for (int i = 0; i < 2 * NB; ++i) {
       const int r = 8 * i + (lane >> 3);
@@ -476,83 +464,11 @@ __global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFol
       dma16(p.x + (size_t)min(r, p.n - 1) * p.x_row_stride + (k < ke ? k : kb), lds_addr(&xs[(st * XR + 8 * i) * 8]));
     }
   }
-  if (tid == 0) {
-    s_done = 0;
-    s_ready = 0;
-    s_pready = 0;
-  }
-  // The shrink rides this launch on the first unit_tiles tiles: their
-  // workgroups take units (pool slot x 16-rank block) 2 g and 2 g + 1, each
-  // on half of the waves, which split the range's stages between them (SP
-  // stages each: the part's A rows, requested between the two halves of the
-  // wave's W rows, against the same x rows).  The parts are summed in LDS
-  // in stage order and stored as the unit's piece of t for every row (the
-  // rows of other slots are simply not read back).
-  constexpr int HW = NSW / 2;           // waves per unit
-  constexpr int SP = kNSt / HW;         // stages per wave's part
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const bool cwg = p.unit_tiles > 0 && g < p.unit_tiles;  // a carrier workgroup
-  const int uk = 2 * g + wv / HW, pi = wv % HW;
-  const bool unit = cwg && uk < p.rd.max_loras * RB;
-  // the unit's A entry: a scalar read in flight while the first half of W
-  // goes out
-  const uint64_t aentry = cwg ? scalar_entry(p.rd.a_table, unit ? uk / RB : 0) : 0;
-  int uslot = -1, urb = 0;
-  uint4 va[2 * SP];
-  const int st0 = pi * SP;
-  f32x4 acc[NB], acct[NB];
-  // The part's A loads: stages st0 .. st0 + SP - 1 below nst; returns how
-  // many went out.
-  auto issue_a = [&](const u16 *A) {
-    const Slice asl = make_slice(A + (size_t)urb * 16 * p.k_in, p.k_in, 0, 16, kb);
-    int na = 0;
-#pragma unroll
-    for (int q = 0; q < SP; ++q) {
-      const int st = st0 + q;
-      if (st < nst) {
-        const bool past = kb + st * 64 + (lane & 7) * 8 >= ke;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          va[2 * q + h] = buf_ld16(asl.rs, past ? asl.off[h] - (lane & 7) * 16 : asl.off[h] + st * 128);
-        na += 2;
-      }
-    }
-    return na;
-  };
-  if (full) {
-    // A whole range: each branch below runs from the W issue to the last
-    // MFMA with no join in between, so every wait is a constant the
-    // compiler can place (a join of paths with different loads in flight
-    // would make it wait for all of them before the first stage).
-    issue_full<0, kNSt / 2>(wsl, v);
-    const u16 *A = (const u16 *)aentry;
-    if (unit && A != nullptr) {  // the part's A rows go out between W's halves
-      uslot = uk / RB;
-      urb = uk % RB;
-      (void)issue_a(A);
-      issue_full<kNSt / 2, kNSt>(wsl, v);
-      wait_vm(2 * kNSt + 2 * SP);  // this wave's x stages have landed
-      __syncthreads();             // x is in LDS
-      slice_mma<NB, true, 2 * SP>(v, xs, wb[wave], kb, ke, nst, acc);
-    } else {
-      issue_full<kNSt / 2, kNSt>(wsl, v);
-      wait_vm(2 * kNSt);
-      __syncthreads();
-      slice_mma<NB, true, 0>(v, xs, wb[wave], kb, ke, nst, acc);
-    }
-  } else {
-    // the last, shorter range: A after all of W; the chunks of x past ke
-    // are zeroed once they land
-    issue_part(wsl, kb, ke, nst, v);
-    const u16 *A = (const u16 *)aentry;
-    int na = 0;
-    if (unit && A != nullptr) {
-      uslot = uk / RB;
-      urb = uk % RB;
-      na = issue_a(A);
-    }
-    wait_vm(2 * nst + na);
-    for (int st = wave; st < nst; st += NSW) {
+  // On the last, shorter range the chunks of x past ke are zeroed once they
+  // have landed (by the wave that requested them), and a block barrier
+  // publishes x.
+  auto zero_tail = [&]() {
+    for (int st = wave; wave < NXW && st < nst; st += NXW) {
       if (kb + st * 64 + 64 <= ke) continue;
 #pragma unroll
       for (int i = 0; i < 2 * NB; ++i) {
@@ -560,15 +476,130 @@ __global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFol
         if (kb + st * 64 + ((lane & 7) ^ ((r >> 1) & 7)) * 8 >= ke) xs[(st * XR + 8 * i) * 8 + lane] = z4();
       }
     }
+  };
+
+  // The shrink rides this launch on the first unit_tiles tiles (the carrier
+  // workgroups): unit wave u of tile g's workgroups takes unit 2 g + u (pool
+  // slot x 16-rank block) over the workgroup's range.  Its slot's 16 A rows
+  // are requested straight into MFMA operand layout before any W load of the
+  // workgroup (a block barrier holds the W waves until then: a request made
+  // behind the W stream would wait for most of it); it then contracts them
+  // with the x rows of its slot's rows only, gathered 16 at a time from LDS,
+  // and stores and counts its piece of t while W still streams.
+  const bool carrier = p.unit_tiles > 0 && g < p.unit_tiles;
+  if (wv < 2) {
+    const int n_units = p.rd.max_loras * RB;
+    const int uk = 2 * g + wv;
+    const bool unit = carrier && uk < n_units;
+    const uint64_t aentry = unit ? scalar_entry(p.rd.a_table, uk / RB) : 0;
+    const bool ua = unit && aentry != 0;  // a unit with A rows to contract
+    const int uslot = uk / RB, urb = uk % RB;
+    // lane l's k chunk in stage st, step h: columns kb + 64 st + 8 (4 h + l / 16) ..
+    // (A through a buffer resource, the step in the immediate offset; a chunk
+    // past ke is zeroed once it lands, and one past the buffer reads 0)
+    const int cl = lane >> 4;
+    auto kcol = [&](int st, int h) { return kb + st * 64 + 8 * (4 * h + cl); };
+    int rslot = -1;
+    uint4 af[2 * kNSt];
+    if (ua) {
+      rslot = lane < p.n ? p.seq_slot[lane] : -1;
+      const auto ars = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)((const u16 *)aentry + (size_t)urb * 16 * p.k_in), 0, 16 * p.k_in * 2, 0x00020000);
+      const uint32_t aoff = ((uint32_t)(lane & 15) * p.k_in + kb + 8 * cl) * 2;
+#pragma unroll
+      for (int st = 0; st < kNSt; ++st)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) af[2 * st + h] = buf_ld16(ars, aoff + st * 128 + h * 64);
+    }
+    if (carrier) block_barrier();  // the W waves may start
+    if (ua) wait_vmcnt<2 * kNSt + 1>();  // this wave's x requests have landed
+    else wait_vmcnt<0>();
+    if (full) {
+      asm volatile("" ::: "memory");
+      if (lane == 0) __hip_atomic_fetch_add(&s_xready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else {
+      zero_tail();
+      __syncthreads();
+    }
+    if (!unit) return;
+    auto count_unit = [&]() {
+      unsigned *ccnt = p.tile_cnt + (size_t)(p.n_tiles + z) * kDecodeCtrStride;
+      if (wave_atomic_add(ccnt, 1u) == (unsigned)n_units - 1) {  // the range's last unit
+        wave_store0(ccnt);
+        for (int t = lane; t < p.n_tiles; t += 64)
+          __hip_atomic_fetch_add(p.tile_cnt + (size_t)t * kDecodeCtrStride, 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
+    };
+    if (!ua) {  // no A: no row reads this slot's pieces
+      count_unit();
+      return;
+    }
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int st = 0; st < kNSt; ++st)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (kcol(st, h) >= ke) af[2 * st + h] = z4();
+    // the rows on the slot, in row order
+    const uint64_t mine = __ballot(rslot == uslot);
+    const int cnt = __popcll(mine);
+    if (rslot == uslot) s_rows[wv][__popcll(mine & ((1ull << lane) - 1))] = lane;
+    if (full) {  // every x stage has landed
+      while (__hip_atomic_load(&s_xready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < NXW)
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+    const int P = p.rd.max_loras;
+    const auto ts = coherent_rsrc(p.t_part, (uint32_t)((size_t)p.S * P * p.n * p.R * 4));
+    for (int j0 = 0; j0 < cnt; j0 += 16) {
+      // lane l: gathered row j0 + l % 16 (the block's first row past cnt);
+      // D[16 ranks][16 gathered rows], stages and steps in the order of a W
+      // slice: lane l holds ranks 4 (l / 16) .. +3 of gathered row l % 16
+      const int j = j0 + (lane & 15);
+      const int row = s_rows[wv][j < cnt ? j : j0];
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < kNSt; ++st) {
+        if (full || st < nst) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int c = 4 * h + cl;
+            const uint4 xx = xs[(st * XR + row) * 8 + (c ^ ((row >> 1) & 7))];
+            acc = mfma16(af[2 * st + h], xx, acc);
+          }
+        }
+      }
+      if (j < cnt)
+        st16_coherent(ts, (uint32_t)(((z * P + uslot) * p.n + row) * p.R + urb * 16 + 4 * cl) * 4, 0, acc);
+    }
+    wait_vmcnt<0>();
+    count_unit();
+    return;
+  }
+  if (carrier) block_barrier();  // the unit waves' requests are out
+
+  // a W wave: slice ww, outputs o0 + 16 ww .. +15
+  const int ww = wv - 2;
+  uint4 v[2 * kNSt];
+  f32x4 acc[NB];
+  const Slice wsl = make_slice(p.W, p.w_row_stride, o0 + 16 * ww, p.n_out, kb);
+  if (full) {
+    issue_full<0, kNSt>(wsl, v);
+    x_ready<2 * kNSt, NXW>(wv, &s_xready);
+    slice_mma<NB, true, 0>(v, xs, wb[ww], kb, ke, nst, acc);
+  } else {
+    issue_part(wsl, kb, ke, nst, v);
+    wait_vm(2 * nst);  // this wave's x requests have landed
+    zero_tail();
     __syncthreads();
-    slice_mma<NB, false>(v, xs, wb[wave], kb, ke, nst, acc, na);
+    slice_mma<NB, false>(v, xs, wb[ww], kb, ke, nst, acc, 0);
   }
   wait_vmcnt<0>();
-  if (uslot >= 0) part_mma<NB, SP>(va, xs, wb[wave], kb, ke, nst, st0, acct);
   if (p.S == 1 && !p.has_lora && f.n_levels == 0) {  // nothing to sum: y directly
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int i = 16 * b + (lane & 15), o = o0 + 16 * wave + 4 * (lane >> 4);
+      const int i = 16 * b + (lane & 15), o = o0 + 16 * ww + 4 * (lane >> 4);
       if (i < p.n && o < p.n_out)
         *(uint2 *)(p.y + (size_t)i * p.y_row_stride + o) =
             make_uint2(pack2(f2bf(acc[b][0]), f2bf(acc[b][1])), pack2(f2bf(acc[b][2]), f2bf(acc[b][3])));
@@ -576,74 +607,32 @@ __global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFol
     return;
   }
   {
-    const auto rs = coherent_rsrc(slice_partial(p, g, z, wave), kDecodeSliceFloats * 4);
+    const auto rs = coherent_rsrc(slice_partial(p, g, z, ww), kDecodeSliceFloats * 4);
 #pragma unroll
     for (int b = 0; b < NB; ++b) st16_coherent(rs, (uint32_t)(b * 64 + lane) * 16, 0, acc[b]);
   }
-  if (cwg) {
-    // the unit's parts meet in LDS (each wave's transpose buffer is free
-    // now); its first wave sums them in stage order and stores the piece:
-    // ranks urb 16 + 4 (l / 16) .. +3 of every row
-    f32x4 *mine = (f32x4 *)&wb[wave][0];
-    if (uslot >= 0) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) mine[b * 64 + lane] = acct[b];
-    }
-    __syncthreads();
-    if (uslot >= 0 && pi == 0) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        f32x4 sum = acct[b];
-        for (int q = 1; q < HW; ++q) sum += ((const f32x4 *)&wb[wave + q][0])[b * 64 + lane];
-        acct[b] = sum;
-      }
-      const int P = p.rd.max_loras;
-      const auto ts = coherent_rsrc(p.t_part, (uint32_t)((size_t)p.S * P * p.n * p.R * 4));
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int i = 16 * b + (lane & 15);
-        if (i < p.n)
-          st16_coherent(ts, (uint32_t)(((z * P + uslot) * p.n + i) * p.R + urb * 16 + 4 * (lane >> 4)) * 4, 0,
-                        acct[b]);
-      }
-    }
-  }
   wait_vmcnt<0>();
-  // the last wave of the workgroup to have stored counts the workgroup in
-  // (a carrier workgroup into every tile: its pieces are stored too); each
-  // tile's words sit on a cache line of their own
+  // the last W wave of the workgroup to have stored counts the workgroup in;
+  // each tile's words sit on a cache line of their own
   unsigned *tcnt = p.tile_cnt + (size_t)g * kDecodeCtrStride;
-  unsigned *tpass = tcnt + 1, *tpieces = tcnt + 2;
+  unsigned *tpass = tcnt + 1;
   int last = 0;
   if (lane == 0) last = atomicAdd(&s_done, 1) == NSW - 1;
-  // a carrier workgroup whose pieces are all stored counts itself into its
-  // range's carrier count; the range's last carrier counts the range into
-  // every tile's pieces word (one atomic per lane) and clears the range
-  // count, so that each tile's finalizers watch their own line and no line
-  // takes more than 2 S increments: a tile's partials are ready at S
-  // arrivals, the pieces at S ranges
-  if (cwg && __builtin_amdgcn_readfirstlane(last)) {
-    unsigned *ccnt = p.tile_cnt + (size_t)(p.n_tiles + z) * kDecodeCtrStride;
-    if (wave_atomic_add(ccnt, 1u) == (unsigned)p.unit_tiles - 1) {
-      wave_store0(ccnt);
-      for (int t = lane; t < p.n_tiles; t += 64)
-        __hip_atomic_fetch_add(p.tile_cnt + (size_t)t * kDecodeCtrStride + 2, 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
   if (__builtin_amdgcn_readfirstlane(last)) (void)wave_atomic_add(tcnt, 1u);
   // finalization items of this contributor: slices j = z, z + S, ... < NSL,
-  // every row block; item m NB + b goes to wave (m NB + b) % NSW
+  // every row block; item m NB + b goes to W wave (m NB + b) % NSW
   const int nsl_mine = z < NSL ? (NSL - 1 - z) / p.S + 1 : 0;
   const int n_items = nsl_mine * NB;
-  if (wave >= n_items) return;
-  // wave 0 alone polls the tile's arrival count (few pollers keep the line
-  // free for the arrivals); the workgroup's other item waves wait on LDS
-  const RowRoute rr0 = row_route_decode(p, 16 * (wave % NB) + (lane & 15));  // in flight during the wait
-  // s_ready: 1 once every arrival is in, 2 if the wait gave up (then the
-  // tile's outputs are written as NaN: a loud failure, never partial sums)
-  if (wave == 0) {
-    const unsigned need = (unsigned)p.S;
+  if (ww >= n_items) return;
+  // W wave 0 alone polls the tile's arrival count (few pollers keep the
+  // line free for the arrivals); the workgroup's other item waves wait on LDS
+  const RowRoute rr0 = row_route_decode(p, 16 * (ww % NB) + (lane & 15));  // in flight during the wait
+  // s_ready: 1 once every arrival is in (the S contributors, and with the
+  // shrink in this launch the S ranges whose units are all counted), 2 if
+  // the wait gave up (then the tile's outputs are written as NaN: a loud
+  // failure, never partial sums)
+  if (ww == 0) {
+    const unsigned need = (unsigned)(p.unit_tiles > 0 ? 2 * p.S : p.S);
     const unsigned got = spin_until(tcnt, need, kTileWaitTicks);
     if (lane == 0) __hip_atomic_store(&s_ready, got >= need ? 1 : 2, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   } else {
@@ -652,39 +641,19 @@ __global__ __launch_bounds__(NSW * 64) void decode_kernel(DecodeArgs p, StackFol
   }
   asm volatile("" ::: "memory");
   const bool gave_up = __hip_atomic_load(&s_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 2;
-  // the shrink's pieces: wave 0 waits for every range's carriers whether or
-  // not its rows need them (so that no carrier counts in after the words are
-  // cleared below), the other waves when theirs do
-  auto wait_pieces = [&](bool need) {
-    if (p.unit_tiles == 0) return true;
-    if (wave == 0) {
-      if (__hip_atomic_load(&s_pready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) {
-        const unsigned got = spin_until(tpieces, (unsigned)p.S, kTileWaitTicks);
-        if (lane == 0)
-          __hip_atomic_store(&s_pready, got >= (unsigned)p.S ? 1 : 2, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
-    } else {
-      if (!need) return true;
-      while (__hip_atomic_load(&s_pready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
-        __builtin_amdgcn_s_sleep(1);
-    }
-    asm volatile("" ::: "memory");
-    return __hip_atomic_load(&s_pready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 1;
-  };
   const unsigned items_per_tile = (unsigned)(NSL * NB);
-  for (int it = wave; it < n_items; it += NSW) {
+  for (int it = ww; it < n_items; it += NSW) {
     const int j = z + p.S * (it / NB), b = it % NB;
-    const RowRoute rr = it == wave ? rr0 : row_route_decode(p, 16 * b + (lane & 15));
+    const RowRoute rr = it == ww ? rr0 : row_route_decode(p, 16 * b + (lane & 15));
     if (gave_up) {
       const int i = 16 * b + (lane & 15), o = g * p.tile_out + 16 * j + 4 * (lane >> 4);
       if (i < p.n && o < p.n_out) *(uint2 *)(p.y + (size_t)i * p.y_row_stride + o) = make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
     } else {
-      finalize_item(p, f, rr, g, j, b, (float *)&wb[wave][0], wait_pieces);
+      finalize_item(p, f, rr, g, j, b, (float *)&wb[ww][0]);
     }
-    if (wave_atomic_add(tpass, 1u) == items_per_tile - 1) {  // every item is past the waits
+    if (wave_atomic_add(tpass, 1u) == items_per_tile - 1) {  // every item is past the wait
       wave_store0(tcnt);
       wave_store0(tpass);
-      wave_store0(tpieces);
     }
   }
 }
@@ -697,7 +666,7 @@ hipError_t launch_decode(const DecodeArgs &a, const StackFold *stack, hipStream_
   const int nb = (a.n + 15) / 16;
   const int nsw = a.tile_out / 16;
 #define LORA_DECODE(NB, NSW) \
-  hipLaunchKernelGGL((decode_kernel<NB, NSW>), dim3(grid), dim3(NSW * 64), 0, st, a, f)
+  hipLaunchKernelGGL((decode_kernel<NB, NSW>), dim3(grid), dim3((NSW + 2) * 64), 0, st, a, f)
   if (nsw == 8) {
     if (nb <= 1) LORA_DECODE(1, 8);
     else if (nb == 2) LORA_DECODE(2, 8);

@@ -91,18 +91,19 @@ struct DecodeArgs {
   int n_tiles;          // ceil(n_out / tile_out)
   int tile_out;         // outputs per tile: 16 x the waves (128 or 64)
   float *partials;      // [n_tiles][S][kDecodeSlices][kDecodeSliceFloats]
-  // The shrink: with unit_tiles > 0 it rides this launch (the upper half of
-  // the waves of the first unit_tiles tiles, see k_decode.hip) and leaves
-  // range pieces [S][max_loras][n][R] in t_part (max_loras x R <=
-  // kDecodeUnitRanks); otherwise a prep launch wrote t [n][R].
+  // The shrink: with unit_tiles > 0 it rides this launch (two unit waves in
+  // each workgroup of the first unit_tiles tiles, see k_decode.hip) and
+  // leaves range pieces [S][max_loras][n][R] in t_part, written for the rows
+  // on each slot (max_loras x R <= kDecodeUnitRanks); otherwise a prep
+  // launch wrote t [n][R].
   int unit_tiles;
   float *t_part;
   const float *t;
   // words that are zero between calls, a cache line each (kDecodeCtrStride
   // words apart): tile g's at tile_cnt + g kDecodeCtrStride, [0]
-  // contributors that stored their partials plus k ranges whose carriers
-  // are all done, [1] finalization items past the wait for them; then range
-  // z's carrier count at tile_cnt + (n_tiles + z) kDecodeCtrStride
+  // contributors that stored their partials plus k ranges whose units are
+  // all done, [1] finalization items past the wait for them; then range z's
+  // unit count at tile_cnt + (n_tiles + z) kDecodeCtrStride
   unsigned *tile_cnt;
 };
 
