@@ -13,12 +13,14 @@
 //    (kKR = 512 columns; S = ceil(k_in / 512) ranges).  Its x rows over the
 //    range go to LDS once (LDS-DMA, whole lines, XOR-swizzled), requested by
 //    its first four waves, which count themselves in on an LDS word once
-//    theirs have landed.  Each of its NSW W waves owns a slice of 16
-//    outputs: it requests its 16 W rows x 512 columns (sixteen 16-byte loads
-//    per lane, whole lines, through a buffer resource), then, one 64-column
-//    stage at a time as the loads land, lays the stage out in a wave-private
-//    LDS buffer and runs the MFMAs of its 16 outputs against every row block
-//    of x.  No block-wide barrier sits in the stream.
+//    theirs have landed.  Each of its W waves owns SPW slices of 16 outputs
+//    (two on 128-output tiles): it requests their W rows x 512 columns
+//    (sixteen 16-byte loads per lane and slice, whole lines, through buffer
+//    resources), then, one 64-column stage at a time as the loads land, lays
+//    the stage out in a wave-private LDS buffer and runs the MFMAs of its
+//    outputs against every row block of x, each x fragment read from LDS
+//    serving all its slices (LDS traffic, not the MFMAs, bounds this phase).
+//    No block-wide barrier sits in the stream.
 //  * split-K: every slice's f32 partial [16 outputs x rows] goes to the
 //    workspace through device-coherent stores; contributor z finalizes the
 //    slices z, z + S, ... of its tile once all S contributors of the tile have
@@ -138,68 +140,85 @@ __device__ __forceinline__ Slice make_slice(const u16 *base, int row_stride, int
 __device__ __forceinline__ uint4 buf_ld16(const __amdgpu_buffer_rsrc_t &rs, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
 }
-// A whole range (512 columns): stages [ST0, ST1), the stage step in the
-// instruction's immediate offset.
-template <int ST0, int ST1>
-__device__ __forceinline__ void issue_full(const Slice &sl, uint4 (&v)[2 * kNSt]) {
+// A W wave's SPW slices (consecutive 16-row blocks) over a range, stage by
+// stage: load (st SPW + s) 2 + h is slice s's rows 8 h .. 8 h + 7 of stage
+// st, so the stages land in order.  A whole range (512 columns): stages
+// [ST0, ST1), the stage step in the instruction's immediate offset.
+template <int SPW, int ST0, int ST1>
+__device__ __forceinline__ void issue_full(const Slice (&sl)[SPW], uint4 (&v)[2 * SPW * kNSt]) {
 #pragma unroll
   for (int st = ST0; st < ST1; ++st)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) v[2 * st + h] = buf_ld16(sl.rs, sl.off[h] + st * 128);
+    for (int s = 0; s < SPW; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) v[(st * SPW + s) * 2 + h] = buf_ld16(sl[s].rs, sl[s].off[h] + st * 128);
 }
 // The last, shorter range: its nst stages; a chunk past ke reads column kb
 // and is zeroed once it lands.
-__device__ __forceinline__ void issue_part(const Slice &sl, int kb, int ke, int nst, uint4 (&v)[2 * kNSt]) {
+template <int SPW>
+__device__ __forceinline__ void issue_part(const Slice (&sl)[SPW], int kb, int ke, int nst,
+                                           uint4 (&v)[2 * SPW * kNSt]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int st = 0; st < kNSt; ++st) {
     if (st < nst) {
       const bool past = kb + st * 64 + (lane & 7) * 8 >= ke;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        v[2 * st + h] = buf_ld16(sl.rs, past ? sl.off[h] - (lane & 7) * 16 : sl.off[h] + st * 128);
+      for (int s = 0; s < SPW; ++s)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          v[(st * SPW + s) * 2 + h] =
+              buf_ld16(sl[s].rs, past ? sl[s].off[h] - (lane & 7) * 16 : sl[s].off[h] + st * 128);
     }
   }
 }
 
-// The MFMAs of a slice against the x rows in LDS, stage by stage as its
-// loads land (on a shorter range `extra` more vector-memory operations were
-// issued after all of them; on a whole range MID more between its halves).
-// acc[b] = D[16 slice rows][16 x rows of row block b]: lane l holds slice
-// rows 4 (l / 16) .. +3 of x row 16 b + l % 16.
-// On a whole range every wait is a constant (MID, the loads issued between
-// the halves, is a template argument): a wait whose count is known only at
-// run time leaves the compiler unsure which loads have landed, and it then
-// waits for all of them before the first stage.
-template <int NB, bool FULL, int MID = 0, int AFTER = 0>
-__device__ __forceinline__ void slice_mma(uint4 (&v)[2 * kNSt], const uint4 *xs, uint4 *wb, int kb, int ke, int nst,
-                                          f32x4 (&acc)[NB], int extra = 0) {
+// The MFMAs of a W wave's slices against the x rows in LDS, stage by stage
+// as its loads land (on a shorter range `extra` more vector-memory
+// operations were issued after all of them).  Each x fragment read from LDS
+// serves the wave's SPW slices.  acc[s][b] = D[16 rows of slice s][16 x rows
+// of row block b]: lane l holds slice rows 4 (l / 16) .. +3 of x row
+// 16 b + l % 16; every element accumulates stage by stage, two 32-column
+// steps each.  On a whole range every wait is a constant: a wait whose count
+// is known only at run time leaves the compiler unsure which loads have
+// landed, and it then waits for all of them before the first stage.
+template <int NB, int SPW, bool FULL>
+__device__ __forceinline__ void slice_mma(uint4 (&v)[2 * SPW * kNSt], const uint4 *xs, uint4 *wb, int kb, int ke,
+                                          int nst, f32x4 (&acc)[SPW][NB], int extra = 0) {
   const int lane = threadIdx.x & 63;
   constexpr int XR = 16 * NB;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < SPW; ++s)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[s][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int st = 0; st < kNSt; ++st) {
     if (FULL || st < nst) {
       if (FULL) {  // a constant once the loop is unrolled
-        wait_vm(2 * (kNSt - 1 - st) + AFTER + (st < kNSt / 2 ? MID : 0));
+        wait_vm(2 * SPW * (kNSt - 1 - st));
       } else {
-        wait_vm(2 * (nst - 1 - st) + extra);
-        if (kb + st * 64 + (lane & 7) * 8 >= ke) v[2 * st] = v[2 * st + 1] = z4();
-      }
-      uint4 *buf = wb + (st & 1) * 128;
+        wait_vm(2 * SPW * (nst - 1 - st) + extra);
+        if (kb + st * 64 + (lane & 7) * 8 >= ke) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int r = 8 * h + (lane >> 3);
-        buf[r * 8 + ((lane & 7) ^ ((r >> 1) & 7))] = v[2 * st + h];
+          for (int q = 0; q < 2 * SPW; ++q) v[st * 2 * SPW + q] = z4();
+        }
       }
+      uint4 *buf = wb + (st & 1) * 128 * SPW;
+#pragma unroll
+      for (int s = 0; s < SPW; ++s)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = 8 * h + (lane >> 3);
+          buf[s * 128 + r * 8 + ((lane & 7) ^ ((r >> 1) & 7))] = v[(st * SPW + s) * 2 + h];
+        }
       const uint4 *xst = xs + st * XR * 8;
-      uint4 af[2], xf[2][NB];
+      uint4 af[SPW][2], xf[2][NB];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int c = 4 * h + (lane >> 4);
         const int r = lane & 15;
-        af[h] = buf[r * 8 + (c ^ ((r >> 1) & 7))];
+#pragma unroll
+        for (int s = 0; s < SPW; ++s) af[s][h] = buf[s * 128 + r * 8 + (c ^ ((r >> 1) & 7))];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           const int rx = 16 * b + (lane & 15);
@@ -209,7 +228,9 @@ __device__ __forceinline__ void slice_mma(uint4 (&v)[2 * kNSt], const uint4 *xs,
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) acc[b] = mfma16(af[h], xf[h][b], acc[b]);
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int s = 0; s < SPW; ++s) acc[s][b] = mfma16(af[s][h], xf[h][b], acc[s][b]);
     }
   }
 }
@@ -419,23 +440,28 @@ __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFo
 
 }  // namespace
 
-// NB: 16-row blocks of the batch (n <= 16 NB); NSW: W waves, one slice of
-// 16 outputs each (TO = 16 NSW outputs per tile).  A workgroup's waves by
-// role (a SIMD issues the requests of its older waves first):
+// NB: 16-row blocks of the batch (n <= 16 NB); NSW: slices of 16 outputs
+// per tile (TO = 16 NSW outputs), two per W wave on 128-output tiles (each x
+// fragment read from LDS then serves two slices) and one on 64-output tiles
+// (their launches are small: more waves keep more loads in flight).  A
+// workgroup's waves by role (a SIMD issues the requests of its older waves
+// first):
 //  * waves 0 and 1, the unit waves, carry the shrink on the first
 //    unit_tiles tiles;
-//  * waves 2 .. NSW + 1, the W waves, stream W;
+//  * waves 2 .. NSW / SPW + 1, the W waves, stream W;
 //  * waves 0 .. 3 also request the range's x rows into LDS; each of them,
 //    once its own have landed, counts itself in on an LDS word that the W
 //    waves watch before their first stage reads x (no block barrier between
 //    the W loads and the first MFMAs).
 template <int NB, int NSW>
-__global__ __launch_bounds__((NSW + 2) * 64) void decode_kernel(DecodeArgs p, StackFold f) {
+__global__ __launch_bounds__((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64) void decode_kernel(DecodeArgs p, StackFold f) {
   constexpr int XR = 16 * NB;
-  constexpr int NSL = NSW;  // slices per tile
-  constexpr int NXW = 4;    // waves that request x
+  constexpr int NSL = NSW;      // slices per tile
+  constexpr int SPW = NSW >= 8 ? 2 : 1;  // slices per W wave
+  constexpr int NWW = NSW / SPW;         // W waves
+  constexpr int NXW = 4;        // waves that request x
   __shared__ __attribute__((aligned(16))) uint4 xs[kNSt * XR * 8];
-  __shared__ __attribute__((aligned(16))) uint4 wb[NSW][2 * 128];
+  __shared__ __attribute__((aligned(16))) uint4 wb[NWW][2 * 128 * SPW];
   __shared__ int s_rows[2][64];
   __shared__ int s_done, s_ready, s_xready;
 
@@ -579,37 +605,42 @@ __global__ __launch_bounds__((NSW + 2) * 64) void decode_kernel(DecodeArgs p, St
   }
   if (carrier) block_barrier();  // the unit waves' requests are out
 
-  // a W wave: slice ww, outputs o0 + 16 ww .. +15
+  // a W wave: slices SPW ww .. SPW ww + SPW - 1, outputs o0 + 16 SPW ww ..
   const int ww = wv - 2;
-  uint4 v[2 * kNSt];
-  f32x4 acc[NB];
-  const Slice wsl = make_slice(p.W, p.w_row_stride, o0 + 16 * ww, p.n_out, kb);
+  uint4 v[2 * SPW * kNSt];
+  f32x4 acc[SPW][NB];
+  Slice wsl[SPW];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) wsl[s] = make_slice(p.W, p.w_row_stride, o0 + 16 * (SPW * ww + s), p.n_out, kb);
   if (full) {
-    issue_full<0, kNSt>(wsl, v);
-    x_ready<2 * kNSt, NXW>(wv, &s_xready);
-    slice_mma<NB, true, 0>(v, xs, wb[ww], kb, ke, nst, acc);
+    issue_full<SPW, 0, kNSt>(wsl, v);
+    x_ready<2 * SPW * kNSt, NXW>(wv, &s_xready);
+    slice_mma<NB, SPW, true>(v, xs, wb[ww], kb, ke, nst, acc);
   } else {
-    issue_part(wsl, kb, ke, nst, v);
-    wait_vm(2 * nst);  // this wave's x requests have landed
+    issue_part<SPW>(wsl, kb, ke, nst, v);
+    wait_vm(2 * SPW * nst);  // this wave's x requests have landed
     zero_tail();
     __syncthreads();
-    slice_mma<NB, false>(v, xs, wb[ww], kb, ke, nst, acc, 0);
+    slice_mma<NB, SPW, false>(v, xs, wb[ww], kb, ke, nst, acc, 0);
   }
   wait_vmcnt<0>();
   if (p.S == 1 && !p.has_lora && f.n_levels == 0) {  // nothing to sum: y directly
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int i = 16 * b + (lane & 15), o = o0 + 16 * ww + 4 * (lane >> 4);
-      if (i < p.n && o < p.n_out)
-        *(uint2 *)(p.y + (size_t)i * p.y_row_stride + o) =
-            make_uint2(pack2(f2bf(acc[b][0]), f2bf(acc[b][1])), pack2(f2bf(acc[b][2]), f2bf(acc[b][3])));
-    }
+    for (int s = 0; s < SPW; ++s)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int i = 16 * b + (lane & 15), o = o0 + 16 * (SPW * ww + s) + 4 * (lane >> 4);
+        if (i < p.n && o < p.n_out)
+          *(uint2 *)(p.y + (size_t)i * p.y_row_stride + o) = make_uint2(pack2(f2bf(acc[s][b][0]), f2bf(acc[s][b][1])),
+                                                                        pack2(f2bf(acc[s][b][2]), f2bf(acc[s][b][3])));
+      }
     return;
   }
-  {
-    const auto rs = coherent_rsrc(slice_partial(p, g, z, ww), kDecodeSliceFloats * 4);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) st16_coherent(rs, (uint32_t)(b * 64 + lane) * 16, 0, acc[b]);
+  for (int s = 0; s < SPW; ++s) {
+    const auto rs = coherent_rsrc(slice_partial(p, g, z, SPW * ww + s), kDecodeSliceFloats * 4);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) st16_coherent(rs, (uint32_t)(b * 64 + lane) * 16, 0, acc[s][b]);
   }
   wait_vmcnt<0>();
   // the last W wave of the workgroup to have stored counts the workgroup in;
@@ -617,10 +648,10 @@ __global__ __launch_bounds__((NSW + 2) * 64) void decode_kernel(DecodeArgs p, St
   unsigned *tcnt = p.tile_cnt + (size_t)g * kDecodeCtrStride;
   unsigned *tpass = tcnt + 1;
   int last = 0;
-  if (lane == 0) last = atomicAdd(&s_done, 1) == NSW - 1;
+  if (lane == 0) last = atomicAdd(&s_done, 1) == NWW - 1;
   if (__builtin_amdgcn_readfirstlane(last)) (void)wave_atomic_add(tcnt, 1u);
   // finalization items of this contributor: slices j = z, z + S, ... < NSL,
-  // every row block; item m NB + b goes to W wave (m NB + b) % NSW
+  // every row block; item m NB + b goes to W wave (m NB + b) % NWW
   const int nsl_mine = z < NSL ? (NSL - 1 - z) / p.S + 1 : 0;
   const int n_items = nsl_mine * NB;
   if (ww >= n_items) return;
@@ -642,7 +673,7 @@ __global__ __launch_bounds__((NSW + 2) * 64) void decode_kernel(DecodeArgs p, St
   asm volatile("" ::: "memory");
   const bool gave_up = __hip_atomic_load(&s_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 2;
   const unsigned items_per_tile = (unsigned)(NSL * NB);
-  for (int it = ww; it < n_items; it += NSW) {
+  for (int it = ww; it < n_items; it += NWW) {
     const int j = z + p.S * (it / NB), b = it % NB;
     const RowRoute rr = it == ww ? rr0 : row_route_decode(p, 16 * b + (lane & 15));
     if (gave_up) {
@@ -666,7 +697,7 @@ hipError_t launch_decode(const DecodeArgs &a, const StackFold *stack, hipStream_
   const int nb = (a.n + 15) / 16;
   const int nsw = a.tile_out / 16;
 #define LORA_DECODE(NB, NSW) \
-  hipLaunchKernelGGL((decode_kernel<NB, NSW>), dim3(grid), dim3((NSW + 2) * 64), 0, st, a, f)
+  hipLaunchKernelGGL((decode_kernel<NB, NSW>), dim3(grid), dim3((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64), 0, st, a, f)
   if (nsw == 8) {
     if (nb <= 1) LORA_DECODE(1, 8);
     else if (nb == 2) LORA_DECODE(2, 8);
