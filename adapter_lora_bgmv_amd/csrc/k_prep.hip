@@ -353,6 +353,7 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
     // that, and the whole batch if the range does not hold every wanted row
     // (offsets that are not non-decreasing, an adapter on several segments)
     int r_lo = 0, r_hi = a.n;
+    bool direct = false;  // pstar's rows are exactly one segment's rows
     if (a.rt.mode == kModeMoeGrouped) {
       const int e = pstar % a.rd.n_experts;
       r_lo = min(max(a.rt.expert_offsets[e], 0), a.n);
@@ -365,8 +366,17 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
           r_hi = min(max(a.rt.seg_indptr[g + 1], r_lo), a.n);
           break;
         }
+      // every row of a segment routes alike, so when the pair's row count is
+      // the segment's, its rows are that segment's: this unit takes the
+      // positions [first, first + want) of the segment (a partition of the
+      // pair's rows like the ranks', and each row's t is its own)
+      direct = r_hi - r_lo == total;
     }
-    for (int pass = 0; pass < 2; ++pass) {
+    if (direct) {
+      if (tid < want) rows[tid] = r_lo + first + tid;
+      if (tid == 0) info[3] = total;
+    }
+    for (int pass = 0; pass < 2 && !direct; ++pass) {
       __syncthreads();  // every thread has read the last pass's count
       if (tid == 0) info[2] = 0;
       __syncthreads();
@@ -392,7 +402,7 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
       r_lo = 0;
       r_hi = a.n;
     }
-    if (tid == 0) info[3] = total;
+    if (tid == 0 && !direct) info[3] = total;
   } else {
     // rows of pstar in row order, ranks [first, first + kShrinkRows): thread t
     // counts them in its 16-row span, an exclusive scan gives its first rank
@@ -528,24 +538,38 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
   __syncthreads();
   if (!info[2]) return;
   // the last of the unit's workgroups: t = sum of the k-chunk partials in
-  // chunk order, every chunk's 16-byte load in flight together
-  for (int e = tid * 4; e < nrows * R; e += 256 * 4) {
-    const int i = e / R, r = e - i * R;
-    if (rows[i] < 0) continue;
-    const size_t off = (size_t)rows[i] * R + r;
-    f32x4 v[kMaxShrinkSplits];
+  // chunk order; a thread's pieces (kSumIt at a time) have every chunk's
+  // 16-byte load in flight together before any is summed
+  constexpr int kSumIt = 2;
+  for (int e0 = tid * 4; e0 < nrows * R; e0 += 256 * 4 * kSumIt) {
+    f32x4 v[kSumIt][kMaxShrinkSplits];
+    size_t off[kSumIt];
+    bool ok[kSumIt];
 #pragma unroll
-    for (int z = 0; z < kMaxShrinkSplits; ++z)
-      v[z] = z < KS ? ld16_coherent(prs, (uint32_t)(off * 4), (uint32_t)((size_t)z * a.n * R * 4))
-                    : f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 sum = v[0];
+    for (int it = 0; it < kSumIt; ++it) {
+      const int e = e0 + it * 256 * 4;
+      const int i = min(e / R, nrows - 1), r = e - (e / R) * R;
+      ok[it] = e < nrows * R && rows[i] >= 0;
+      off[it] = ok[it] ? (size_t)rows[i] * R + r : 0;
 #pragma unroll
-    for (int z = 1; z < kMaxShrinkSplits; ++z)
-      if (z < KS) sum += v[z];
-    *(f32x4 *)(a.t_final + off) = sum;
-    if (a.tt) {
-      const float vv[4] = {sum[0], sum[1], sum[2], sum[3]};
-      store_tt(a.tt, R, rows[i], r, sig, vv, 4);
+      for (int z = 0; z < kMaxShrinkSplits; ++z)
+        v[it][z] = ok[it] && z < KS
+                       ? ld16_coherent(prs, (uint32_t)(off[it] * 4), (uint32_t)((size_t)z * a.n * R * 4))
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int it = 0; it < kSumIt; ++it) {
+      if (!ok[it]) continue;
+      f32x4 sum = v[it][0];
+#pragma unroll
+      for (int z = 1; z < kMaxShrinkSplits; ++z)
+        if (z < KS) sum += v[it][z];
+      *(f32x4 *)(a.t_final + off[it]) = sum;
+      if (a.tt) {
+        const int e = e0 + it * 256 * 4;
+        const float vv[4] = {sum[0], sum[1], sum[2], sum[3]};
+        store_tt(a.tt, R, rows[e / R], e - (e / R) * R, sig, vv, 4);
+      }
     }
   }
   if (tid == 0) __hip_atomic_store(&a.counters[u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
