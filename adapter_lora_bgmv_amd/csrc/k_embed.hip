@@ -6,8 +6,9 @@
 // Memory-bound: a gathered row of E, one row of B per row, and each touched
 // slot's A, which every row on that slot shares.  A workgroup takes 64 rows
 // and 256 columns (wave w its rows 16 w .. +15, 4 columns per lane); for
-// every 8 ranks the A rows of the workgroup's pairs go to LDS once and all
-// four waves read them there, so each pair's A is read once per workgroup.
+// every 8 ranks the A rows of the workgroup's pairs go to LDS once (bf16:
+// by LDS-DMA, every piece of the pass in flight at once) and all four waves
+// read them there, so each pair's A is read once per workgroup.
 // The rank sum runs k ascending in f32; y is rounded once.
 #include "common.hpp"
 #include "launch.hpp"
@@ -158,15 +159,28 @@ __global__ __launch_bounds__(256) void embed_rows_kernel(EmbedArgs a) {
     for (int g0 = 0; g0 < nd; g0 += PG) {
       __syncthreads();  // every wave is done with the last pass's A (and this pass's B has landed)
       const int np = min(PG, nd - g0);
-      // the pass's A: pair g0 + ps, rank kc + kk, the workgroup's columns, in
-      // pieces of kEmbedVec columns (consecutive threads, consecutive pieces)
-      for (int e = tid; e < np * kEmbedKC * 64; e += 256) {
-        const int ps = e / (kEmbedKC * 64), kk = (e / 64) % kEmbedKC, cl = e % 64;
-        const int cc = blockIdx.x * kEmbedCols + cl * kEmbedVec;
-        const int vv = cc < a.n_embd ? min(kEmbedVec, a.n_embd - cc) : 0;
-        T *dst = &ash[ps][kk][cl * kEmbedVec];
-        if (kc + kk < R && vv > 0)
-          Vec4<T>::store_raw(dst, Vec4<T>::load_raw(d_a[g0 + ps] + (size_t)(kc + kk) * a.n_embd + cc, vv), kEmbedVec);
+      if constexpr (sizeof(T) == 2) {
+        // LDS-DMA: instruction m carries the 512-byte rows 2 m and 2 m + 1
+        // (row = (pair ps, rank kk); lane l: row 2 m + l / 32, 8 columns from
+        // (l % 32) 8); a piece outside the pass reads the first pair's row 0
+        const int nrow = np * kEmbedKC;
+        for (int m = wave; 2 * m < nrow; m += 4) {
+          const int row = 2 * m + (lane >> 5), ps = row / kEmbedKC, kk = row % kEmbedKC;
+          const int cc = blockIdx.x * kEmbedCols + (lane & 31) * 8;
+          const bool in = kc + kk < R && cc < a.n_embd;
+          dma16(in ? d_a[g0 + ps] + (size_t)(kc + kk) * a.n_embd + cc : d_a[g0],
+                lds_addr(&ash[0][0][0] + (size_t)m * 512));
+        }
+        wait_vmcnt<0>();
+      } else {
+        for (int e = tid; e < np * kEmbedKC * 64; e += 256) {
+          const int ps = e / (kEmbedKC * 64), kk = (e / 64) % kEmbedKC, cl = e % 64;
+          const int cc = blockIdx.x * kEmbedCols + cl * kEmbedVec;
+          const int vv = cc < a.n_embd ? min(kEmbedVec, a.n_embd - cc) : 0;
+          T *dst = &ash[ps][kk][cl * kEmbedVec];
+          if (kc + kk < R && vv > 0)
+            Vec4<T>::store_raw(dst, Vec4<T>::load_raw(d_a[g0 + ps] + (size_t)(kc + kk) * a.n_embd + cc, vv), kEmbedVec);
+        }
       }
       __syncthreads();
       if (valid > 0) {
