@@ -291,10 +291,12 @@ __device__ __forceinline__ uint64_t scalar_entry(const void *const *tab, int idx
 // contributor's partial (and, with the shrink in this launch, every piece
 // of t) has been stored; rr is the route of this lane's row.  Every load the
 // item needs goes out before any arithmetic: the S partials, B over the
-// first 16 ranks, then t (from the pieces of the row's slot, or as a prep
-// launch left it).
+// first 16 ranks (PRE: a wave's first item's were requested before the wait
+// for the tile's arrivals, in bpre), then t (from the pieces of the row's
+// slot, or as a prep launch left it).
+template <bool PRE>
 __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFold &f, const RowRoute &rr, int g, int j,
-                                              int b, float *tb) {
+                                              int b, float *tb, const uint4 (&bpre)[4][2]) {
   const int lane = threadIdx.x & 63;
   const int i = 16 * b + (lane & 15);
   const int ic = min(i, p.n - 1);
@@ -320,7 +322,7 @@ __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFo
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) b0[c][h] = expand ? ldg16(bq + (size_t)c * R + 8 * h) : z4();
+    for (int h = 0; h < 2; ++h) b0[c][h] = PRE ? bpre[c][h] : expand ? ldg16(bq + (size_t)c * R + 8 * h) : z4();
   // t of row i, ranks 4 (l / 16) .. +3 of every 16-rank block, from the
   // pieces of its slot's units: the S ranges summed in range order; the
   // row's four lanes meet in tb
@@ -658,6 +660,18 @@ __global__ __launch_bounds__((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64) void decode_ke
   // W wave 0 alone polls the tile's arrival count (few pollers keep the
   // line free for the arrivals); the workgroup's other item waves wait on LDS
   const RowRoute rr0 = row_route_decode(p, 16 * (ww % NB) + (lane & 15));  // in flight during the wait
+  // the first item's B rows depend on nothing this launch stores: they are
+  // in flight during the wait too
+  uint4 bpre[4][2];
+  {
+    const int j = z + p.S * (ww / NB), i = 16 * (ww % NB) + (lane & 15), o = g * p.tile_out + 16 * j + 4 * (lane >> 4);
+    const bool expand = rr0.bq != nullptr && i < p.n && o < p.n_out;
+    const u16 *bq = expand ? rr0.bq + (size_t)o * p.R : nullptr;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) bpre[c][h] = expand ? ldg16(bq + (size_t)c * p.R + 8 * h) : z4();
+  }
   // s_ready: 1 once every arrival is in (the S contributors, and with the
   // shrink in this launch the S ranges whose units are all counted), 2 if
   // the wait gave up (then the tile's outputs are written as NaN: a loud
@@ -680,7 +694,8 @@ __global__ __launch_bounds__((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64) void decode_ke
       const int i = 16 * b + (lane & 15), o = g * p.tile_out + 16 * j + 4 * (lane >> 4);
       if (i < p.n && o < p.n_out) *(uint2 *)(p.y + (size_t)i * p.y_row_stride + o) = make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
     } else {
-      finalize_item(p, f, rr, g, j, b, (float *)&wb[ww][0]);
+      if (it == ww) finalize_item<true>(p, f, rr, g, j, b, (float *)&wb[ww][0], bpre);
+      else finalize_item<false>(p, f, rr, g, j, b, (float *)&wb[ww][0], bpre);
     }
     if (wave_atomic_add(tpass, 1u) == items_per_tile - 1) {  // every item is past the wait
       wave_store0(tcnt);
