@@ -290,13 +290,15 @@ __device__ __forceinline__ uint64_t scalar_entry(const void *const *tab, int idx
 // One finalization item, by one wave: slice j of tile g, row block b.  Every
 // contributor's partial (and, with the shrink in this launch, every piece
 // of t) has been stored; rr is the route of this lane's row.  Every load the
-// item needs goes out before any arithmetic: the S partials, B over the
+// item needs goes out before any arithmetic: the S partials and B over the
 // first 16 ranks (PRE: a wave's first item's were requested before the wait
-// for the tile's arrivals, in bpre), then t (from the pieces of the row's
-// slot, or as a prep launch left it).
+// for the tile's arrivals, in bpre).  t comes from the workgroup's LDS copy
+// (tsh, rows from r0 on, summed from the pieces by the unit waves; they count
+// themselves in on *tready), or as a prep launch left it.
 template <bool PRE>
 __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFold &f, const RowRoute &rr, int g, int j,
-                                              int b, float *tb, const uint4 (&bpre)[4][2]) {
+                                              int b, const float *tsh, int r0, const int *tready,
+                                              const uint4 (&bpre)[4][2]) {
   const int lane = threadIdx.x & 63;
   const int i = 16 * b + (lane & 15);
   const int ic = min(i, p.n - 1);
@@ -314,7 +316,6 @@ __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFo
                                : f32x4{0.f, 0.f, 0.f, 0.f};
   };
   load_parts(0);
-  const bool any = __ballot(routed && i < p.n) != 0;
   // B_q[o .. o+3] over the first 16 ranks: it goes out with the partials
   const bool expand = routed && i < p.n && o < p.n_out;
   const u16 *bq = expand ? rr.bq + (size_t)o * R : nullptr;
@@ -323,45 +324,14 @@ __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFo
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int h = 0; h < 2; ++h) b0[c][h] = PRE ? bpre[c][h] : expand ? ldg16(bq + (size_t)c * R + 8 * h) : z4();
-  // t of row i, ranks 4 (l / 16) .. +3 of every 16-rank block, from the
-  // pieces of its slot's units: the S ranges summed in range order; the
-  // row's four lanes meet in tb
-  if (p.unit_tiles > 0 && any) {
-    const int P = p.rd.max_loras;
-    const auto tall = coherent_rsrc(p.t_part, (uint32_t)((size_t)p.S * P * p.n * R * 4));
-    const int q = routed ? rr.slot : 0;
-    auto piece_off = [&](int rb) { return (uint32_t)((q * p.n + ic) * R + rb * 16 + 4 * (lane >> 4)) * 4; };
-    const uint32_t zstep = (uint32_t)(P * p.n * R) * 4;
-    // the first rank block's first eight ranges go out right after the
-    // partials and B, in straight-line code (a loop would start with a wait
-    // for them)
-    f32x4 pz[8];
-    {
-      const uint32_t off = piece_off(0);
-#pragma unroll
-      for (int zz = 0; zz < 8; ++zz)
-        pz[zz] = zz < p.S ? ld16_coherent(tall, off, zz * zstep) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int rb = 0; rb < R / 16; ++rb) {
-      const uint32_t off = piece_off(rb);
-      f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int z0 = 0; z0 < p.S; z0 += 8) {
-        if (rb > 0 || z0 > 0) {
-#pragma unroll
-          for (int zz = 0; zz < 8; ++zz)
-            pz[zz] = z0 + zz < p.S ? ld16_coherent(tall, off, (z0 + zz) * zstep) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int zz = 0; zz < 8; ++zz)
-          if (z0 + zz < p.S) sum = z0 + zz == 0 ? pz[zz] : sum + pz[zz];
-      }
-      *(f32x4 *)(tb + (lane & 15) * R + rb * 16 + 4 * (lane >> 4)) = sum;
-    }
+  if (p.unit_tiles > 0) {  // the unit waves' sums of t are in LDS
+    while (__hip_atomic_load(tready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < 2) __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");
   }
   if (i >= p.n || o >= p.n_out) return;
   float d[4] = {0.f, 0.f, 0.f, 0.f};
   if (routed) {  // B_q[o .. o+3] t_i, ranks in order, 16 at a time
-    const float *ti = p.unit_tiles > 0 ? tb + (lane & 15) * R : p.t + (size_t)i * R;
+    const float *ti = p.unit_tiles > 0 ? tsh + (i - r0) * R : p.t + (size_t)i * R;
     for (int r0 = 0; r0 < R; r0 += 16) {  // 16 ranks: every B load of the step in flight together
       uint4 bb[4][2];
 #pragma unroll
@@ -465,7 +435,7 @@ __global__ __launch_bounds__((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64) void decode_ke
   __shared__ __attribute__((aligned(16))) uint4 xs[kNSt * XR * 8];
   __shared__ __attribute__((aligned(16))) uint4 wb[NWW][2 * 128 * SPW];
   __shared__ int s_rows[2][64];
-  __shared__ int s_done, s_ready, s_xready;
+  __shared__ int s_done, s_ready, s_xready, s_tready;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -479,8 +449,16 @@ __global__ __launch_bounds__((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64) void decode_ke
     s_done = 0;
     s_ready = 0;
     s_xready = 0;
+    s_tready = 0;
   }
   __syncthreads();
+  // Finalization items of the tile: (row block b, slice j), item m = b NSL + j
+  // over the batch's row blocks; contributor z takes items [it_lo, it_hi), so
+  // its items share one or two row blocks (rows r0 ..), whose t the unit
+  // waves sum from the pieces once for the workgroup.
+  const int T = max(1, (p.n + 15) / 16) * NSL;
+  const int it_lo = z * T / p.S, it_hi = (z + 1) * T / p.S;
+  const int r0 = 16 * (it_lo / NSL);
 
   // x rows over the range: stages st = wave, wave + NXW, ... (2 NB DMAs each)
   for (int st = wave; wave < NXW && st < nst; st += NXW) {
@@ -515,6 +493,43 @@ __global__ __launch_bounds__((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64) void decode_ke
   // with the x rows of its slot's rows only, gathered 16 at a time from LDS,
   // and stores and counts its piece of t while W still streams.
   const bool carrier = p.unit_tiles > 0 && g < p.unit_tiles;
+  // A unit wave, its shrink work done: once the tile's arrivals are in (the
+  // pieces are all stored), t of the workgroup's finalization rows, each
+  // row's pieces summed in range order, into LDS over x (no wave reads x
+  // any more); then it counts itself in on s_tready.
+  auto t_sums = [&]() {
+    if (p.unit_tiles == 0 || it_lo >= it_hi) return;
+    while (__hip_atomic_load(&s_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+      __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");
+    if (__hip_atomic_load(&s_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 1) {
+      const int nrow = min(16 * ((it_hi - 1) / NSL + 1), p.n) - r0;
+      const int R = p.R, nq = R / 4, P = p.rd.max_loras;
+      const auto tall = coherent_rsrc(p.t_part, (uint32_t)((size_t)p.S * P * p.n * R * 4));
+      const uint32_t zstep = (uint32_t)(P * p.n * R) * 4;
+      float *tsh = (float *)xs;
+      for (int w = lane + 64 * wv; w < nrow * nq; w += 128) {
+        const int i = r0 + w / nq, qd = w % nq;
+        const RowRoute rr = row_route_decode(p, i);
+        if (rr.bq == nullptr) continue;
+        const uint32_t off = (uint32_t)((rr.slot * p.n + i) * R + 4 * qd) * 4;
+        f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int z0 = 0; z0 < p.S; z0 += 8) {
+          f32x4 pz[8];
+#pragma unroll
+          for (int zz = 0; zz < 8; ++zz)
+            pz[zz] = z0 + zz < p.S ? ld16_coherent(tall, off, (z0 + zz) * zstep) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int zz = 0; zz < 8; ++zz)
+            if (z0 + zz < p.S) sum = z0 + zz == 0 ? pz[zz] : sum + pz[zz];
+        }
+        *(f32x4 *)(tsh + (i - r0) * R + 4 * qd) = sum;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the sums are in LDS
+    asm volatile("" ::: "memory");
+    if (lane == 0) __hip_atomic_fetch_add(&s_tready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
   if (wv < 2) {
     const int n_units = p.rd.max_loras * RB;
     const int uk = 2 * g + wv;
@@ -549,7 +564,10 @@ __global__ __launch_bounds__((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64) void decode_ke
       zero_tail();
       __syncthreads();
     }
-    if (!unit) return;
+    if (!unit) {
+      t_sums();
+      return;
+    }
     auto count_unit = [&]() {
       unsigned *ccnt = p.tile_cnt + (size_t)(p.n_tiles + z) * kDecodeCtrStride;
       if (wave_atomic_add(ccnt, 1u) == (unsigned)n_units - 1) {  // the range's last unit
@@ -561,6 +579,7 @@ __global__ __launch_bounds__((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64) void decode_ke
     };
     if (!ua) {  // no A: no row reads this slot's pieces
       count_unit();
+      t_sums();
       return;
     }
     wait_vmcnt<0>();
@@ -603,6 +622,7 @@ __global__ __launch_bounds__((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64) void decode_ke
     }
     wait_vmcnt<0>();
     count_unit();
+    t_sums();
     return;
   }
   if (carrier) block_barrier();  // the unit waves' requests are out
@@ -652,19 +672,17 @@ __global__ __launch_bounds__((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64) void decode_ke
   int last = 0;
   if (lane == 0) last = atomicAdd(&s_done, 1) == NWW - 1;
   if (__builtin_amdgcn_readfirstlane(last)) (void)wave_atomic_add(tcnt, 1u);
-  // finalization items of this contributor: slices j = z, z + S, ... < NSL,
-  // every row block; item m NB + b goes to W wave (m NB + b) % NWW
-  const int nsl_mine = z < NSL ? (NSL - 1 - z) / p.S + 1 : 0;
-  const int n_items = nsl_mine * NB;
-  if (ww >= n_items) return;
+  // this contributor's finalization items it_lo + ww, it_lo + ww + NWW, ... < it_hi
+  const int m0 = it_lo + ww;
+  if (m0 >= it_hi) return;
   // W wave 0 alone polls the tile's arrival count (few pollers keep the
   // line free for the arrivals); the workgroup's other item waves wait on LDS
-  const RowRoute rr0 = row_route_decode(p, 16 * (ww % NB) + (lane & 15));  // in flight during the wait
+  const RowRoute rr0 = row_route_decode(p, 16 * (m0 / NSL) + (lane & 15));  // in flight during the wait
   // the first item's B rows depend on nothing this launch stores: they are
   // in flight during the wait too
   uint4 bpre[4][2];
   {
-    const int j = z + p.S * (ww / NB), i = 16 * (ww % NB) + (lane & 15), o = g * p.tile_out + 16 * j + 4 * (lane >> 4);
+    const int j = m0 % NSL, i = 16 * (m0 / NSL) + (lane & 15), o = g * p.tile_out + 16 * j + 4 * (lane >> 4);
     const bool expand = rr0.bq != nullptr && i < p.n && o < p.n_out;
     const u16 *bq = expand ? rr0.bq + (size_t)o * p.R : nullptr;
 #pragma unroll
@@ -686,16 +704,16 @@ __global__ __launch_bounds__((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64) void decode_ke
   }
   asm volatile("" ::: "memory");
   const bool gave_up = __hip_atomic_load(&s_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 2;
-  const unsigned items_per_tile = (unsigned)(NSL * NB);
-  for (int it = ww; it < n_items; it += NWW) {
-    const int j = z + p.S * (it / NB), b = it % NB;
-    const RowRoute rr = it == ww ? rr0 : row_route_decode(p, 16 * b + (lane & 15));
+  const unsigned items_per_tile = (unsigned)T;
+  for (int it = m0; it < it_hi; it += NWW) {
+    const int j = it % NSL, b = it / NSL;
+    const RowRoute rr = it == m0 ? rr0 : row_route_decode(p, 16 * b + (lane & 15));
     if (gave_up) {
       const int i = 16 * b + (lane & 15), o = g * p.tile_out + 16 * j + 4 * (lane >> 4);
       if (i < p.n && o < p.n_out) *(uint2 *)(p.y + (size_t)i * p.y_row_stride + o) = make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
     } else {
-      if (it == ww) finalize_item<true>(p, f, rr, g, j, b, (float *)&wb[ww][0], bpre);
-      else finalize_item<false>(p, f, rr, g, j, b, (float *)&wb[ww][0], bpre);
+      if (it == m0) finalize_item<true>(p, f, rr, g, j, b, (const float *)xs, r0, &s_tready, bpre);
+      else finalize_item<false>(p, f, rr, g, j, b, (const float *)xs, r0, &s_tready, bpre);
     }
     if (wave_atomic_add(tpass, 1u) == items_per_tile - 1) {  // every item is past the wait
       wave_store0(tcnt);
