@@ -16,7 +16,8 @@
 //    theirs have landed.  Each of its W waves owns SPW slices of 16 outputs
 //    (two on 128-output tiles): it requests their W rows x 512 columns
 //    (sixteen 16-byte loads per lane and slice, whole lines, through buffer
-//    resources), then, one 64-column stage at a time as the loads land, lays
+//    resources: half of them, then, once x has landed, the other half),
+//    then, one 64-column stage at a time as the loads land, lays
 //    the stage out in a wave-private LDS buffer and runs the MFMAs of its
 //    outputs against every row block of x, each x fragment read from LDS
 //    serving all its slices (LDS traffic, not the MFMAs, bounds this phase).
@@ -635,8 +636,14 @@ __global__ __launch_bounds__((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64) void decode_ke
 #pragma unroll
   for (int s = 0; s < SPW; ++s) wsl[s] = make_slice(p.W, p.w_row_stride, o0 + 16 * (SPW * ww + s), p.n_out, kb);
   if (full) {
-    issue_full<SPW, 0, kNSt>(wsl, v);
-    x_ready<2 * SPW * kNSt, NXW>(wv, &s_xready);
+    // half of the range's W, then the wait for x, then the other half: x
+    // comes from HBM behind whatever W the chip has asked for, so holding
+    // half of it back until x is in lets x land sooner while the first half
+    // keeps the stream going; the MFMAs then follow the second half's loads
+    // (all of W before the wait, or none, measured slower)
+    issue_full<SPW, 0, kNSt / 2>(wsl, v);
+    x_ready<2 * SPW * (kNSt / 2), NXW>(wv, &s_xready);
+    issue_full<SPW, kNSt / 2, kNSt>(wsl, v);
     slice_mma<NB, SPW, true>(v, xs, wb[ww], kb, ke, nst, acc);
   } else {
     issue_part<SPW>(wsl, kb, ke, nst, v);
