@@ -30,9 +30,9 @@
 //    always runs them together).  Finalizing sums the S partials in range
 //    order, adds s_q B_q t_i in f32 (ranks in order), an adapter stack's
 //    further levels, and rounds y once.
-//  * the shrink: when the pool's units (slot x 16-rank block) fit, the two
-//    unit waves of the workgroups of the first few tiles ("carriers") take
-//    one unit each over their k range.  The unit's 16 A rows are requested
+//  * the shrink: when the pool's units (slot x 16-rank block) fit, wave 0
+//    of the workgroups of the first few tiles ("carriers") takes one unit
+//    over its k range.  The unit's 16 A rows are requested
 //    into MFMA operand layout before the workgroup's W (the W waves wait at
 //    a block barrier until then: on this chip a request made behind a CU's
 //    W stream waits for most of it), then contracted with the x rows of the
@@ -42,8 +42,8 @@
 //    into every tile's arrival word, and every tile waits for its S
 //    contributors and the S ranges before it finalizes.  Carriers never wait
 //    before they count themselves in; the carrier workgroups are the first
-//    of the launch and at most 64, so they all run whatever else is
-//    resident.  A larger pool takes a prep launch (k_prep.hip) that leaves
+//    of the launch and at most half the device's CUs, so they all run
+//    whatever else is resident.  A larger pool takes a prep launch (k_prep.hip) that leaves
 //    t in the workspace first.
 //
 // Skipped rows (slot < 0 or past the pool, NULL table entry, zero scale) get
@@ -419,8 +419,9 @@ __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFo
 // (their launches are small: more waves keep more loads in flight).  A
 // workgroup's waves by role (a SIMD issues the requests of its older waves
 // first):
-//  * waves 0 and 1, the unit waves, carry the shrink on the first
-//    unit_tiles tiles;
+//  * waves 0 and 1, the unit waves: wave 0 carries a unit of the shrink on
+//    the first unit_tiles tiles; after the tile's wait both sum the pieces
+//    of t for the workgroup's finalization rows;
 //  * waves 2 .. NSW / SPW + 1, the W waves, stream W;
 //  * waves 0 .. 3 also request the range's x rows into LDS; each of them,
 //    once its own have landed, counts itself in on an LDS word that the W
@@ -486,8 +487,8 @@ __global__ __launch_bounds__((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64) void decode_ke
   };
 
   // The shrink rides this launch on the first unit_tiles tiles (the carrier
-  // workgroups): unit wave u of tile g's workgroups takes unit 2 g + u (pool
-  // slot x 16-rank block) over the workgroup's range.  Its slot's 16 A rows
+  // workgroups): wave 0 of tile g's workgroups takes unit g (pool slot x
+  // 16-rank block) over the workgroup's range.  Its slot's 16 A rows
   // are requested straight into MFMA operand layout before any W load of the
   // workgroup (a block barrier holds the W waves until then: a request made
   // behind the W stream would wait for most of it); it then contracts them
@@ -533,8 +534,8 @@ __global__ __launch_bounds__((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64) void decode_ke
   };
   if (wv < 2) {
     const int n_units = p.rd.max_loras * RB;
-    const int uk = 2 * g + wv;
-    const bool unit = carrier && uk < n_units;
+    const int uk = g;
+    const bool unit = carrier && wv == 0 && uk < n_units;
     const uint64_t aentry = unit ? scalar_entry(p.rd.a_table, uk / RB) : 0;
     const bool ua = unit && aentry != 0;  // a unit with A rows to contract
     const int uslot = uk / RB, urb = uk % RB;

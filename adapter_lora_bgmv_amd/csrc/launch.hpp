@@ -91,8 +91,8 @@ struct DecodeArgs {
   int n_tiles;          // ceil(n_out / tile_out)
   int tile_out;         // outputs per tile: 16 x the waves (128 or 64)
   float *partials;      // [n_tiles][S][kDecodeSlices][kDecodeSliceFloats]
-  // The shrink: with unit_tiles > 0 it rides this launch (two unit waves in
-  // each workgroup of the first unit_tiles tiles, see k_decode.hip) and
+  // The shrink: with unit_tiles > 0 it rides this launch (one unit, on wave
+  // 0 of each workgroup of the first unit_tiles tiles, see k_decode.hip) and
   // leaves range pieces [S][max_loras][n][R] in t_part, written for the rows
   // on each slot (max_loras x R <= kDecodeUnitRanks); otherwise a prep
   // launch wrote t [n][R].
@@ -124,8 +124,9 @@ constexpr int kDecodeTileOut = 128;
 // outputs, so that their launch still spreads over the chip.
 constexpr int kDecodeTileOutSmall = 64;
 constexpr int kDecodeSmallTileMaxOut = 2048;
-// Workgroups of a decode launch that may carry the shrink's units.
-constexpr int kDecodeMaxCarrierWgs = 64;
+// Workgroups of a decode launch that may carry the shrink's units (one
+// each); the host also keeps them to half the device's compute units.
+constexpr int kDecodeMaxCarrierWgs = 128;
 
 // Rows per shrink unit; its 64-column stages in LDS at a time (16 KB each).
 constexpr int kShrinkRows = 64;

@@ -48,7 +48,8 @@ int launch_status(hipError_t e, const char *what) {
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // ------------------------------------------------------------ device check
-int g_dev_ok[64];  // 0 unknown, 1 gfx950, -1 other
+int g_dev_ok[64];   // 0 unknown, 1 gfx950, -1 other
+int g_dev_cus[64];  // compute units, once known
 
 int check_device(const char *what) {
   int dev = 0;
@@ -59,6 +60,7 @@ int check_device(const char *what) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
       return fail(LORA_ERR_LAUNCH, "%s: cannot query device %d", what, dev);
+    g_dev_cus[dev] = prop.multiProcessorCount;
     g_dev_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
     if (g_dev_ok[dev] < 0)
       return fail(LORA_ERR_LAUNCH, "%s: device %d is %s, the kernels are built for gfx950 only",
@@ -66,6 +68,13 @@ int check_device(const char *what) {
   }
   if (g_dev_ok[dev] < 0) return fail(LORA_ERR_LAUNCH, "%s: device %d is not a gfx950", what, dev);
   return LORA_OK;
+}
+
+// The current device's compute units (0 if it was never checked).
+int current_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  return g_dev_cus[dev];
 }
 
 // ------------------------------------------------------------ scratch for callers that cannot allocate
@@ -487,16 +496,18 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
     da.t_part = (float *)(ws + L.t);
     da.tile_cnt = (unsigned *)(ws + L.tile_cnt);
     // The shrink rides the decode launch when its units (pool slots x
-    // 16-rank blocks, two per carrier workgroup) fit on a few tiles: those
+    // 16-rank blocks, one per carrier workgroup) fit on a few tiles: those
     // workgroups, the first ones of the launch, never wait before they
-    // count themselves in, and every other workgroup waits for them, so at
-    // most kDecodeMaxCarrierWgs of them keeps the launch safe wherever that
-    // many workgroups fit at once (a quarter of the chip's CUs).  Otherwise
-    // a prep launch computes t first.
+    // count themselves in, and every other workgroup waits for them, so
+    // they must all be resident at once: at most kDecodeMaxCarrierWgs of
+    // them, and at most half the device's compute units (a workgroup of
+    // this kernel takes a whole CU).  Otherwise a prep launch computes t
+    // first.
     const int units = R > 0 ? rd.max_loras * (R / 16) : 0;
-    const int ut = (units + 1) / 2;
+    const int ut = units;
+    const int carrier_cap = std::min(kDecodeMaxCarrierWgs, current_cus() / 2);
     da.unit_tiles = R > 0 && R <= 64 && rd.max_loras * R <= kDecodeUnitRanks && ut <= c.n_ntiles &&
-                            ut * c.splits <= kDecodeMaxCarrierWgs
+                            ut * c.splits <= carrier_cap
                         ? ut
                         : 0;
     const bool fold = stack && stack->n_levels > 0 && has_lora;
