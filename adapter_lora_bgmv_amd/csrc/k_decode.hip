@@ -501,20 +501,35 @@ __global__ __launch_bounds__((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64) void decode_ke
   // any more); then it counts itself in on s_tready.
   auto t_sums = [&]() {
     if (p.unit_tiles == 0 || it_lo >= it_hi) return;
+    // (row, 4-rank quad) pairs w = lane + 64 wv + 128 k: at most 64 rows of
+    // at most 16 quads (R <= 64 whenever the shrink rides this launch), so
+    // k < 8.  Their rows' routes depend on nothing this launch stores: they
+    // are looked up before the wait.
+    const int nrow = min(16 * ((it_hi - 1) / NSL + 1), p.n) - r0;
+    const int R = p.R, nq = R / 4, P = p.rd.max_loras;
+    int sl[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int w = lane + 64 * wv + 128 * k;
+      sl[k] = -1;
+      if (w < nrow * nq) {
+        const RowRoute rr = row_route_decode(p, r0 + w / nq);
+        if (rr.bq != nullptr) sl[k] = rr.slot;
+      }
+    }
     while (__hip_atomic_load(&s_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
       __builtin_amdgcn_s_sleep(1);
     asm volatile("" ::: "memory");
     if (__hip_atomic_load(&s_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 1) {
-      const int nrow = min(16 * ((it_hi - 1) / NSL + 1), p.n) - r0;
-      const int R = p.R, nq = R / 4, P = p.rd.max_loras;
       const auto tall = coherent_rsrc(p.t_part, (uint32_t)((size_t)p.S * P * p.n * R * 4));
       const uint32_t zstep = (uint32_t)(P * p.n * R) * 4;
       float *tsh = (float *)xs;
-      for (int w = lane + 64 * wv; w < nrow * nq; w += 128) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int w = lane + 64 * wv + 128 * k;
+        if (w >= nrow * nq || sl[k] < 0) continue;
         const int i = r0 + w / nq, qd = w % nq;
-        const RowRoute rr = row_route_decode(p, i);
-        if (rr.bq == nullptr) continue;
-        const uint32_t off = (uint32_t)((rr.slot * p.n + i) * R + 4 * qd) * 4;
+        const uint32_t off = (uint32_t)((sl[k] * p.n + i) * R + 4 * qd) * 4;
         f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int z0 = 0; z0 < p.S; z0 += 8) {
           f32x4 pz[8];
