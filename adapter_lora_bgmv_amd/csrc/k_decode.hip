@@ -80,6 +80,17 @@ __device__ __forceinline__ void wait_vm(int n) {
 // every wave reaches the end of the kernel; the tile's outputs are then NaN.
 constexpr uint64_t kTileWaitTicks = 50000000ull;
 
+// A tile's partials when its contributors all run on one XCD
+// (DecodeArgs::xcd_local), cache policy sc0: a store lands in that XCD's L2
+// and a load misses the CU's L1 and reads the L2.
+constexpr int kCachePolicySc0 = 1;
+__device__ __forceinline__ void st16_l2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)voff, (int)soff, kCachePolicySc0);
+}
+__device__ __forceinline__ f32x4 ld16_l2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kCachePolicySc0));
+}
+
 // Polls a counter until it reaches `target` or `ticks` pass.  Each poll is
 // a device-scope atomic load, which reads past this XCD's L2.
 __device__ __forceinline__ unsigned poll(unsigned *ctr) {
@@ -296,7 +307,7 @@ __device__ __forceinline__ uint64_t scalar_entry(const void *const *tab, int idx
 // for the tile's arrivals, in bpre).  t comes from the workgroup's LDS copy
 // (tsh, rows from r0 on, summed from the pieces by the unit waves; they count
 // themselves in on *tready), or as a prep launch left it.
-template <bool PRE>
+template <bool PRE, bool XL>
 __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFold &f, const RowRoute &rr, int g, int j,
                                               int b, const float *tsh, int r0, const int *tready,
                                               const uint4 (&bpre)[4][2]) {
@@ -312,9 +323,11 @@ __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFo
   auto load_parts = [&](int z0) {
 #pragma unroll
     for (int zz = 0; zz < kG; ++zz)
-      part[zz] = z0 + zz < p.S ? ld16_coherent(coherent_rsrc(slice_partial(p, g, z0 + zz, j), kDecodeSliceFloats * 4),
-                                               (uint32_t)(b * 64 + lane) * 16, 0)
-                               : f32x4{0.f, 0.f, 0.f, 0.f};
+      part[zz] = z0 + zz >= p.S ? f32x4{0.f, 0.f, 0.f, 0.f}
+                 : XL ? ld16_l2(coherent_rsrc(slice_partial(p, g, z0 + zz, j), kDecodeSliceFloats * 4),
+                                         (uint32_t)(b * 64 + lane) * 16, 0)
+                               : ld16_coherent(coherent_rsrc(slice_partial(p, g, z0 + zz, j), kDecodeSliceFloats * 4),
+                                               (uint32_t)(b * 64 + lane) * 16, 0);
   };
   load_parts(0);
   // B_q[o .. o+3] over the first 16 ranks: it goes out with the partials
@@ -416,7 +429,10 @@ __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFo
 // NB: 16-row blocks of the batch (n <= 16 NB); NSW: slices of 16 outputs
 // per tile (TO = 16 NSW outputs), two per W wave on 128-output tiles (each x
 // fragment read from LDS then serves two slices) and one on 64-output tiles
-// (their launches are small: more waves keep more loads in flight).  A
+// (their launches are small: more waves keep more loads in flight); XL: the
+// tile's contributors on one XCD, their partials through its L2
+// (DecodeArgs::xcd_local; its own instantiation, so that the other keeps the
+// code it had).  A
 // workgroup's waves by role (a SIMD issues the requests of its older waves
 // first):
 //  * waves 0 and 1, the unit waves: wave 0 carries a unit of the shrink on
@@ -427,7 +443,7 @@ __device__ __forceinline__ void finalize_item(const DecodeArgs &p, const StackFo
 //    once its own have landed, counts itself in on an LDS word that the W
 //    waves watch before their first stage reads x (no block barrier between
 //    the W loads and the first MFMAs).
-template <int NB, int NSW>
+template <int NB, int NSW, bool XL>
 __global__ __launch_bounds__((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64) void decode_kernel(DecodeArgs p, StackFold f) {
   constexpr int XR = 16 * NB;
   constexpr int NSL = NSW;      // slices per tile
@@ -441,7 +457,9 @@ __global__ __launch_bounds__((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64) void decode_ke
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int g = blockIdx.x / p.S, z = blockIdx.x % p.S;
+  const int b8 = blockIdx.x >> 3;
+  const int g = XL ? (b8 / p.S) * 8 + (blockIdx.x & 7) : blockIdx.x / p.S;
+  const int z = XL ? b8 % p.S : blockIdx.x % p.S;
   const int kb = z * kKR, ke = min(kb + kKR, p.k_in);
   const int nst = (ke - kb + 63) / 64;
   const int o0 = g * p.tile_out;
@@ -684,8 +702,13 @@ __global__ __launch_bounds__((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64) void decode_ke
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
     const auto rs = coherent_rsrc(slice_partial(p, g, z, SPW * ww + s), kDecodeSliceFloats * 4);
+    if constexpr (XL) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) st16_coherent(rs, (uint32_t)(b * 64 + lane) * 16, 0, acc[s][b]);
+      for (int b = 0; b < NB; ++b) st16_l2(rs, (uint32_t)(b * 64 + lane) * 16, 0, acc[s][b]);
+    } else {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) st16_coherent(rs, (uint32_t)(b * 64 + lane) * 16, 0, acc[s][b]);
+    }
   }
   wait_vmcnt<0>();
   // the last W wave of the workgroup to have stored counts the workgroup in;
@@ -735,8 +758,8 @@ __global__ __launch_bounds__((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64) void decode_ke
       const int i = 16 * b + (lane & 15), o = g * p.tile_out + 16 * j + 4 * (lane >> 4);
       if (i < p.n && o < p.n_out) *(uint2 *)(p.y + (size_t)i * p.y_row_stride + o) = make_uint2(0x7fc07fc0u, 0x7fc07fc0u);
     } else {
-      if (it == m0) finalize_item<true>(p, f, rr, g, j, b, (const float *)xs, r0, &s_tready, bpre);
-      else finalize_item<false>(p, f, rr, g, j, b, (const float *)xs, r0, &s_tready, bpre);
+      if (it == m0) finalize_item<true, XL>(p, f, rr, g, j, b, (const float *)xs, r0, &s_tready, bpre);
+      else finalize_item<false, XL>(p, f, rr, g, j, b, (const float *)xs, r0, &s_tready, bpre);
     }
     if (wave_atomic_add(tpass, 1u) == items_per_tile - 1) {  // every item is past the wait
       wave_store0(tcnt);
@@ -752,8 +775,15 @@ hipError_t launch_decode(const DecodeArgs &a, const StackFold *stack, hipStream_
   if (stack) f = *stack;
   const int nb = (a.n + 15) / 16;
   const int nsw = a.tile_out / 16;
-#define LORA_DECODE(NB, NSW) \
-  hipLaunchKernelGGL((decode_kernel<NB, NSW>), dim3(grid), dim3((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64), 0, st, a, f)
+#define LORA_DECODE(NB, NSW)                                                                                     \
+  do {                                                                                                           \
+    if (a.xcd_local)                                                                                             \
+      hipLaunchKernelGGL((decode_kernel<NB, NSW, true>), dim3(grid), dim3((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64), 0, \
+                         st, a, f);                                                                              \
+    else                                                                                                         \
+      hipLaunchKernelGGL((decode_kernel<NB, NSW, false>), dim3(grid), dim3((NSW / (NSW >= 8 ? 2 : 1) + 2) * 64),   \
+                         0, st, a, f);                                                                           \
+  } while (0)
   if (nsw == 8) {
     if (nb <= 1) LORA_DECODE(1, 8);
     else if (nb == 2) LORA_DECODE(2, 8);

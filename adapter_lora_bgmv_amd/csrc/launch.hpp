@@ -105,6 +105,12 @@ struct DecodeArgs {
   // all done, [1] finalization items past the wait for them; then range z's
   // unit count at tile_cnt + (n_tiles + z) kDecodeCtrStride
   unsigned *tile_cnt;
+  // 1: tile g's S contributors are the workgroups 8 (S (g / 8) + z) + g % 8,
+  // which the chip's round-robin hand-out of workgroups to its 8 XCDs puts
+  // on one XCD, and their partials pass through that XCD's L2; 0: tile g's
+  // contributors are workgroups S g .. S g + S - 1 and their partials pass
+  // through the memory side
+  int xcd_local;
 };
 
 // Largest batch the decode kernel takes; columns per k range; the largest

@@ -503,11 +503,26 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
     // them, and at most half the device's compute units (a workgroup of
     // this kernel takes a whole CU).  Otherwise a prep launch computes t
     // first.
+    //
+    // A tile's contributors share their partials through one XCD's L2 when
+    // the chip's round-robin hand-out of workgroups to its 8 XCDs puts them
+    // on one XCD (DecodeArgs::xcd_local): tiles in multiples of 8, and the
+    // whole launch resident at once (a workgroup per CU), so that every
+    // contributor of a tile runs alongside the others whatever their places
+    // in the launch.  Each XCD then fetches every k range of x instead of
+    // one; measured, that costs more than the L2 saves once the launch
+    // fills the chip (64 x 4096 x 4096: 16.0 -> 17.4 us a step), and less on
+    // launches of at most half the CUs (36 x 4096 x 1024: 11.6 -> 11.1 us),
+    // which alone take it.  Carriers are then the first 8 S
+    // ceil(unit_tiles / 8) workgroups.
+    const int cus = current_cus();
+    da.xcd_local = c.n_ntiles % 8 == 0 && 2 * c.n_ntiles * c.splits <= cus ? 1 : 0;
     const int units = R > 0 ? rd.max_loras * (R / 16) : 0;
     const int ut = units;
-    const int carrier_cap = std::min(kDecodeMaxCarrierWgs, current_cus() / 2);
+    const int carrier_wgs = (da.xcd_local ? (ut + 7) / 8 * 8 : ut) * c.splits;
+    const int carrier_cap = std::min(kDecodeMaxCarrierWgs, cus / 2);
     da.unit_tiles = R > 0 && R <= 64 && rd.max_loras * R <= kDecodeUnitRanks && ut <= c.n_ntiles &&
-                            ut * c.splits <= carrier_cap
+                            carrier_wgs <= carrier_cap
                         ? ut
                         : 0;
     const bool fold = stack && stack->n_levels > 0 && has_lora;
