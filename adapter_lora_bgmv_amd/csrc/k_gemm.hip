@@ -488,10 +488,17 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
 
   // ---------------------------------------------------------- epilogue
   // The tile goes through LDS as bf16 (16-byte chunk c of tile row r at slot
-  // c ^ (r % CPR), so the fragment-ordered writes spread over the banks) and
-  // leaves in whole 16-byte pieces, each tile row's by consecutive lanes.
+  // c ^ (r % CPR), or within its group of 8 chunks c ^ (r % 8) when CPR is
+  // not a power of two, so the fragment-ordered writes spread over the
+  // banks) and leaves in whole 16-byte pieces, each tile row's by
+  // consecutive lanes.
   constexpr int CPR = BO / 8;  // 16-byte chunks per tile row
   static_assert(BR * CPR <= NS * RS * 8, "the bf16 tile fits the ring");
+  static_assert((CPR & (CPR - 1)) == 0 || CPR % 8 == 0, "chunk swizzle");
+  auto yslot = [](int r, int c) {
+    if constexpr ((CPR & (CPR - 1)) == 0) return r * CPR + (c ^ (r & (CPR - 1)));
+    else return r * CPR + ((c & ~7) | ((c ^ r) & 7));
+  };
   uint4 *const ylds = &ring[0][0];
   __syncthreads();  // every wave is done with the ring
 #pragma unroll
@@ -502,7 +509,7 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
       const int lr = wr * WR + br * 16 + (lane & 15);  // tile row
       const f32x4 v = acc[bo][br];
       const uint2 pk = make_uint2(pack2(f2bf(v[0]), f2bf(v[1])), pack2(f2bf(v[2]), f2bf(v[3])));
-      uint2 *dst = (uint2 *)&ylds[lr * CPR + ((oc >> 3) ^ (lr & (CPR - 1)))];
+      uint2 *dst = (uint2 *)&ylds[yslot(lr, oc >> 3)];
       dst[(oc >> 2) & 1] = pk;
     }
   }
@@ -511,7 +518,7 @@ __global__ __launch_bounds__(WGO *WGR * 64) void gemm_bf16_kernel(GemmArgs p) {
     const int r = idx / CPR, c = idx % CPR;
     const int grow = s_row[r], o = o0 + c * 8;
     if (grow >= 0 && o < p.n_out)
-      *(uint4 *)(p.y + (size_t)grow * p.y_row_stride + o) = ylds[r * CPR + (c ^ (r & (CPR - 1)))];
+      *(uint4 *)(p.y + (size_t)grow * p.y_row_stride + o) = ylds[yslot(r, c)];
   }
   };  // segment
 
@@ -535,6 +542,7 @@ hipError_t launch_gemm(const GemmArgs &a, int to, int tr, hipStream_t st) {
   else if (to == 128 && tr == 128 && mode == kSplitK) LORA_GEMM(128, 128, 2, 2, 4, kSplitK);
   else if (to == 256 && tr == 64 && mode == kOneTile) LORA_GEMM(256, 64, 4, 1, 3, kOneTile);
   else if (to == 256 && tr == 128 && mode == kOneTile) LORA_GEMM(256, 128, 4, 2, 3, kOneTile);
+  else if (to == 192 && tr == 128 && mode == kOneTile) LORA_GEMM(192, 128, 4, 2, 3, kOneTile);
   else if (to == 256 && tr == 256 && mode == kOneTile) LORA_GEMM(256, 256, 2, 4, 2, kOneTile);
   else
     return hipErrorInvalidValue;

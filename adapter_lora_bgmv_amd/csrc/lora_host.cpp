@@ -166,6 +166,12 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
     const bool lds_rank = R == 0 || (R <= 64 && 64 % R == 0);
     c.to = 256; c.tr = n <= kNarrowTileMaxRows || !lds_rank ? 128 : 256;
     c.splits = 1;
+    // 128-row tiles 192 outputs wide when they still make one round of
+    // workgroups on the device: a stage's fragment reads and MFMAs, not its
+    // DMA, bound these tiles, so more busy CUs finish sooner (the fused
+    // gate/up shape: 172 workgroups of 256 x 128, or 230 of 192 x 128)
+    const int mt = (n + 127) / 128, cus = current_cus();
+    if (c.tr == 128 && (n_out + 191) / 192 * mt <= cus) c.to = 192;
   }
   if (c.decode) {
     c.k_per_split = kDecodeKR;
