@@ -299,6 +299,11 @@ __device__ __forceinline__ void store_tt(u16 *tt, int R, int row, int r, float s
   }
 }
 
+// REG: the unit's operands go straight into registers, all of a 512-column
+// chunk's in flight at once (fewer round trips on large units; 236
+// registers, two workgroups per CU); otherwise by LDS-DMA in batches of
+// kShrinkStages stages (three workgroups per CU).
+template <bool REG>
 __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = a.n_pairs;
@@ -309,8 +314,9 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
   int *wsum = cnt + P;        // [4]
   int *info = wsum + 4;       // [4]
   int *rows = info + 4;       // [kShrinkRows]
-  uint4 *stg = (uint4 *)(lds + ((P + 8 + kShrinkRows + 3) & ~3));  // [kShrinkStages][128 rows][8] stages
-  int *pk = (int *)(stg + kShrinkStages * 128 * 8);  // [n] the rows' packed routes (standalone shrink)
+  // [kShrinkStages][128 rows][8] stages, or (REG) the waves' sums
+  uint4 *stg = (uint4 *)(lds + ((P + 8 + kShrinkRows + 3) & ~3));
+  int *pk = (int *)(stg + kShrinkLdsBytes / 16);  // [n] the rows' packed routes (standalone shrink)
 
   const bool ranked = a.ranks != nullptr;  // the route kernel counted and ranked the rows
   if (ranked) {
@@ -457,74 +463,170 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
   float *tout = KS == 1 ? a.t_final : a.t + (size_t)kz * a.n * R;
   const auto prs = coherent_rsrc(a.t, (uint32_t)((size_t)KS * a.n * R * 4));  // the k-chunk partials
 
-  // 64 ranks at a time.  A stage is 64 k columns of the group's rank rows of
-  // A, then of the unit's x rows (gathered, 16 G of them), in whole 128-byte
-  // lines by LDS-DMA (chunk c of row r at slot c ^ ((r >> 1) & 7)); up to
-  // kShrinkStages stages go out together, then wave w takes rank block w
-  // through them, every row group, in k order.
-  for (int rg = 0; rg * 64 < R; ++rg) {
-    const int RA = min(64, R - rg * 64);  // rank rows of the group
-    const int RU = RA + 16 * G;           // rows of a stage
-    const int per = RU / 8;               // DMA instructions per stage
-    f32x4 acc[kShrinkRows / 16];
-#pragma unroll
-    for (int g = 0; g < kShrinkRows / 16; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int sb = 0; sb < nst; sb += kShrinkStages) {
-      const int nsn = min(kShrinkStages, nst - sb), kb0 = kc0 + sb * 64;
-      __syncthreads();  // the previous batch is read
-      for (int ii = wave; ii < nsn * per; ii += 4) {
-        const int st = ii / per, k8 = ii % per;
-        const int rr = k8 * 8 + (lane >> 3);  // row of the stage
-        const u16 *rowp = rr < RA ? A + (size_t)(rg * 64 + rr) * K
-                                  : a.x + (size_t)max(rows[min(rr - RA, nrows - 1)], 0) * a.x_stride;
-        const int kk = kb0 + st * 64 + ((lane & 7) ^ ((rr >> 1) & 7)) * 8;
-        dma16(rowp + (kk < kc1 ? kk : kc0), lds_addr(stg + (st * RU + k8 * 8) * 8));
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      if (kb0 + nsn * 64 > kc1) {  // zero what the last stage fetched past the chunk
-        for (int ii = wave; ii < nsn * per; ii += 4) {
-          const int st = ii / per, k8 = ii % per;
-          const int rr = k8 * 8 + (lane >> 3);
-          if (kb0 + st * 64 + ((lane & 7) ^ ((rr >> 1) & 7)) * 8 >= kc1) stg[(st * RU + k8 * 8) * 8 + lane] = z4();
+  if constexpr (REG) {
+    // 64 ranks at a time.  The chunk's 32-column steps are shared out over the
+    // four waves (wave w: steps w, w + 4, ...).  Per step a wave loads, straight
+    // into MFMA operand layout, the group's rank rows of A (one 16-byte load
+    // per 16-rank block: lane l holds rank 16 rb + l % 16, columns 8 (l / 16)
+    // .. + 7 of the step) and the unit's gathered x rows (one per 16-row
+    // group, the same way), kShrinkSteps steps' loads in flight together, and
+    // accumulates D[16 ranks][16 rows] per (rank block, row group).  Wave w
+    // then adds rank block w's sums of the four waves in wave order: its own
+    // from registers, the other three's from LDS (block (w', rb), w' != rb, at
+    // slot 3 rb + w' - (w' > rb)).
+    const int nstep = (kc1 - kc0 + 31) / 32;
+    f32x4 *red = (f32x4 *)stg;  // [12 blocks][4 row groups][64 lanes]
+    int xrow[kShrinkRows / 16];  // this lane's x row per group (row 0 where none: never stored)
+  #pragma unroll
+    for (int g = 0; g < kShrinkRows / 16; ++g) {
+      const int i = g * 16 + (lane & 15);
+      const int r = i < nrows ? rows[i] : -1;
+      xrow[g] = r < 0 ? 0 : r;
+    }
+    for (int rg = 0; rg * 64 < R; ++rg) {
+      const int RB = min(64, R - rg * 64) / 16;  // rank blocks of the group
+      f32x4 acc[4][kShrinkRows / 16];
+  #pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+  #pragma unroll
+        for (int g = 0; g < kShrinkRows / 16; ++g) acc[rb][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const u16 *Ag = A + (size_t)(rg * 64 + (lane & 15)) * K;
+      for (int j0 = 0; wave + 4 * j0 < nstep; j0 += kShrinkSteps) {
+        uint4 af[kShrinkSteps][4], xf[kShrinkSteps][kShrinkRows / 16];
+  #pragma unroll
+        for (int d = 0; d < kShrinkSteps; ++d) {
+          const int st = wave + 4 * (j0 + d);
+          const bool live = st < nstep;  // uniform over the wave
+          const int k = kc0 + st * 32 + (lane >> 4) * 8;
+          const bool in = live && k < kc1;  // k_in is a multiple of 8: a lane's 8 columns are all in or all out
+          const int kk = in ? k : kc0;
+  #pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+            af[d][rb] = live && rb < RB ? ldg16(Ag + (size_t)rb * 16 * K + kk) : z4();
+            if (!in) af[d][rb] = z4();
+          }
+  #pragma unroll
+          for (int g = 0; g < kShrinkRows / 16; ++g) {
+            xf[d][g] = live && g < G ? ldg16(a.x + (size_t)xrow[g] * a.x_stride + kk) : z4();
+            if (!in) xf[d][g] = z4();
+          }
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-      }
-      __syncthreads();
-      if (wave * 16 < RA) {
-        const int ra = wave * 16 + (lane & 15);
-        for (int st = 0; st < nsn; ++st) {
-          const uint4 *sl = stg + st * RU * 8;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int c = 4 * h + (lane >> 4);
-            const uint4 av = sl[ra * 8 + (c ^ ((ra >> 1) & 7))];
-#pragma unroll
+  #pragma unroll
+        for (int d = 0; d < kShrinkSteps; ++d) {
+          if (wave + 4 * (j0 + d) >= nstep) break;
+  #pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+            if (rb >= RB) break;
+  #pragma unroll
             for (int g = 0; g < kShrinkRows / 16; ++g) {
               if (g >= G) break;
-              const int rx = RA + g * 16 + (lane & 15);
-              acc[g] = mfma16(av, sl[rx * 8 + (c ^ ((rx >> 1) & 7))], acc[g]);
+              acc[rb][g] = mfma16(af[d][rb], xf[d][g], acc[rb][g]);
             }
           }
         }
       }
-    }
-    if (wave * 16 < RA) {
-#pragma unroll
-      for (int g = 0; g < kShrinkRows / 16; ++g) {
-        const int i = g * 16 + (lane & 15);
-        if (g >= G || i >= nrows || rows[i] < 0) continue;
-        // D column = lane%16 (the row), D rows = ranks 4*(lane/16) .. +3 of the wave's block
-        const int rk = rg * 64 + wave * 16 + (lane >> 4) * 4;
-        float *dst = tout + (size_t)rows[i] * R + rk;
-        const f32x4 v = acc[g];
-        if (KS == 1) {
-          *(f32x4 *)dst = v;
-          if (a.tt) {
-            const float vv[4] = {v[0], v[1], v[2], v[3]};
-            store_tt(a.tt, R, rows[i], rk, sig, vv, 4);
+      __syncthreads();  // the last rank group's sums are read
+  #pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+  #pragma unroll
+        for (int g = 0; g < kShrinkRows / 16; ++g)
+          if (rb != wave && rb < RB && g < G)
+            red[((3 * rb + wave - (wave > rb)) * 4 + g) * 64 + lane] = acc[rb][g];
+      __syncthreads();
+      if (wave < RB) {  // wave w: rank block w, every row group, the four waves' sums in order
+  #pragma unroll
+        for (int g = 0; g < kShrinkRows / 16; ++g) {
+          const int i = g * 16 + (lane & 15);
+          if (g >= G || i >= nrows || rows[i] < 0) continue;
+          const f32x4 own = wave == 0 ? acc[0][g] : wave == 1 ? acc[1][g] : wave == 2 ? acc[2][g] : acc[3][g];
+          f32x4 v = wave == 0 ? own : red[((3 * wave + 0) * 4 + g) * 64 + lane];
+  #pragma unroll
+          for (int w = 1; w < 4; ++w) v += w == wave ? own : red[((3 * wave + w - (w > wave)) * 4 + g) * 64 + lane];
+          // D column = lane%16 (the row), D rows = ranks 4*(lane/16) .. +3 of the wave's block
+          const int rk = rg * 64 + wave * 16 + (lane >> 4) * 4;
+          float *dst = tout + (size_t)rows[i] * R + rk;
+          if (KS == 1) {
+            *(f32x4 *)dst = v;
+            if (a.tt) {
+              const float vv[4] = {v[0], v[1], v[2], v[3]};
+              store_tt(a.tt, R, rows[i], rk, sig, vv, 4);
+            }
+          } else {  // 16-byte device-coherent store into this chunk's partial
+            st16_coherent(prs, (uint32_t)((dst - a.t) * 4), 0, v);
           }
-        } else {  // 16-byte device-coherent store into this chunk's partial
-          st16_coherent(prs, (uint32_t)((dst - a.t) * 4), 0, v);
+        }
+      }
+    }
+  } else {
+    // 64 ranks at a time.  A stage is 64 k columns of the group's rank rows of
+    // A, then of the unit's x rows (gathered, 16 G of them), in whole 128-byte
+    // lines by LDS-DMA (chunk c of row r at slot c ^ ((r >> 1) & 7)); up to
+    // kShrinkStages stages go out together, then wave w takes rank block w
+    // through them, every row group, in k order.
+    for (int rg = 0; rg * 64 < R; ++rg) {
+      const int RA = min(64, R - rg * 64);  // rank rows of the group
+      const int RU = RA + 16 * G;           // rows of a stage
+      const int per = RU / 8;               // DMA instructions per stage
+      f32x4 acc[kShrinkRows / 16];
+  #pragma unroll
+      for (int g = 0; g < kShrinkRows / 16; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int sb = 0; sb < nst; sb += kShrinkStages) {
+        const int nsn = min(kShrinkStages, nst - sb), kb0 = kc0 + sb * 64;
+        __syncthreads();  // the previous batch is read
+        for (int ii = wave; ii < nsn * per; ii += 4) {
+          const int st = ii / per, k8 = ii % per;
+          const int rr = k8 * 8 + (lane >> 3);  // row of the stage
+          const u16 *rowp = rr < RA ? A + (size_t)(rg * 64 + rr) * K
+                                    : a.x + (size_t)max(rows[min(rr - RA, nrows - 1)], 0) * a.x_stride;
+          const int kk = kb0 + st * 64 + ((lane & 7) ^ ((rr >> 1) & 7)) * 8;
+          dma16(rowp + (kk < kc1 ? kk : kc0), lds_addr(stg + (st * RU + k8 * 8) * 8));
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        if (kb0 + nsn * 64 > kc1) {  // zero what the last stage fetched past the chunk
+          for (int ii = wave; ii < nsn * per; ii += 4) {
+            const int st = ii / per, k8 = ii % per;
+            const int rr = k8 * 8 + (lane >> 3);
+            if (kb0 + st * 64 + ((lane & 7) ^ ((rr >> 1) & 7)) * 8 >= kc1) stg[(st * RU + k8 * 8) * 8 + lane] = z4();
+          }
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        }
+        __syncthreads();
+        if (wave * 16 < RA) {
+          const int ra = wave * 16 + (lane & 15);
+          for (int st = 0; st < nsn; ++st) {
+            const uint4 *sl = stg + st * RU * 8;
+  #pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int c = 4 * h + (lane >> 4);
+              const uint4 av = sl[ra * 8 + (c ^ ((ra >> 1) & 7))];
+  #pragma unroll
+              for (int g = 0; g < kShrinkRows / 16; ++g) {
+                if (g >= G) break;
+                const int rx = RA + g * 16 + (lane & 15);
+                acc[g] = mfma16(av, sl[rx * 8 + (c ^ ((rx >> 1) & 7))], acc[g]);
+              }
+            }
+          }
+        }
+      }
+      if (wave * 16 < RA) {
+  #pragma unroll
+        for (int g = 0; g < kShrinkRows / 16; ++g) {
+          const int i = g * 16 + (lane & 15);
+          if (g >= G || i >= nrows || rows[i] < 0) continue;
+          // D column = lane%16 (the row), D rows = ranks 4*(lane/16) .. +3 of the wave's block
+          const int rk = rg * 64 + wave * 16 + (lane >> 4) * 4;
+          float *dst = tout + (size_t)rows[i] * R + rk;
+          const f32x4 v = acc[g];
+          if (KS == 1) {
+            *(f32x4 *)dst = v;
+            if (a.tt) {
+              const float vv[4] = {v[0], v[1], v[2], v[3]};
+              store_tt(a.tt, R, rows[i], rk, sig, vv, 4);
+            }
+          } else {  // 16-byte device-coherent store into this chunk's partial
+            st16_coherent(prs, (uint32_t)((dst - a.t) * 4), 0, v);
+          }
         }
       }
     }
@@ -538,9 +640,10 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
   __syncthreads();
   if (!info[2]) return;
   // the last of the unit's workgroups: t = sum of the k-chunk partials in
-  // chunk order; a thread's pieces (kSumIt at a time) have every chunk's
-  // 16-byte load in flight together before any is summed
-  constexpr int kSumIt = 2;
+  // chunk order; a thread's pieces (kSumIt at a time: with REG all of a
+  // 64-row unit's at rank 64, within the registers that path has anyway)
+  // have every chunk's 16-byte load in flight together before any is summed
+  constexpr int kSumIt = REG ? 4 : 2;
   for (int e0 = tid * 4; e0 < nrows * R; e0 += 256 * 4 * kSumIt) {
     f32x4 v[kSumIt][kMaxShrinkSplits];
     size_t off[kSumIt];
@@ -591,12 +694,17 @@ __global__ __launch_bounds__(256) void route_kernel(PrepArgs a) {
   route_all<1>(a, a.routes, sl ? seg : nullptr, (int)blockIdx.x * 256, a.ranks != nullptr);
 }
 
+// The plan is workgroup 0, or with plan_last the last one: with two units
+// per CU a batch whose units fill every slot then keeps them all in the
+// first round, and the plan starts as the first units finish.
+template <bool REG>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   extern __shared__ int lds[];
-  if (a.do_plan && blockIdx.x == 0)
+  const int pb = a.plan_last ? (int)gridDim.x - 1 : 0;
+  if (a.do_plan && (int)blockIdx.x == pb)
     plan_block(a, lds);
   else
-    shrink_unit(a, (int)blockIdx.x - a.do_plan, lds);
+    shrink_unit<REG>(a, (int)blockIdx.x - (a.do_plan && !a.plan_last ? 1 : 0), lds);
   if (a.ranks == nullptr) return;
   // every workgroup has read the pair counts once all have arrived: the last
   // one zeroes them (and the arrival count) for the next call
@@ -614,7 +722,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
 __global__ __launch_bounds__(256) void shrink_levels_kernel(ShrinkLevels s) {
   extern __shared__ int lds[];
   const int l = (int)blockIdx.x / s.blocks_per_level;
-  shrink_unit(s.lv[l], (int)blockIdx.x - l * s.blocks_per_level, lds);
+  shrink_unit<false>(s.lv[l], (int)blockIdx.x - l * s.blocks_per_level, lds);
 }
 
 size_t prep_lds_bytes(const PrepArgs &a) {
@@ -622,7 +730,7 @@ size_t prep_lds_bytes(const PrepArgs &a) {
   const int NG = a.rt.n_experts;
   const int NK = NG * (ml + 1);
   size_t plan = a.do_plan ? (size_t)(2 * NK + NG + 8 + a.n) * 4 : 0;
-  size_t shr = a.n_units ? (size_t)((a.n_pairs + 8 + kShrinkRows + 3) & ~3) * 4 + (size_t)kShrinkStages * 128 * 128 +
+  size_t shr = a.n_units ? (size_t)((a.n_pairs + 8 + kShrinkRows + 3) & ~3) * 4 + (size_t)kShrinkLdsBytes +
                                (a.ranks ? 0 : (size_t)a.n * 4)
                          : 0;
   return plan > shr ? plan : shr;
@@ -643,7 +751,10 @@ hipError_t launch_prep(const PrepArgs &a, hipStream_t st) {
   const int grid = a.do_plan + a.n_units * a.k_splits;
   if (grid == 0) return hipSuccess;
   if (a.routes) hipLaunchKernelGGL(route_kernel, dim3((a.n + 255) / 256), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(prep_kernel, dim3(grid), dim3(256), prep_lds_bytes(a), st, a);
+  if (a.reg_units)
+    hipLaunchKernelGGL(prep_kernel<true>, dim3(grid), dim3(256), prep_lds_bytes(a), st, a);
+  else
+    hipLaunchKernelGGL(prep_kernel<false>, dim3(grid), dim3(256), prep_lds_bytes(a), st, a);
   return hipGetLastError();
 }
 

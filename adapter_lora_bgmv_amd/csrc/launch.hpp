@@ -32,7 +32,9 @@ struct PrepArgs {
   unsigned *counters;  // [n_units] arrival counters (k_splits > 1), zero between calls
   int k_splits;    // k chunks per shrink unit
   int n_pairs;    // table entries = max_loras * n_experts
-  int do_plan;    // block 0 writes the plan
+  int do_plan;    // a workgroup writes the plan: the first, or with plan_last the last
+  int plan_last;
+  int reg_units;  // the shrink units load their operands into registers (k_prep.hip)
   PlanDev plan;
   int tile_rows;  // main kernel rows per tile
   int n_units;    // shrink units (grid = do_plan + n_units * k_splits)
@@ -134,9 +136,17 @@ constexpr int kDecodeSmallTileMaxOut = 2048;
 // each); the host also keeps them to half the device's compute units.
 constexpr int kDecodeMaxCarrierWgs = 128;
 
-// Rows per shrink unit; its 64-column stages in LDS at a time (16 KB each).
+// Rows per shrink unit; its 64-column stages in LDS at a time (16 KB each);
+// with register loads, the 32-column steps whose loads a wave has in flight
+// together, and the LDS where its four waves' sums meet (12 blocks (wave,
+// rank block) of another wave's rank block x 4 row groups x 64 lanes x 16
+// bytes); the LDS either way.
 constexpr int kShrinkRows = 64;
 constexpr int kShrinkStages = 3;
+constexpr int kShrinkSteps = 4;
+constexpr int kShrinkRedBytes = 12 * (kShrinkRows / 16) * 64 * 16;
+constexpr int kShrinkLdsBytes =
+    kShrinkStages * 128 * 128 > kShrinkRedBytes ? kShrinkStages * 128 * 128 : kShrinkRedBytes;
 // Largest k split of the shrink units.
 constexpr int kMaxShrinkSplits = 8;
 // Largest key space the one-workgroup plan handles (LDS histogram).
