@@ -198,7 +198,12 @@ __device__ __forceinline__ void route_all(const PrepArgs &a, int *pk, const int 
         if (q >= 0 && lane == lead) got = atomicAdd(&a.pair_cnt[q], (unsigned)cnt);
         const int base = __shfl((int)got, lead, 64);
         const int r = r0 + 256 * j;
-        if (r < a.n) a.ranks[r] = q >= 0 ? base + off : -1;
+        if (r < a.n) {
+          a.ranks[r] = q >= 0 ? base + off : -1;
+          // the pair's first kShrinkRows rows, by rank, in its bucket
+          if (a.bucket != nullptr && q >= 0 && q < a.bucket_pairs && base + off < kShrinkRows)
+            a.bucket[q * kShrinkRows + base + off] = r;
+        }
       }
     }
   }
@@ -381,6 +386,16 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
     if (direct) {
       if (tid < want) rows[tid] = r_lo + first + tid;
       if (tid == 0) info[3] = total;
+    } else if (a.bucket != nullptr && pstar < a.bucket_pairs && first == 0 && total <= kShrinkRows) {
+      // every row of the pair is in its bucket (the route kernel's, by
+      // rank); an entry outside the batch (a stale workspace) reads row 0
+      // and stores nothing
+      if (tid < want) {
+        const int r = a.bucket[pstar * kShrinkRows + tid];
+        rows[tid] = r >= 0 && r < a.n ? r : -1;
+      }
+      if (tid == 0) info[3] = total;
+      direct = true;
     }
     for (int pass = 0; pass < 2 && !direct; ++pass) {
       __syncthreads();  // every thread has read the last pass's count

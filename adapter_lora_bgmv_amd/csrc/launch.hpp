@@ -46,6 +46,11 @@ struct PrepArgs {
   int *ranks;              // [n] the row's rank within its pair, or -1
   unsigned *pair_cnt;      // [n_pairs] rows per pair, zero between calls
   unsigned *prep_done;     // [1] prep workgroups finished, zero between calls
+  // With ranks: pair q's rows of rank below kShrinkRows at
+  // bucket[q kShrinkRows + rank], for q < bucket_pairs (or null), so that a
+  // unit of a pair with at most kShrinkRows rows takes them without a scan.
+  int *bucket;
+  int bucket_pairs;
 };
 
 struct GemmArgs {
