@@ -115,16 +115,19 @@ __device__ __forceinline__ void block_barrier() {
 }
 
 // The route-resolve rule of every entry point: slot in range, both table
-// entries non-NULL, scale non-zero.  Returns the table index or kSkip.
+// entries non-NULL, scale non-zero.  Returns the table index or kSkip.  The
+// three entries of an in-range slot are read together, one round trip, and
+// the rule applied to what they hold.
 __device__ __forceinline__ int resolve_slot(int slot, int expert, int max_loras, int n_experts,
                                             const void *const *a_table,
                                             const void *const *b_table,
                                             const float *scale_table) {
   if (slot < 0 || slot >= max_loras) return kSkip;
-  int idx = slot * n_experts + expert;
-  if (a_table[idx] == nullptr || b_table[idx] == nullptr) return kSkip;
-  if (scale_table[slot] == 0.0f) return kSkip;
-  return idx;
+  const int idx = slot * n_experts + expert;
+  const void *ae = a_table[idx], *be = b_table[idx];
+  const float sc = scale_table[slot];
+  __builtin_amdgcn_sched_barrier(0);  // all three loads out before the first compare
+  return (ae == nullptr) | (be == nullptr) | (sc == 0.0f) ? kSkip : idx;
 }
 
 // Routing inputs of one call, in the form the caller handed them over.
@@ -149,6 +152,20 @@ struct RouteDev {
   int n_experts;
   int R;  // max_rank
 };
+
+// resolve_slot on a one-expert table (index = slot), handing back the
+// entries it read: A, B and the scale of a resolved slot.
+__device__ __forceinline__ int resolve_slot_entries(int slot, const RouteDev &rd, const void *&ae, const void *&be,
+                                                    float &sc) {
+  ae = be = nullptr;
+  sc = 0.f;
+  if (slot < 0 || slot >= rd.max_loras) return kSkip;
+  ae = rd.a_table[slot];
+  be = rd.b_table[slot];
+  sc = rd.scale_table[slot];
+  __builtin_amdgcn_sched_barrier(0);  // all three loads out before the first compare
+  return (ae == nullptr) | (be == nullptr) | (sc == 0.0f) ? kSkip : slot;
+}
 
 // Segment of row r (binary search over seg_indptr), or -1.
 __device__ __forceinline__ int segment_of(const int32_t *indptr, int n_seg, int r) {
