@@ -149,6 +149,9 @@ Cfg choose_cfg(int op, int n, int n_out, int k_in, int groups, int R, int n_pair
     const int per = n / std::max(1, groups);
     const bool lds_rank = R == 0 || (R <= 64 && 64 % R == 0);
     c.to = 256; c.tr = per >= 160 && lds_rank ? 256 : (per >= 96 ? 128 : 64); c.splits = 1;
+    // 64-row tiles 512 outputs wide when one row tile per expert makes one
+    // round of workgroups on the device (256 wide would take two)
+    if (c.tr == 64 && lds_rank && n_out >= 512 && groups * ((n_out + 511) / 512) <= current_cus()) c.to = 512;
   } else if (n <= 64) {
     c.to = 64; c.tr = 64; c.splits = clampi(k_in / 1024, 1, 8);
   } else if (n <= 128) {

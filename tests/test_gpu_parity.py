@@ -125,6 +125,19 @@ def test_moe_small(orc, seed, dtype, E, top_k, n_tok, R):
     check(dw.y_host(), ref, dtype, wl.name)
 
 
+def test_moe_wide_tiles(orc):
+    """The gather on 512-output tiles (64-row tiles, one row tile per expert
+    making one round of workgroups): 600 outputs, so the second column tile
+    is ragged, and about 30 rows per expert."""
+    wl = WL.random_small(26, dtype="bf16", k=136, n_out=600, n=90, n_slots=3, max_rank=16,
+                         kind="moe", n_experts=6, top_k=2)
+    dw = DeviceWorkload(wl)
+    dw.run()
+    torch.cuda.synchronize()
+    ref = orc.run(wl, scale_table=dw.scale_table_host)
+    check(dw.y_host(), ref, "bf16", wl.name)
+
+
 def test_moe_invalid_expert_rows_not_written(orc):
     wl = WL.random_small(23, dtype="bf16", k=64, n_out=32, n=10, n_slots=2, max_rank=16,
                          kind="moe", n_experts=3, top_k=2)
