@@ -323,9 +323,17 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
   uint4 *stg = (uint4 *)(lds + ((P + 8 + kShrinkRows + 3) & ~3));
   int *pk = (int *)(stg + kShrinkLdsBytes / 16);  // [n] the rows' packed routes (standalone shrink)
 
+  // the pairs' row counts, read once, wait in the staging space until the
+  // unit's own count has been taken from them
+  int *raw = (int *)stg;
+  static_assert(kMaxKeys * 4 <= kShrinkLdsBytes, "every pair's count fits the staging space");
   const bool ranked = a.ranks != nullptr;  // the route kernel counted and ranked the rows
   if (ranked) {
-    for (int p = tid; p < P; p += 256) cnt[p] = ((int)a.pair_cnt[p] + kShrinkRows - 1) / kShrinkRows;
+    for (int p = tid; p < P; p += 256) {
+      const int c = (int)a.pair_cnt[p];
+      raw[p] = c;
+      cnt[p] = (c + kShrinkRows - 1) / kShrinkRows;
+    }
   } else {  // the standalone shrink: route and count here
     for (int p = tid; p < P; p += 256) cnt[p] = 0;
     for (int r0 = 0; r0 < a.n; r0 += 256 * 8) route_all(a, pk, nullptr, r0);
@@ -355,9 +363,12 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
   __syncthreads();
   const int pstar = info[0];
   const int first = info[1] * kShrinkRows;
+  // the pair's table entry and scale go out now, beside the row lookups
+  const u16 *A = (const u16 *)a.rd.a_table[pstar];
+  const float sig = a.rd.scale_table[pstar / a.rd.n_experts];
 
   if (ranked) {  // the rows of pstar whose rank falls in [first, first + kShrinkRows)
-    const int total = (int)a.pair_cnt[pstar];
+    const int total = raw[pstar];
     const int want = min(kShrinkRows, total - first);
     // a grouped call's pair lives in its expert's row range, a segmented
     // call's usually in the first segment bound to its adapter: scan only
@@ -370,13 +381,18 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
       r_lo = min(max(a.rt.expert_offsets[e], 0), a.n);
       r_hi = min(max(a.rt.expert_offsets[e + 1], r_lo), a.n);
     } else if (a.rt.mode == kModeSegmented && a.rt.n_seg <= kSegScan) {
-      // pairs of a segmented call are pool slots (one W group)
-      for (int g = 0; g < a.rt.n_seg; ++g)
-        if (a.rt.seg_slot[g] == pstar) {
-          r_lo = min(max(a.rt.seg_indptr[g], 0), a.n);
-          r_hi = min(max(a.rt.seg_indptr[g + 1], r_lo), a.n);
-          break;
-        }
+      // pairs of a segmented call are pool slots (one W group); the first
+      // segment bound to pstar: lane g of every wave reads segment g's slot
+      // and bounds, all in one round trip
+      const bool in = lane < a.rt.n_seg;
+      const int gs = in ? a.rt.seg_slot[lane] : -1;
+      const int glo = in ? a.rt.seg_indptr[lane] : 0, ghi = in ? a.rt.seg_indptr[lane + 1] : 0;
+      const uint64_t hit = __ballot(gs == pstar);
+      if (hit) {  // uniform
+        const int g = __ffsll((unsigned long long)hit) - 1;
+        r_lo = min(max(__builtin_amdgcn_readlane(glo, g), 0), a.n);
+        r_hi = min(max(__builtin_amdgcn_readlane(ghi, g), r_lo), a.n);
+      }
       // every row of a segment routes alike, so when the pair's row count is
       // the segment's, its rows are that segment's: this unit takes the
       // positions [first, first + want) of the segment (a partition of the
@@ -461,12 +477,10 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
   __syncthreads();
   const int nrows = max(0, min(kShrinkRows, info[3] - first));
 
-  const u16 *A = (const u16 *)a.rd.a_table[pstar];
   // a stale count may name a pair that has no table entry: nothing to shrink
   // (uniform over the workgroup)
   if (A == nullptr || nrows == 0) return;
   const int R = a.rd.R, K = a.k_in;
-  const float sig = a.rd.scale_table[pstar / a.rd.n_experts];
   const int G = (nrows + 15) / 16;  // row groups of 16 (<= kShrinkRows / 16)
   // this unit's k chunk, in 64-wide stages
   const int chunk = ((K + KS - 1) / KS + 127) / 128 * 128;
