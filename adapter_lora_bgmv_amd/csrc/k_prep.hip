@@ -222,7 +222,66 @@ __device__ __forceinline__ void count_rows(const int *pk, int n, int *cnt, F f) 
   }
 }
 
+// The plan of a segmented call over at most 64 segments whose bounds never
+// decrease: every row of a segment routes alike (its slot is the segment's),
+// so the rows sorted by key are the segments sorted by key (stably, by
+// segment index), each segment's rows in row order.  Segment g owns the rows
+// [indptr[g], indptr[g + 1]) clamped to the batch, which are the rows
+// segment_of assigns it when the bounds never decrease.  No per-row counting:
+// one round trip for the bounds and slots, then every row placed directly.
+// Returns false (uniform) where the call does not have that form.
+__device__ __forceinline__ bool plan_segments(const PrepArgs &a, int *lds) {
+  const Routing &rt = a.rt;
+  if (rt.mode != kModeSegmented || rt.n_seg > 64 || rt.n_experts != 1) return false;
+  const int tid = threadIdx.x, lane = tid & 63, ns = rt.n_seg;
+  int *s_off = lds, *s_lo = lds + 64, *s_len = lds + 128, *s_q = lds + 192, *s_ok = lds + 256;
+  if (tid < 64) {
+    const bool in = lane < ns;
+    const int ilo = in ? rt.seg_indptr[lane] : 0, ihi = in ? rt.seg_indptr[lane + 1] : 0;
+    const int slot = in ? rt.seg_slot[lane] : -1;
+    const int ml = a.has_lora ? a.rd.max_loras : 0;
+    const int q = in && a.has_lora ? resolve_slot(slot, 0, ml, a.rd.n_experts, a.rd.a_table, a.rd.b_table, a.rd.scale_table)
+                                   : kSkip;
+    const int key = q >= 0 ? slot : ml;
+    const int lo = min(max(ilo, 0), a.n), hi = min(max(ihi, 0), a.n);
+    const int len = in ? max(hi - lo, 0) : 0;
+    int off = 0;
+    for (int g = 0; g < ns; ++g) {  // uniform: the segments before this one in (key, index) order
+      const int kg = __builtin_amdgcn_readlane(key, g), lg = __builtin_amdgcn_readlane(len, g);
+      if (kg < key || (kg == key && g < lane)) off += lg;
+    }
+    if (in) {
+      s_off[lane] = off;
+      s_lo[lane] = lo;
+      s_len[lane] = len;
+      s_q[lane] = q;
+    }
+    const uint64_t bad = __ballot(in && ilo > ihi);
+    if (lane == 0) s_ok[0] = bad == 0ull;
+  }
+  __syncthreads();
+  if (!s_ok[0]) {  // uniform: the general plan, which may reuse this LDS
+    __syncthreads();
+    return false;
+  }
+  int total = 0;
+  for (int g = 0; g < ns; ++g) {  // uniform
+    const int off = s_off[g], lo = s_lo[g], len = s_len[g], q = s_q[g];
+    for (int i = tid; i < len; i += 256) {
+      a.plan.pos_row[off + i] = lo + i;
+      a.plan.pos_pair[off + i] = q;
+    }
+    total += len;
+  }
+  const int ntiles = (total + a.tile_rows - 1) / a.tile_rows;
+  for (int t = tid; t < ntiles; t += 256)
+    a.plan.tiles[t] = make_int4(0, t * a.tile_rows, min(a.tile_rows, total - t * a.tile_rows), 0);
+  if (tid == 0) *a.plan.n_tiles = ntiles;
+  return true;
+}
+
 __device__ __forceinline__ void plan_block(const PrepArgs &a, int *lds) {
+  if (plan_segments(a, lds)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ml = a.has_lora ? a.rd.max_loras : 0;
   const int NG = a.rt.n_experts;
@@ -723,17 +782,18 @@ __global__ __launch_bounds__(256) void route_kernel(PrepArgs a) {
   route_all<1>(a, a.routes, sl ? seg : nullptr, (int)blockIdx.x * 256, a.ranks != nullptr);
 }
 
-// The plan is workgroup 0, or with plan_last the last one: with two units
-// per CU a batch whose units fill every slot then keeps them all in the
-// first round, and the plan starts as the first units finish.
+// The plan is workgroup plan_at: the first, or after the units that fill
+// the device's first round (with two units per CU those then all run in the
+// first round, and the plan takes the first slot a unit frees, ahead of any
+// unit slots past the batch's actual units).
 template <bool REG>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   extern __shared__ int lds[];
-  const int pb = a.plan_last ? (int)gridDim.x - 1 : 0;
+  const int pb = a.plan_at;
   if (a.do_plan && (int)blockIdx.x == pb)
     plan_block(a, lds);
   else
-    shrink_unit<REG>(a, (int)blockIdx.x - (a.do_plan && !a.plan_last ? 1 : 0), lds);
+    shrink_unit<REG>(a, (int)blockIdx.x - (a.do_plan && (int)blockIdx.x > pb ? 1 : 0), lds);
   if (a.ranks == nullptr) return;
   // every workgroup has read the pair counts once all have arrived: the last
   // one zeroes them (and the arrival count) for the next call
@@ -758,7 +818,8 @@ size_t prep_lds_bytes(const PrepArgs &a) {
   const int ml = a.has_lora ? a.rd.max_loras : 0;
   const int NG = a.rt.n_experts;
   const int NK = NG * (ml + 1);
-  size_t plan = a.do_plan ? (size_t)(2 * NK + NG + 8 + a.n) * 4 : 0;
+  // (the segmented plan's five 64-entry arrays fit beside any n)
+  size_t plan = a.do_plan ? (size_t)(2 * NK + NG + 8 + std::max(a.n, 5 * 64)) * 4 : 0;
   size_t shr = a.n_units ? (size_t)((a.n_pairs + 8 + kShrinkRows + 3) & ~3) * 4 + (size_t)kShrinkLdsBytes +
                                (a.ranks ? 0 : (size_t)a.n * 4)
                          : 0;

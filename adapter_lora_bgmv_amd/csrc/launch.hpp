@@ -32,8 +32,8 @@ struct PrepArgs {
   unsigned *counters;  // [n_units] arrival counters (k_splits > 1), zero between calls
   int k_splits;    // k chunks per shrink unit
   int n_pairs;    // table entries = max_loras * n_experts
-  int do_plan;    // a workgroup writes the plan: the first, or with plan_last the last
-  int plan_last;
+  int do_plan;    // a workgroup writes the plan: workgroup plan_at of the grid
+  int plan_at;
   int reg_units;  // the shrink units load their operands into registers (k_prep.hip)
   PlanDev plan;
   int tile_rows;  // main kernel rows per tile

@@ -595,7 +595,8 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
   pa.k_splits = c.t_splits;
   pa.n_pairs = n_pairs;
   pa.do_plan = 1;
-  // The shrink units' register loads and the plan as the last workgroup
+  // The shrink units' register loads and the plan behind the units (the last
+  // workgroup when they all fit one round)
   // (measured against the LDS-DMA units and the plan first, steps: segmented
   // prefill 186.5 -> 174.4 us, fused gate/up ~109 -> 105.3 us) suit every
   // call but the MoE ones, whose many small units run better three to a CU
@@ -603,10 +604,12 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
   // against 199.5 us).
   const bool moe_op = op == LORA_OP_MOE_GATHER || op == LORA_OP_MOE_GROUPED;
   pa.reg_units = moe_op ? 0 : 1;
-  pa.plan_last = moe_op ? 0 : 1;
   pa.plan = plan;
   pa.tile_rows = c.tr;
   pa.n_units = c.units;
+  // the plan right after the units of the first round (two per CU), before
+  // the unit slots the batch may not need
+  pa.plan_at = moe_op ? 0 : std::min(pa.n_units * pa.k_splits, 2 * current_cus());
   prof_record(0, st);
   if (int e = launch_status(launch_prep(pa, st), what)) return e;
   prof_record(1, st);

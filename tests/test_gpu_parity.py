@@ -108,6 +108,26 @@ def test_segmented_small(orc, seed, dtype, lens):
     check(dw.y_host(), ref, dtype, wl.name)
 
 
+def test_segmented_rows_outside_and_unsorted_slots(orc):
+    """Segments that start after row 0 and end before the last row (the rows
+    outside every segment are not written), an empty segment, one slot on two
+    segments, slots out of order and a skipping slot: the plan sorts whole
+    segments by slot and the result is the oracle's, row by row."""
+    wl = WL.random_small(14, dtype="bf16", k=136, n_out=96, n_slots=4, max_rank=16,
+                         kind="segmented", seg_lens=[40, 0, 70, 30, 55, 20])
+    wl.seg_indptr = np.array([10, 50, 50, 120, 150, 185, 200], np.int32)
+    wl.seg_slot = np.array([2, 0, 3, 2, -1, 1], np.int32)
+    dw = DeviceWorkload(wl)
+    dw.y.fill_(float("nan"))
+    dw.run()
+    torch.cuda.synchronize()
+    got = dw.y_host()
+    ref = orc.run(wl, scale_table=dw.scale_table_host)
+    out = np.isnan(ref[:, 0])
+    assert out.sum() == 10 + 15 and np.all(np.isnan(got[out]))
+    check(got[~out], ref[~out], "bf16", wl.name)
+
+
 @pytest.mark.parametrize("seed,dtype,E,top_k,n_tok,R", [
     (20, "bf16", 5, 2, 37, 16),
     (21, "bf16", 9, 3, 70, 16),
