@@ -648,9 +648,9 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
   } else {
     // 64 ranks at a time.  A stage is 64 k columns of the group's rank rows of
     // A, then of the unit's x rows (gathered, 16 G of them), in whole 128-byte
-    // lines by LDS-DMA (chunk c of row r at slot c ^ ((r >> 1) & 7)); up to
-    // kShrinkStages stages go out together, then wave w takes rank block w
-    // through them, every row group, in k order.
+    // lines by LDS-DMA (chunk c of row r at slot c ^ ((r >> 1) & 7)); a batch
+    // of stages (as many as the staging space holds) goes out together, then
+    // wave w takes rank block w through them, every row group, in k order.
     for (int rg = 0; rg * 64 < R; ++rg) {
       const int RA = min(64, R - rg * 64);  // rank rows of the group
       const int RU = RA + 16 * G;           // rows of a stage
@@ -658,8 +658,11 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
       f32x4 acc[kShrinkRows / 16];
   #pragma unroll
       for (int g = 0; g < kShrinkRows / 16; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int sb = 0; sb < nst; sb += kShrinkStages) {
-        const int nsn = min(kShrinkStages, nst - sb), kb0 = kc0 + sb * 64;
+      // as many stages to a batch as the staging space holds (at least
+      // kShrinkStages): a unit of few rows and ranks takes its chunk in one
+      const int SB = max(kShrinkStages, kShrinkLdsBytes / (RU * 128));
+      for (int sb = 0; sb < nst; sb += SB) {
+        const int nsn = min(SB, nst - sb), kb0 = kc0 + sb * 64;
         __syncthreads();  // the previous batch is read
         for (int ii = wave; ii < nsn * per; ii += 4) {
           const int st = ii / per, k8 = ii % per;
