@@ -387,12 +387,45 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
   int *raw = (int *)stg;
   static_assert(kMaxKeys * 4 <= kShrinkLdsBytes, "every pair's count fits the staging space");
   const bool ranked = a.ranks != nullptr;  // the route kernel counted and ranked the rows
+  // A segmented call over at most 64 segments whose bounds never decrease,
+  // without the route kernel: a pair's rows are its segments' rows in
+  // segment order, so the counts and each unit's rows follow from the
+  // segments alone (segment g: rows [lo, hi) clamped to the batch, the rows
+  // segment_of assigns it when the bounds never decrease).
+  int *s_lo = raw + kMaxKeys, *s_len = s_lo + 64, *s_q = s_len + 64, *s_ok = s_q + 64;
+  static_assert((kMaxKeys + 3 * 64 + 1) * 4 <= kShrinkLdsBytes, "the segment table fits beside the counts");
+  bool seg_ok = false;
+  if (!ranked && a.seg_units) {
+    for (int p = tid; p < P; p += 256) raw[p] = 0;
+    __syncthreads();
+    if (tid < 64) {
+      const Routing &rt = a.rt;
+      const bool in = lane < rt.n_seg;
+      const int ilo = in ? rt.seg_indptr[lane] : 0, ihi = in ? rt.seg_indptr[lane + 1] : 0;
+      const int slot = in ? rt.seg_slot[lane] : -1;
+      const int q = in && a.has_lora ? resolve_slot(slot, 0, a.rd.max_loras, a.rd.n_experts, a.rd.a_table,
+                                                    a.rd.b_table, a.rd.scale_table)
+                                     : kSkip;
+      const int lo = min(max(ilo, 0), a.n), hi = min(max(ihi, 0), a.n);
+      const int len = in ? max(hi - lo, 0) : 0;
+      s_lo[lane] = lo;
+      s_len[lane] = len;
+      s_q[lane] = q;
+      const uint64_t bad = __ballot(in && ilo > ihi);
+      if (lane == 0) s_ok[0] = bad == 0ull;
+      if (bad == 0ull && q >= 0 && len > 0) atomicAdd(&raw[q], len);
+    }
+    __syncthreads();
+    seg_ok = s_ok[0] != 0;  // uniform
+  }
   if (ranked) {
     for (int p = tid; p < P; p += 256) {
       const int c = (int)a.pair_cnt[p];
       raw[p] = c;
       cnt[p] = (c + kShrinkRows - 1) / kShrinkRows;
     }
+  } else if (seg_ok) {
+    for (int p = tid; p < P; p += 256) cnt[p] = (raw[p] + kShrinkRows - 1) / kShrinkRows;
   } else {  // the standalone shrink: route and count here
     for (int p = tid; p < P; p += 256) cnt[p] = 0;
     for (int r0 = 0; r0 < a.n; r0 += 256 * 8) route_all(a, pk, nullptr, r0);
@@ -499,6 +532,25 @@ __device__ __forceinline__ void shrink_unit(const PrepArgs &a, int u, int *lds) 
       r_hi = a.n;
     }
     if (tid == 0 && !direct) info[3] = total;
+  } else if (seg_ok) {
+    // segment g holds the pair's positions [pre, pre + len) (an exclusive
+    // scan over the pair's segments in order); this unit takes [first,
+    // first + kShrinkRows)
+    if (tid < 64) {
+      const int len = s_len[lane], lo = s_lo[lane];
+      const int v = s_q[lane] == pstar && len > 0 ? len : 0;
+      int pre = v;
+  #pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(pre, off, 64);
+        if (lane >= off) pre += t;
+      }
+      const int total = __shfl(pre, 63, 64);
+      pre -= v;
+      const int b0 = max(first, pre), b1 = min(first + kShrinkRows, pre + v);
+      for (int pos = b0; pos < b1; ++pos) rows[pos - first] = lo + (pos - pre);
+      if (lane == 0) info[3] = total;
+    }
   } else {
     // rows of pstar in row order, ranks [first, first + kShrinkRows): thread t
     // counts them in its 16-row span, an exclusive scan gives its first rank

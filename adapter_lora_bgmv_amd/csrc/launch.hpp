@@ -34,6 +34,7 @@ struct PrepArgs {
   int n_pairs;    // table entries = max_loras * n_experts
   int do_plan;    // a workgroup writes the plan: workgroup plan_at of the grid
   int plan_at;
+  int seg_units;  // segmented, no route kernel: units take their rows from the segments
   int reg_units;  // the shrink units load their operands into registers (k_prep.hip)
   PlanDev plan;
   int tile_rows;  // main kernel rows per tile

@@ -577,8 +577,14 @@ int run_fused(const char *what, int op, const Routing &rt, const RouteDev &rd, b
   pa.t = (float *)(ws + L.t);
   pa.t_final = (float *)(ws + L.t_final);
   pa.tt = R > 0 ? (u16 *)(ws + L.tt) : nullptr;
-  pa.routes = (int *)(ws + L.routes);
-  if (R > 0) {
+  // a segmented call over at most 64 segments needs no per-row routes: the
+  // plan and the shrink units work from the segments (up to 4096 rows, where
+  // a unit's fallback for bounds that decrease, which routes every row into
+  // LDS, still leaves two units per CU)
+  const bool seg_direct = rt.mode == kModeSegmented && rt.n_seg <= 64 && n <= 4096;
+  pa.seg_units = seg_direct ? 1 : 0;
+  pa.routes = seg_direct ? nullptr : (int *)(ws + L.routes);
+  if (R > 0 && !seg_direct) {
     pa.ranks = (int *)(ws + L.ranks);
     // the pairs' row buckets spare a unit its scan of the whole batch:
     // worth it on large batches routed by row (measured: the MoE gather's

@@ -95,6 +95,7 @@ def test_decode_small(orc, case):
     (10, "bf16", [5, 0, 17, 64, 3, 100]),
     (11, "bf16", [512, 300, 1, 0]),
     (13, "bf16", [60, 0, 90, 50]),       # 200 rows: 256 x 128 tiles
+    (15, "bf16", [2000, 100, 2100]),     # over 4096 rows: the route kernel ranks the rows
     (12, "f32", [4, 0, 9, 2]),
 ])
 def test_segmented_small(orc, seed, dtype, lens):
