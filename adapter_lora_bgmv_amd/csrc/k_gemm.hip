@@ -5,15 +5,16 @@
 // contraction over k_in runs on v_mfma_f32_16x16x32_bf16 with W as the A
 // operand and the gathered x rows as the B operand.
 //
-// Staging: a CU takes in far more bytes per second through the LDS-DMA path
-// (global_load_lds_dwordx4) than through loads into registers, so both
-// operands go to LDS that way.  Each DMA instruction moves exactly one MFMA
-// operand fragment -- 16 rows x 32 k, 1 KB, lane l holding row l%16, k
-// 8*(l/16)..+7 -- into a contiguous 1 KB LDS block, so the MFMA's operand read
-// is a linear, conflict-free ds_read_b128.  A stage is one 32-wide k step (one
-// fragment per 16-row block); NS stages form a ring with NS-1 stages in
-// flight.  The waits are explicit (s_waitcnt vmcnt + s_barrier): a stage is
-// consumed only after every wave's DMA for it has landed.
+// Staging: both operands go to LDS by LDS-DMA (global_load_lds_dwordx4),
+// which takes in as much per CU as loads into registers do and holds no
+// registers while in flight.  A stage is 64 k columns of every row of the
+// tile (W rows, then the gathered x rows), row-major at 128 bytes a row,
+// each row's eight 16-byte chunks stored XOR-swizzled by row; one DMA
+// instruction moves eight whole 128-byte row segments (full cache lines),
+// and the MFMA fragments are read from the swizzled slots with ds_read_b128
+// on distinct banks.  NS stages form a ring with NS-1 stages in flight.  The
+// waits are explicit (s_waitcnt vmcnt + s_barrier): a stage is consumed only
+// after every wave's DMA for it has landed.
 //
 // Ragged tiles: rows past the tile's end (x) or past n_out (W) load a valid
 // row instead; they only feed output rows and columns that are never stored.
