@@ -1,17 +1,23 @@
 // k_prep.hip -- route resolve, the row plan, and the grouped MFMA shrink (bf16).
 //
-// One launch does two independent jobs:
-//  * block 0 (when a plan is wanted) resolves every row's route (slot ->
-//    pair or skip, atlas apply_lora_bgmv doc) and groups the rows by
-//    (W group, adapter) with a counting sort in LDS, then cuts each W group
-//    into the main kernel's row tiles.  Within a key the order is whatever
-//    the LDS atomics give: no output value depends on it, because every
-//    output element is reduced row-locally with the same instruction sequence.
-//  * every other block is one shrink unit: up to 16 rows that share one
-//    pair, t[rows] = x[rows] . A_pair^T (ferrox LoraDelta::project), on bf16
-//    MFMA with f32 accumulation.  Each block finds its unit by histogramming
-//    the pairs itself, so the shrink does not wait for the plan.  The four
-//    waves split k_in; their partial sums meet in LDS in a fixed order.
+// route_kernel resolves every row's route once (slot -> pair or skip, atlas
+// apply_lora_bgmv doc), counts each pair's rows and ranks every row within
+// its pair; a segmented call of up to 4096 rows over at most 64 segments does
+// without it, since every row of a segment routes alike.  Then one launch of
+// prep_kernel does two independent jobs:
+//  * workgroup plan_at groups the rows by (W group, adapter) -- a counting
+//    sort in LDS, or for a segmented call whole segments sorted by key --
+//    and cuts each W group into the main kernel's row tiles.  Within a key
+//    the order is whatever the LDS atomics give: no output value depends on
+//    it, because every output element is reduced row-locally with the same
+//    instruction sequence.
+//  * every other workgroup is one shrink unit: up to 64 rows that share one
+//    pair over one k chunk, t[rows] = x[rows] . A_pair^T (ferrox
+//    LoraDelta::project), on bf16 MFMA with f32 accumulation.  A unit finds
+//    its pair and rows from the pair counts (the route kernel's, the
+//    segments', or its own histogram), so the shrink does not wait for the
+//    plan; its waves' sums meet in a fixed order, and the k chunks' partials
+//    are summed in chunk order by the pair's last unit to arrive.
 #include "common.hpp"
 #include "launch.hpp"
 
