@@ -16,8 +16,8 @@
 //  * shrink: workgroup (s, r) = rank r of slot s, four waves that split
 //    k_in into 512-column steps; lane l takes columns 8 l of each step of
 //    A's row and of each row of x, so a wave reads whole 1 KiB stretches.
-//    A's row goes out before the slot's rows are known, then x for four
-//    rows at a time.  A lane sums its columns in k order (bf16 pair dot
+//    A's row goes out before the slot's rows are known, then x for eight
+//    rows at a time (four in the levels kernel).  A lane sums its columns in k order (bf16 pair dot
 //    products into f32), the wave adds its 64 sums with a butterfly of lane
 //    shuffles and wave 0 adds the four waves' in order.
 //  * expand+fold: workgroup (c, s) = 512 outputs of slot s; lane l of each
@@ -82,17 +82,18 @@ constexpr int kShrinkWaves = 4;
 // Workgroup (s, r): rank r of slot s.  Wave w takes the 512-column k steps
 // w, w + 4, ...; lane l the 8 columns 8 l of each step.  A lane's sum over
 // its columns (k order), the wave's butterfly, then the four waves in order.
+template <int RC>  // rows of the slot at a time
 __device__ __forceinline__ void shrink_slot_rank(const RouteDev &rd, const int32_t *seq_slot, int n, const u16 *x,
                                                  int x_stride, int k_in, float *t, int s, int r) {
   __shared__ int rows[kBgmvMaxRows];
   __shared__ int s_cnt;
-  __shared__ float part[kShrinkWaves][4];
+  __shared__ float part[kShrinkWaves][RC];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int v0 = wave == 0 && lane < n ? seq_slot[lane] : -1;  // in flight with the table reads
   if (!slot_live(rd, s)) return;  // the same for the whole workgroup
   const u16 *Ar = (const u16 *)rd.a_table[s] + (size_t)r * k_in;
   // A's row goes out before the rows are known: this wave's steps, KS at a time
-  constexpr int KS = 4, RC = 4;  // k steps held; rows at a time
+  constexpr int KS = 4;  // k steps held
   const int kstep = 512 * kShrinkWaves;
   uint4 a[KS];
   auto load_a = [&](int kc) {
@@ -113,7 +114,7 @@ __device__ __forceinline__ void shrink_slot_rank(const RouteDev &rd, const int32
     const u16 *xr[RC];
 #pragma unroll
     for (int c = 0; c < RC; ++c) xr[c] = x + (size_t)rows[min(j0 + c, cnt - 1)] * x_stride;
-    float acc[RC] = {0.f, 0.f, 0.f, 0.f};
+    float acc[RC] = {};
     for (int kc = 0; kc < k_in; kc += KS * kstep) {
       if (kc > 0 || j0 > 0) load_a(kc);
       uint4 xv[RC][KS];
@@ -148,7 +149,7 @@ __device__ __forceinline__ void shrink_slot_rank(const RouteDev &rd, const int32
 __global__ __launch_bounds__(64 * kShrinkWaves) void bgmv_shrink_kernel(RouteDev rd, const int32_t *seq_slot, int n,
                                                                          const u16 *x, int x_stride, int k_in,
                                                                          float *t) {
-  shrink_slot_rank(rd, seq_slot, n, x, x_stride, k_in, t, blockIdx.x / rd.R, blockIdx.x % rd.R);
+  shrink_slot_rank<8>(rd, seq_slot, n, x, x_stride, k_in, t, blockIdx.x / rd.R, blockIdx.x % rd.R);
 }
 
 // An adapter stack's further levels: level l takes workgroups
@@ -158,7 +159,8 @@ __global__ __launch_bounds__(64 * kShrinkWaves) void bgmv_shrink_levels_kernel(B
   const int l = blockIdx.x / L.blocks_per_level, b = blockIdx.x % L.blocks_per_level;
   const RouteDev &rd = L.rd[l];
   if (b >= rd.max_loras * rd.R) return;  // the same for the whole workgroup
-  shrink_slot_rank(rd, L.seq_slot[l], n, x, x_stride, k_in, L.t[l], b / rd.R, b % rd.R);
+  // four rows at a time here: eight measured slower on the stack's levels
+  shrink_slot_rank<4>(rd, L.seq_slot[l], n, x, x_stride, k_in, L.t[l], b / rd.R, b % rd.R);
 }
 
 constexpr int kExpandWaves = 4;
