@@ -37,7 +37,16 @@ __device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
 
 __device__ __forceinline__ uint4 z4() { return make_uint4(0u, 0u, 0u, 0u); }
 
-__device__ __forceinline__ uint4 ldg16(const void *p) { return *(const uint4 *)p; }
+// 16 bytes from device memory.  The global address space is explicit (set
+// through an integer: a direct pointer cast is folded back to a generic
+// pointer): a pointer read from a route table would otherwise give a flat
+// load, which may reach LDS, and the compiler then waits for it before every
+// LDS access.
+typedef unsigned int u32x4n __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldg16(const void *p) {
+  const u32x4n v = *(const __attribute__((address_space(1))) u32x4n *)(uintptr_t)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ uint32_t pack2(u16 lo, u16 hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
 
@@ -127,7 +136,7 @@ __device__ __forceinline__ int resolve_slot(int slot, int expert, int max_loras,
   const void *ae = a_table[idx], *be = b_table[idx];
   const float sc = scale_table[slot];
   __builtin_amdgcn_sched_barrier(0);  // all three loads out before the first compare
-  return (ae == nullptr) | (be == nullptr) | (sc == 0.0f) ? kSkip : idx;
+  return ((ae == nullptr) | (be == nullptr) | (sc == 0.0f)) ? kSkip : idx;
 }
 
 // Routing inputs of one call, in the form the caller handed them over.
@@ -164,7 +173,7 @@ __device__ __forceinline__ int resolve_slot_entries(int slot, const RouteDev &rd
   be = rd.b_table[slot];
   sc = rd.scale_table[slot];
   __builtin_amdgcn_sched_barrier(0);  // all three loads out before the first compare
-  return (ae == nullptr) | (be == nullptr) | (sc == 0.0f) ? kSkip : slot;
+  return ((ae == nullptr) | (be == nullptr) | (sc == 0.0f)) ? kSkip : slot;
 }
 
 // Segment of row r (binary search over seg_indptr), or -1.
