@@ -6,7 +6,7 @@
 // Memory-bound: a gathered row of E, one row of B per row, and each touched
 // slot's A, which every row on that slot shares.  A workgroup takes 64 rows
 // and 256 columns (wave w 16 of the rows, 4 columns per lane).  bf16 tables
-// of rank 8 or 16 take embed_rows_bf16_kernel (rows sorted by pair, A in
+// of rank 16 take embed_rows_bf16_kernel (rows sorted by pair, A in
 // registers per run, two ranks per v_dot2); every other call the general
 // kernel: for every 8 ranks the A rows of the workgroup's pairs go to LDS
 // once (bf16: by LDS-DMA, every piece of the pass in flight at once) and all
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(256) void embed_rows_kernel(EmbedArgs a) {
   }
 }
 
-// bf16 tables of rank 8 or 16 (and calls without a route): the workgroup's
+// bf16 tables of rank 16 (and calls without a route): the workgroup's
 // 64 rows are sorted by pair before any work, so a wave meets its 16 rows'
 // pairs in runs.  A lane holds the current run's A for its 4 columns in
 // registers, two ranks packed per register, and takes a row's rank sum two
@@ -415,10 +415,8 @@ hipError_t launch_embed_rows(const EmbedArgs &a, int dtype, hipStream_t st) {
   static_assert(kEmbedSortRows == kEmbedRows, "the two kernels share the grid");
   // the sorted kernel's buffer loads address A by 32-bit offsets
   const bool sorted = dtype != 0 && (size_t)32 * a.n_embd < 0x7ffffff0u;
-  if (sorted && (!a.has_lora || a.rd.R == 16))
+  if (sorted && (!a.has_lora || a.rd.R == 16))  // bf16 pools pad max_rank to a multiple of 16
     hipLaunchKernelGGL(embed_rows_bf16_kernel<16>, grid, dim3(256), 0, st, a);
-  else if (sorted && a.rd.R == 8)
-    hipLaunchKernelGGL(embed_rows_bf16_kernel<8>, grid, dim3(256), 0, st, a);
   else if (dtype == 0)
     hipLaunchKernelGGL(embed_rows_kernel<float>, grid, dim3(256), 0, st, a);
   else

@@ -63,7 +63,7 @@ def _route(orc, wl, dw):
 @pytest.mark.parametrize("seed,k,n,n_slots,R,many", [
     (90, 4096, 64, 16, 16, False),   # the decode batch's shape
     (91, 520, 200, 7, 48, False),    # ragged k, rank 48, rows over 64 in the scan
-    (92, 2048, 100, 3, 128, True),   # many rows per slot: row chunks of four, rank 128
+    (92, 2048, 100, 3, 128, True),   # many rows per slot: row chunks of eight, rank 128
     (93, 8200, 5, 4, 16, False),     # k past one 8192-column pass of the four waves
     (94, 64, 1, 4, 32, False),       # one row
     (95, 1024, 1024, 5, 16, True),   # the most rows the by-slot path takes
