@@ -543,7 +543,7 @@ hipError_t launch_gemm(const GemmArgs &a, int to, int tr, hipStream_t st) {
   else if (to == 128 && tr == 128 && mode == kSplitK) LORA_GEMM(128, 128, 2, 2, 4, kSplitK);
   else if (to == 256 && tr == 64 && mode == kOneTile) LORA_GEMM(256, 64, 4, 1, 3, kOneTile);
   else if (to == 512 && tr == 64 && mode == kOneTile) LORA_GEMM(512, 64, 8, 1, 2, kOneTile);
-  else if (to == 256 && tr == 128 && mode == kOneTile) LORA_GEMM(256, 128, 4, 2, 3, kOneTile);
+  else if (to == 256 && tr == 128 && mode == kOneTile) LORA_GEMM(256, 128, 4, 4, 3, kOneTile);  // 16 waves of 64 x 32
   else if (to == 192 && tr == 128 && mode == kOneTile) LORA_GEMM(192, 128, 4, 2, 3, kOneTile);
   else if (to == 256 && tr == 256 && mode == kOneTile) LORA_GEMM(256, 256, 4, 4, 2, kOneTile);  // 16 waves of 64 x 64
   else
